@@ -1,0 +1,196 @@
+"""CPU oracle for gated grouped-query attention (fp64) -- test infrastructure.
+
+Only the test suite, the smoke check in ``__graft_entry__`` and the CPU-baseline
+leg of ``bench.py`` may import this package.  It wraps ``liboracle.so`` (plain
+C, built by ``oracle/build.py``) with ctypes and numpy; it does not import the
+GPU package and the GPU package does not import it.
+
+All bf16 tensors cross this interface as ``numpy.uint16`` arrays of bit
+patterns.  See ``gqa_oracle.c`` for the definition that is computed and the
+passages of the pages it follows.
+
+Parity status of each function (what pins it is in tests/test_oracle_*.py):
+  bf16_rne, bf16_value, sigmoid_bf16, gate_output : pinned (exact-rational
+      rounding, 40-digit decimal sigmoid over all 65,536 gates, closed forms)
+  decode, prefill : pinned (closed forms, invariants, 50-digit brute force)
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+import numpy as np
+
+from . import compare  # noqa: F401  (tolerance helpers, re-exported)
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(HERE, "liboracle.so")
+
+_lib = None
+
+_u16p = ctypes.POINTER(ctypes.c_uint16)
+_i32p = ctypes.POINTER(ctypes.c_int32)
+_f64p = ctypes.POINTER(ctypes.c_double)
+
+
+def _load():
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(LIB_PATH):
+        from .build import build
+
+        build()
+    lib = ctypes.CDLL(LIB_PATH)
+    lib.oracle_bf16_value.restype = ctypes.c_double
+    lib.oracle_bf16_value.argtypes = [ctypes.c_uint16]
+    lib.oracle_bf16_rne.restype = ctypes.c_uint16
+    lib.oracle_bf16_rne.argtypes = [ctypes.c_double]
+    lib.oracle_bf16_rne_array.restype = None
+    lib.oracle_bf16_rne_array.argtypes = [_f64p, _u16p, ctypes.c_int64]
+    lib.oracle_sigmoid_bf16.restype = ctypes.c_uint16
+    lib.oracle_sigmoid_bf16.argtypes = [ctypes.c_uint16]
+    lib.oracle_sigmoid_table.restype = None
+    lib.oracle_sigmoid_table.argtypes = [_u16p]
+    lib.oracle_gate_output.restype = ctypes.c_uint16
+    lib.oracle_gate_output.argtypes = [ctypes.c_uint16, ctypes.c_uint16]
+    lib.oracle_decode.restype = ctypes.c_int
+    lib.oracle_decode.argtypes = [
+        _u16p, _u16p, _u16p, _u16p, _i32p, _i32p, ctypes.c_double,
+        ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int,
+        ctypes.c_int64, _u16p, _f64p, _f64p, ctypes.c_int,
+    ]
+    lib.oracle_prefill.restype = ctypes.c_int
+    lib.oracle_prefill.argtypes = [
+        _u16p, _u16p, _u16p, _u16p, ctypes.c_double, ctypes.c_int,
+        ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int,
+        _i32p, ctypes.c_int, _u16p, _f64p, _f64p, ctypes.c_int,
+    ]
+    _lib = lib
+    return lib
+
+
+def default_threads() -> int:
+    """Host threads the oracle uses: the process affinity set, at most 16."""
+    try:
+        n = len(os.sched_getaffinity(0))
+    except AttributeError:  # pragma: no cover
+        n = os.cpu_count() or 1
+    return max(1, min(n, 16))
+
+
+def _ptr(a: np.ndarray, ctype):
+    return a.ctypes.data_as(ctypes.POINTER(ctype))
+
+
+def _u16(a) -> np.ndarray:
+    a = np.ascontiguousarray(a)
+    if a.dtype != np.uint16:
+        a = a.view(np.uint16)
+    return a
+
+
+# --------------------------------------------------------------------------
+# Scalar / table routines
+# --------------------------------------------------------------------------
+def bf16_value(bits) -> np.ndarray:
+    """fp64 values of bf16 bit patterns (exact)."""
+    lib = _load()
+    bits = np.asarray(bits, dtype=np.uint16)
+    return np.array([lib.oracle_bf16_value(int(b)) for b in bits.ravel()],
+                    dtype=np.float64).reshape(bits.shape)
+
+
+def bf16_rne(x) -> np.ndarray:
+    """Round fp64 values to bf16 (ties to even), as uint16 bit patterns."""
+    lib = _load()
+    x = np.ascontiguousarray(x, dtype=np.float64)
+    out = np.empty(x.shape, dtype=np.uint16)
+    lib.oracle_bf16_rne_array(_ptr(x, ctypes.c_double), _ptr(out, ctypes.c_uint16), x.size)
+    return out
+
+
+def sigmoid_bf16(gate_bits: int) -> int:
+    return int(_load().oracle_sigmoid_bf16(int(gate_bits)))
+
+
+def sigmoid_table() -> np.ndarray:
+    """The 65,536-entry map gate bits -> bf16 bits of sigmoid(gate)."""
+    t = np.empty(65536, dtype=np.uint16)
+    _load().oracle_sigmoid_table(_ptr(t, ctypes.c_uint16))
+    return t
+
+
+def gate_output(ob_bits: int, sigma_bits: int) -> int:
+    return int(_load().oracle_gate_output(int(ob_bits), int(sigma_bits)))
+
+
+# --------------------------------------------------------------------------
+# Attention
+# --------------------------------------------------------------------------
+class OracleError(RuntimeError):
+    pass
+
+
+def decode(q, gate, k_pool, v_pool, block_table, seq_lens, scale, nthreads=None):
+    """Gated GQA decode over a paged pool.
+
+    q, gate: [B, H_q, D] bf16 bits; k_pool, v_pool: [P, page, H_kv, D];
+    block_table: [B, W] int32; seq_lens: [B] int32.
+    Returns (out bits [B,H_q,D], O fp64 [B,H_q,D], Mref fp64 [B,H_q,D]).
+    """
+    lib = _load()
+    q, gate, k_pool, v_pool = (_u16(a) for a in (q, gate, k_pool, v_pool))
+    block_table = np.ascontiguousarray(block_table, dtype=np.int32)
+    seq_lens = np.ascontiguousarray(seq_lens, dtype=np.int32)
+    B, Hq, D = q.shape
+    P, page, Hkv, D2 = k_pool.shape
+    assert D2 == D and v_pool.shape == k_pool.shape and gate.shape == q.shape
+    W = block_table.shape[1] if block_table.ndim == 2 else 0
+    out = np.zeros((B, Hq, D), dtype=np.uint16)
+    o = np.zeros((B, Hq, D), dtype=np.float64)
+    mref = np.zeros((B, Hq, D), dtype=np.float64)
+    st = lib.oracle_decode(
+        _ptr(q, ctypes.c_uint16), _ptr(gate, ctypes.c_uint16),
+        _ptr(k_pool, ctypes.c_uint16), _ptr(v_pool, ctypes.c_uint16),
+        _ptr(block_table, ctypes.c_int32), _ptr(seq_lens, ctypes.c_int32),
+        float(scale), B, Hq, Hkv, D, page, W, P,
+        _ptr(out, ctypes.c_uint16), _ptr(o, ctypes.c_double), _ptr(mref, ctypes.c_double),
+        nthreads or default_threads())
+    if st != 0:
+        raise OracleError(f"oracle_decode failed with status {st}")
+    return out, o, mref
+
+
+def prefill(q, gate, k, v, scale, causal=True, rows=None, nthreads=None):
+    """Gated dense prefill.  q, gate: [B,S,H_q,D]; k, v: [B,S,H_kv,D].
+
+    rows: optional int array [n, 2] of (b, i) query positions; results are
+    then [n, H_q, D].  Without rows, results are [B, S, H_q, D].
+    """
+    lib = _load()
+    q, gate, k, v = (_u16(a) for a in (q, gate, k, v))
+    B, S, Hq, D = q.shape
+    Hkv = k.shape[2]
+    assert k.shape == (B, S, Hkv, D) and v.shape == k.shape and gate.shape == q.shape
+    if rows is None:
+        n = B * S
+        rows_p = None
+        shape = (B, S, Hq, D)
+    else:
+        rows = np.ascontiguousarray(rows, dtype=np.int32).reshape(-1, 2)
+        n = rows.shape[0]
+        rows_p = _ptr(rows, ctypes.c_int32)
+        shape = (n, Hq, D)
+    out = np.zeros(shape, dtype=np.uint16)
+    o = np.zeros(shape, dtype=np.float64)
+    mref = np.zeros(shape, dtype=np.float64)
+    st = lib.oracle_prefill(
+        _ptr(q, ctypes.c_uint16), _ptr(gate, ctypes.c_uint16),
+        _ptr(k, ctypes.c_uint16), _ptr(v, ctypes.c_uint16),
+        float(scale), int(bool(causal)), B, S, Hq, Hkv, D, rows_p, n,
+        _ptr(out, ctypes.c_uint16), _ptr(o, ctypes.c_double), _ptr(mref, ctypes.c_double),
+        nthreads or default_threads())
+    if st != 0:
+        raise OracleError(f"oracle_prefill failed with status {st}")
+    return out, o, mref

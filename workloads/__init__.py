@@ -1,0 +1,189 @@
+"""Seeded synthetic inputs for gated GQA decode and prefill.
+
+This module is shared by the test suite, the benchmark and the smoke check.  It
+only draws random numbers and lays them out (paged pools, block tables,
+lengths); it performs none of the attention arithmetic and imports neither the
+GPU package nor the oracle.
+
+Value recipe (the same for every workload): q, K, V ~ N(0, 1) and gate ~ N(0, 2)
+(standard deviation 2), drawn in float32 from numpy's PCG64 with one
+``SeedSequence([seed, stream])`` per tensor, then rounded to bf16 by torch's
+float32 -> bfloat16 conversion.  The rounding of the inputs does not affect
+parity: the GPU and the oracle receive the identical bits.
+
+Paged layout: pools are [num_pages][16][H_kv][D]; sequence b owns
+ceil(L_b / 16) pages whose ids are a seeded permutation of [0, num_pages),
+assigned in logical order (or the identity for a contiguous workload).  Unused
+block-table entries hold -1.  With ``poison=True`` the slots past L_b in each
+sequence's last page and every unused page hold NaN (bf16 0x7FC0), so a kernel
+that reads past a sequence's end produces NaN instead of a plausible number.
+"""
+from __future__ import annotations
+
+import dataclasses
+from typing import Optional, Sequence
+
+import numpy as np
+
+PAGE_SIZE = 16
+NAN_BF16 = 0x7FC0
+
+# Stream ids for SeedSequence([seed, stream]).
+_S_Q, _S_GATE, _S_K, _S_V, _S_LEN, _S_PERM, _S_PAD = range(1, 8)
+
+
+def _rng(seed: int, stream: int) -> np.random.Generator:
+    return np.random.Generator(np.random.PCG64(np.random.SeedSequence([int(seed), int(stream)])))
+
+
+def _f32_to_bf16_bits(x: np.ndarray) -> np.ndarray:
+    import torch
+
+    t = torch.from_numpy(np.ascontiguousarray(x, dtype=np.float32))
+    return t.to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16).copy()
+
+
+def normal_bf16(seed: int, stream: int, shape, std: float = 1.0, chunk: int = 1 << 24) -> np.ndarray:
+    """bf16 bits of N(0, std^2) draws, generated in chunks to bound memory."""
+    rng = _rng(seed, stream)
+    n = int(np.prod(shape)) if len(shape) else 1
+    out = np.empty(n, dtype=np.uint16)
+    for s in range(0, n, chunk):
+        e = min(n, s + chunk)
+        x = rng.standard_normal(e - s, dtype=np.float32)
+        if std != 1.0:
+            x *= np.float32(std)
+        out[s:e] = _f32_to_bf16_bits(x)
+    return out.reshape(shape)
+
+
+@dataclasses.dataclass
+class DecodeCase:
+    name: str
+    q: np.ndarray            # [B, H_q, D] uint16 (bf16 bits)
+    gate: np.ndarray         # [B, H_q, D]
+    k_pool: np.ndarray       # [P, 16, H_kv, D]
+    v_pool: np.ndarray       # [P, 16, H_kv, D]
+    block_table: np.ndarray  # [B, W] int32, -1 where unused
+    seq_lens: np.ndarray     # [B] int32, 0 for padded slots
+    scale: float
+
+    @property
+    def dims(self):
+        B, Hq, D = self.q.shape
+        P, ps, Hkv, _ = self.k_pool.shape
+        return dict(batch=B, num_q_heads=Hq, num_kv_heads=Hkv, head_dim=D, page_size=ps,
+                    max_pages_per_seq=self.block_table.shape[1], num_pages=P)
+
+    def kv_bytes(self) -> int:
+        """Algorithmic K+V bytes a decode call reads: sum_b L_b * H_kv * D * 2 B * 2."""
+        _, _, Hkv, D = self.k_pool.shape
+        return int(np.clip(self.seq_lens, 0, None).astype(np.int64).sum()) * Hkv * D * 2 * 2
+
+
+@dataclasses.dataclass
+class PrefillCase:
+    name: str
+    q: np.ndarray      # [B, S, H_q, D]
+    gate: np.ndarray   # [B, S, H_q, D]
+    k: np.ndarray      # [B, S, H_kv, D]
+    v: np.ndarray      # [B, S, H_kv, D]
+    scale: float
+    causal: bool
+
+
+def make_decode(name: str, seq_lens: Sequence[int], *, seed: int, num_q_heads: int = 16,
+                num_kv_heads: int = 2, head_dim: int = 256, max_pages_per_seq: Optional[int] = None,
+                shuffle: bool = True, poison: bool = True, extra_pages: int = 0,
+                scale: Optional[float] = None, gate_std: float = 2.0) -> DecodeCase:
+    lens = np.asarray(seq_lens, dtype=np.int32)
+    B = lens.shape[0]
+    npages = (np.clip(lens, 0, None).astype(np.int64) + PAGE_SIZE - 1) // PAGE_SIZE
+    W = int(max_pages_per_seq if max_pages_per_seq is not None else max(1, int(npages.max(initial=1))))
+    assert np.all(npages <= W), "a sequence needs more pages than the block table holds"
+    used = int(npages.sum())
+    P = used + int(extra_pages)
+    if shuffle:
+        ids = _rng(seed, _S_PERM).permutation(P).astype(np.int32)
+    else:
+        ids = np.arange(P, dtype=np.int32)
+    block_table = np.full((B, W), -1, dtype=np.int32)
+    cursor = 0
+    for b in range(B):
+        n = int(npages[b])
+        block_table[b, :n] = ids[cursor:cursor + n]
+        cursor += n
+    Hq, Hkv, D = num_q_heads, num_kv_heads, head_dim
+    q = normal_bf16(seed, _S_Q, (B, Hq, D))
+    gate = normal_bf16(seed, _S_GATE, (B, Hq, D), std=gate_std)
+    k_pool = normal_bf16(seed, _S_K, (max(P, 1), PAGE_SIZE, Hkv, D))
+    v_pool = normal_bf16(seed, _S_V, (max(P, 1), PAGE_SIZE, Hkv, D))
+    if poison:
+        for b in range(B):
+            n = int(npages[b])
+            tail = int(lens[b]) - (n - 1) * PAGE_SIZE if n > 0 else PAGE_SIZE
+            if n > 0 and tail < PAGE_SIZE:
+                last = block_table[b, n - 1]
+                k_pool[last, tail:] = NAN_BF16
+                v_pool[last, tail:] = NAN_BF16
+        if extra_pages or P == 0:
+            unused = ids[used:] if P else np.array([0])
+            k_pool[unused] = NAN_BF16
+            v_pool[unused] = NAN_BF16
+    return DecodeCase(name, q, gate, k_pool, v_pool, block_table, lens,
+                      float(scale if scale is not None else 1.0 / np.sqrt(D)))
+
+
+def make_prefill(name: str, batch: int, seq_len: int, *, seed: int, num_q_heads: int = 16,
+                 num_kv_heads: int = 2, head_dim: int = 256, causal: bool = True,
+                 scale: Optional[float] = None, gate_std: float = 2.0) -> PrefillCase:
+    B, S, Hq, Hkv, D = batch, seq_len, num_q_heads, num_kv_heads, head_dim
+    return PrefillCase(
+        name,
+        normal_bf16(seed, _S_Q, (B, S, Hq, D)),
+        normal_bf16(seed, _S_GATE, (B, S, Hq, D), std=gate_std),
+        normal_bf16(seed, _S_K, (B, S, Hkv, D)),
+        normal_bf16(seed, _S_V, (B, S, Hkv, D)),
+        float(scale if scale is not None else 1.0 / np.sqrt(D)),
+        causal,
+    )
+
+
+# --------------------------------------------------------------------------
+# The five workloads.  Workload i is generated with seed i.
+# --------------------------------------------------------------------------
+WORKLOADS = {
+    0: "decode B=1 L=512 contiguous pages",
+    1: "decode B=4 L=512/495/478/461 paged shuffled",
+    2: "decode B=64 L=4096 paged shuffled",
+    3: "decode B=224 L~U[4094,6142] paged shuffled, 11 padded slots",
+    4: "prefill B=2 S=2048 causal",
+}
+
+
+def config3_lengths(seed: int = 3, batch: int = 224, lo: int = 4094, hi: int = 6142,
+                    pad_fraction: float = 0.05) -> np.ndarray:
+    lens = _rng(seed, _S_LEN).integers(lo, hi, size=batch, endpoint=True).astype(np.int32)
+    npad = int(round(pad_fraction * batch))
+    pad = _rng(seed, _S_PAD).choice(batch, size=npad, replace=False)
+    lens[pad] = 0
+    return lens
+
+
+def workload(i: int, *, poison: bool = True):
+    """Build workload i (0..4) with seed i."""
+    if i == 0:
+        return make_decode("decode_b1_l512_contiguous", [512], seed=0, shuffle=False,
+                           poison=poison, max_pages_per_seq=32)
+    if i == 1:
+        return make_decode("decode_b4_l512_495_478_461_paged", [512, 495, 478, 461], seed=1,
+                           poison=poison, max_pages_per_seq=32)
+    if i == 2:
+        return make_decode("decode_b64_l4096_paged", [4096] * 64, seed=2, poison=poison,
+                           max_pages_per_seq=256)
+    if i == 3:
+        return make_decode("decode_b224_l4094_6142_pad11_paged", config3_lengths(), seed=3,
+                           poison=poison, max_pages_per_seq=384)
+    if i == 4:
+        return make_prefill("prefill_b2_s2048_causal", 2, 2048, seed=4, causal=True)
+    raise ValueError(f"no workload {i}")
