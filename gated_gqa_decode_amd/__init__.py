@@ -1,0 +1,261 @@
+"""Gated grouped-query attention for AMD Instinct MI355X (gfx950).
+
+Python binding of ``libgated_attn.so`` (C ABI declared in
+``include/gated_attn.h``).  This module only marshals arguments: it checks
+tensor dtypes, shapes and devices, allocates outputs and workspaces with torch
+(device memory and streams are torch's job here), and calls the library.  Every
+step of the computation runs in the library's HIP kernels; there is no other
+code path, and importing fails loudly when the library has not been built.
+
+    out = bf16( bf16(softmax(q K^T * scale) V) * bf16(sigmoid(gate)) )
+
+Entry points: :func:`decode` (paged split-KV decode, two kernel launches),
+:func:`prefill` (dense causal/non-causal MFMA prefill, one launch),
+:func:`decode_plan` / :func:`decode_workspace_size`.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from dataclasses import dataclass
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(HERE, "libgated_attn.so")
+
+GA_OK = 0
+GA_ERR_INVALID_ARGUMENT = 1
+GA_ERR_UNSUPPORTED = 2
+GA_ERR_WORKSPACE_TOO_SMALL = 3
+GA_ERR_HIP = 4
+
+# Every symbol include/gated_attn.h declares.
+EXPORTED_SYMBOLS = (
+    "gated_attn_decode_plan",
+    "gated_attn_decode_workspace_size",
+    "gated_attn_decode",
+    "gated_attn_prefill",
+    "gated_attn_status_string",
+    "gated_attn_last_hip_error",
+)
+
+
+class DecodeDims(ctypes.Structure):
+    _fields_ = [
+        ("batch", ctypes.c_int32),
+        ("num_q_heads", ctypes.c_int32),
+        ("num_kv_heads", ctypes.c_int32),
+        ("head_dim", ctypes.c_int32),
+        ("page_size", ctypes.c_int32),
+        ("max_pages_per_seq", ctypes.c_int32),
+        ("num_pages", ctypes.c_int64),
+    ]
+
+
+class DecodePlan(ctypes.Structure):
+    _fields_ = [
+        ("tokens_per_split", ctypes.c_int32),
+        ("num_splits", ctypes.c_int32),
+        ("workspace_bytes", ctypes.c_size_t),
+    ]
+
+
+class PrefillDims(ctypes.Structure):
+    _fields_ = [
+        ("batch", ctypes.c_int32),
+        ("seq_len", ctypes.c_int32),
+        ("num_q_heads", ctypes.c_int32),
+        ("num_kv_heads", ctypes.c_int32),
+        ("head_dim", ctypes.c_int32),
+    ]
+
+
+def _load_library() -> ctypes.CDLL:
+    # torch ships its own HIP runtime (same SONAME, libamdhip64.so.7).  Loading
+    # torch first makes the library bind to that runtime instead of pulling a
+    # second one into the process: one runtime, one view of devices, streams
+    # and memory.
+    import torch  # noqa: F401
+
+    if not os.path.exists(LIB_PATH):
+        raise ImportError(
+            f"{LIB_PATH} is missing: build it with `python -c 'import __graft_entry__ as g; g.build()'` "
+            "or `python gated_gqa_decode_amd/build.py`")
+    lib = ctypes.CDLL(LIB_PATH)
+    vp, sz = ctypes.c_void_p, ctypes.c_size_t
+    lib.gated_attn_decode_plan.restype = ctypes.c_int
+    lib.gated_attn_decode_plan.argtypes = [ctypes.POINTER(DecodeDims), ctypes.POINTER(DecodePlan)]
+    lib.gated_attn_decode_workspace_size.restype = sz
+    lib.gated_attn_decode_workspace_size.argtypes = [ctypes.POINTER(DecodeDims)]
+    lib.gated_attn_decode.restype = ctypes.c_int
+    lib.gated_attn_decode.argtypes = [vp, vp, vp, vp, vp, vp, ctypes.c_float, vp, vp,
+                                      ctypes.POINTER(DecodeDims), vp, sz]
+    lib.gated_attn_prefill.restype = ctypes.c_int
+    lib.gated_attn_prefill.argtypes = [vp, vp, vp, vp, ctypes.c_float, ctypes.c_int, vp, vp,
+                                       ctypes.POINTER(PrefillDims)]
+    lib.gated_attn_status_string.restype = ctypes.c_char_p
+    lib.gated_attn_status_string.argtypes = [ctypes.c_int]
+    lib.gated_attn_last_hip_error.restype = ctypes.c_int
+    lib.gated_attn_last_hip_error.argtypes = []
+    return lib
+
+
+lib = _load_library()
+
+
+class GatedAttnError(RuntimeError):
+    def __init__(self, status: int, where: str):
+        name = lib.gated_attn_status_string(status).decode()
+        msg = f"{where}: {name}"
+        if status == GA_ERR_HIP:
+            msg += f" (hipError_t {lib.gated_attn_last_hip_error()})"
+        super().__init__(msg)
+        self.status = status
+
+
+class InvalidArgument(GatedAttnError, ValueError):
+    pass
+
+
+class Unsupported(GatedAttnError, NotImplementedError):
+    pass
+
+
+class WorkspaceTooSmall(GatedAttnError, ValueError):
+    pass
+
+
+def check(status: int, where: str) -> None:
+    """Raise the typed exception for a non-OK status."""
+    if status == GA_OK:
+        return
+    cls = {GA_ERR_INVALID_ARGUMENT: InvalidArgument, GA_ERR_UNSUPPORTED: Unsupported,
+           GA_ERR_WORKSPACE_TOO_SMALL: WorkspaceTooSmall}.get(status, GatedAttnError)
+    raise cls(status, where)
+
+
+@dataclass
+class Plan:
+    tokens_per_split: int
+    num_splits: int
+    workspace_bytes: int
+
+
+def decode_dims(batch, num_q_heads, num_kv_heads, head_dim, page_size, max_pages_per_seq,
+                num_pages) -> DecodeDims:
+    return DecodeDims(batch, num_q_heads, num_kv_heads, head_dim, page_size, max_pages_per_seq,
+                      num_pages)
+
+
+def decode_plan(dims: DecodeDims) -> Plan:
+    p = DecodePlan()
+    check(lib.gated_attn_decode_plan(ctypes.byref(dims), ctypes.byref(p)), "gated_attn_decode_plan")
+    return Plan(p.tokens_per_split, p.num_splits, p.workspace_bytes)
+
+
+def decode_workspace_size(dims: DecodeDims) -> int:
+    return int(lib.gated_attn_decode_workspace_size(ctypes.byref(dims)))
+
+
+# ---------------------------------------------------------------------------
+# torch-facing wrappers (marshalling only)
+# ---------------------------------------------------------------------------
+def _torch():
+    import torch
+
+    return torch
+
+
+def _need(t, name, dtype, ndim, device):
+    torch = _torch()
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch.Tensor")
+    if t.dtype != dtype:
+        raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
+    if t.dim() != ndim:
+        raise ValueError(f"{name} must have {ndim} dims, got shape {tuple(t.shape)}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if device is not None and t.device != device:
+        raise ValueError(f"{name} is on {t.device}, expected {device}")
+
+
+def _stream_handle(stream, device):
+    torch = _torch()
+    if stream is None:
+        stream = torch.cuda.current_stream(device)
+    return ctypes.c_void_p(stream.cuda_stream)
+
+
+def decode_dims_for(q, k_pool, block_table) -> DecodeDims:
+    B, Hq, D = q.shape
+    P, ps, Hkv, _ = k_pool.shape
+    return decode_dims(B, Hq, Hkv, D, ps, block_table.shape[1], P)
+
+
+def decode(q, gate, k_pool, v_pool, block_table, seq_lens, scale, *, out=None, workspace=None,
+           stream=None):
+    """Gated GQA decode over a paged pool; returns ``out`` [B, H_q, D] bf16.
+
+    q, gate: [B, H_q, D] bf16; k_pool, v_pool: [P, 16, H_kv, D] bf16;
+    block_table: [B, W] int32; seq_lens: [B] int32 (<= 0: padded slot).
+    ``workspace`` (uint8, >= decode_workspace_size bytes) is allocated when
+    not given; pass one to keep the call allocation-free (e.g. under graph
+    capture).  Work is enqueued on ``stream`` (default: torch's current stream).
+    """
+    torch = _torch()
+    dev = q.device
+    _need(q, "q", torch.bfloat16, 3, dev)
+    _need(gate, "gate", torch.bfloat16, 3, dev)
+    _need(k_pool, "k_pool", torch.bfloat16, 4, dev)
+    _need(v_pool, "v_pool", torch.bfloat16, 4, dev)
+    _need(block_table, "block_table", torch.int32, 2, dev)
+    _need(seq_lens, "seq_lens", torch.int32, 1, dev)
+    if gate.shape != q.shape or v_pool.shape != k_pool.shape:
+        raise ValueError("gate must match q and v_pool must match k_pool")
+    B, Hq, D = q.shape
+    if k_pool.shape[3] != D or block_table.shape[0] != B or seq_lens.shape[0] != B:
+        raise ValueError("inconsistent shapes")
+    dims = decode_dims_for(q, k_pool, block_table)
+    if out is None:
+        out = torch.empty_like(q)
+    else:
+        _need(out, "out", torch.bfloat16, 3, dev)
+        if out.shape != q.shape:
+            raise ValueError("out must match q")
+    need = decode_workspace_size(dims)
+    if workspace is None:
+        workspace = torch.empty(max(need, 16), dtype=torch.uint8, device=dev)
+    else:
+        _need(workspace, "workspace", torch.uint8, 1, dev)
+    st = lib.gated_attn_decode(
+        q.data_ptr(), gate.data_ptr(), k_pool.data_ptr(), v_pool.data_ptr(),
+        block_table.data_ptr(), seq_lens.data_ptr(), float(scale), out.data_ptr(),
+        _stream_handle(stream, dev), ctypes.byref(dims), workspace.data_ptr(), workspace.numel())
+    check(st, "gated_attn_decode")
+    return out
+
+
+def prefill(q, gate, k, v, scale, causal=True, *, out=None, stream=None):
+    """Gated dense prefill; q, gate: [B, S, H_q, D]; k, v: [B, S, H_kv, D] bf16."""
+    torch = _torch()
+    dev = q.device
+    _need(q, "q", torch.bfloat16, 4, dev)
+    _need(gate, "gate", torch.bfloat16, 4, dev)
+    _need(k, "k", torch.bfloat16, 4, dev)
+    _need(v, "v", torch.bfloat16, 4, dev)
+    B, S, Hq, D = q.shape
+    Hkv = k.shape[2]
+    if gate.shape != q.shape or k.shape != (B, S, Hkv, D) or v.shape != k.shape:
+        raise ValueError("inconsistent shapes")
+    if out is None:
+        out = torch.empty_like(q)
+    else:
+        _need(out, "out", torch.bfloat16, 4, dev)
+        if out.shape != q.shape:
+            raise ValueError("out must match q")
+    dims = PrefillDims(B, S, Hq, Hkv, D)
+    st = lib.gated_attn_prefill(q.data_ptr(), gate.data_ptr(), k.data_ptr(), v.data_ptr(),
+                                float(scale), int(bool(causal)), out.data_ptr(),
+                                _stream_handle(stream, dev), ctypes.byref(dims))
+    check(st, "gated_attn_prefill")
+    return out

@@ -1,0 +1,209 @@
+// capi.cpp -- the extern "C" boundary of libgated_attn.so (include/gated_attn.h):
+// argument validation, split planning, workspace sizing, device check, launch.
+//
+// Every check that the host can make runs before anything is enqueued (cuDNN
+// "Gated Attention Block", Forward: typed errors rather than a failed launch;
+// FreeToken PR #781, Summary: validate before touching KV storage).  Nothing
+// here allocates, synchronises or reads device memory.
+#include <hip/hip_runtime.h>
+
+#include <atomic>
+#include <cmath>
+#include <cstdint>
+#include <cstring>
+
+#include "ga_internal.h"
+#include "gated_attn.h"
+
+#ifndef GA_DECODE_TARGET_BLOCKS
+// Stage-1 workgroups a decode call aims for: about eight per compute unit of
+// the 256-CU MI355X, enough to keep every CU busy through the ragged end of
+// the grid without making the fp32 partials (and stage 2) needlessly large.
+#define GA_DECODE_TARGET_BLOCKS 2048
+#endif
+
+namespace {
+
+constexpr int kHeadDim = 256;
+constexpr int kGroup = 8;
+constexpr int kPageSize = 16;
+constexpr int kSplitQuantum = 32;   // 4 waves x 8-token steps
+constexpr int kMaxSplitTokens = 1024;  // 64 pages: one page id per lane
+constexpr int kMaxGridYZ = 65535;
+
+thread_local int g_last_hip_error = 0;
+
+bool aligned(const void* p, size_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
+
+ga_status hip_fail(hipError_t e) {
+  g_last_hip_error = static_cast<int>(e);
+  return GA_ERR_HIP;
+}
+
+// gfx950 check for the current device, cached per device id.
+ga_status check_device() {
+  static std::atomic<int> cache[64];  // 0 unknown, 1 gfx950, 2 other
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return hip_fail(e);
+  if (dev >= 0 && dev < 64) {
+    int c = cache[dev].load(std::memory_order_relaxed);
+    if (c == 1) return GA_OK;
+    if (c == 2) return GA_ERR_UNSUPPORTED;
+  }
+  hipDeviceProp_t prop;
+  e = hipGetDeviceProperties(&prop, dev);
+  if (e != hipSuccess) return hip_fail(e);
+  const bool ok = std::strncmp(prop.gcnArchName, "gfx950", 6) == 0;
+  if (dev >= 0 && dev < 64) cache[dev].store(ok ? 1 : 2, std::memory_order_relaxed);
+  return ok ? GA_OK : GA_ERR_UNSUPPORTED;
+}
+
+ga_status check_heads(int32_t hq, int32_t hkv, int32_t d) {
+  if (hq <= 0 || hkv <= 0 || d <= 0) return GA_ERR_INVALID_ARGUMENT;
+  if (hq % hkv != 0) return GA_ERR_INVALID_ARGUMENT;
+  if (hq / hkv != kGroup) return GA_ERR_UNSUPPORTED;
+  if (d != kHeadDim) return GA_ERR_UNSUPPORTED;
+  if (hkv > kMaxGridYZ) return GA_ERR_UNSUPPORTED;
+  return GA_OK;
+}
+
+ga_status check_decode_dims(const ga_decode_dims* d) {
+  if (d == nullptr) return GA_ERR_INVALID_ARGUMENT;
+  if (d->batch < 0 || d->page_size <= 0 || d->max_pages_per_seq <= 0 || d->num_pages <= 0)
+    return GA_ERR_INVALID_ARGUMENT;
+  ga_status st = check_heads(d->num_q_heads, d->num_kv_heads, d->head_dim);
+  if (st != GA_OK) return st;
+  if (d->page_size != kPageSize) return GA_ERR_UNSUPPORTED;
+  if (d->batch > kMaxGridYZ) return GA_ERR_UNSUPPORTED;
+  // capacity in tokens must fit an int32
+  if ((int64_t)d->max_pages_per_seq * kPageSize > INT32_MAX / 2) return GA_ERR_UNSUPPORTED;
+  return GA_OK;
+}
+
+// Split plan from the dims alone (allocated capacity, not current lengths).
+void make_plan(const ga_decode_dims* d, ga_decode_plan* p) {
+  const int64_t cap = (int64_t)d->max_pages_per_seq * kPageSize;
+  const int64_t bkv = (int64_t)d->batch * d->num_kv_heads;
+  int64_t t = (cap * (bkv > 0 ? bkv : 1) + GA_DECODE_TARGET_BLOCKS - 1) / GA_DECODE_TARGET_BLOCKS;
+  t = ((t + kSplitQuantum - 1) / kSplitQuantum) * kSplitQuantum;
+  if (t < kSplitQuantum) t = kSplitQuantum;
+  if (t > kMaxSplitTokens) t = kMaxSplitTokens;
+  const int64_t ns = (cap + t - 1) / t;
+  p->tokens_per_split = (int32_t)t;
+  p->num_splits = (int32_t)ns;
+  const int64_t rows = (int64_t)d->batch * d->num_q_heads * ns;
+  size_t bytes = (size_t)rows * (size_t)(kHeadDim + 2) * sizeof(float);
+  p->workspace_bytes = (bytes + 255) & ~(size_t)255;
+}
+
+}  // namespace
+
+extern "C" {
+
+ga_status gated_attn_decode_plan(const ga_decode_dims* dims, ga_decode_plan* plan) {
+  if (plan == nullptr) return GA_ERR_INVALID_ARGUMENT;
+  ga_status st = check_decode_dims(dims);
+  if (st != GA_OK) return st;
+  make_plan(dims, plan);
+  return GA_OK;
+}
+
+size_t gated_attn_decode_workspace_size(const ga_decode_dims* dims) {
+  ga_decode_plan p;
+  if (gated_attn_decode_plan(dims, &p) != GA_OK) return 0;
+  return p.workspace_bytes;
+}
+
+ga_status gated_attn_decode(const uint16_t* q, const uint16_t* gate, const uint16_t* k_pool,
+                            const uint16_t* v_pool, const int32_t* block_table,
+                            const int32_t* seq_lens, float scale, uint16_t* out, void* stream,
+                            const ga_decode_dims* dims, void* workspace, size_t workspace_bytes) {
+  ga_status st = check_decode_dims(dims);
+  if (st != GA_OK) return st;
+  if (!(std::isfinite(scale) && scale > 0.f)) return GA_ERR_INVALID_ARGUMENT;
+  if (dims->batch == 0) return GA_OK;
+  const void* ptr16[] = {q, gate, k_pool, v_pool, out, workspace};
+  for (const void* p : ptr16)
+    if (p == nullptr || !aligned(p, 16)) return GA_ERR_INVALID_ARGUMENT;
+  if (block_table == nullptr || seq_lens == nullptr || !aligned(block_table, 4) ||
+      !aligned(seq_lens, 4))
+    return GA_ERR_INVALID_ARGUMENT;
+  ga_decode_plan plan;
+  make_plan(dims, &plan);
+  if (workspace_bytes < plan.workspace_bytes) return GA_ERR_WORKSPACE_TOO_SMALL;
+  st = check_device();
+  if (st != GA_OK) return st;
+
+  ga::DecodeLaunch L;
+  L.q = q;
+  L.gate = gate;
+  L.k_pool = k_pool;
+  L.v_pool = v_pool;
+  L.block_table = block_table;
+  L.seq_lens = seq_lens;
+  L.out = out;
+  const size_t rows = (size_t)dims->batch * dims->num_q_heads * plan.num_splits;
+  L.part_acc = static_cast<float*>(workspace);
+  L.part_ml = L.part_acc + rows * kHeadDim;
+  L.scale = scale;
+  L.batch = dims->batch;
+  L.num_kv_heads = dims->num_kv_heads;
+  L.max_pages = dims->max_pages_per_seq;
+  L.num_pages = dims->num_pages;
+  L.tokens_per_split = plan.tokens_per_split;
+  L.num_splits = plan.num_splits;
+  hipError_t e = ga::launch_decode(L, static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return hip_fail(e);
+  return GA_OK;
+}
+
+ga_status gated_attn_prefill(const uint16_t* q, const uint16_t* gate, const uint16_t* k,
+                             const uint16_t* v, float scale, int causal, uint16_t* out,
+                             void* stream, const ga_prefill_dims* dims) {
+  if (dims == nullptr) return GA_ERR_INVALID_ARGUMENT;
+  if (dims->batch < 0 || dims->seq_len < 0) return GA_ERR_INVALID_ARGUMENT;
+  ga_status st = check_heads(dims->num_q_heads, dims->num_kv_heads, dims->head_dim);
+  if (st != GA_OK) return st;
+  if (!(std::isfinite(scale) && scale > 0.f)) return GA_ERR_INVALID_ARGUMENT;
+  if (dims->batch > kMaxGridYZ) return GA_ERR_UNSUPPORTED;
+  if (dims->batch == 0 || dims->seq_len == 0) return GA_OK;
+  // q/gate/out hold B*S*H_q*D elements; keep every element index in int32 range.
+  if ((int64_t)dims->batch * dims->seq_len * dims->num_q_heads * kHeadDim > INT32_MAX)
+    return GA_ERR_UNSUPPORTED;
+  const void* ptr16[] = {q, gate, k, v, out};
+  for (const void* p : ptr16)
+    if (p == nullptr || !aligned(p, 16)) return GA_ERR_INVALID_ARGUMENT;
+  st = check_device();
+  if (st != GA_OK) return st;
+
+  ga::PrefillLaunch P;
+  P.q = q;
+  P.gate = gate;
+  P.k = k;
+  P.v = v;
+  P.out = out;
+  P.scale = scale;
+  P.causal = causal != 0;
+  P.batch = dims->batch;
+  P.seq_len = dims->seq_len;
+  P.num_kv_heads = dims->num_kv_heads;
+  hipError_t e = ga::launch_prefill(P, static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return hip_fail(e);
+  return GA_OK;
+}
+
+const char* gated_attn_status_string(ga_status status) {
+  switch (status) {
+    case GA_OK: return "GA_OK";
+    case GA_ERR_INVALID_ARGUMENT: return "GA_ERR_INVALID_ARGUMENT";
+    case GA_ERR_UNSUPPORTED: return "GA_ERR_UNSUPPORTED";
+    case GA_ERR_WORKSPACE_TOO_SMALL: return "GA_ERR_WORKSPACE_TOO_SMALL";
+    case GA_ERR_HIP: return "GA_ERR_HIP";
+  }
+  return "GA_ERR_UNKNOWN";
+}
+
+int gated_attn_last_hip_error(void) { return g_last_hip_error; }
+
+}  // extern "C"

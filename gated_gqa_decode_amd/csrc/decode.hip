@@ -1,0 +1,388 @@
+// decode.hip -- split-KV gated GQA decode for gfx950 (CDNA4, wave64).
+//
+// Stage 1 (one workgroup per (sequence b, kv head g, split s)): stream the
+// split's tokens of the paged K/V pool with coalesced 16-byte loads, score the
+// 8 query heads of the GQA group against every key, and keep an fp32 online
+// softmax state (running max m, running sum l, unnormalised acc[256]) per head.
+// FreeToken PR #781, Summary: stage1 partials are kept in fp32 for stage2.
+//
+// Stage 2 (one wave per (b, query head)): merge the splits' partials by their
+// log-sum-exp in fp32, round O to bf16, and apply the bf16 sigmoid gate with a
+// rounded product -- the gate costs no launch of its own (FreeToken PR #781,
+// Summary; cuDNN "Gated Attention Block", fuse_gate).
+//
+// Work layout inside a stage-1 wave (64 lanes), per step of 8 tokens, which
+// all lie in one half of one 16-token page:
+//   scores : lane = (token tq in 0..3) x (16-byte chunk c16 in 0..15).  A pass
+//            covers 4 tokens; each lane holds q chunks c16 and c16+16 of all 8
+//            heads (64 VGPRs) and forms 8 partial dot products with bf16 dot2
+//            instructions; a 16-lane DPP sum completes them.  Two passes per step.
+//   values : lane = (token parity tp) x (16-byte chunk c32 in 0..31); the lane
+//            owns d = 8*c32 .. 8*c32+7 of all 8 heads (64 fp32 accumulators)
+//            for the tokens of its parity.
+//   softmax: probabilities go through a 288-byte per-wave LDS slot from the
+//            score lanes to the value lanes.
+// Both K and V loads read whole 256/512-byte row segments per instruction, and
+// the next step's loads are issued before the current step is computed.
+#include <hip/hip_runtime.h>
+#include <math.h>
+#include <stdint.h>
+
+#include "ga_device.h"
+#include "ga_internal.h"
+
+namespace ga {
+
+namespace {
+
+constexpr int kD = 256;          // head dim
+constexpr int kGroup = 8;        // query heads per kv head
+constexpr int kPage = 16;        // tokens per page
+constexpr int kStep = 8;         // tokens per wave step
+constexpr int kWaves = 4;        // waves per stage-1 workgroup
+constexpr float kLog2e = 1.4426950408889634f;
+
+struct Stage1Args {
+  const uint16_t* q;
+  const uint16_t* k_pool;
+  const uint16_t* v_pool;
+  const int32_t* block_table;
+  const int32_t* seq_lens;
+  float* part_acc;   // [B][H_q][NS][D]
+  float* part_ml;    // [B][H_q][NS][2]  (m in log2 units, l)
+  float scale_log2;  // scale * log2(e)
+  int num_kv_heads;
+  int max_pages;     // W
+  long long num_pages;
+  int tokens_per_split;
+  int num_splits;
+};
+
+struct alignas(16) WaveSlot {
+  float p[kStep][kGroup];  // probabilities of the step's 8 tokens x 8 heads
+  float alpha[kGroup];     // rescale factor of the running state per head
+};
+
+struct alignas(16) MergeSlot {
+  float acc[kWaves][kGroup][kD];
+  float m[kWaves][kGroup];
+  float l[kWaves][kGroup];
+};
+
+__device__ __forceinline__ uint4 ldg16(const uint16_t* p) {
+  return *reinterpret_cast<const uint4*>(p);
+}
+
+}  // namespace
+
+__global__ __launch_bounds__(256, 2) void decode_stage1_kernel(Stage1Args a) {
+  __shared__ WaveSlot wslot[kWaves];
+  __shared__ MergeSlot merge;
+
+  const int s = blockIdx.x;
+  const int g = blockIdx.y;
+  const int b = blockIdx.z;
+  // Lengths past the capacity and page ids outside the pool break the
+  // documented preconditions; both are clamped so such input yields garbage
+  // in its own row instead of an access outside the buffers.
+  const int L = min(a.seq_lens[b], a.max_pages * kPage);
+  const int tok_begin = s * a.tokens_per_split;
+  if (tok_begin >= L) return;  // empty split: stage 2 never reads its slot
+  const int tok_end = min(L, tok_begin + a.tokens_per_split);
+
+  const int lane = __lane_id();
+  const int wave = threadIdx.x >> 6;
+  const int Hkv = a.num_kv_heads;
+  const int Hq = Hkv * kGroup;
+
+  // score-lane coordinates
+  const int tq = lane >> 4;    // token within a pass
+  const int c16 = lane & 15;   // 16-byte chunk (and chunk + 16)
+  const int hs = c16 & 7;      // head whose score this lane keeps
+  // value-lane coordinates
+  const int tp = lane >> 5;    // token parity
+  const int c32 = lane & 31;   // 16-byte chunk of the value row
+
+  // q chunks c16 and c16 + 16 of the group's 8 heads (bf16 pairs).
+  uint4 qa[kGroup], qb[kGroup];
+  {
+    const uint16_t* qbase = a.q + ((size_t)b * Hq + (size_t)g * kGroup) * kD;
+#pragma unroll
+    for (int h = 0; h < kGroup; ++h) {
+      qa[h] = ldg16(qbase + h * kD + c16 * 8);
+      qb[h] = ldg16(qbase + h * kD + (c16 + 16) * 8);
+    }
+  }
+
+  float acc[kGroup][8];
+#pragma unroll
+  for (int h = 0; h < kGroup; ++h)
+#pragma unroll
+    for (int e = 0; e < 8; ++e) acc[h][e] = 0.f;
+  float m_run = -INFINITY;  // running max (log2 units) of head hs
+  float l_run = 0.f;        // this lane's share of the running sum of head hs
+
+  const int n_steps = (tok_end - tok_begin + kStep - 1) / kStep;
+  const int32_t* bt = a.block_table + (size_t)b * a.max_pages;
+  const size_t row_stride = (size_t)Hkv * kD;            // elements between tokens
+  const size_t page_stride = (size_t)kPage * row_stride; // elements between pages
+
+  // Page ids of this split, one per lane (a split covers at most 64 pages).
+  const int first_page = tok_begin / kPage;
+  const int n_pages = (tok_end - 1) / kPage - first_page + 1;
+  int my_page = lane < n_pages ? bt[first_page + lane] : 0;
+  my_page = (int)min((long long)max(my_page, 0), a.num_pages - 1);
+
+  auto step_base = [&](int step, const uint16_t* pool) -> const uint16_t* {
+    const int t0 = tok_begin + step * kStep;
+    const int pg = __builtin_amdgcn_readlane(my_page, t0 / kPage - first_page);
+    return pool + (size_t)pg * page_stride + (size_t)(t0 % kPage) * row_stride + (size_t)g * kD;
+  };
+
+  uint4 kc[2][2], vc[4];
+  auto load_step = [&](int step, uint4 (&kk)[2][2], uint4 (&vv)[4]) {
+    const uint16_t* kb = step_base(step, a.k_pool);
+    const uint16_t* vb = step_base(step, a.v_pool);
+#pragma unroll
+    for (int pass = 0; pass < 2; ++pass) {
+      const uint16_t* row = kb + (size_t)(pass * 4 + tq) * row_stride;
+      kk[pass][0] = ldg16(row + c16 * 8);
+      kk[pass][1] = ldg16(row + (c16 + 16) * 8);
+    }
+#pragma unroll
+    for (int j = 0; j < 4; ++j) vv[j] = ldg16(vb + (size_t)(2 * j + tp) * row_stride + c32 * 8);
+  };
+
+  WaveSlot& ws = wslot[wave];
+  int step = wave;
+  if (step < n_steps) load_step(step, kc, vc);
+  for (; step < n_steps; step += kWaves) {
+    uint4 kn[2][2], vn[4];
+    const bool has_next = step + kWaves < n_steps;
+    if (has_next) load_step(step + kWaves, kn, vn);
+
+    const int t0 = tok_begin + step * kStep;
+    // ---- scores: two passes of 4 tokens -------------------------------------
+    float sc[2];
+#pragma unroll
+    for (int pass = 0; pass < 2; ++pass) {
+      float part[kGroup];
+#pragma unroll
+      for (int h = 0; h < kGroup; ++h) {
+        float x = 0.f;
+        x = dot2_bf16(qa[h].x, kc[pass][0].x, x);
+        x = dot2_bf16(qa[h].y, kc[pass][0].y, x);
+        x = dot2_bf16(qa[h].z, kc[pass][0].z, x);
+        x = dot2_bf16(qa[h].w, kc[pass][0].w, x);
+        x = dot2_bf16(qb[h].x, kc[pass][1].x, x);
+        x = dot2_bf16(qb[h].y, kc[pass][1].y, x);
+        x = dot2_bf16(qb[h].z, kc[pass][1].z, x);
+        x = dot2_bf16(qb[h].w, kc[pass][1].w, x);
+        part[h] = sum16(x);
+      }
+      float mine = part[0];
+#pragma unroll
+      for (int h = 1; h < kGroup; ++h) mine = (hs == h) ? part[h] : mine;
+      const int t = t0 + pass * 4 + tq;
+      sc[pass] = (t < tok_end) ? mine * a.scale_log2 : -INFINITY;
+    }
+    // ---- online softmax for head hs ----------------------------------------
+    float mx = fmaxf(sc[0], sc[1]);
+    mx = fmaxf(mx, shfl_xor(mx, 16));
+    mx = fmaxf(mx, shfl_xor(mx, 32));
+    const float m_new = fmaxf(m_run, mx);
+    const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
+    const float p0 = __builtin_amdgcn_exp2f(sc[0] - m_new);
+    const float p1 = __builtin_amdgcn_exp2f(sc[1] - m_new);
+    l_run = l_run * alpha + (p0 + p1);
+    m_run = m_new;
+    if (c16 < kGroup) {
+      ws.p[tq][hs] = p0;
+      ws.p[4 + tq][hs] = p1;
+      if (tq == 0) ws.alpha[hs] = alpha;
+    }
+    wave_lds_sync();
+    // ---- values ------------------------------------------------------------
+    {
+      const float4 al0 = *reinterpret_cast<const float4*>(&ws.alpha[0]);
+      const float4 al1 = *reinterpret_cast<const float4*>(&ws.alpha[4]);
+      const float al[kGroup] = {al0.x, al0.y, al0.z, al0.w, al1.x, al1.y, al1.z, al1.w};
+      bool rescale = false;
+#pragma unroll
+      for (int h = 0; h < kGroup; ++h) rescale |= (al[h] != 1.f);
+      if (rescale) {  // same decision in every lane: al[] is the wave's LDS copy
+#pragma unroll
+        for (int h = 0; h < kGroup; ++h)
+#pragma unroll
+          for (int e = 0; e < 8; ++e) acc[h][e] *= al[h];
+      }
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const int kk = 2 * j + tp;
+        uint4 v = vc[j];
+        if (t0 + kk >= tok_end) v = make_uint4(0, 0, 0, 0);  // tail slots may hold anything
+        const float vf[8] = {bf16_lo(v.x), bf16_hi(v.x), bf16_lo(v.y), bf16_hi(v.y),
+                             bf16_lo(v.z), bf16_hi(v.z), bf16_lo(v.w), bf16_hi(v.w)};
+        const float4 pa = *reinterpret_cast<const float4*>(&ws.p[kk][0]);
+        const float4 pb = *reinterpret_cast<const float4*>(&ws.p[kk][4]);
+        const float pr[kGroup] = {pa.x, pa.y, pa.z, pa.w, pb.x, pb.y, pb.z, pb.w};
+#pragma unroll
+        for (int h = 0; h < kGroup; ++h)
+#pragma unroll
+          for (int e = 0; e < 8; ++e) acc[h][e] = fmaf(pr[h], vf[e], acc[h][e]);
+      }
+    }
+    wave_lds_sync();  // the next step rewrites the slot
+    if (has_next) {
+#pragma unroll
+      for (int pass = 0; pass < 2; ++pass) {
+        kc[pass][0] = kn[pass][0];
+        kc[pass][1] = kn[pass][1];
+      }
+#pragma unroll
+      for (int j = 0; j < 4; ++j) vc[j] = vn[j];
+    }
+  }
+
+  // ---- merge the 4 waves' states and write the split's partial -------------
+  l_run += shfl_xor(l_run, 16);
+  l_run += shfl_xor(l_run, 32);
+  if (lane < kGroup) {  // tq == 0, c16 == lane: head lane
+    merge.m[wave][lane] = m_run;
+    merge.l[wave][lane] = l_run;
+  }
+#pragma unroll
+  for (int h = 0; h < kGroup; ++h)
+#pragma unroll
+    for (int e = 0; e < 8; ++e) acc[h][e] += shfl_xor(acc[h][e], 32);
+  if (tp == 0) {
+#pragma unroll
+    for (int h = 0; h < kGroup; ++h) {
+      float4* dst = reinterpret_cast<float4*>(&merge.acc[wave][h][c32 * 8]);
+      dst[0] = make_float4(acc[h][0], acc[h][1], acc[h][2], acc[h][3]);
+      dst[1] = make_float4(acc[h][4], acc[h][5], acc[h][6], acc[h][7]);
+    }
+  }
+  __syncthreads();
+  {
+    const int h = threadIdx.x >> 5;   // 0..7
+    const int c = threadIdx.x & 31;   // 8 values each
+    float M = -INFINITY;
+#pragma unroll
+    for (int w = 0; w < kWaves; ++w) M = fmaxf(M, merge.m[w][h]);
+    float wgt[kWaves];
+    float lam = 0.f;
+#pragma unroll
+    for (int w = 0; w < kWaves; ++w) {
+      wgt[w] = __builtin_amdgcn_exp2f(merge.m[w][h] - M);  // 0 for a wave without tokens
+      lam += merge.l[w][h] * wgt[w];
+    }
+    float out[8];
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      float x = 0.f;
+#pragma unroll
+      for (int w = 0; w < kWaves; ++w) x = fmaf(merge.acc[w][h][c * 8 + e], wgt[w], x);
+      out[e] = x;
+    }
+    const size_t row = ((size_t)b * Hq + (size_t)g * kGroup + h) * a.num_splits + s;
+    float4* dst = reinterpret_cast<float4*>(a.part_acc + row * kD + c * 8);
+    dst[0] = make_float4(out[0], out[1], out[2], out[3]);
+    dst[1] = make_float4(out[4], out[5], out[6], out[7]);
+    if (c == 0) {
+      a.part_ml[row * 2 + 0] = M;
+      a.part_ml[row * 2 + 1] = lam;
+    }
+  }
+}
+
+struct Stage2Args {
+  const uint16_t* gate;
+  const int32_t* seq_lens;
+  const float* part_acc;
+  const float* part_ml;
+  uint16_t* out;
+  int num_q_heads;
+  int tokens_per_split;
+  int num_splits;
+  int batch;
+  int capacity;  // max_pages * page size
+};
+
+// One wave per (b, h); lane owns d = 4*lane .. 4*lane+3.  4 waves per block.
+__global__ __launch_bounds__(256) void decode_stage2_gate_kernel(Stage2Args a) {
+  const int row = blockIdx.x * 4 + (threadIdx.x >> 6);  // b * H_q + h
+  if (row >= a.batch * a.num_q_heads) return;
+  const int lane = __lane_id();
+  const int b = row / a.num_q_heads;
+  const int L = min(a.seq_lens[b], a.capacity);  // same clamp as stage 1
+  uint16_t o16[4] = {0, 0, 0, 0};
+  if (L > 0) {  // L <= 0: padded slot, output +0
+    const int ns = (L + a.tokens_per_split - 1) / a.tokens_per_split;
+    const float* ml = a.part_ml + (size_t)row * a.num_splits * 2;
+    const float* pa = a.part_acc + (size_t)row * a.num_splits * kD + lane * 4;
+    float M = -INFINITY;
+    for (int s = 0; s < ns; ++s) M = fmaxf(M, ml[2 * s]);
+    float lam = 0.f;
+    float o[4] = {0.f, 0.f, 0.f, 0.f};
+    for (int s = 0; s < ns; ++s) {
+      const float w = __builtin_amdgcn_exp2f(ml[2 * s] - M);
+      lam = fmaf(ml[2 * s + 1], w, lam);
+      const float4 x = *reinterpret_cast<const float4*>(pa + (size_t)s * kD);
+      o[0] = fmaf(x.x, w, o[0]);
+      o[1] = fmaf(x.y, w, o[1]);
+      o[2] = fmaf(x.z, w, o[2]);
+      o[3] = fmaf(x.w, w, o[3]);
+    }
+    const uint2 graw = *reinterpret_cast<const uint2*>(a.gate + (size_t)row * kD + lane * 4);
+    const uint16_t gt[4] = {(uint16_t)(graw.x & 0xffff), (uint16_t)(graw.x >> 16),
+                            (uint16_t)(graw.y & 0xffff), (uint16_t)(graw.y >> 16)};
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const uint16_t ob = bf16_rne_f32(o[e] / lam);
+      o16[e] = gate_output(ob, gt[e]);
+    }
+  }
+  uint2 w;
+  w.x = (uint32_t)o16[0] | ((uint32_t)o16[1] << 16);
+  w.y = (uint32_t)o16[2] | ((uint32_t)o16[3] << 16);
+  *reinterpret_cast<uint2*>(a.out + (size_t)row * kD + lane * 4) = w;
+}
+
+hipError_t launch_decode(const DecodeLaunch& d, hipStream_t stream) {
+  Stage1Args a1;
+  a1.q = d.q;
+  a1.k_pool = d.k_pool;
+  a1.v_pool = d.v_pool;
+  a1.block_table = d.block_table;
+  a1.seq_lens = d.seq_lens;
+  a1.part_acc = d.part_acc;
+  a1.part_ml = d.part_ml;
+  a1.scale_log2 = d.scale * kLog2e;
+  a1.num_kv_heads = d.num_kv_heads;
+  a1.max_pages = d.max_pages;
+  a1.num_pages = d.num_pages;
+  a1.tokens_per_split = d.tokens_per_split;
+  a1.num_splits = d.num_splits;
+  dim3 grid1(d.num_splits, d.num_kv_heads, d.batch);
+  hipLaunchKernelGGL(decode_stage1_kernel, grid1, dim3(256), 0, stream, a1);
+  hipError_t err = hipGetLastError();
+  if (err != hipSuccess) return err;
+
+  Stage2Args a2;
+  a2.gate = d.gate;
+  a2.seq_lens = d.seq_lens;
+  a2.part_acc = d.part_acc;
+  a2.part_ml = d.part_ml;
+  a2.out = d.out;
+  a2.num_q_heads = d.num_kv_heads * kGroup;
+  a2.tokens_per_split = d.tokens_per_split;
+  a2.num_splits = d.num_splits;
+  a2.batch = d.batch;
+  a2.capacity = d.max_pages * kPage;
+  const int rows = d.batch * a2.num_q_heads;
+  hipLaunchKernelGGL(decode_stage2_gate_kernel, dim3((rows + 3) / 4), dim3(256), 0, stream, a2);
+  return hipGetLastError();
+}
+
+}  // namespace ga

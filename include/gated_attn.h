@@ -1,0 +1,140 @@
+/*
+ * gated_attn.h -- C ABI of the MI355X (gfx950) gated grouped-query attention
+ * library (libgated_attn.so).
+ *
+ * The operation (cuDNN FE-OSS "Gated Attention Block (SM107)", Overview,
+ * stages (4) and (5); FreeToken PR #781, Summary, for the bf16 rounding chain):
+ *
+ *     O   = softmax(q K^T * scale) V          fp32 accumulation on the GPU
+ *     out = bf16( bf16(O) * bf16(sigmoid(gate)) )   each rounding to nearest even
+ *
+ * with grouped-query attention: query head h reads kv head h / (H_q / H_kv).
+ * A padded slot (sequence length <= 0) produces out = +0 (ROCm/ATOM PR #838,
+ * "PAD_SLOT_ID (-1) handling"; cuDNN page, fuse_gate "dead-row select").
+ *
+ * Conventions shared by every entry point (cuDNN page, Forward: one caller-owned
+ * workspace, nothing allocated, nothing read back to the host, every stage on
+ * the one stream given; Requirements: unsupported cases are declined with a
+ * typed error rather than served slowly):
+ *   - bf16 tensors are passed as pointers to their 16-bit patterns (uint16_t).
+ *   - Every pointer is a device pointer owned by the caller.  The library never
+ *     allocates, frees, synchronises or copies device memory to the host, so a
+ *     call can be captured into a HIP graph.  Inputs are never written.
+ *   - All work is enqueued on `stream` (a hipStream_t; NULL means the null
+ *     stream).  A call returns once the work is enqueued, not when it is done.
+ *   - Every argument the host can see is checked before anything is launched;
+ *     on any status other than GA_OK nothing has been enqueued and no memory
+ *     has been touched.  Values that live only in device memory (sequence
+ *     lengths, page ids) are preconditions and are not checked.
+ *   - All tensors are dense, contiguous, row-major, and 16-byte aligned
+ *     (block_table / seq_lens: 4-byte aligned).
+ */
+#ifndef GATED_ATTN_H
+#define GATED_ATTN_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum ga_status {
+    GA_OK = 0,
+    GA_ERR_INVALID_ARGUMENT = 1,    /* null/misaligned pointer, bad size or scale */
+    GA_ERR_UNSUPPORTED = 2,         /* valid but not served: device, head dim, group size */
+    GA_ERR_WORKSPACE_TOO_SMALL = 3, /* workspace_bytes < gated_attn_decode_workspace_size() */
+    GA_ERR_HIP = 4                  /* the HIP runtime reported an error; see gated_attn_last_hip_error() */
+} ga_status;
+
+/* Shape of a paged decode call. */
+typedef struct ga_decode_dims {
+    int32_t batch;             /* B >= 0 sequences, one query token each */
+    int32_t num_q_heads;       /* H_q */
+    int32_t num_kv_heads;      /* H_kv; H_q / H_kv must be 8 */
+    int32_t head_dim;          /* D; must be 256 */
+    int32_t page_size;         /* tokens per page; must be 16 */
+    int32_t max_pages_per_seq; /* W: columns of block_table (the allocated capacity) */
+    int64_t num_pages;         /* P: pages in each of k_pool / v_pool */
+} ga_decode_dims;
+
+/* How a decode call splits each sequence (chosen from the dims alone, i.e. from
+ * the allocated capacity W * page_size and not from the current lengths, so one
+ * captured graph serves every length up to the capacity -- FreeToken PR #781,
+ * Automatic dispatch: "capacity refers to the allocated buffer"). */
+typedef struct ga_decode_plan {
+    int32_t tokens_per_split;  /* T: each (sequence, kv head, split) block covers T tokens */
+    int32_t num_splits;        /* ceil(W * page_size / T) */
+    size_t workspace_bytes;    /* fp32 partials: B * H_q * num_splits * (D + 2) * 4, rounded up */
+} ga_decode_plan;
+
+/* Fill *plan for dims.  GA_ERR_INVALID_ARGUMENT / GA_ERR_UNSUPPORTED as
+ * gated_attn_decode would return for these dims. */
+ga_status gated_attn_decode_plan(const ga_decode_dims *dims, ga_decode_plan *plan);
+
+/* Bytes of device workspace gated_attn_decode needs for dims (0 if dims are
+ * invalid or batch == 0). */
+size_t gated_attn_decode_workspace_size(const ga_decode_dims *dims);
+
+/*
+ * Gated GQA decode over a paged bf16 KV pool: split-KV partial attention
+ * (FreeToken PR #781, Summary: stage1, then a stage2 fp32 reduction) followed,
+ * in the same second kernel, by the bf16 rounding of O, the bf16 sigmoid of the
+ * gate and the rounded product -- two kernel launches per call, none of them
+ * for the gate.
+ *
+ *   q, gate     [B][H_q][D]                       bf16, read
+ *   k_pool,
+ *   v_pool      [num_pages][page_size][H_kv][D]   bf16, read
+ *   block_table [B][max_pages_per_seq]            int32 page ids, read; entries
+ *               at or past ceil(seq_lens[b] / page_size) are never read
+ *   seq_lens    [B]                               int32 KV lengths, read;
+ *               <= 0 marks a padded slot (its output row is +0)
+ *   scale       softmax scale (finite, > 0), e.g. 1/sqrt(D)
+ *   out         [B][H_q][D]                       bf16, written
+ *   workspace   >= gated_attn_decode_workspace_size(dims) bytes, 16-byte
+ *               aligned, contents need not be initialised; overwritten
+ *
+ * Preconditions in device memory (not checked): 0 <= seq_lens[b] <=
+ * max_pages_per_seq * page_size, and every block_table entry that is read is
+ * in [0, num_pages).  Concurrent calls must not share a workspace.
+ */
+ga_status gated_attn_decode(const uint16_t *q, const uint16_t *gate, const uint16_t *k_pool,
+                            const uint16_t *v_pool, const int32_t *block_table,
+                            const int32_t *seq_lens, float scale, uint16_t *out, void *stream,
+                            const ga_decode_dims *dims, void *workspace, size_t workspace_bytes);
+
+/* Shape of a dense prefill call: S_q = S_kv = seq_len. */
+typedef struct ga_prefill_dims {
+    int32_t batch;        /* B >= 0 */
+    int32_t seq_len;      /* S >= 0 */
+    int32_t num_q_heads;  /* H_q */
+    int32_t num_kv_heads; /* H_kv; H_q / H_kv must be 8 */
+    int32_t head_dim;     /* D; must be 256 */
+} ga_prefill_dims;
+
+/*
+ * Gated dense prefill attention with bf16 matrix-core (MFMA) products and the
+ * same gate epilogue (cuDNN page, Forward: fuse_gate folds stage (5) into the
+ * SDPA epilogue), one kernel launch per call.
+ *
+ *   q, gate, out  [B][S][H_q][D]   bf16 (q, gate read; out written)
+ *   k, v          [B][S][H_kv][D]  bf16, read
+ *   causal        non-zero: query i sees keys j <= i; zero: every key
+ */
+ga_status gated_attn_prefill(const uint16_t *q, const uint16_t *gate, const uint16_t *k,
+                             const uint16_t *v, float scale, int causal, uint16_t *out,
+                             void *stream, const ga_prefill_dims *dims);
+
+/* Static, human-readable name of a status. */
+const char *gated_attn_status_string(ga_status status);
+
+/* The hipError_t value behind the calling thread's most recent GA_ERR_HIP
+ * (0 if none). */
+int gated_attn_last_hip_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* GATED_ATTN_H */

@@ -1,0 +1,164 @@
+"""The C ABI on the host: symbols, split plans, and every argument check that
+returns before anything touches a GPU.  No call here reaches a launch: each
+one carries at least one invalid argument (fake device addresses are never
+dereferenced), or has batch 0.
+"""
+import ctypes
+import os
+import re
+
+import pytest
+
+import gated_gqa_decode_amd as ga
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "gated_attn.h")
+
+FAKE = 0x7f0000000000  # 16-byte aligned, never dereferenced
+
+
+def header_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(gated_attn_\w+)\s*\(", text)))
+
+
+def test_every_declared_symbol_is_exported():
+    declared = header_functions()
+    assert declared == sorted(ga.EXPORTED_SYMBOLS)
+    raw = ctypes.CDLL(ga.LIB_PATH)
+    for name in declared:
+        assert hasattr(raw, name), name
+
+
+def test_status_strings():
+    for st, name in [(0, "GA_OK"), (1, "GA_ERR_INVALID_ARGUMENT"), (2, "GA_ERR_UNSUPPORTED"),
+                     (3, "GA_ERR_WORKSPACE_TOO_SMALL"), (4, "GA_ERR_HIP")]:
+        assert ga.lib.gated_attn_status_string(st).decode() == name
+    assert ga.lib.gated_attn_last_hip_error() == 0
+
+
+def _dims(**kw):
+    base = dict(batch=64, num_q_heads=16, num_kv_heads=2, head_dim=256, page_size=16,
+                max_pages_per_seq=256, num_pages=16384)
+    base.update(kw)
+    return ga.decode_dims(**base)
+
+
+@pytest.mark.parametrize("B,W", [(1, 32), (4, 32), (64, 256), (224, 384), (2, 2048), (65535, 1),
+                                 (1, 1), (3, 100000)])
+def test_plan_covers_capacity(B, W):
+    p = ga.decode_plan(_dims(batch=B, max_pages_per_seq=W))
+    cap = W * 16
+    assert p.tokens_per_split % 32 == 0 and 32 <= p.tokens_per_split <= 1024
+    assert p.num_splits * p.tokens_per_split >= cap
+    assert (p.num_splits - 1) * p.tokens_per_split < cap
+    rows = B * 16 * p.num_splits
+    assert p.workspace_bytes >= rows * 258 * 4 and p.workspace_bytes % 256 == 0
+    assert ga.decode_workspace_size(_dims(batch=B, max_pages_per_seq=W)) == p.workspace_bytes
+
+
+def test_plan_depends_on_capacity_not_lengths():
+    a = ga.decode_plan(_dims(batch=64, max_pages_per_seq=256))
+    b = ga.decode_plan(_dims(batch=64, max_pages_per_seq=256, num_pages=1 << 30))
+    assert a == b
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(head_dim=128), ga.GA_ERR_UNSUPPORTED),
+    (dict(num_q_heads=8), ga.GA_ERR_UNSUPPORTED),          # group of 4
+    (dict(num_q_heads=32), ga.GA_ERR_UNSUPPORTED),         # group of 16
+    (dict(num_q_heads=15), ga.GA_ERR_INVALID_ARGUMENT),    # not a multiple of H_kv
+    (dict(page_size=32), ga.GA_ERR_UNSUPPORTED),
+    (dict(page_size=0), ga.GA_ERR_INVALID_ARGUMENT),
+    (dict(batch=-1), ga.GA_ERR_INVALID_ARGUMENT),
+    (dict(batch=70000), ga.GA_ERR_UNSUPPORTED),
+    (dict(num_pages=0), ga.GA_ERR_INVALID_ARGUMENT),
+    (dict(max_pages_per_seq=0), ga.GA_ERR_INVALID_ARGUMENT),
+    (dict(num_kv_heads=0), ga.GA_ERR_INVALID_ARGUMENT),
+    (dict(head_dim=0), ga.GA_ERR_INVALID_ARGUMENT),
+])
+def test_bad_dims_are_declined(kw, status):
+    d = _dims(**kw)
+    p = ga.DecodePlan()
+    assert ga.lib.gated_attn_decode_plan(ctypes.byref(d), ctypes.byref(p)) == status
+    assert ga.decode_workspace_size(d) == 0
+    st = ga.lib.gated_attn_decode(FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 0.0625, FAKE, None,
+                                  ctypes.byref(d), FAKE, 1 << 40)
+    assert st == status
+
+
+def _call(q=FAKE, gate=FAKE, k=FAKE, v=FAKE, bt=FAKE, sl=FAKE, scale=0.0625, out=FAKE,
+          ws=FAKE, wsb=1 << 40, dims=None):
+    d = dims or _dims()
+    return ga.lib.gated_attn_decode(q, gate, k, v, bt, sl, scale, out, None, ctypes.byref(d),
+                                    ws, wsb)
+
+
+@pytest.mark.parametrize("field", ["q", "gate", "k", "v", "bt", "sl", "out", "ws"])
+def test_null_pointers_are_rejected(field):
+    assert _call(**{field: None}) == ga.GA_ERR_INVALID_ARGUMENT
+
+
+@pytest.mark.parametrize("field,off", [("q", 8), ("gate", 2), ("k", 4), ("v", 8), ("out", 2),
+                                       ("ws", 4), ("bt", 2), ("sl", 1)])
+def test_misaligned_pointers_are_rejected(field, off):
+    assert _call(**{field: FAKE + off}) == ga.GA_ERR_INVALID_ARGUMENT
+
+
+@pytest.mark.parametrize("scale", [0.0, -1.0, float("inf"), float("nan")])
+def test_bad_scale_is_rejected(scale):
+    assert _call(scale=scale) == ga.GA_ERR_INVALID_ARGUMENT
+
+
+def test_small_workspace_is_rejected():
+    need = ga.decode_workspace_size(_dims())
+    assert _call(wsb=need - 1) == ga.GA_ERR_WORKSPACE_TOO_SMALL
+
+
+def test_null_dims_rejected():
+    assert ga.lib.gated_attn_decode(FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 0.0625, FAKE, None,
+                                    None, FAKE, 1 << 40) == ga.GA_ERR_INVALID_ARGUMENT
+    assert ga.lib.gated_attn_prefill(FAKE, FAKE, FAKE, FAKE, 0.0625, 1, FAKE, None,
+                                     None) == ga.GA_ERR_INVALID_ARGUMENT
+
+
+def test_empty_batch_is_a_no_op():
+    # batch 0 returns before any pointer is examined or any HIP call is made
+    assert _call(dims=_dims(batch=0), q=None, ws=None, wsb=0) == ga.GA_OK
+    d = ga.PrefillDims(0, 128, 16, 2, 256)
+    assert ga.lib.gated_attn_prefill(None, None, None, None, 0.0625, 1, None, None,
+                                     ctypes.byref(d)) == ga.GA_OK
+    d = ga.PrefillDims(2, 0, 16, 2, 256)
+    assert ga.lib.gated_attn_prefill(None, None, None, None, 0.0625, 1, None, None,
+                                     ctypes.byref(d)) == ga.GA_OK
+
+
+@pytest.mark.parametrize("dims,status", [
+    ((2, 128, 16, 2, 128), ga.GA_ERR_UNSUPPORTED),
+    ((2, 128, 16, 4, 256), ga.GA_ERR_UNSUPPORTED),
+    ((2, 128, 15, 2, 256), ga.GA_ERR_INVALID_ARGUMENT),
+    ((-1, 128, 16, 2, 256), ga.GA_ERR_INVALID_ARGUMENT),
+    ((2, -5, 16, 2, 256), ga.GA_ERR_INVALID_ARGUMENT),
+])
+def test_prefill_bad_dims(dims, status):
+    d = ga.PrefillDims(*dims)
+    assert ga.lib.gated_attn_prefill(FAKE, FAKE, FAKE, FAKE, 0.0625, 1, FAKE, None,
+                                     ctypes.byref(d)) == status
+
+
+@pytest.mark.parametrize("field", range(5))
+def test_prefill_null_or_misaligned(field):
+    d = ga.PrefillDims(2, 128, 16, 2, 256)
+    for bad in (None, FAKE + 2):
+        args = [FAKE] * 5
+        args[field] = bad
+        q, g, k, v, o = args
+        assert ga.lib.gated_attn_prefill(q, g, k, v, 0.0625, 1, o, None,
+                                         ctypes.byref(d)) == ga.GA_ERR_INVALID_ARGUMENT
+
+
+def test_prefill_bad_scale():
+    d = ga.PrefillDims(2, 128, 16, 2, 256)
+    assert ga.lib.gated_attn_prefill(FAKE, FAKE, FAKE, FAKE, float("nan"), 1, FAKE, None,
+                                     ctypes.byref(d)) == ga.GA_ERR_INVALID_ARGUMENT

@@ -1,0 +1,182 @@
+"""GPU parity of gated_attn_decode against the CPU oracle (gfx950 only).
+
+Pass criterion (the floored two-ulp rule in oracle/compare.py) on every
+element; where the computation is exact by construction (a single key,
+identical K and V rows, the gate epilogue given the same bf16 O) the GPU must
+match bit for bit.
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import workloads
+from gpu_helpers import DEV, decode_parity, gpu_decode, to_dev, to_np
+
+import gated_gqa_decode_amd as ga
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.mark.parametrize("wl", [0, 1, 2, 3])
+def test_workload_parity(wl):
+    """The four decode workloads at full size, every output element."""
+    c = workloads.workload(wl)
+    res = decode_parity(c)
+    assert res["ok"], res
+    if wl == 3:
+        pad = c.seq_lens <= 0
+        assert pad.sum() == 11
+
+
+def test_ragged_lengths_across_steps_pages_and_splits():
+    lens = [1, 2, 7, 8, 9, 15, 16, 17, 31, 32, 33, 63, 64, 65, 100, 257, 513, 640]
+    c = workloads.make_decode("ragged", lens, seed=31, max_pages_per_seq=48, extra_pages=7)
+    res = decode_parity(c)
+    assert res["ok"], res
+
+
+def test_long_sequences_largest_split():
+    """Capacity 32768 tokens at batch 64 gives the largest split (1024 tokens,
+    64 pages per workgroup)."""
+    lens = [32768, 1, 1025, 32767, 0, 4096] + [17] * 58
+    c = workloads.make_decode("long", lens, seed=32, max_pages_per_seq=2048)
+    plan = ga.decode_plan(ga.decode_dims(**c.dims))
+    assert plan.tokens_per_split == 1024
+    res = decode_parity(c)
+    assert res["ok"], res
+
+
+def test_single_key_is_bit_exact():
+    c = workloads.make_decode("L1", [1] * 24, seed=33)
+    got = gpu_decode(c)
+    ref, _, _ = oracle.decode(c.q, c.gate, c.k_pool, c.v_pool, c.block_table, c.seq_lens, c.scale)
+    assert np.array_equal(got, ref)
+
+
+def test_identical_kv_rows_are_bit_exact():
+    """Every key and value row equal: O = v exactly in fp32 as well."""
+    c = workloads.make_decode("same_kv", [1, 5, 16, 100, 700, 2000], seed=34, poison=False)
+    c.k_pool[:] = c.k_pool[0, 0]
+    c.v_pool[:] = c.v_pool[0, 0]
+    got = gpu_decode(c)
+    ref, _, _ = oracle.decode(c.q, c.gate, c.k_pool, c.v_pool, c.block_table, c.seq_lens, c.scale)
+    assert np.array_equal(got, ref)
+
+
+def test_every_gate_bit_pattern_through_the_api():
+    """L = 1 and V = 1.0: out = bf16(sigmoid(gate)) for all 65,536 gate values,
+    which must equal the oracle's correctly rounded table bit for bit."""
+    B = 16
+    c = workloads.make_decode("all_gates", [1] * B, seed=35)
+    c.v_pool[:] = 0x3F80
+    c.gate = np.arange(65536, dtype=np.uint32).astype(np.uint16).reshape(B, 16, 256)
+    got = gpu_decode(c)
+    table = oracle.sigmoid_table()
+    exp = table[c.gate]
+    nan = (exp & 0x7F80) == 0x7F80
+    nan &= (exp & 0x7F) != 0
+    assert np.array_equal(got[~nan], exp[~nan])
+    assert np.all(((got[nan] & 0x7F80) == 0x7F80) & ((got[nan] & 0x7F) != 0))
+
+
+def test_gate_epilogue_zero_and_forty():
+    """Same attention, gate 0 vs gate +40: sigma_b = 0.5 and 1.0, so the two
+    outputs differ by exactly a factor of two (the product is bit-exact given
+    the same bf16 O)."""
+    c = workloads.make_decode("gate_c", [300, 17, 4096], seed=36)
+    c.gate[:] = 0x4220
+    out40 = gpu_decode(c)
+    c.gate[:] = 0x0000
+    out0 = gpu_decode(c)
+    vals40 = oracle.compare.bf16_bits_to_f64(out40)
+    vals0 = oracle.compare.bf16_bits_to_f64(out0)
+    normal = np.abs(vals40) >= 2.0 ** -125
+    assert np.array_equal(vals0[normal], vals40[normal] / 2)
+    res = decode_parity(c, out0)
+    assert res["ok"], res
+
+
+def test_page_layout_does_not_change_bits():
+    """Contiguous pages, one shuffle, another shuffle: bit-identical outputs."""
+    lens = [512, 495, 478, 461]
+    a = workloads.make_decode("contig", lens, seed=37, shuffle=False)
+    outs = [gpu_decode(a)]
+    for seed in (1, 2):
+        perm = np.random.default_rng(seed).permutation(a.k_pool.shape[0]).astype(np.int32)
+        inv = np.empty_like(perm)
+        inv[perm] = np.arange(perm.size, dtype=np.int32)
+        b = workloads.make_decode("contig", lens, seed=37, shuffle=False)
+        b.k_pool = a.k_pool[inv].copy()
+        b.v_pool = a.v_pool[inv].copy()
+        b.block_table = np.where(a.block_table >= 0, perm[np.clip(a.block_table, 0, None)], -1)
+        outs.append(gpu_decode(b))
+    assert np.array_equal(outs[0], outs[1]) and np.array_equal(outs[0], outs[2])
+
+
+def test_batch_permutation_permutes_outputs():
+    lens = [100, 2000, 37, 0, 1500]
+    c = workloads.make_decode("perm", lens, seed=38)
+    out = gpu_decode(c)
+    order = np.array([3, 1, 4, 0, 2])
+    c.q, c.gate = c.q[order].copy(), c.gate[order].copy()
+    c.block_table, c.seq_lens = c.block_table[order].copy(), c.seq_lens[order].copy()
+    assert np.array_equal(gpu_decode(c), out[order])
+
+
+def test_padded_slots_are_positive_zero_and_nan_does_not_leak():
+    c = workloads.make_decode("pad", [0, 33, 0, 1, 4094], seed=39, extra_pages=4)
+    got = gpu_decode(c)
+    assert np.all(got[0] == 0) and np.all(got[2] == 0)
+    finite = (got & 0x7F80) != 0x7F80
+    assert finite.all()
+    assert decode_parity(c, got)["ok"]
+
+
+def test_inputs_are_not_modified_and_output_is_fully_written():
+    c = workloads.make_decode("ro", [700, 3], seed=40)
+    ins = [to_dev(x) for x in (c.q, c.gate, c.k_pool, c.v_pool, c.block_table, c.seq_lens)]
+    before = [t.clone() for t in ins]
+    out = torch.full_like(ins[0], float("nan"))
+    ga.decode(*ins, c.scale, out=out)
+    torch.cuda.synchronize()
+    for a, b in zip(ins, before):
+        assert torch.equal(a.view(torch.uint8) if a.dtype == torch.bfloat16 else a,
+                           b.view(torch.uint8) if b.dtype == torch.bfloat16 else b)
+    assert not torch.isnan(out.float()).any()
+
+
+def test_graph_replay_with_changed_inputs():
+    """Capture one call into a HIP graph with a caller-owned workspace, then
+    replay it with new q / gate / lengths; every replay equals an eager call."""
+    c = workloads.make_decode("graph", [1024, 777, 16, 2048], seed=41, max_pages_per_seq=128)
+    args = [to_dev(x) for x in (c.q, c.gate, c.k_pool, c.v_pool, c.block_table, c.seq_lens)]
+    dims = ga.decode_dims_for(args[0], args[2], args[4])
+    ws = torch.empty(ga.decode_workspace_size(dims), dtype=torch.uint8, device=DEV)
+    out = torch.empty_like(args[0])
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        ga.decode(*args, c.scale, out=out, workspace=ws)  # warm-up outside capture
+    torch.cuda.current_stream().wait_stream(s)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        ga.decode(*args, c.scale, out=out, workspace=ws)
+    rng = np.random.default_rng(5)
+    for it in range(4):
+        nq = workloads.normal_bf16(100 + it, 1, c.q.shape)
+        ng = workloads.normal_bf16(200 + it, 2, c.gate.shape, std=2.0)
+        nl = c.seq_lens.copy()
+        # a new length may only use pages the block table already holds
+        i = int(rng.integers(0, 4))
+        nl[i] = int(rng.integers(0, int(c.seq_lens[i]) + 1))
+        args[0].copy_(to_dev(nq))
+        args[1].copy_(to_dev(ng))
+        args[5].copy_(to_dev(nl))
+        graph.replay()
+        torch.cuda.synchronize()
+        replayed = to_np(out)
+        eager = to_np(ga.decode(*args, c.scale))
+        torch.cuda.synchronize()
+        assert np.array_equal(replayed, eager), it
