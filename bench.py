@@ -1,0 +1,351 @@
+#!/usr/bin/env python3
+"""Benchmark of gated GQA decode (and prefill) on one MI355X.
+
+A step is one gated_attn_decode call -- stage 1 and stage 2 with the fused
+gate, the whole decode path -- over the B=64, L=4096 paged workload (512 MiB of
+K/V), inputs resident in HBM.  ``value`` is K/V bytes per second over the timed
+steps.  The same JSON line also carries:
+  * roofline   -- the stage-1 kernel's achieved HBM rate, from HIP events
+                  recorded around every stage-1 launch of the timed steps;
+                  ``traffic`` from the committed rocprofv3 counter summary when
+                  it was taken on the current kernel source, else null;
+  * cold       -- median of single calls, each after a 1 GiB cache flush;
+  * b1_l512    -- B=1, L=512 µs/call from replays of a 4-call HIP graph;
+  * prefill    -- B=2, S=2048 causal gated prefill µs/call and MFMA rate;
+  * cpu_baseline -- the fp64 CPU oracle on the same B=64 workload.
+
+    python bench.py [--steps K] [--warmup W] [--gpus 1]
+"""
+from __future__ import annotations
+
+import argparse
+import ctypes
+import hashlib
+import json
+import os
+import statistics
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+METRIC = "gated decode attention µs/call + KV HBM GB/s (% of peak), B1/L512 and B64/L4096"
+HBM_PEAK_GBS = 8000.0          # MI355X HBM3E
+BF16_MFMA_PEAK_TFLOPS = 2500.0  # MI355X dense bf16 matrix peak
+COUNTERS = os.path.join(ROOT, "profiles", "decode_stage1_b64_l4096_counters.json")
+KERNEL_SOURCES = ["gated_gqa_decode_amd/csrc/decode.hip", "gated_gqa_decode_amd/csrc/ga_device.h",
+                  "gated_gqa_decode_amd/csrc/ga_internal.h", "gated_gqa_decode_amd/csrc/capi.cpp"]
+
+
+def kernel_source_hash() -> str:
+    h = hashlib.sha256()
+    for rel in KERNEL_SOURCES:
+        with open(os.path.join(ROOT, rel), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()
+
+
+def parse_args():
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-extras", action="store_true",
+                    help="only the timed decode steps (cold, B1, prefill, CPU legs skipped)")
+    ap.add_argument("--calibration-copy", action="store_true",
+                    help="also run one plain 1 GiB device copy (counter calibration)")
+    ap.add_argument("--json-out", default=None)
+    return ap.parse_args()
+
+
+class Hip:
+    """The few HIP event calls the timing needs, from the runtime torch loaded."""
+
+    def __init__(self):
+        import torch  # noqa: F401  (loads the runtime this binds to)
+
+        self.lib = ctypes.CDLL("libamdhip64.so.7")
+        self.lib.hipEventCreate.argtypes = [ctypes.POINTER(ctypes.c_void_p)]
+        self.lib.hipEventElapsedTime.argtypes = [ctypes.POINTER(ctypes.c_float), ctypes.c_void_p,
+                                                 ctypes.c_void_p]
+        self.lib.hipEventDestroy.argtypes = [ctypes.c_void_p]
+
+    def events(self, n):
+        out = []
+        for _ in range(n):
+            e = ctypes.c_void_p()
+            if self.lib.hipEventCreate(ctypes.byref(e)) != 0:
+                raise RuntimeError("hipEventCreate failed")
+            out.append(e.value)
+        return out
+
+    def elapsed_ms(self, a, b) -> float:
+        ms = ctypes.c_float()
+        if self.lib.hipEventElapsedTime(ctypes.byref(ms), ctypes.c_void_p(a), ctypes.c_void_p(b)) != 0:
+            raise RuntimeError("hipEventElapsedTime failed")
+        return float(ms.value)
+
+    def destroy(self, evs):
+        for e in evs:
+            self.lib.hipEventDestroy(ctypes.c_void_p(e))
+
+
+def to_dev(a, dev):
+    import numpy as np
+    import torch
+
+    t = torch.from_numpy(np.ascontiguousarray(a))
+    if a.dtype == np.uint16:
+        t = t.view(torch.int16).view(torch.bfloat16)
+    return t.to(dev)
+
+
+class DecodeCall:
+    """Pre-marshalled arguments of one gated_attn_decode call (raw C entry)."""
+
+    def __init__(self, ga, case, dev):
+        import torch
+
+        self.ga = ga
+        self.t = [to_dev(x, dev) for x in (case.q, case.gate, case.k_pool, case.v_pool,
+                                          case.block_table, case.seq_lens)]
+        self.dims = ga.decode_dims(**case.dims)
+        self.plan = ga.decode_plan(self.dims)
+        self.ws = torch.empty(max(self.plan.workspace_bytes, 16), dtype=torch.uint8, device=dev)
+        self.out = torch.empty_like(self.t[0])
+        self.scale = ctypes.c_float(case.scale)
+        self.stream = ctypes.c_void_p(torch.cuda.current_stream(dev).cuda_stream)
+        self.args = [ctypes.c_void_p(x.data_ptr()) for x in self.t]
+        self.outp = ctypes.c_void_p(self.out.data_ptr())
+        self.wsp = ctypes.c_void_p(self.ws.data_ptr())
+        self.wsb = ctypes.c_size_t(self.ws.numel())
+        self.dref = ctypes.byref(self.dims)
+        self.fn = ga.lib.gated_attn_decode
+
+    def __call__(self):
+        st = self.fn(*self.args, self.scale, self.outp, self.stream, self.dref, self.wsp, self.wsb)
+        if st != 0:
+            self.ga.check(st, "gated_attn_decode")
+
+
+def main() -> int:
+    args = parse_args()
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print(f"bench.py measures one GPU only (asked for --gpus {args.gpus}, WORLD_SIZE {world}): "
+              "this build has no multi-GPU path; decode shards by sequence or kv head with no "
+              "exchange, so the per-GPU rate is the number to read.", file=sys.stderr)
+        return 2
+
+    import numpy as np
+    import torch
+
+    import gated_gqa_decode_amd as ga
+    import workloads
+
+    dev = torch.device("cuda:0")
+    hip = Hip()
+    K, W = args.steps, args.warmup
+
+    # ---------------- headline: B=64, L=4096 paged decode --------------------
+    t_gen = time.time()
+    case = workloads.workload(2, poison=False)
+    gen_s = time.time() - t_gen
+    kv_bytes = case.kv_bytes()
+    call = DecodeCall(ga, case, dev)
+    torch.cuda.synchronize()
+
+    if args.calibration_copy:
+        src = torch.empty(1 << 30, dtype=torch.uint8, device=dev).fill_(1)
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        dst.copy_(src)  # plain copy kernel: reads 1 GiB, writes 1 GiB
+        torch.cuda.synchronize()
+        del src, dst
+
+    for _ in range(W):
+        call()
+    torch.cuda.synchronize()
+
+    starts, stops = hip.events(K), hip.events(K)
+    arr_s = (ctypes.c_void_p * K)(*starts)
+    arr_e = (ctypes.c_void_p * K)(*stops)
+    ga.check(ga.lib.gated_attn_decode_time_stage1(arr_s, arr_e, K), "time_stage1")
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    e0.record()
+    for _ in range(K):
+        call()
+    e1.record()
+    torch.cuda.synchronize()
+    ga.check(ga.lib.gated_attn_decode_time_stage1(None, None, 0), "time_stage1")
+    total_ms = e0.elapsed_time(e1)
+    stage1_ms = [hip.elapsed_ms(a, b) for a, b in zip(starts, stops)]
+    hip.destroy(starts + stops)
+
+    ms_per_step = total_ms / K
+    value = kv_bytes / (ms_per_step * 1e-3) / 1e9
+    s1_mean = statistics.fmean(stage1_ms)
+    achieved = kv_bytes / (s1_mean * 1e-3) / 1e9
+    traffic = None
+    counters = None
+    if os.path.exists(COUNTERS):
+        with open(COUNTERS) as f:
+            counters = json.load(f)
+        if counters.get("kernel_sources_sha256") == kernel_source_hash():
+            traffic = counters.get("hbm_bytes_per_launch")
+
+    result = {
+        "metric": METRIC,
+        "value": round(value, 2),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": K,
+        "warmup": W,
+        "ms_per_step": round(ms_per_step, 6),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "accumulate_dtype": "fp32",
+        "data": "synthetic",
+        "config": {
+            "workload": "gated GQA decode B=64 L=4096, paged bf16 KV (16-token pages, shuffled), "
+                        "H_q=16 H_kv=2 D=256",
+            "batch": 64, "kv_len": 4096, "num_q_heads": 16, "num_kv_heads": 2, "head_dim": 256,
+            "page_size": 16, "tokens_per_split": call.plan.tokens_per_split,
+            "num_splits": call.plan.num_splits,
+        },
+        "us_per_call": round(ms_per_step * 1e3, 3),
+        "kv_bytes_per_call": kv_bytes,
+        "hbm_frac": round(value / HBM_PEAK_GBS, 4),
+        "launches_per_call": 2,
+        "roofline": {
+            "kernel": "decode_stage1_kernel",
+            "bound": "hbm",
+            "achieved": round(achieved, 2),
+            "peak": HBM_PEAK_GBS,
+            "unit": "GB/s",
+            "frac": round(achieved / HBM_PEAK_GBS, 4),
+            "traffic": traffic,
+            "algorithmic_bytes_per_launch": kv_bytes,
+            "avg_launch_us": round(s1_mean * 1e3, 3),
+            "launches_timed": K,
+        },
+    }
+
+    if not args.no_extras:
+        # ---- cold: each call after a 1 GiB flush (outside the timed span) ----
+        flush = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
+        cold = []
+        for _ in range(31):
+            flush.fill_(0)
+            a = torch.cuda.Event(enable_timing=True)
+            b = torch.cuda.Event(enable_timing=True)
+            a.record()
+            call()
+            b.record()
+            torch.cuda.synchronize()
+            cold.append(a.elapsed_time(b))
+        del flush
+        cold_ms = statistics.median(cold)
+        result["cold"] = {"us_per_call": round(cold_ms * 1e3, 3),
+                          "gbs": round(kv_bytes / (cold_ms * 1e-3) / 1e9, 2),
+                          "hbm_frac": round(kv_bytes / (cold_ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+                          "samples": 31, "flush_bytes": 1 << 30}
+
+        # ---- B=1, L=512: replays of a graph of 4 calls (launch-bound) -------
+        small = workloads.workload(0, poison=False)
+        sc = DecodeCall(ga, small, dev)
+        s = torch.cuda.Stream()
+        s.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(s):
+            sc.stream = ctypes.c_void_p(s.cuda_stream)
+            sc()
+        torch.cuda.current_stream().wait_stream(s)
+        torch.cuda.synchronize()
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            sc.stream = ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+            for _ in range(4):
+                sc()
+        for _ in range(10):
+            g.replay()
+        torch.cuda.synchronize()
+        samples = []
+        for _ in range(7):
+            a = torch.cuda.Event(enable_timing=True)
+            b = torch.cuda.Event(enable_timing=True)
+            a.record()
+            for _ in range(50):
+                g.replay()
+            b.record()
+            torch.cuda.synchronize()
+            samples.append(a.elapsed_time(b) * 1e3 / 200)
+        us = statistics.median(samples)
+        result["b1_l512"] = {"us_per_call": round(us, 3),
+                             "kv_gbs": round(small.kv_bytes() / (us * 1e-6) / 1e9, 2),
+                             "method": "HIP graph of 4 calls, 50 replays per sample, median of 7",
+                             "samples_us": [round(x, 3) for x in samples]}
+        del g
+
+        # ---- prefill B=2, S=2048 causal --------------------------------------
+        p = workloads.workload(4)
+        pt = [to_dev(x, dev) for x in (p.q, p.gate, p.k, p.v)]
+        pout = torch.empty_like(pt[0])
+        for _ in range(3):
+            ga.prefill(*pt, p.scale, causal=True, out=pout)
+        torch.cuda.synchronize()
+        a = torch.cuda.Event(enable_timing=True)
+        b = torch.cuda.Event(enable_timing=True)
+        n_p = 20
+        a.record()
+        for _ in range(n_p):
+            ga.prefill(*pt, p.scale, causal=True, out=pout)
+        b.record()
+        torch.cuda.synchronize()
+        pms = a.elapsed_time(b) / n_p
+        B, S, Hq, D = p.q.shape
+        flops = 4.0 * D * Hq * B * S * (S + 1) / 2
+        tflops = flops / (pms * 1e-3) / 1e12
+        result["prefill"] = {"workload": "gated causal prefill B=2 S=2048 H_q=16 H_kv=2 D=256",
+                             "us_per_call": round(pms * 1e3, 3),
+                             "algorithmic_flop": flops,
+                             "tflops": round(tflops, 2),
+                             "mfma_bf16_frac": round(tflops / BF16_MFMA_PEAK_TFLOPS, 4),
+                             "note": "P is split into two bf16 terms, so the kernel issues 1.5x "
+                                     "the algorithmic MFMA work"}
+
+    if not args.no_cpu_baseline and not args.no_extras:
+        import oracle
+
+        # The oracle as it stands, on the same B=64 workload, repeated until
+        # about 12 thread-seconds of CPU work have been done.
+        threads = oracle.default_threads()
+        reps, busy = 0, 0.0
+        t = time.time()
+        while reps == 0 or busy * threads < 12.0:
+            oracle.decode(case.q, case.gate, case.k_pool, case.v_pool, case.block_table,
+                          case.seq_lens, case.scale, nthreads=threads)
+            reps += 1
+            busy = time.time() - t
+        result["cpu_baseline"] = {"value": round(reps * kv_bytes / busy / 1e9, 4), "unit": "GB/s",
+                                  "cores": threads, "kind": "oracle",
+                                  "sample": f"the whole B=64 L=4096 workload, {reps} call(s) "
+                                            f"({busy:.2f} s wall, fp64, {threads} threads)",
+                                  "seconds_per_call": round(busy / reps, 3)}
+    result["input_generation_s"] = round(gen_s, 2)
+    line = json.dumps(result)
+    print(line, flush=True)
+    if args.json_out:
+        with open(args.json_out, "w") as f:
+            f.write(line + "\n")
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

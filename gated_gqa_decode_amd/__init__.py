@@ -33,6 +33,7 @@ EXPORTED_SYMBOLS = (
     "gated_attn_decode_plan",
     "gated_attn_decode_workspace_size",
     "gated_attn_decode",
+    "gated_attn_decode_time_stage1",
     "gated_attn_prefill",
     "gated_attn_status_string",
     "gated_attn_last_hip_error",
@@ -92,6 +93,9 @@ def _load_library() -> ctypes.CDLL:
     lib.gated_attn_prefill.restype = ctypes.c_int
     lib.gated_attn_prefill.argtypes = [vp, vp, vp, vp, ctypes.c_float, ctypes.c_int, vp, vp,
                                        ctypes.POINTER(PrefillDims)]
+    lib.gated_attn_decode_time_stage1.restype = ctypes.c_int
+    lib.gated_attn_decode_time_stage1.argtypes = [ctypes.POINTER(ctypes.c_void_p),
+                                                  ctypes.POINTER(ctypes.c_void_p), ctypes.c_int]
     lib.gated_attn_status_string.restype = ctypes.c_char_p
     lib.gated_attn_status_string.argtypes = [ctypes.c_int]
     lib.gated_attn_last_hip_error.restype = ctypes.c_int

@@ -24,6 +24,8 @@ struct DecodeLaunch {
   long long num_pages;
   int tokens_per_split;
   int num_splits;
+  hipEvent_t stage1_start;  // recorded around stage 1 when non-null
+  hipEvent_t stage1_stop;
 };
 
 struct PrefillLaunch {

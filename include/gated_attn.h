@@ -97,12 +97,23 @@ size_t gated_attn_decode_workspace_size(const ga_decode_dims *dims);
  *
  * Preconditions in device memory (not checked): 0 <= seq_lens[b] <=
  * max_pages_per_seq * page_size, and every block_table entry that is read is
- * in [0, num_pages).  Concurrent calls must not share a workspace.
+ * in [0, num_pages).  A violation gives an unspecified output row, never an
+ * access outside the buffers: the kernels clamp lengths to the capacity and
+ * page ids into [0, num_pages).  Concurrent calls must not share a workspace.
  */
 ga_status gated_attn_decode(const uint16_t *q, const uint16_t *gate, const uint16_t *k_pool,
                             const uint16_t *v_pool, const int32_t *block_table,
                             const int32_t *seq_lens, float scale, uint16_t *out, void *stream,
                             const ga_decode_dims *dims, void *workspace, size_t workspace_bytes);
+
+/* Measurement hook for benchmarks and profilers.  Arms the calling thread's
+ * next n gated_attn_decode calls: the i-th of them records starts[i] on its
+ * stream immediately before its stage-1 kernel and stops[i] immediately after
+ * it, so hipEventElapsedTime(starts[i], stops[i]) is that kernel's duration.
+ * The events (hipEvent_t) are created, owned and destroyed by the caller and
+ * must stay valid until recorded.  n == 0 disarms.  Results are unaffected.
+ * GA_ERR_INVALID_ARGUMENT for n < 0, or n > 0 with a NULL array. */
+ga_status gated_attn_decode_time_stage1(void *const *starts, void *const *stops, int n);
 
 /* Shape of a dense prefill call: S_q = S_kv = seq_len. */
 typedef struct ga_prefill_dims {

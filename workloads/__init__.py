@@ -6,9 +6,9 @@ lengths); it performs none of the attention arithmetic and imports neither the
 GPU package nor the oracle.
 
 Value recipe (the same for every workload): q, K, V ~ N(0, 1) and gate ~ N(0, 2)
-(standard deviation 2), drawn in float32 from numpy's PCG64 with one
-``SeedSequence([seed, stream])`` per tensor, then rounded to bf16 by torch's
-float32 -> bfloat16 conversion.  The rounding of the inputs does not affect
+(standard deviation 2), drawn in float32 from numpy's PCG64 -- chunk i of the
+tensor with stream id s comes from ``SeedSequence([seed, s, i])`` -- then
+rounded to bf16 by torch's float32 -> bfloat16 conversion.  The rounding of the inputs does not affect
 parity: the GPU and the oracle receive the identical bits.
 
 Paged layout: pools are [num_pages][16][H_kv][D]; sequence b owns
@@ -21,6 +21,7 @@ that reads past a sequence's end produces NaN instead of a plausible number.
 from __future__ import annotations
 
 import dataclasses
+import os
 from typing import Optional, Sequence
 
 import numpy as np
@@ -43,17 +44,33 @@ def _f32_to_bf16_bits(x: np.ndarray) -> np.ndarray:
     return t.to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16).copy()
 
 
-def normal_bf16(seed: int, stream: int, shape, std: float = 1.0, chunk: int = 1 << 24) -> np.ndarray:
-    """bf16 bits of N(0, std^2) draws, generated in chunks to bound memory."""
-    rng = _rng(seed, stream)
+def normal_bf16(seed: int, stream: int, shape, std: float = 1.0, chunk: int = 1 << 22) -> np.ndarray:
+    """bf16 bits of N(0, std^2) draws.
+
+    The array is cut into fixed chunks; chunk i comes from its own generator
+    SeedSequence([seed, stream, i]), so the values do not depend on how many
+    threads fill them (generation runs on a small thread pool)."""
     n = int(np.prod(shape)) if len(shape) else 1
     out = np.empty(n, dtype=np.uint16)
-    for s in range(0, n, chunk):
-        e = min(n, s + chunk)
+
+    def fill(i: int) -> None:
+        s, e = i * chunk, min(n, (i + 1) * chunk)
+        rng = np.random.Generator(np.random.PCG64(np.random.SeedSequence([int(seed), int(stream), i])))
         x = rng.standard_normal(e - s, dtype=np.float32)
         if std != 1.0:
             x *= np.float32(std)
         out[s:e] = _f32_to_bf16_bits(x)
+
+    nchunks = (n + chunk - 1) // chunk
+    if nchunks <= 1:
+        for i in range(nchunks):
+            fill(i)
+    else:
+        from concurrent.futures import ThreadPoolExecutor
+
+        workers = max(1, min(16, len(os.sched_getaffinity(0))))
+        with ThreadPoolExecutor(workers) as ex:
+            list(ex.map(fill, range(nchunks)))
     return out.reshape(shape)
 
 
