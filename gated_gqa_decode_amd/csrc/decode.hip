@@ -40,6 +40,7 @@ constexpr int kPage = 16;        // tokens per page
 constexpr int kStep = 8;         // tokens per wave step
 constexpr int kWaves = 4;        // waves per stage-1 workgroup
 constexpr float kLog2e = 1.4426950408889634f;
+constexpr float kSlack = 8.f;    // lazy-rescale threshold, log2 units
 
 struct Stage1Args {
   const uint16_t* q;
@@ -135,7 +136,7 @@ __global__ __launch_bounds__(256, 2) void decode_stage1_kernel(Stage1Args a) {
   for (int h = 0; h < kGroup; ++h)
 #pragma unroll
     for (int e = 0; e < 4; ++e) acc[h][e] = 0.f;
-  float m_run = -INFINITY;  // running max (log2 units) of head hs
+  float m_run = -INFINITY;  // reference max (log2 units) of head hs
   float l_run = 0.f;        // this lane's share of the running sum of head hs
 
   const int n_steps = (tok_end - tok_begin + kStep - 1) / kStep;
@@ -210,35 +211,41 @@ __global__ __launch_bounds__(256, 2) void decode_stage1_kernel(Stage1Args a) {
       sc[pass] = (t < tok_end) ? mine * a.scale_log2 : -INFINITY;
     }
     // ---- online softmax for head hs ----------------------------------------
-    float mx = fmaxf(sc[0], sc[1]);
-    mx = fmaxf(mx, shfl_xor(mx, 16));
-    mx = fmaxf(mx, shfl_xor(mx, 32));
-    const float m_new = fmaxf(m_run, mx);
-    const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
-    const float p0 = __builtin_amdgcn_exp2f(sc[0] - m_new);
-    const float p1 = __builtin_amdgcn_exp2f(sc[1] - m_new);
-    l_run = l_run * alpha + (p0 + p1);
-    m_run = m_new;
+    // Lazy rescaling: probabilities are taken relative to a reference max
+    // m_run that is only raised (with a rescale of l and acc) when some score
+    // of the step exceeds it by more than kSlack (log2 units), i.e. when a
+    // probability would exceed 2^kSlack.  On the common path there is then no
+    // cross-lane max and no rescale; any reference gives the same O, and
+    // probabilities stay in [0, 2^kSlack].
+    const bool raise = (sc[0] > m_run + kSlack) || (sc[1] > m_run + kSlack);
+    if (__builtin_amdgcn_ballot_w64(raise) != 0) {  // wave-uniform
+      float mx = fmaxf(sc[0], sc[1]);
+      mx = fmaxf(mx, shfl_xor(mx, 16));
+      mx = fmaxf(mx, shfl_xor(mx, 32));
+      const float m_new = fmaxf(m_run, mx);
+      const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
+      l_run *= alpha;
+      m_run = m_new;
+      if ((c16 & 1) == 0 && tq == 0) ws.alpha[hs] = alpha;
+      wave_lds_sync();
+      const float4 al0 = *reinterpret_cast<const float4*>(&ws.alpha[0]);
+      const float4 al1 = *reinterpret_cast<const float4*>(&ws.alpha[4]);
+      const float al[kGroup] = {al0.x, al0.y, al0.z, al0.w, al1.x, al1.y, al1.z, al1.w};
+#pragma unroll
+      for (int h = 0; h < kGroup; ++h)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) acc[h][e] *= al[h];
+    }
+    const float p0 = __builtin_amdgcn_exp2f(sc[0] - m_run);
+    const float p1 = __builtin_amdgcn_exp2f(sc[1] - m_run);
+    l_run += p0 + p1;
     if ((c16 & 1) == 0) {  // odd lanes hold the same (token, head) as their even neighbour
       ws.p[tq][hs] = p0;
       ws.p[4 + tq][hs] = p1;
-      if (tq == 0) ws.alpha[hs] = alpha;
     }
     wave_lds_sync();
     // ---- values ------------------------------------------------------------
     {
-      const float4 al0 = *reinterpret_cast<const float4*>(&ws.alpha[0]);
-      const float4 al1 = *reinterpret_cast<const float4*>(&ws.alpha[4]);
-      const float al[kGroup] = {al0.x, al0.y, al0.z, al0.w, al1.x, al1.y, al1.z, al1.w};
-      bool rescale = false;
-#pragma unroll
-      for (int h = 0; h < kGroup; ++h) rescale |= (al[h] != 1.f);
-      if (rescale) {  // same decision in every lane: al[] is the wave's LDS copy
-#pragma unroll
-        for (int h = 0; h < kGroup; ++h)
-#pragma unroll
-          for (int e = 0; e < 4; ++e) acc[h][e] *= al[h];
-      }
       uint2 vv[kStep];
 #pragma unroll
       for (int t = 0; t < kStep; ++t) vv[t] = r.v[t];
