@@ -8,18 +8,26 @@
 // the one of FreeToken PR #781, Summary.
 //
 // Workgroup = (16 query positions, kv head g, sequence b); 8 waves, wave w is
-// query head 8g + w, so every K/V tile staged in LDS feeds 8 heads x 16 rows.
-// Per 64-key tile and wave:
-//   S (16x64)  = Q K^T   : 4 column tiles x 8 k-steps of v_mfma_f32_16x16x32_bf16
-//   online softmax in fp32 on the accumulator layout
-//   P = Phi + Plo, two bf16 values per fp32 probability (~16 significant bits)
-//              -> per-wave LDS tiles, re-read in the MFMA A-operand layout
-//   O (16x256) += Phi V + Plo V : 16 column tiles x 2 k-steps x 2; V is stored transposed
-//                          in LDS so each lane's 8 keys of one column are
-//                          contiguous.
-// MFMA 16x16x32 operand layout (wave64): A row i = lane % 16, k = 8*(lane/16)
-// + 0..7; B column j = lane % 16, same k; C row = 4*(lane/16) + r, column =
-// lane % 16, r = 0..3.
+// query head 8g + w, so every 64-key K/V tile staged in LDS feeds 8 heads x 16
+// rows.  Tiles are double-buffered in LDS; the next tile's global loads are in
+// flight (in registers) while the current one is computed.
+//
+// MFMA v_mfma_f32_16x16x32_bf16 operand layout (wave64): A row = lane % 16,
+// k = 8*(lane/16) + 0..7; B column = lane % 16, same k; C row = 4*(lane/16) + r,
+// column = lane % 16, r = 0..3.  Per tile and wave:
+//   S^T (64 keys x 16 rows) = K Q^T : 4 key tiles x 8 k-steps.  Computing the
+//        transpose leaves each lane 4 consecutive keys of one query row, which
+//        is already the A-operand layout of P for the P V product (k-slot
+//        order: keys 4*(lane/16)+0..3 of two neighbouring key tiles).
+//   online softmax in fp32 on that layout (lazy rescaling, see decode.hip);
+//   P = Phi + Plo, two bf16 values per fp32 probability (~16 significant bits);
+//   O (16 rows x 256) += Phi V + Plo V : 16 column tiles x 2 k-steps x 2.  The
+//        B operand (4 consecutive keys of one V column per lane and read) comes
+//        straight from row-major V in LDS through the gfx950 transpose read
+//        ds_read_b64_tr_b16: within a 16-lane group, lane i of the result gets
+//        element (i % 4) of the source lane 4k + i/4 in slot k, so source lane
+//        s points at V[key0 + s/4][d0 + 4*(s % 4)] and result lane i receives
+//        V[key0 + k][d0 + i], k = 0..3.
 #include <hip/hip_runtime.h>
 #include <math.h>
 #include <stdint.h>
@@ -35,13 +43,16 @@ constexpr int kD = 256;
 constexpr int kGroup = 8;
 constexpr int kBM = 16;    // query positions per workgroup
 constexpr int kBN = 64;    // keys per tile
-constexpr int kKRow = kD + 8;     // K row stride in LDS (bf16): +16 B breaks bank aliasing
-constexpr int kVRow = kBN + 8;    // V^T row stride in LDS (bf16)
-constexpr int kPRow = kBN + 8;    // P row stride in LDS (bf16)
+constexpr int kKRow = kD + 8;    // K row stride in LDS (bf16 elements): +16 B
+constexpr int kVRow = kD + 16;   // V row stride in LDS (bf16 elements): +32 B
+constexpr int kThreads = 512;
 constexpr float kLog2e = 1.4426950408889634f;
+constexpr float kSlack = 8.f;  // lazy-rescale threshold, log2 units
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef short s16x4 __attribute__((ext_vector_type(4)));
+typedef s16x4 __attribute__((address_space(3))) lds_s16x4;
 
 struct PrefillArgs {
   const uint16_t* q;
@@ -53,195 +64,254 @@ struct PrefillArgs {
   int causal;
   int seq_len;
   int num_kv_heads;
+  int batch;
   int num_m_tiles;
+};
+
+// Workgroup order.  Workgroups are dispatched round-robin over the 8 XCDs of
+// an MI355X, each with its own L2.  Every query tile of one (sequence, kv
+// head) slice re-reads that slice's K/V, so the slices are pinned to XCDs
+// (8 / slices XCDs per slice, or slices / 8 slices per XCD) to keep a slice's
+// K/V in one L2, and within an XCD the heaviest causal tiles (latest query
+// positions) go first.  Returns false for the few padding ids of the grid.
+constexpr int kXcds = 8;
+
+__device__ __forceinline__ bool map_workgroup(const PrefillArgs& a, int id, int& mt, int& g, int& b) {
+  const int slices = a.batch * a.num_kv_heads;
+  const int nm = a.num_m_tiles;
+  int slice, slot;
+  const int xcd = id % kXcds, k = id / kXcds;
+  if (slices <= kXcds && kXcds % slices == 0) {
+    const int per = kXcds / slices;  // XCDs per slice
+    slice = xcd / per;
+    slot = k * per + xcd % per;
+  } else if (slices % kXcds == 0) {
+    const int per = slices / kXcds;  // slices per XCD
+    slice = xcd * per + k % per;
+    slot = k / per;
+  } else {  // no even split: heaviest first across all slices
+    slice = id % slices;
+    slot = id / slices;
+  }
+  if (slot >= nm) return false;
+  mt = nm - 1 - slot;
+  g = slice % a.num_kv_heads;
+  b = slice / a.num_kv_heads;
+  return true;
+}
+
+// Grid size for map_workgroup: every (slice, m tile) pair gets an id.
+__host__ __forceinline__ int grid_size(int slices, int nm) {
+  if (slices <= kXcds && kXcds % slices == 0) {
+    const int per = kXcds / slices;
+    return kXcds * ((nm + per - 1) / per);
+  }
+  if (slices % kXcds == 0) return kXcds * (slices / kXcds) * nm;
+  return slices * nm;
+}
+
+struct alignas(16) TileBuf {
+  uint16_t k[kBN * kKRow];
+  uint16_t v[kBN * kVRow];
 };
 
 __device__ __forceinline__ bf16x8 as_bf16x8(uint4 u) { return __builtin_bit_cast(bf16x8, u); }
 
-__device__ __forceinline__ float rowmax16(float v) {
-  v = fmaxf(v, dpp<kDppXor1>(v));
-  v = fmaxf(v, dpp<kDppXor2>(v));
-  v = fmaxf(v, dpp<kDppHalfMirror>(v));
-  v = fmaxf(v, dpp<kDppMirror>(v));
-  return v;
+// p must point into LDS (8-byte aligned).
+__device__ __forceinline__ uint2 tr_read(const uint16_t* p) {
+  const s16x4 r = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(p));
+  return __builtin_bit_cast(uint2, r);
+}
+
+__device__ __forceinline__ uint32_t pack2(uint16_t lo, uint16_t hi) {
+  return (uint32_t)lo | ((uint32_t)hi << 16);
 }
 
 }  // namespace
 
-__global__ __launch_bounds__(512) void prefill_gate_kernel(PrefillArgs a) {
-  __shared__ uint16_t ks[kBN * kKRow];          // K tile  [key][d]
-  __shared__ uint16_t vts[kD * kVRow];          // V tile transposed [d][key]
-  __shared__ uint16_t ps[kGroup][2][kBM * kPRow];  // per-wave P hi/lo [row][key]
+__global__ __launch_bounds__(kThreads) void prefill_gate_kernel(PrefillArgs a) {
+  __shared__ TileBuf buf[2];
 
-  // heaviest (latest) query tiles first under the causal mask
-  const int mt = a.num_m_tiles - 1 - (int)blockIdx.x;
-  const int g = blockIdx.y;
-  const int b = blockIdx.z;
+  int mt, g, b;
+  if (!map_workgroup(a, (int)blockIdx.x, mt, g, b)) return;
   const int S = a.seq_len;
   const int Hkv = a.num_kv_heads;
   const int Hq = Hkv * kGroup;
-  const int wave = threadIdx.x >> 6;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int lane = __lane_id();
   const int h = g * kGroup + wave;
   const int p0 = mt * kBM;
 
-  const int li = lane & 15;   // A row / B column / C column
-  const int lk = lane >> 4;   // k group (8 values) / C row group (4 rows)
+  const int li = lane & 15;  // query row of this lane's S^T column / MFMA column
+  const int lg = lane >> 4;  // lane group: k-slot block / C row block
 
-  // Q fragments: row p0 + li, d = 32*kstep + 8*lk .. +7
+  // Q fragments (B operand of K Q^T): row p0 + li, d = 32*ks + 8*lg .. +7
   bf16x8 qf[8];
   {
     const int pos = min(p0 + li, S - 1);
     const uint16_t* qrow = a.q + (((size_t)b * S + pos) * Hq + h) * kD;
 #pragma unroll
-    for (int s = 0; s < 8; ++s) qf[s] = as_bf16x8(*reinterpret_cast<const uint4*>(qrow + 32 * s + 8 * lk));
+    for (int s = 0; s < 8; ++s)
+      qf[s] = as_bf16x8(*reinterpret_cast<const uint4*>(qrow + 32 * s + 8 * lg));
   }
 
-  f32x4 o[16];
+  f32x4 o[16];  // O[row 4*lg + r][d = 16*t + li]
 #pragma unroll
   for (int t = 0; t < 16; ++t) o[t] = f32x4{0.f, 0.f, 0.f, 0.f};
-  float m_run[4], l_run[4];
-#pragma unroll
-  for (int r = 0; r < 4; ++r) {
-    m_run[r] = -INFINITY;
-    l_run[r] = 0.f;
-  }
+  float m_ref = -INFINITY;  // reference max (log2 units) of row li
+  float l_row = 0.f;        // this lane's share of the sum of row li
 
+  const int qi = p0 + li;
   const int kv_end = a.causal ? min(S, p0 + kBM) : S;
   const int n_tiles = (kv_end + kBN - 1) / kBN;
   const size_t kv_row_stride = (size_t)Hkv * kD;
   const uint16_t* kbase = a.k + ((size_t)b * S * Hkv + g) * kD;
   const uint16_t* vbase = a.v + ((size_t)b * S * Hkv + g) * kD;
 
-  for (int kt = 0; kt < n_tiles; ++kt) {
+  // staging: thread covers 16-byte pieces idx = it*512 + tid of each 64 x 256 tile
+  uint4 sk[4], sv[4];
+  auto load_tile = [&](int kt) {
     const int j0 = kt * kBN;
-    __syncthreads();  // previous tile fully consumed
-    // ---- stage K (row-major) and V (transposed) for keys j0 .. j0+63 -------
-    // K: a wave reads two whole 512-byte rows per instruction.
 #pragma unroll
     for (int it = 0; it < 4; ++it) {
-      const int idx = it * 512 + threadIdx.x;  // 2048 16-byte pieces per tile
+      const int idx = it * kThreads + threadIdx.x;
       const int key = idx >> 5;
       const int c = idx & 31;
-      uint4 kv4 = make_uint4(0, 0, 0, 0);
-      if (j0 + key < kv_end)
-        kv4 = *reinterpret_cast<const uint4*>(kbase + (size_t)(j0 + key) * kv_row_stride + c * 8);
-      *reinterpret_cast<uint4*>(&ks[key * kKRow + c * 8]) = kv4;
-    }
-    // V: consecutive lanes take consecutive keys of one 16-byte column chunk, so
-    // the transposed 2-byte LDS writes of a wave land in consecutive addresses.
-#pragma unroll
-    for (int it = 0; it < 4; ++it) {
-      const int idx = it * 512 + threadIdx.x;
-      const int key = idx & 63;
-      const int c = idx >> 6;
-      uint4 vv4 = make_uint4(0, 0, 0, 0);
-      if (j0 + key < kv_end)
-        vv4 = *reinterpret_cast<const uint4*>(vbase + (size_t)(j0 + key) * kv_row_stride + c * 8);
-      const uint32_t w[4] = {vv4.x, vv4.y, vv4.z, vv4.w};
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        vts[(c * 8 + 2 * e) * kVRow + key] = (uint16_t)(w[e] & 0xffff);
-        vts[(c * 8 + 2 * e + 1) * kVRow + key] = (uint16_t)(w[e] >> 16);
+      sk[it] = make_uint4(0, 0, 0, 0);
+      sv[it] = make_uint4(0, 0, 0, 0);
+      if (j0 + key < kv_end) {
+        sk[it] = *reinterpret_cast<const uint4*>(kbase + (size_t)(j0 + key) * kv_row_stride + c * 8);
+        sv[it] = *reinterpret_cast<const uint4*>(vbase + (size_t)(j0 + key) * kv_row_stride + c * 8);
       }
     }
-    __syncthreads();
+  };
+  auto store_tile = [&](TileBuf& tb) {
+#pragma unroll
+    for (int it = 0; it < 4; ++it) {
+      const int idx = it * kThreads + threadIdx.x;
+      const int key = idx >> 5;
+      const int c = idx & 31;
+      *reinterpret_cast<uint4*>(&tb.k[key * kKRow + c * 8]) = sk[it];
+      *reinterpret_cast<uint4*>(&tb.v[key * kVRow + c * 8]) = sv[it];
+    }
+  };
 
-    // ---- S = Q K^T -----------------------------------------------------------
-    f32x4 sacc[4];
+  load_tile(0);
+  store_tile(buf[0]);
+  if (n_tiles > 1) load_tile(1);
+  __syncthreads();
+
+  for (int kt = 0; kt < n_tiles; ++kt) {
+    const TileBuf& tb = buf[kt & 1];
+    const int j0 = kt * kBN;
+
+    // ---- S^T = K Q^T ---------------------------------------------------------
+    f32x4 st[4];  // st[ct][r] = S[row li][key j0 + 16*ct + 4*lg + r]
 #pragma unroll
     for (int ct = 0; ct < 4; ++ct) {
-      sacc[ct] = f32x4{0.f, 0.f, 0.f, 0.f};
-      const uint16_t* krow = &ks[(ct * 16 + li) * kKRow + 8 * lk];
+      st[ct] = f32x4{0.f, 0.f, 0.f, 0.f};
+      const uint16_t* krow = &tb.k[(ct * 16 + li) * kKRow + 8 * lg];
 #pragma unroll
       for (int s = 0; s < 8; ++s) {
         const bf16x8 kf = as_bf16x8(*reinterpret_cast<const uint4*>(krow + 32 * s));
-        sacc[ct] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(qf[s], kf, sacc[ct], 0, 0, 0);
+        st[ct] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf, qf[s], st[ct], 0, 0, 0);
       }
     }
-    // ---- mask + online softmax (rows 4*lk + r, columns 16*ct + li) ----------
-    float pv[4][4];
-    uint16_t phi[4][4], plo[4][4];
+
+    // ---- mask, lazy online softmax (row li), split P ------------------------
+    float sv_[4][4];
+    bool raise = false;
 #pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      const int qi = p0 + 4 * lk + r;
+    for (int ct = 0; ct < 4; ++ct)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int kj = j0 + ct * 16 + 4 * lg + r;
+        const bool ok = (kj < kv_end) && (!a.causal || kj <= qi);
+        const float x = ok ? st[ct][r] * a.scale_log2 : -INFINITY;
+        sv_[ct][r] = x;
+        raise |= x > m_ref + kSlack;
+      }
+    if (__builtin_amdgcn_ballot_w64(raise) != 0) {  // wave-uniform, rare
       float mx = -INFINITY;
 #pragma unroll
-      for (int ct = 0; ct < 4; ++ct) {
-        const int kj = j0 + ct * 16 + li;
-        const bool ok = (kj < kv_end) && (!a.causal || kj <= qi);
-        const float sv = ok ? sacc[ct][r] * a.scale_log2 : -INFINITY;
-        pv[r][ct] = sv;
-        mx = fmaxf(mx, sv);
-      }
-      mx = rowmax16(mx);
-      const float m_new = fmaxf(m_run[r], mx);
-      // a row whose keys so far are all masked keeps m = -inf; use 0 as the
-      // reference so exp2 sees -inf - 0 (never -inf - -inf).
-      const float m_ref = (m_new == -INFINITY) ? 0.f : m_new;
-      const float alpha = __builtin_amdgcn_exp2f(m_run[r] - m_ref);
-      float rs = 0.f;
+      for (int ct = 0; ct < 4; ++ct)
 #pragma unroll
-      for (int ct = 0; ct < 4; ++ct) {
-        pv[r][ct] = __builtin_amdgcn_exp2f(pv[r][ct] - m_ref);
-        // split p = hi + lo into two bf16 values (together ~16 significant
-        // bits), so the bf16 MFMA products keep the fp32 softmax's precision
-        const uint16_t hi = bf16_rne_f32(pv[r][ct]);
-        const uint16_t lo = bf16_rne_f32(pv[r][ct] - bf16_to_f32(hi));
-        phi[r][ct] = hi;
-        plo[r][ct] = lo;
-        rs += bf16_to_f32(hi) + bf16_to_f32(lo);
-      }
-      rs += dpp<kDppXor1>(rs);
-      rs += dpp<kDppXor2>(rs);
-      rs += dpp<kDppHalfMirror>(rs);
-      rs += dpp<kDppMirror>(rs);
-      l_run[r] = l_run[r] * alpha + rs;
-      m_run[r] = m_new;
+        for (int r = 0; r < 4; ++r) mx = fmaxf(mx, sv_[ct][r]);
+      mx = fmaxf(mx, shfl_xor(mx, 16));
+      mx = fmaxf(mx, shfl_xor(mx, 32));
+      const float m_new = fmaxf(m_ref, mx);
+      // a row with no visible key so far keeps -inf; its factor is then 1
+      const float alpha = (m_new == -INFINITY) ? 1.f : __builtin_amdgcn_exp2f(m_ref - m_new);
+      l_row *= alpha;
+      m_ref = m_new;
+      // O holds rows 4*lg + r: fetch those rows' factors from lanes li = 4*lg + r
 #pragma unroll
-      for (int t = 0; t < 16; ++t) o[t][r] *= alpha;
-    }
-    // ---- P (bf16 hi/lo) to LDS: accumulator layout -> A-operand layout ------
-    uint16_t* pwh = ps[wave][0];
-    uint16_t* pwl = ps[wave][1];
+      for (int r = 0; r < 4; ++r) {
+        const float ar = __int_as_float(
+            __builtin_amdgcn_ds_bpermute((4 * lg + r) << 2, __float_as_int(alpha)));
 #pragma unroll
-    for (int r = 0; r < 4; ++r)
-#pragma unroll
-      for (int ct = 0; ct < 4; ++ct) {
-        pwh[(4 * lk + r) * kPRow + ct * 16 + li] = phi[r][ct];
-        pwl[(4 * lk + r) * kPRow + ct * 16 + li] = plo[r][ct];
-      }
-    wave_lds_sync();
-    bf16x8 pfh[2], pfl[2];
-#pragma unroll
-    for (int s = 0; s < 2; ++s) {
-      pfh[s] = as_bf16x8(*reinterpret_cast<const uint4*>(&pwh[li * kPRow + 32 * s + 8 * lk]));
-      pfl[s] = as_bf16x8(*reinterpret_cast<const uint4*>(&pwl[li * kPRow + 32 * s + 8 * lk]));
-    }
-    // ---- O += P V --------------------------------------------------------------
-#pragma unroll
-    for (int t = 0; t < 16; ++t) {
-      const uint16_t* vrow = &vts[(t * 16 + li) * kVRow + 8 * lk];
-#pragma unroll
-      for (int s = 0; s < 2; ++s) {
-        const bf16x8 vf = as_bf16x8(*reinterpret_cast<const uint4*>(vrow + 32 * s));
-        o[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(pfh[s], vf, o[t], 0, 0, 0);
-        o[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(pfl[s], vf, o[t], 0, 0, 0);
+        for (int t = 0; t < 16; ++t) o[t][r] *= ar;
       }
     }
-    wave_lds_sync();
+    uint32_t phw[2][4], plw[2][4];  // packed bf16 A operands, k-step ks = ct / 2
+#pragma unroll
+    for (int ct = 0; ct < 4; ++ct) {
+      uint16_t hi[4], lo[4];
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const float p = (m_ref == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f(sv_[ct][r] - m_ref);
+        hi[r] = bf16_rne_f32(p);
+        const float hf = bf16_to_f32(hi[r]);
+        lo[r] = bf16_rne_f32(p - hf);
+        l_row += hf + bf16_to_f32(lo[r]);
+      }
+      const int ks = ct >> 1, half = (ct & 1) * 2;
+      phw[ks][half + 0] = pack2(hi[0], hi[1]);
+      phw[ks][half + 1] = pack2(hi[2], hi[3]);
+      plw[ks][half + 0] = pack2(lo[0], lo[1]);
+      plw[ks][half + 1] = pack2(lo[2], lo[3]);
+    }
+
+    // ---- O += P V  (B operand through the LDS transpose read) ---------------
+#pragma unroll
+    for (int ks = 0; ks < 2; ++ks) {
+      const bf16x8 ph = as_bf16x8(make_uint4(phw[ks][0], phw[ks][1], phw[ks][2], phw[ks][3]));
+      const bf16x8 pl = as_bf16x8(make_uint4(plw[ks][0], plw[ks][1], plw[ks][2], plw[ks][3]));
+      // k-slots 0..3: keys 32ks + 4lg + 0..3; k-slots 4..7: keys 32ks + 16 + 4lg + 0..3
+      const uint16_t* v0 = &tb.v[(32 * ks + 4 * lg + (li >> 2)) * kVRow + 4 * (li & 3)];
+      const uint16_t* v1 = v0 + 16 * kVRow;
+#pragma unroll
+      for (int t = 0; t < 16; ++t) {
+        const uint2 a0 = tr_read(v0 + 16 * t);
+        const uint2 a1 = tr_read(v1 + 16 * t);
+        const bf16x8 vf = as_bf16x8(make_uint4(a0.x, a0.y, a1.x, a1.y));
+        o[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ph, vf, o[t], 0, 0, 0);
+        o[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(pl, vf, o[t], 0, 0, 0);
+      }
+    }
+
+    // ---- next tile: staged registers -> the other buffer ---------------------
+    if (kt + 1 < n_tiles) {
+      store_tile(buf[(kt + 1) & 1]);
+      if (kt + 2 < n_tiles) load_tile(kt + 2);
+    }
+    __syncthreads();
   }
 
-  // ---- epilogue: O / l -> bf16, gate, store -----------------------------------
+  // ---- epilogue: O / l -> bf16, gate, store ------------------------------------
+  l_row += shfl_xor(l_row, 16);  // the row's four lanes hold disjoint keys
+  l_row += shfl_xor(l_row, 32);
 #pragma unroll
   for (int r = 0; r < 4; ++r) {
-    const int qi = p0 + 4 * lk + r;
-    if (qi >= S) continue;
-    const size_t rowoff = (((size_t)b * S + qi) * Hq + h) * kD;
+    const int row = 4 * lg + r;
+    const float lr = __int_as_float(__builtin_amdgcn_ds_bpermute(row << 2, __float_as_int(l_row)));
+    const int qr = p0 + row;
+    if (qr >= S) continue;
+    const size_t rowoff = (((size_t)b * S + qr) * Hq + h) * kD;
 #pragma unroll
     for (int t = 0; t < 16; ++t) {
       const int d = t * 16 + li;
-      const uint16_t ob = bf16_rne_f32(o[t][r] / l_run[r]);
+      const uint16_t ob = bf16_rne_f32(o[t][r] / lr);
       a.out[rowoff + d] = gate_output(ob, a.gate[rowoff + d]);
     }
   }
@@ -258,9 +328,10 @@ hipError_t launch_prefill(const PrefillLaunch& p, hipStream_t stream) {
   a.causal = p.causal;
   a.seq_len = p.seq_len;
   a.num_kv_heads = p.num_kv_heads;
+  a.batch = p.batch;
   a.num_m_tiles = (p.seq_len + kBM - 1) / kBM;
-  dim3 grid(a.num_m_tiles, p.num_kv_heads, p.batch);
-  hipLaunchKernelGGL(prefill_gate_kernel, grid, dim3(512), 0, stream, a);
+  dim3 grid(grid_size(p.batch * p.num_kv_heads, a.num_m_tiles));
+  hipLaunchKernelGGL(prefill_gate_kernel, grid, dim3(kThreads), 0, stream, a);
   return hipGetLastError();
 }
 
