@@ -56,6 +56,8 @@ def parse_args():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-extras", action="store_true",
                     help="only the timed decode steps (cold, B1, prefill, CPU legs skipped)")
+    ap.add_argument("--prefill-only", action="store_true",
+                    help="time only the B=2, S=2048 causal prefill (for profiling)")
     ap.add_argument("--calibration-copy", action="store_true",
                     help="also run one plain 1 GiB device copy (counter calibration)")
     ap.add_argument("--json-out", default=None)
@@ -132,6 +134,37 @@ class DecodeCall:
             self.ga.check(st, "gated_attn_decode")
 
 
+def time_prefill(ga, workloads, dev, n_calls: int) -> dict:
+    """B=2, S=2048 causal gated prefill: n_calls back-to-back calls."""
+    import torch
+
+    p = workloads.workload(4)
+    pt = [to_dev(x, dev) for x in (p.q, p.gate, p.k, p.v)]
+    pout = torch.empty_like(pt[0])
+    for _ in range(3):
+        ga.prefill(*pt, p.scale, causal=True, out=pout)
+    torch.cuda.synchronize()
+    a = torch.cuda.Event(enable_timing=True)
+    b = torch.cuda.Event(enable_timing=True)
+    a.record()
+    for _ in range(n_calls):
+        ga.prefill(*pt, p.scale, causal=True, out=pout)
+    b.record()
+    torch.cuda.synchronize()
+    pms = a.elapsed_time(b) / n_calls
+    B, S, Hq, D = p.q.shape
+    flops = 4.0 * D * Hq * B * S * (S + 1) / 2
+    tflops = flops / (pms * 1e-3) / 1e12
+    return {"workload": "gated causal prefill B=2 S=2048 H_q=16 H_kv=2 D=256",
+            "us_per_call": round(pms * 1e3, 3),
+            "calls": n_calls,
+            "algorithmic_flop": flops,
+            "tflops": round(tflops, 2),
+            "mfma_bf16_frac": round(tflops / BF16_MFMA_PEAK_TFLOPS, 4),
+            "note": "P is split into two bf16 terms, so the kernel issues 1.5x "
+                    "the algorithmic MFMA work"}
+
+
 def main() -> int:
     args = parse_args()
     world = int(os.environ.get("WORLD_SIZE", "1"))
@@ -150,6 +183,10 @@ def main() -> int:
     dev = torch.device("cuda:0")
     hip = Hip()
     K, W = args.steps, args.warmup
+
+    if args.prefill_only:
+        print(json.dumps({"prefill": time_prefill(ga, workloads, dev, K)}), flush=True)
+        return 0
 
     # ---------------- headline: B=64, L=4096 paged decode --------------------
     t_gen = time.time()
@@ -301,32 +338,7 @@ def main() -> int:
                              "samples_us": [round(x, 3) for x in samples]}
         del g
 
-        # ---- prefill B=2, S=2048 causal --------------------------------------
-        p = workloads.workload(4)
-        pt = [to_dev(x, dev) for x in (p.q, p.gate, p.k, p.v)]
-        pout = torch.empty_like(pt[0])
-        for _ in range(3):
-            ga.prefill(*pt, p.scale, causal=True, out=pout)
-        torch.cuda.synchronize()
-        a = torch.cuda.Event(enable_timing=True)
-        b = torch.cuda.Event(enable_timing=True)
-        n_p = 20
-        a.record()
-        for _ in range(n_p):
-            ga.prefill(*pt, p.scale, causal=True, out=pout)
-        b.record()
-        torch.cuda.synchronize()
-        pms = a.elapsed_time(b) / n_p
-        B, S, Hq, D = p.q.shape
-        flops = 4.0 * D * Hq * B * S * (S + 1) / 2
-        tflops = flops / (pms * 1e-3) / 1e12
-        result["prefill"] = {"workload": "gated causal prefill B=2 S=2048 H_q=16 H_kv=2 D=256",
-                             "us_per_call": round(pms * 1e3, 3),
-                             "algorithmic_flop": flops,
-                             "tflops": round(tflops, 2),
-                             "mfma_bf16_frac": round(tflops / BF16_MFMA_PEAK_TFLOPS, 4),
-                             "note": "P is split into two bf16 terms, so the kernel issues 1.5x "
-                                     "the algorithmic MFMA work"}
+        result["prefill"] = time_prefill(ga, workloads, dev, 20)
 
     if not args.no_cpu_baseline and not args.no_extras:
         import oracle

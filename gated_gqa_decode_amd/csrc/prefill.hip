@@ -123,8 +123,14 @@ __device__ __forceinline__ uint2 tr_read(const uint16_t* p) {
   return __builtin_bit_cast(uint2, r);
 }
 
-__device__ __forceinline__ uint32_t pack2(uint16_t lo, uint16_t hi) {
-  return (uint32_t)lo | ((uint32_t)hi << 16);
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+
+// Two fp32 -> packed bf16 pair (v_cvt_pk_bf16_f32, round to nearest even);
+// used for the P operand only, whose precision the hi/lo split restores.
+__device__ __forceinline__ uint32_t cvt_pk_bf16(float x, float y) {
+  const f32x2 v = {x, y};
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, bf16x2));
 }
 
 }  // namespace
@@ -168,31 +174,33 @@ __global__ __launch_bounds__(kThreads) void prefill_gate_kernel(PrefillArgs a) {
   const uint16_t* kbase = a.k + ((size_t)b * S * Hkv + g) * kD;
   const uint16_t* vbase = a.v + ((size_t)b * S * Hkv + g) * kD;
 
-  // staging: thread covers 16-byte pieces idx = it*512 + tid of each 64 x 256 tile
+  // staging: thread covers 16-byte pieces idx = it*512 + tid of each 64 x 256
+  // tile: key it*16 + tid/32, column chunk tid%32 (offsets fixed per thread)
+  const int st_key = threadIdx.x >> 5;
+  const int st_c = threadIdx.x & 31;
+  const unsigned g_off = (unsigned)(st_key * (int)kv_row_stride + st_c * 8);
   uint4 sk[4], sv[4];
   auto load_tile = [&](int kt) {
     const int j0 = kt * kBN;
+    const uint16_t* kb = kbase + (size_t)j0 * kv_row_stride;
+    const uint16_t* vb = vbase + (size_t)j0 * kv_row_stride;
 #pragma unroll
     for (int it = 0; it < 4; ++it) {
-      const int idx = it * kThreads + threadIdx.x;
-      const int key = idx >> 5;
-      const int c = idx & 31;
+      const unsigned off = g_off + (unsigned)(it * 16 * (int)kv_row_stride);
       sk[it] = make_uint4(0, 0, 0, 0);
       sv[it] = make_uint4(0, 0, 0, 0);
-      if (j0 + key < kv_end) {
-        sk[it] = *reinterpret_cast<const uint4*>(kbase + (size_t)(j0 + key) * kv_row_stride + c * 8);
-        sv[it] = *reinterpret_cast<const uint4*>(vbase + (size_t)(j0 + key) * kv_row_stride + c * 8);
+      if (j0 + it * 16 + st_key < kv_end) {
+        sk[it] = *reinterpret_cast<const uint4*>(kb + off);
+        sv[it] = *reinterpret_cast<const uint4*>(vb + off);
       }
     }
   };
   auto store_tile = [&](TileBuf& tb) {
 #pragma unroll
     for (int it = 0; it < 4; ++it) {
-      const int idx = it * kThreads + threadIdx.x;
-      const int key = idx >> 5;
-      const int c = idx & 31;
-      *reinterpret_cast<uint4*>(&tb.k[key * kKRow + c * 8]) = sk[it];
-      *reinterpret_cast<uint4*>(&tb.v[key * kVRow + c * 8]) = sv[it];
+      const int key = it * 16 + st_key;
+      *reinterpret_cast<uint4*>(&tb.k[key * kKRow + st_c * 8]) = sk[it];
+      *reinterpret_cast<uint4*>(&tb.v[key * kVRow + st_c * 8]) = sv[it];
     }
   };
 
@@ -206,31 +214,55 @@ __global__ __launch_bounds__(kThreads) void prefill_gate_kernel(PrefillArgs a) {
     const int j0 = kt * kBN;
 
     // ---- S^T = K Q^T ---------------------------------------------------------
+    // k-step outer, key tile inner: the four accumulators interleave, so no
+    // MFMA waits on the one just issued.
     f32x4 st[4];  // st[ct][r] = S[row li][key j0 + 16*ct + 4*lg + r]
 #pragma unroll
-    for (int ct = 0; ct < 4; ++ct) {
-      st[ct] = f32x4{0.f, 0.f, 0.f, 0.f};
-      const uint16_t* krow = &tb.k[(ct * 16 + li) * kKRow + 8 * lg];
+    for (int ct = 0; ct < 4; ++ct) st[ct] = f32x4{0.f, 0.f, 0.f, 0.f};
+    {
+      const uint16_t* krow = &tb.k[li * kKRow + 8 * lg];
+      bf16x8 kf[2][4];
+#pragma unroll
+      for (int ct = 0; ct < 4; ++ct)
+        kf[0][ct] = as_bf16x8(*reinterpret_cast<const uint4*>(krow + ct * 16 * kKRow));
 #pragma unroll
       for (int s = 0; s < 8; ++s) {
-        const bf16x8 kf = as_bf16x8(*reinterpret_cast<const uint4*>(krow + 32 * s));
-        st[ct] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf, qf[s], st[ct], 0, 0, 0);
+        if (s + 1 < 8) {
+#pragma unroll
+          for (int ct = 0; ct < 4; ++ct)
+            kf[(s + 1) & 1][ct] =
+                as_bf16x8(*reinterpret_cast<const uint4*>(krow + ct * 16 * kKRow + 32 * (s + 1)));
+        }
+#pragma unroll
+        for (int ct = 0; ct < 4; ++ct)
+          st[ct] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf[s & 1][ct], qf[s], st[ct], 0, 0, 0);
       }
     }
 
     // ---- mask, lazy online softmax (row li), split P ------------------------
+    // Only a tile that reaches past the first row of the query tile (causal)
+    // or past the last key needs the mask; the test is uniform.
+    const bool need_mask = (j0 + kBN > kv_end) || (a.causal && j0 + kBN - 1 > p0);
     float sv_[4][4];
     bool raise = false;
 #pragma unroll
     for (int ct = 0; ct < 4; ++ct)
 #pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const int kj = j0 + ct * 16 + 4 * lg + r;
-        const bool ok = (kj < kv_end) && (!a.causal || kj <= qi);
-        const float x = ok ? st[ct][r] * a.scale_log2 : -INFINITY;
-        sv_[ct][r] = x;
-        raise |= x > m_ref + kSlack;
-      }
+      for (int r = 0; r < 4; ++r) sv_[ct][r] = st[ct][r] * a.scale_log2;
+    if (need_mask) {
+#pragma unroll
+      for (int ct = 0; ct < 4; ++ct)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const int kj = j0 + ct * 16 + 4 * lg + r;
+          const bool ok = (kj < kv_end) && (!a.causal || kj <= qi);
+          sv_[ct][r] = ok ? sv_[ct][r] : -INFINITY;
+        }
+    }
+#pragma unroll
+    for (int ct = 0; ct < 4; ++ct)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) raise |= sv_[ct][r] > m_ref + kSlack;
     if (__builtin_amdgcn_ballot_w64(raise) != 0) {  // wave-uniform, rare
       float mx = -INFINITY;
 #pragma unroll
@@ -253,26 +285,27 @@ __global__ __launch_bounds__(kThreads) void prefill_gate_kernel(PrefillArgs a) {
         for (int t = 0; t < 16; ++t) o[t][r] *= ar;
       }
     }
+    // p = hi + lo, both bf16 (hardware round-to-nearest-even conversion); the
+    // row sum takes p itself (hi + lo equals p to ~2^-18 relative).
+    const float mref_safe = (m_ref == -INFINITY) ? 0.f : m_ref;
     uint32_t phw[2][4], plw[2][4];  // packed bf16 A operands, k-step ks = ct / 2
 #pragma unroll
     for (int ct = 0; ct < 4; ++ct) {
-      uint16_t hi[4], lo[4];
 #pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const float p = (m_ref == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f(sv_[ct][r] - m_ref);
-        hi[r] = bf16_rne_f32(p);
-        const float hf = bf16_to_f32(hi[r]);
-        lo[r] = bf16_rne_f32(p - hf);
-        l_row += hf + bf16_to_f32(lo[r]);
+      for (int rp = 0; rp < 2; ++rp) {
+        const float pa = __builtin_amdgcn_exp2f(sv_[ct][2 * rp] - mref_safe);
+        const float pb = __builtin_amdgcn_exp2f(sv_[ct][2 * rp + 1] - mref_safe);
+        l_row += pa + pb;
+        const uint32_t hi = cvt_pk_bf16(pa, pb);
+        const uint32_t lo = cvt_pk_bf16(pa - bf16_lo(hi), pb - bf16_hi(hi));
+        phw[ct >> 1][(ct & 1) * 2 + rp] = hi;
+        plw[ct >> 1][(ct & 1) * 2 + rp] = lo;
       }
-      const int ks = ct >> 1, half = (ct & 1) * 2;
-      phw[ks][half + 0] = pack2(hi[0], hi[1]);
-      phw[ks][half + 1] = pack2(hi[2], hi[3]);
-      plw[ks][half + 0] = pack2(lo[0], lo[1]);
-      plw[ks][half + 1] = pack2(lo[2], lo[3]);
     }
 
     // ---- O += P V  (B operand through the LDS transpose read) ---------------
+    // The V fragments of the next group of four column tiles are requested
+    // before the current group's MFMAs are issued.
 #pragma unroll
     for (int ks = 0; ks < 2; ++ks) {
       const bf16x8 ph = as_bf16x8(make_uint4(phw[ks][0], phw[ks][1], phw[ks][2], phw[ks][3]));
@@ -280,13 +313,30 @@ __global__ __launch_bounds__(kThreads) void prefill_gate_kernel(PrefillArgs a) {
       // k-slots 0..3: keys 32ks + 4lg + 0..3; k-slots 4..7: keys 32ks + 16 + 4lg + 0..3
       const uint16_t* v0 = &tb.v[(32 * ks + 4 * lg + (li >> 2)) * kVRow + 4 * (li & 3)];
       const uint16_t* v1 = v0 + 16 * kVRow;
+      bf16x8 vf[2][4];
 #pragma unroll
-      for (int t = 0; t < 16; ++t) {
-        const uint2 a0 = tr_read(v0 + 16 * t);
-        const uint2 a1 = tr_read(v1 + 16 * t);
-        const bf16x8 vf = as_bf16x8(make_uint4(a0.x, a0.y, a1.x, a1.y));
-        o[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ph, vf, o[t], 0, 0, 0);
-        o[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(pl, vf, o[t], 0, 0, 0);
+      for (int u = 0; u < 4; ++u) {
+        const uint2 a0 = tr_read(v0 + 16 * u);
+        const uint2 a1 = tr_read(v1 + 16 * u);
+        vf[0][u] = as_bf16x8(make_uint4(a0.x, a0.y, a1.x, a1.y));
+      }
+#pragma unroll
+      for (int tg = 0; tg < 4; ++tg) {
+        if (tg + 1 < 4) {
+#pragma unroll
+          for (int u = 0; u < 4; ++u) {
+            const int t = 4 * (tg + 1) + u;
+            const uint2 a0 = tr_read(v0 + 16 * t);
+            const uint2 a1 = tr_read(v1 + 16 * t);
+            vf[(tg + 1) & 1][u] = as_bf16x8(make_uint4(a0.x, a0.y, a1.x, a1.y));
+          }
+        }
+#pragma unroll
+        for (int u = 0; u < 4; ++u)
+          o[4 * tg + u] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ph, vf[tg & 1][u], o[4 * tg + u], 0, 0, 0);
+#pragma unroll
+        for (int u = 0; u < 4; ++u)
+          o[4 * tg + u] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(pl, vf[tg & 1][u], o[4 * tg + u], 0, 0, 0);
       }
     }
 
