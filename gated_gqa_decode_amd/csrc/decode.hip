@@ -93,7 +93,7 @@ __device__ __forceinline__ uint2 ldg8_stream(const char* p) {
 }  // namespace
 
 __global__ __launch_bounds__(256, 2) void decode_stage1_kernel(Stage1Args a) {
-  __shared__ WaveSlot wslot[kWaves];
+  __shared__ WaveSlot wslot[kWaves][2];
   __shared__ MergeSlot merge;
 
   const int s = blockIdx.x;
@@ -168,27 +168,38 @@ __global__ __launch_bounds__(256, 2) void decode_stage1_kernel(Stage1Args a) {
 
   // One step's data: K as 4 x 16 bytes (two passes of 4 tokens), V as 8 x 8
   // bytes (one per token, a whole 512-byte row per wave instruction).
-  struct StepRegs {
+  struct KRegs {
     uint4 k[2][2];
+  };
+  struct VRegs {
     uint2 v[kStep];
   };
-  auto load_step = [&](int step, StepRegs& r) {
+  auto load_k = [&](int step, KRegs& r) {
     const char* kb = reinterpret_cast<const char*>(step_base(step, a.k_pool));
-    const char* vb = reinterpret_cast<const char*>(step_base(step, a.v_pool));
 #pragma unroll
     for (int pass = 0; pass < 2; ++pass) {
       r.k[pass][0] = ldg16_stream(kb + k_off[pass]);
       r.k[pass][1] = ldg16_stream(kb + (k_off[pass] + 256u));
     }
+  };
+  auto load_v = [&](int step, VRegs& r) {
+    const char* vb = reinterpret_cast<const char*>(step_base(step, a.v_pool));
 #pragma unroll
     for (int t = 0; t < kStep; ++t) r.v[t] = ldg8_stream(vb + v_off[t]);
   };
 
-  WaveSlot& ws = wslot[wave];
+  // Two probability slots per wave: the scores of step i+1 are computed into
+  // one while the values of step i are accumulated from the other, so the two
+  // dependency chains can be interleaved; one fence per step separates a
+  // slot's writes from its reads.
+  WaveSlot* slots = wslot[wave];
 
-  auto compute_step = [&](int step, const StepRegs& r) {
+  // Scores of one step -> probabilities in the step's slot.  Returns (wave-
+  // uniform) whether the reference max was raised, in which case the slot's
+  // alpha[] holds the factors the value accumulators must take before this
+  // step's probabilities are added (l_run is rescaled here).
+  auto score_step = [&](int step, const KRegs& r, WaveSlot& ws) -> bool {
     const int t0 = tok_begin + step * kStep;
-    // ---- scores: two passes of 4 tokens -------------------------------------
     float sc[2];
 #pragma unroll
     for (int pass = 0; pass < 2; ++pass) {
@@ -210,7 +221,6 @@ __global__ __launch_bounds__(256, 2) void decode_stage1_kernel(Stage1Args a) {
       const int t = t0 + pass * 4 + tq;
       sc[pass] = (t < tok_end) ? mine * a.scale_log2 : -INFINITY;
     }
-    // ---- online softmax for head hs ----------------------------------------
     // Lazy rescaling: probabilities are taken relative to a reference max
     // m_run that is only raised (with a rescale of l and acc) when some score
     // of the step exceeds it by more than kSlack (log2 units), i.e. when a
@@ -218,7 +228,8 @@ __global__ __launch_bounds__(256, 2) void decode_stage1_kernel(Stage1Args a) {
     // cross-lane max and no rescale; any reference gives the same O, and
     // probabilities stay in [0, 2^kSlack].
     const bool raise = (sc[0] > m_run + kSlack) || (sc[1] > m_run + kSlack);
-    if (__builtin_amdgcn_ballot_w64(raise) != 0) {  // wave-uniform
+    const bool raised = __builtin_amdgcn_ballot_w64(raise) != 0;  // wave-uniform
+    if (raised) {
       float mx = fmaxf(sc[0], sc[1]);
       mx = fmaxf(mx, shfl_xor(mx, 16));
       mx = fmaxf(mx, shfl_xor(mx, 32));
@@ -227,14 +238,6 @@ __global__ __launch_bounds__(256, 2) void decode_stage1_kernel(Stage1Args a) {
       l_run *= alpha;
       m_run = m_new;
       if ((c16 & 1) == 0 && tq == 0) ws.alpha[hs] = alpha;
-      wave_lds_sync();
-      const float4 al0 = *reinterpret_cast<const float4*>(&ws.alpha[0]);
-      const float4 al1 = *reinterpret_cast<const float4*>(&ws.alpha[4]);
-      const float al[kGroup] = {al0.x, al0.y, al0.z, al0.w, al1.x, al1.y, al1.z, al1.w};
-#pragma unroll
-      for (int h = 0; h < kGroup; ++h)
-#pragma unroll
-        for (int e = 0; e < 4; ++e) acc[h][e] *= al[h];
     }
     const float p0 = __builtin_amdgcn_exp2f(sc[0] - m_run);
     const float p1 = __builtin_amdgcn_exp2f(sc[1] - m_run);
@@ -243,51 +246,83 @@ __global__ __launch_bounds__(256, 2) void decode_stage1_kernel(Stage1Args a) {
       ws.p[tq][hs] = p0;
       ws.p[4 + tq][hs] = p1;
     }
-    wave_lds_sync();
-    // ---- values ------------------------------------------------------------
-    {
-      uint2 vv[kStep];
-#pragma unroll
-      for (int t = 0; t < kStep; ++t) vv[t] = r.v[t];
-      if (t0 + kStep > tok_end) {  // last step of the sequence: tail slots may hold anything
-#pragma unroll
-        for (int t = 0; t < kStep; ++t)
-          if (t0 + t >= tok_end) vv[t] = make_uint2(0, 0);
-      }
-#pragma unroll
-      for (int t = 0; t < kStep; ++t) {
-        const uint2 v = vv[t];
-        const float vf[4] = {bf16_lo(v.x), bf16_hi(v.x), bf16_lo(v.y), bf16_hi(v.y)};
-        const float4 pa = *reinterpret_cast<const float4*>(&ws.p[t][0]);
-        const float4 pb = *reinterpret_cast<const float4*>(&ws.p[t][4]);
-        const float pr[kGroup] = {pa.x, pa.y, pa.z, pa.w, pb.x, pb.y, pb.z, pb.w};
-#pragma unroll
-        for (int h = 0; h < kGroup; ++h)
-#pragma unroll
-          for (int e = 0; e < 4; ++e) acc[h][e] = fmaf(pr[h], vf[e], acc[h][e]);
-      }
-    }
-    wave_lds_sync();  // the next step rewrites the slot
+    return raised;
   };
 
-  // Two steps stay in flight while one is computed: the loads of step i+2 are
-  // issued before step i's arithmetic.  Three register sets take turns (the
-  // loop is unrolled three times, so no set is copied), and loads are issued
-  // unconditionally (past the end a wave re-reads its last step), so the wait
-  // before a step's arithmetic covers only that step's own loads.
+  // Values of one step from its slot (after the rescale its scores asked for).
+  auto value_step = [&](int step, const VRegs& r, const WaveSlot& ws, bool rescale) {
+    const int t0 = tok_begin + step * kStep;
+    if (rescale) {
+      const float4 al0 = *reinterpret_cast<const float4*>(&ws.alpha[0]);
+      const float4 al1 = *reinterpret_cast<const float4*>(&ws.alpha[4]);
+      const float al[kGroup] = {al0.x, al0.y, al0.z, al0.w, al1.x, al1.y, al1.z, al1.w};
+#pragma unroll
+      for (int h = 0; h < kGroup; ++h)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) acc[h][e] *= al[h];
+    }
+    uint2 vv[kStep];
+#pragma unroll
+    for (int t = 0; t < kStep; ++t) vv[t] = r.v[t];
+    if (t0 + kStep > tok_end) {  // last step of the sequence: tail slots may hold anything
+#pragma unroll
+      for (int t = 0; t < kStep; ++t)
+        if (t0 + t >= tok_end) vv[t] = make_uint2(0, 0);
+    }
+#pragma unroll
+    for (int t = 0; t < kStep; ++t) {
+      const uint2 v = vv[t];
+      const float vf[4] = {bf16_lo(v.x), bf16_hi(v.x), bf16_lo(v.y), bf16_hi(v.y)};
+      const float4 pa = *reinterpret_cast<const float4*>(&ws.p[t][0]);
+      const float4 pb = *reinterpret_cast<const float4*>(&ws.p[t][4]);
+      const float pr[kGroup] = {pa.x, pa.y, pa.z, pa.w, pb.x, pb.y, pb.z, pb.w};
+#pragma unroll
+      for (int h = 0; h < kGroup; ++h)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) acc[h][e] = fmaf(pr[h], vf[e], acc[h][e]);
+    }
+  };
+
+  // Steps of this wave: wave, wave + 4, ...; consecutive steps use slots 0
+  // and 1 in turn.  Each iteration scores step s + 4 and accumulates the
+  // values of step s; the K rows of a step are loaded one iteration before
+  // its scores and its V rows one iteration before its values, into two K
+  // and two V register sets used in turn (the loop is unrolled twice, so no
+  // set is copied).  Loads are issued unconditionally (past the end a wave
+  // re-reads its last step), so the wait before a step's arithmetic covers
+  // only that step's own loads.
   int step = wave;
   if (step < n_steps) {
     const int last = n_steps - 1;
-    StepRegs r0, r1, r2;
-    load_step(step, r0);
-    load_step(min(step + kWaves, last), r1);
-    for (; step < n_steps; step += 3 * kWaves) {
-      load_step(min(step + 2 * kWaves, last), r2);
-      compute_step(step, r0);
-      load_step(min(step + 3 * kWaves, last), r0);
-      if (step + kWaves < n_steps) compute_step(step + kWaves, r1);
-      load_step(min(step + 4 * kWaves, last), r1);
-      if (step + 2 * kWaves < n_steps) compute_step(step + 2 * kWaves, r2);
+    KRegs kA, kB;
+    VRegs vA, vB;
+    load_k(step, kA);
+    load_v(step, vA);
+    load_k(min(step + kWaves, last), kB);
+    bool resc = score_step(step, kA, slots[0]);
+    wave_lds_sync();
+    for (;;) {
+      // kB: K of step + 4; vA: V of step (scored, slot 0)
+      load_k(min(step + 2 * kWaves, last), kA);
+      load_v(min(step + kWaves, last), vB);
+      bool resc_next = false;
+      if (step + kWaves < n_steps) resc_next = score_step(step + kWaves, kB, slots[1]);
+      value_step(step, vA, slots[0], resc);
+      wave_lds_sync();
+      step += kWaves;
+      resc = resc_next;
+      if (step >= n_steps) break;
+
+      // kA: K of step + 4; vB: V of step (scored, slot 1)
+      load_k(min(step + 2 * kWaves, last), kB);
+      load_v(min(step + kWaves, last), vA);
+      resc_next = false;
+      if (step + kWaves < n_steps) resc_next = score_step(step + kWaves, kA, slots[0]);
+      value_step(step, vB, slots[1], resc);
+      wave_lds_sync();
+      step += kWaves;
+      resc = resc_next;
+      if (step >= n_steps) break;
     }
   }
 
