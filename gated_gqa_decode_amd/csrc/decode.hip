@@ -99,20 +99,21 @@ __global__ __launch_bounds__(256, 2) void decode_stage1_kernel(Stage1Args a) {
   const int s = blockIdx.x;
   const int g = blockIdx.y;
   const int b = blockIdx.z;
-  // Lengths past the capacity and page ids outside the pool break the
-  // documented preconditions; both are clamped so such input yields garbage
-  // in its own row instead of an access outside the buffers.
-  const int L = min(a.seq_lens[b], a.max_pages * kPage);
-  const int tok_begin = s * a.tokens_per_split;
-  if (tok_begin >= L) return;  // empty split: stage 2 never reads its slot
-  const int tok_end = min(L, tok_begin + a.tokens_per_split);
-
   const int lane = __lane_id();
   // wave-uniform by construction; readfirstlane lets the compiler keep the
   // step bookkeeping and the load base addresses in scalar registers
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int Hkv = a.num_kv_heads;
   const int Hq = Hkv * kGroup;
+  const int tok_begin = s * a.tokens_per_split;  // < capacity, since s < num_splits
+
+  // Issued together, before the length is known: the page ids of the whole
+  // split (one per lane; ids past the sequence's end are never used), the
+  // length, and q.
+  const int first_page = tok_begin / kPage;
+  const int split_pages = min(a.tokens_per_split / kPage, a.max_pages - first_page);
+  const int32_t* bt = a.block_table + (size_t)b * a.max_pages;
+  int my_page = lane < split_pages ? bt[first_page + lane] : 0;
 
   // score-lane coordinates
   const int tq = lane >> 4;    // token within a pass
@@ -130,6 +131,14 @@ __global__ __launch_bounds__(256, 2) void decode_stage1_kernel(Stage1Args a) {
     }
   }
 
+  // Lengths past the capacity and page ids outside the pool break the
+  // documented preconditions; both are clamped so such input yields garbage
+  // in its own row instead of an access outside the buffers.
+  const int L = min(a.seq_lens[b], a.max_pages * kPage);
+  if (tok_begin >= L) return;  // empty split: stage 2 never reads its slot
+  const int tok_end = min(L, tok_begin + a.tokens_per_split);
+  my_page = (int)min((long long)max(my_page, 0), a.num_pages - 1);
+
   // value lanes: lane owns d = 4*lane .. 4*lane+3 of all 8 heads
   float acc[kGroup][4];
 #pragma unroll
@@ -140,15 +149,8 @@ __global__ __launch_bounds__(256, 2) void decode_stage1_kernel(Stage1Args a) {
   float l_run = 0.f;        // this lane's share of the running sum of head hs
 
   const int n_steps = (tok_end - tok_begin + kStep - 1) / kStep;
-  const int32_t* bt = a.block_table + (size_t)b * a.max_pages;
   const size_t row_stride = (size_t)Hkv * kD;            // elements between tokens
   const size_t page_stride = (size_t)kPage * row_stride; // elements between pages
-
-  // Page ids of this split, one per lane (a split covers at most 64 pages).
-  const int first_page = tok_begin / kPage;
-  const int n_pages = (tok_end - 1) / kPage - first_page + 1;
-  int my_page = lane < n_pages ? bt[first_page + lane] : 0;
-  my_page = (int)min((long long)max(my_page, 0), a.num_pages - 1);
 
   // Element offsets of this lane's pieces inside one 8-token step (the same
   // for every step); the step's base address is wave-uniform.
@@ -392,18 +394,42 @@ __global__ __launch_bounds__(256) void decode_stage2_gate_kernel(Stage2Args a) {
   if (row >= a.batch * a.num_q_heads) return;
   const int lane = __lane_id();
   const int b = row / a.num_q_heads;
+  const float* ml = a.part_ml + (size_t)row * a.num_splits * 2;
+  const float* pa = a.part_acc + (size_t)row * a.num_splits * kD + lane * 4;
+  // Issued before the length is known: the gate, the length, and the first
+  // eight splits' partials (only the valid ones are used below).
   const uint2 graw = *reinterpret_cast<const uint2*>(a.gate + (size_t)row * kD + lane * 4);
+  const int n0 = min(a.num_splits, 8);
+  float4 x0[8];
+  float2 ml0[8];
+#pragma unroll
+  for (int u = 0; u < 8; ++u)
+    if (u < n0) {
+      x0[u] = *reinterpret_cast<const float4*>(pa + (size_t)u * kD);
+      ml0[u] = *reinterpret_cast<const float2*>(ml + 2 * u);
+    }
   const int L = min(a.seq_lens[b], a.capacity);  // same clamp as stage 1
   uint16_t o16[4] = {0, 0, 0, 0};
   if (L > 0) {  // L <= 0: padded slot, output +0
     const int ns = (L + a.tokens_per_split - 1) / a.tokens_per_split;
-    const float* ml = a.part_ml + (size_t)row * a.num_splits * 2;
-    const float* pa = a.part_acc + (size_t)row * a.num_splits * kD + lane * 4;
     float M = -INFINITY;
-    for (int s = 0; s < ns; ++s) M = fmaxf(M, ml[2 * s]);
+#pragma unroll
+    for (int u = 0; u < 8; ++u)
+      if (u < ns) M = fmaxf(M, ml0[u].x);
+    for (int s = 8; s < ns; ++s) M = fmaxf(M, ml[2 * s]);
     float lam = 0.f;
     float o[4] = {0.f, 0.f, 0.f, 0.f};
-    for (int s0 = 0; s0 < ns; s0 += 8) {
+#pragma unroll
+    for (int u = 0; u < 8; ++u)
+      if (u < ns) {
+        const float w = __builtin_amdgcn_exp2f(ml0[u].x - M);
+        lam = fmaf(ml0[u].y, w, lam);
+        o[0] = fmaf(x0[u].x, w, o[0]);
+        o[1] = fmaf(x0[u].y, w, o[1]);
+        o[2] = fmaf(x0[u].z, w, o[2]);
+        o[3] = fmaf(x0[u].w, w, o[3]);
+      }
+    for (int s0 = 8; s0 < ns; s0 += 8) {
       float4 x[8];
 #pragma unroll
       for (int u = 0; u < 8; ++u)
