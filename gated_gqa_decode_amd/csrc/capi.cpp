@@ -16,12 +16,13 @@
 #include "gated_attn.h"
 
 #ifndef GA_DECODE_TARGET_BLOCKS
-// Stage-1 workgroups a decode call aims for: two per compute unit of the
-// 256-CU MI355X, i.e. one resident round of the grid (stage 1 holds two
-// 4-wave workgroups per CU), so long sequences run as few, long workgroups
-// whose start-up and merge costs are amortised over many tokens.  Measured on
-// B=64, L=4096: 512 -> 109 us, 1024 -> 116 us, 2048 -> 125 us, 4096 -> 134 us.
-#define GA_DECODE_TARGET_BLOCKS 512
+// Stage-1 workgroups a decode call aims for: one per compute unit of the
+// 256-CU MI355X (stage 1 runs one 8-wave workgroup per CU), so long sequences
+// run as few, long workgroups whose start-up and merge costs are amortised
+// over many tokens.  Two 4-wave workgroups per CU were measured to finish far
+// apart (the CU serves the older one first: 72 us vs 104 us at B=64, L=4096),
+// leaving half the CU idle for the last third of the kernel.
+#define GA_DECODE_TARGET_BLOCKS 256
 #endif
 
 namespace {
@@ -29,8 +30,8 @@ namespace {
 constexpr int kHeadDim = 256;
 constexpr int kGroup = 8;
 constexpr int kPageSize = 16;
-constexpr int kSplitQuantum = 32;   // 4 waves x 8-token steps
-constexpr int kMaxSplitTokens = 1024;  // 64 pages: one page id per lane
+constexpr int kSplitQuantum = 64;   // 8 waves x 8-token steps
+constexpr int kMaxSplitTokens = 2048;  // 128 pages: two page ids per lane
 constexpr int kMaxGridYZ = 65535;
 
 thread_local int g_last_hip_error = 0;

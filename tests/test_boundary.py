@@ -50,7 +50,7 @@ def _dims(**kw):
 def test_plan_covers_capacity(B, W):
     p = ga.decode_plan(_dims(batch=B, max_pages_per_seq=W))
     cap = W * 16
-    assert p.tokens_per_split % 32 == 0 and 32 <= p.tokens_per_split <= 1024
+    assert p.tokens_per_split % 64 == 0 and 64 <= p.tokens_per_split <= 2048
     assert p.num_splits * p.tokens_per_split >= cap
     assert (p.num_splits - 1) * p.tokens_per_split < cap
     rows = B * 16 * p.num_splits

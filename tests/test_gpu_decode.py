@@ -37,12 +37,12 @@ def test_ragged_lengths_across_steps_pages_and_splits():
 
 
 def test_long_sequences_largest_split():
-    """Capacity 32768 tokens at batch 64 gives the largest split (1024 tokens,
-    64 pages per workgroup)."""
+    """Capacity 32768 tokens at batch 64 gives the largest split (2048 tokens,
+    128 pages per workgroup, so page ids sit in both per-lane registers)."""
     lens = [32768, 1, 1025, 32767, 0, 4096] + [17] * 58
     c = workloads.make_decode("long", lens, seed=32, max_pages_per_seq=2048)
     plan = ga.decode_plan(ga.decode_dims(**c.dims))
-    assert plan.tokens_per_split == 1024
+    assert plan.tokens_per_split == 2048
     res = decode_parity(c)
     assert res["ok"], res
 
