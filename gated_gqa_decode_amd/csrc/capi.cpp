@@ -28,11 +28,14 @@
 namespace {
 
 constexpr int kHeadDim = 256;
-constexpr int kGroup = 8;
 constexpr int kPageSize = 16;
 constexpr int kSplitQuantum = 64;   // 8 waves x 8-token steps
 constexpr int kMaxSplitTokens = 2048;  // 128 pages: two page ids per lane
 constexpr int kMaxGridYZ = 65535;
+// A launch's grid size times its workgroup size must stay below 2^32 threads:
+// stage 1 has 512 threads per workgroup, stage 2 has 256 (4 rows each).
+constexpr int64_t kMaxStage1Workgroups = (int64_t)1 << 22;
+constexpr int64_t kMaxDecodeRows = (int64_t)1 << 26;
 
 thread_local int g_last_hip_error = 0;
 
@@ -74,9 +77,9 @@ ga_status check_device() {
 ga_status check_heads(int32_t hq, int32_t hkv, int32_t d) {
   if (hq <= 0 || hkv <= 0 || d <= 0) return GA_ERR_INVALID_ARGUMENT;
   if (hq % hkv != 0) return GA_ERR_INVALID_ARGUMENT;
-  if (hq / hkv != kGroup) return GA_ERR_UNSUPPORTED;
+  if (!ga::group_supported(hq / hkv)) return GA_ERR_UNSUPPORTED;
   if (d != kHeadDim) return GA_ERR_UNSUPPORTED;
-  if (hkv > kMaxGridYZ) return GA_ERR_UNSUPPORTED;
+  if ((int64_t)hkv * ga::head_parts(hq / hkv) > kMaxGridYZ) return GA_ERR_UNSUPPORTED;
   return GA_OK;
 }
 
@@ -88,25 +91,34 @@ ga_status check_decode_dims(const ga_decode_dims* d) {
   if (st != GA_OK) return st;
   if (d->page_size != kPageSize) return GA_ERR_UNSUPPORTED;
   if (d->batch > kMaxGridYZ) return GA_ERR_UNSUPPORTED;
+  if ((int64_t)d->batch * d->num_q_heads > kMaxDecodeRows) return GA_ERR_UNSUPPORTED;
   // capacity in tokens must fit an int32
   if ((int64_t)d->max_pages_per_seq * kPageSize > INT32_MAX / 2) return GA_ERR_UNSUPPORTED;
   return GA_OK;
 }
 
 // Split plan from the dims alone (allocated capacity, not current lengths).
-void make_plan(const ga_decode_dims* d, ga_decode_plan* p) {
+// GA_ERR_UNSUPPORTED when the stage-1 grid would not fit one launch.
+ga_status make_plan(const ga_decode_dims* d, ga_decode_plan* p) {
   const int64_t cap = (int64_t)d->max_pages_per_seq * kPageSize;
-  const int64_t bkv = (int64_t)d->batch * d->num_kv_heads;
+  // stage-1 workgroups per split: one per (sequence, kv head, head part)
+  const int64_t bkv = (int64_t)d->batch * d->num_kv_heads *
+                      ga::head_parts(d->num_q_heads / d->num_kv_heads);
   int64_t t = (cap * (bkv > 0 ? bkv : 1) + GA_DECODE_TARGET_BLOCKS - 1) / GA_DECODE_TARGET_BLOCKS;
   t = ((t + kSplitQuantum - 1) / kSplitQuantum) * kSplitQuantum;
   if (t < kSplitQuantum) t = kSplitQuantum;
   if (t > kMaxSplitTokens) t = kMaxSplitTokens;
   const int64_t ns = (cap + t - 1) / t;
+  // stage-1 grid: (B * H_kv * NS) units rounded up to 8, times the head parts
+  const int64_t units = (int64_t)d->batch * d->num_kv_heads * ns;
+  const int64_t wgs = (units + 7) / 8 * 8 * ga::head_parts(d->num_q_heads / d->num_kv_heads);
+  if (units > INT32_MAX / 2 || wgs > kMaxStage1Workgroups) return GA_ERR_UNSUPPORTED;
   p->tokens_per_split = (int32_t)t;
   p->num_splits = (int32_t)ns;
   const int64_t rows = (int64_t)d->batch * d->num_q_heads * ns;
   size_t bytes = (size_t)rows * (size_t)(kHeadDim + 2) * sizeof(float);
   p->workspace_bytes = (bytes + 255) & ~(size_t)255;
+  return GA_OK;
 }
 
 }  // namespace
@@ -117,8 +129,7 @@ ga_status gated_attn_decode_plan(const ga_decode_dims* dims, ga_decode_plan* pla
   if (plan == nullptr) return GA_ERR_INVALID_ARGUMENT;
   ga_status st = check_decode_dims(dims);
   if (st != GA_OK) return st;
-  make_plan(dims, plan);
-  return GA_OK;
+  return make_plan(dims, plan);
 }
 
 size_t gated_attn_decode_workspace_size(const ga_decode_dims* dims) {
@@ -142,7 +153,8 @@ ga_status gated_attn_decode(const uint16_t* q, const uint16_t* gate, const uint1
       !aligned(seq_lens, 4))
     return GA_ERR_INVALID_ARGUMENT;
   ga_decode_plan plan;
-  make_plan(dims, &plan);
+  st = make_plan(dims, &plan);
+  if (st != GA_OK) return st;
   if (workspace_bytes < plan.workspace_bytes) return GA_ERR_WORKSPACE_TOO_SMALL;
   st = check_device();
   if (st != GA_OK) return st;
@@ -160,6 +172,7 @@ ga_status gated_attn_decode(const uint16_t* q, const uint16_t* gate, const uint1
   L.part_ml = L.part_acc + rows * kHeadDim;
   L.scale = scale;
   L.batch = dims->batch;
+  L.num_q_heads = dims->num_q_heads;
   L.num_kv_heads = dims->num_kv_heads;
   L.max_pages = dims->max_pages_per_seq;
   L.num_pages = dims->num_pages;
@@ -206,6 +219,7 @@ ga_status gated_attn_prefill(const uint16_t* q, const uint16_t* gate, const uint
   P.causal = causal != 0;
   P.batch = dims->batch;
   P.seq_len = dims->seq_len;
+  P.num_q_heads = dims->num_q_heads;
   P.num_kv_heads = dims->num_kv_heads;
   hipError_t e = ga::launch_prefill(P, static_cast<hipStream_t>(stream));
   if (e != hipSuccess) return hip_fail(e);

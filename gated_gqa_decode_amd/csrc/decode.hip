@@ -38,7 +38,7 @@ namespace ga {
 namespace {
 
 constexpr int kD = 256;          // head dim
-constexpr int kGroup = 8;        // query heads per kv head
+constexpr int kGroup = 8;        // query-head slots of a stage-1 workgroup
 constexpr int kPage = 16;        // tokens per page
 constexpr int kStep = 8;         // tokens per wave step
 constexpr int kWaves = 8;        // waves per stage-1 workgroup (one workgroup per CU)
@@ -55,7 +55,11 @@ struct Stage1Args {
   float* part_acc;   // [B][H_q][NS][D]
   float* part_ml;    // [B][H_q][NS][2]  (m in log2 units, l)
   float scale_log2;  // scale * log2(e)
+  int num_q_heads;
   int num_kv_heads;
+  int heads_per_part;  // query heads of this workgroup: G or G / 2 (<= 8)
+  int parts;           // workgroups per (sequence, kv head, split): 1 or 2
+  int num_units;       // B * H_kv * num_splits
   int max_pages;     // W
   long long num_pages;
   int tokens_per_split;
@@ -101,15 +105,27 @@ __global__ __launch_bounds__(512, 1) void decode_stage1_kernel(Stage1Args a) {
   __shared__ MergeSlot merge;
   __shared__ int progress[kWaves];  // last step each wave started
 
-  const int s = blockIdx.x;
-  const int g = blockIdx.y;
-  const int b = blockIdx.z;
+  // Workgroup id -> (split s, kv head g, head part, sequence b).  Ids are
+  // dispatched round-robin over the 8 XCDs; the parts of one (s, g, b) unit
+  // get ids 8 apart, i.e. the same XCD and consecutive there, so the second
+  // part finds the unit's K/V rows in that XCD's L2.
+  const int id = blockIdx.x;
+  const int xcd = id & 7;
+  const int r = id >> 3;
+  const int part = r % a.parts;
+  const int unit = (r / a.parts) * 8 + xcd;  // (b * H_kv + g) * num_splits + s
+  if (unit >= a.num_units) return;
+  const int s = unit % a.num_splits;
+  const int g = (unit / a.num_splits) % a.num_kv_heads;
+  const int b = unit / (a.num_splits * a.num_kv_heads);
   const int lane = __lane_id();
   // wave-uniform by construction; readfirstlane lets the compiler keep the
   // step bookkeeping and the load base addresses in scalar registers
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int Hkv = a.num_kv_heads;
-  const int Hq = Hkv * kGroup;
+  const int Hq = a.num_q_heads;
+  const int nh = a.heads_per_part;  // head slots 0..nh-1 are real, the rest idle
+  const int h0 = g * (Hq / Hkv) + part * nh;  // first query head of this workgroup
   const int tok_begin = s * a.tokens_per_split;  // < capacity, since s < num_splits
 
   // Issued together, before the length is known: the page ids of the whole
@@ -127,15 +143,20 @@ __global__ __launch_bounds__(512, 1) void decode_stage1_kernel(Stage1Args a) {
   const int c16 = lane & 15;   // 16-byte chunk (and chunk + 16)
   const int hs = c16 >> 1;     // head whose score this lane keeps (see reduce_scatter8)
 
-  // q chunks c16 and c16 + 16 of the group's 8 heads (bf16 pairs).
+  // q chunks c16 and c16 + 16 of the workgroup's heads (bf16 pairs); idle
+  // head slots get q = 0 (their scores and sums are computed and dropped).
   uint4 qa[kGroup], qb[kGroup];
   {
-    const uint16_t* qbase = a.q + ((size_t)b * Hq + (size_t)g * kGroup) * kD;
+    const uint16_t* qbase = a.q + ((size_t)b * Hq + (size_t)h0) * kD;
 #pragma unroll
     for (int h = 0; h < kGroup; ++h) {
-      qa[h] = ldg16(qbase + h * kD + c16 * 8);
-      qb[h] = ldg16(qbase + h * kD + (c16 + 16) * 8);
+      const int hh = min(h, nh - 1);
+      qa[h] = ldg16(qbase + hh * kD + c16 * 8);
+      qb[h] = ldg16(qbase + hh * kD + (c16 + 16) * 8);
     }
+#pragma unroll
+    for (int h = 0; h < kGroup; ++h)
+      if (h >= nh) qa[h] = qb[h] = make_uint4(0, 0, 0, 0);
   }
 
   // Lengths past the capacity and page ids outside the pool break the
@@ -399,12 +420,14 @@ __global__ __launch_bounds__(512, 1) void decode_stage1_kernel(Stage1Args a) {
       out[2] = fmaf(x.z, wgt[w], out[2]);
       out[3] = fmaf(x.w, wgt[w], out[3]);
     }
-    const size_t row = ((size_t)b * Hq + (size_t)g * kGroup + h) * a.num_splits + s;
-    *reinterpret_cast<float4*>(a.part_acc + row * kD + c * 4) =
-        make_float4(out[0], out[1], out[2], out[3]);
-    if (c == 0) {
-      a.part_ml[row * 2 + 0] = M;
-      a.part_ml[row * 2 + 1] = lam;
+    if (h < nh) {
+      const size_t row = ((size_t)b * Hq + (size_t)(h0 + h)) * a.num_splits + s;
+      *reinterpret_cast<float4*>(a.part_acc + row * kD + c * 4) =
+          make_float4(out[0], out[1], out[2], out[3]);
+      if (c == 0) {
+        a.part_ml[row * 2 + 0] = M;
+        a.part_ml[row * 2 + 1] = lam;
+      }
     }
   }
 }
@@ -507,12 +530,17 @@ hipError_t launch_decode(const DecodeLaunch& d, hipStream_t stream) {
   a1.part_acc = d.part_acc;
   a1.part_ml = d.part_ml;
   a1.scale_log2 = d.scale * kLog2e;
+  a1.num_q_heads = d.num_q_heads;
   a1.num_kv_heads = d.num_kv_heads;
+  const int group = d.num_q_heads / d.num_kv_heads;
+  a1.parts = head_parts(group);
+  a1.heads_per_part = group / a1.parts;
   a1.max_pages = d.max_pages;
   a1.num_pages = d.num_pages;
   a1.tokens_per_split = d.tokens_per_split;
   a1.num_splits = d.num_splits;
-  dim3 grid1(d.num_splits, d.num_kv_heads, d.batch);
+  a1.num_units = d.batch * d.num_kv_heads * d.num_splits;
+  dim3 grid1(((a1.num_units + 7) / 8) * 8 * a1.parts);
   hipError_t err;
   if (d.stage1_start != nullptr) {
     err = hipEventRecord(d.stage1_start, stream);
@@ -532,7 +560,7 @@ hipError_t launch_decode(const DecodeLaunch& d, hipStream_t stream) {
   a2.part_acc = d.part_acc;
   a2.part_ml = d.part_ml;
   a2.out = d.out;
-  a2.num_q_heads = d.num_kv_heads * kGroup;
+  a2.num_q_heads = d.num_q_heads;
   a2.tokens_per_split = d.tokens_per_split;
   a2.num_splits = d.num_splits;
   a2.batch = d.batch;

@@ -7,6 +7,16 @@
 
 namespace ga {
 
+// Query heads per kv head (the GQA group G = H_q / H_kv) that the kernels
+// handle in one workgroup: at most 8.  Groups of up to 8 run whole (missing
+// head slots are idle); even groups of 10..16 run as two halves of G/2 heads,
+// each half streaming the kv head's K/V.
+constexpr int kMaxHeadsPerPart = 8;
+inline int head_parts(int group) { return group > kMaxHeadsPerPart ? 2 : 1; }
+inline bool group_supported(int group) {
+  return group >= 1 && (group <= kMaxHeadsPerPart || (group <= 2 * kMaxHeadsPerPart && group % 2 == 0));
+}
+
 struct DecodeLaunch {
   const uint16_t* q;
   const uint16_t* gate;
@@ -19,6 +29,7 @@ struct DecodeLaunch {
   float* part_ml;   // workspace: [B][H_q][num_splits][2] fp32
   float scale;
   int batch;
+  int num_q_heads;
   int num_kv_heads;
   int max_pages;
   long long num_pages;
@@ -38,6 +49,7 @@ struct PrefillLaunch {
   int causal;
   int batch;
   int seq_len;
+  int num_q_heads;
   int num_kv_heads;
 };
 

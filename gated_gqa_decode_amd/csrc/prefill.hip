@@ -40,7 +40,6 @@ namespace ga {
 namespace {
 
 constexpr int kD = 256;
-constexpr int kGroup = 8;
 constexpr int kBM = 16;    // query positions per workgroup
 constexpr int kBN = 64;    // keys per tile
 constexpr int kKRow = kD + 8;    // K row stride in LDS (bf16 elements): +16 B
@@ -63,21 +62,24 @@ struct PrefillArgs {
   float scale_log2;
   int causal;
   int seq_len;
+  int num_q_heads;
   int num_kv_heads;
+  int parts;           // workgroups per (sequence, kv head, query tile): 1 or 2
+  int heads_per_part;  // query heads of a workgroup: G or G / 2 (<= 8)
   int batch;
   int num_m_tiles;
 };
 
 // Workgroup order.  Workgroups are dispatched round-robin over the 8 XCDs of
 // an MI355X, each with its own L2.  Every query tile of one (sequence, kv
-// head) slice re-reads that slice's K/V, so the slices are pinned to XCDs
+// head, head part) slice re-reads that slice's K/V, so the slices are pinned to XCDs
 // (8 / slices XCDs per slice, or slices / 8 slices per XCD) to keep a slice's
 // K/V in one L2, and within an XCD the heaviest causal tiles (latest query
 // positions) go first.  Returns false for the few padding ids of the grid.
 constexpr int kXcds = 8;
 
-__device__ __forceinline__ bool map_workgroup(const PrefillArgs& a, int id, int& mt, int& g, int& b) {
-  const int slices = a.batch * a.num_kv_heads;
+__device__ __forceinline__ bool map_workgroup(const PrefillArgs& a, int id, int& mt, int& gp, int& b) {
+  const int slices = a.batch * a.num_kv_heads * a.parts;
   const int nm = a.num_m_tiles;
   int slice, slot;
   const int xcd = id % kXcds, k = id / kXcds;
@@ -95,8 +97,8 @@ __device__ __forceinline__ bool map_workgroup(const PrefillArgs& a, int id, int&
   }
   if (slot >= nm) return false;
   mt = nm - 1 - slot;
-  g = slice % a.num_kv_heads;
-  b = slice / a.num_kv_heads;
+  gp = slice % (a.num_kv_heads * a.parts);  // kv head * parts + part
+  b = slice / (a.num_kv_heads * a.parts);
   return true;
 }
 
@@ -138,14 +140,18 @@ __device__ __forceinline__ uint32_t cvt_pk_bf16(float x, float y) {
 __global__ __launch_bounds__(kThreads) void prefill_gate_kernel(PrefillArgs a) {
   __shared__ TileBuf buf[2];
 
-  int mt, g, b;
-  if (!map_workgroup(a, (int)blockIdx.x, mt, g, b)) return;
+  int mt, gp, b;
+  if (!map_workgroup(a, (int)blockIdx.x, mt, gp, b)) return;
   const int S = a.seq_len;
   const int Hkv = a.num_kv_heads;
-  const int Hq = Hkv * kGroup;
+  const int Hq = a.num_q_heads;
+  const int g = gp / a.parts;  // kv head
+  const int part = gp - g * a.parts;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int lane = __lane_id();
-  const int h = g * kGroup + wave;
+  // Waves past the workgroup's head count only help stage K/V tiles.
+  const bool active = wave < a.heads_per_part;
+  const int h = g * (Hq / Hkv) + part * a.heads_per_part + min(wave, a.heads_per_part - 1);
   const int p0 = mt * kBM;
 
   const int li = lane & 15;  // query row of this lane's S^T column / MFMA column
@@ -213,130 +219,132 @@ __global__ __launch_bounds__(kThreads) void prefill_gate_kernel(PrefillArgs a) {
     const TileBuf& tb = buf[kt & 1];
     const int j0 = kt * kBN;
 
-    // ---- S^T = K Q^T ---------------------------------------------------------
-    // k-step outer, key tile inner: the four accumulators interleave, so no
-    // MFMA waits on the one just issued.
-    f32x4 st[4];  // st[ct][r] = S[row li][key j0 + 16*ct + 4*lg + r]
+    if (active) {
+      // ---- S^T = K Q^T ---------------------------------------------------------
+      // k-step outer, key tile inner: the four accumulators interleave, so no
+      // MFMA waits on the one just issued.
+      f32x4 st[4];  // st[ct][r] = S[row li][key j0 + 16*ct + 4*lg + r]
 #pragma unroll
-    for (int ct = 0; ct < 4; ++ct) st[ct] = f32x4{0.f, 0.f, 0.f, 0.f};
-    {
-      const uint16_t* krow = &tb.k[li * kKRow + 8 * lg];
-      bf16x8 kf[2][4];
-#pragma unroll
-      for (int ct = 0; ct < 4; ++ct)
-        kf[0][ct] = as_bf16x8(*reinterpret_cast<const uint4*>(krow + ct * 16 * kKRow));
-#pragma unroll
-      for (int s = 0; s < 8; ++s) {
-        if (s + 1 < 8) {
-#pragma unroll
-          for (int ct = 0; ct < 4; ++ct)
-            kf[(s + 1) & 1][ct] =
-                as_bf16x8(*reinterpret_cast<const uint4*>(krow + ct * 16 * kKRow + 32 * (s + 1)));
-        }
+      for (int ct = 0; ct < 4; ++ct) st[ct] = f32x4{0.f, 0.f, 0.f, 0.f};
+      {
+        const uint16_t* krow = &tb.k[li * kKRow + 8 * lg];
+        bf16x8 kf[2][4];
 #pragma unroll
         for (int ct = 0; ct < 4; ++ct)
-          st[ct] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf[s & 1][ct], qf[s], st[ct], 0, 0, 0);
+          kf[0][ct] = as_bf16x8(*reinterpret_cast<const uint4*>(krow + ct * 16 * kKRow));
+#pragma unroll
+        for (int s = 0; s < 8; ++s) {
+          if (s + 1 < 8) {
+#pragma unroll
+            for (int ct = 0; ct < 4; ++ct)
+              kf[(s + 1) & 1][ct] =
+                  as_bf16x8(*reinterpret_cast<const uint4*>(krow + ct * 16 * kKRow + 32 * (s + 1)));
+          }
+#pragma unroll
+          for (int ct = 0; ct < 4; ++ct)
+            st[ct] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf[s & 1][ct], qf[s], st[ct], 0, 0, 0);
+        }
       }
-    }
 
-    // ---- mask, lazy online softmax (row li), split P ------------------------
-    // Only a tile that reaches past the first row of the query tile (causal)
-    // or past the last key needs the mask; the test is uniform.
-    const bool need_mask = (j0 + kBN > kv_end) || (a.causal && j0 + kBN - 1 > p0);
-    float sv_[4][4];
-    bool raise = false;
-#pragma unroll
-    for (int ct = 0; ct < 4; ++ct)
-#pragma unroll
-      for (int r = 0; r < 4; ++r) sv_[ct][r] = st[ct][r] * a.scale_log2;
-    if (need_mask) {
+      // ---- mask, lazy online softmax (row li), split P ------------------------
+      // Only a tile that reaches past the first row of the query tile (causal)
+      // or past the last key needs the mask; the test is uniform.
+      const bool need_mask = (j0 + kBN > kv_end) || (a.causal && j0 + kBN - 1 > p0);
+      float sv_[4][4];
+      bool raise = false;
 #pragma unroll
       for (int ct = 0; ct < 4; ++ct)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) sv_[ct][r] = st[ct][r] * a.scale_log2;
+      if (need_mask) {
+#pragma unroll
+        for (int ct = 0; ct < 4; ++ct)
+#pragma unroll
+          for (int r = 0; r < 4; ++r) {
+            const int kj = j0 + ct * 16 + 4 * lg + r;
+            const bool ok = (kj < kv_end) && (!a.causal || kj <= qi);
+            sv_[ct][r] = ok ? sv_[ct][r] : -INFINITY;
+          }
+      }
+#pragma unroll
+      for (int ct = 0; ct < 4; ++ct)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) raise |= sv_[ct][r] > m_ref + kSlack;
+      if (__builtin_amdgcn_ballot_w64(raise) != 0) {  // wave-uniform, rare
+        float mx = -INFINITY;
+#pragma unroll
+        for (int ct = 0; ct < 4; ++ct)
+#pragma unroll
+          for (int r = 0; r < 4; ++r) mx = fmaxf(mx, sv_[ct][r]);
+        mx = fmaxf(mx, shfl_xor(mx, 16));
+        mx = fmaxf(mx, shfl_xor(mx, 32));
+        const float m_new = fmaxf(m_ref, mx);
+        // a row with no visible key so far keeps -inf; its factor is then 1
+        const float alpha = (m_new == -INFINITY) ? 1.f : __builtin_amdgcn_exp2f(m_ref - m_new);
+        l_row *= alpha;
+        m_ref = m_new;
+        // O holds rows 4*lg + r: fetch those rows' factors from lanes li = 4*lg + r
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
-          const int kj = j0 + ct * 16 + 4 * lg + r;
-          const bool ok = (kj < kv_end) && (!a.causal || kj <= qi);
-          sv_[ct][r] = ok ? sv_[ct][r] : -INFINITY;
+          const float ar = __int_as_float(
+              __builtin_amdgcn_ds_bpermute((4 * lg + r) << 2, __float_as_int(alpha)));
+#pragma unroll
+          for (int t = 0; t < 16; ++t) o[t][r] *= ar;
         }
-    }
-#pragma unroll
-    for (int ct = 0; ct < 4; ++ct)
-#pragma unroll
-      for (int r = 0; r < 4; ++r) raise |= sv_[ct][r] > m_ref + kSlack;
-    if (__builtin_amdgcn_ballot_w64(raise) != 0) {  // wave-uniform, rare
-      float mx = -INFINITY;
-#pragma unroll
-      for (int ct = 0; ct < 4; ++ct)
-#pragma unroll
-        for (int r = 0; r < 4; ++r) mx = fmaxf(mx, sv_[ct][r]);
-      mx = fmaxf(mx, shfl_xor(mx, 16));
-      mx = fmaxf(mx, shfl_xor(mx, 32));
-      const float m_new = fmaxf(m_ref, mx);
-      // a row with no visible key so far keeps -inf; its factor is then 1
-      const float alpha = (m_new == -INFINITY) ? 1.f : __builtin_amdgcn_exp2f(m_ref - m_new);
-      l_row *= alpha;
-      m_ref = m_new;
-      // O holds rows 4*lg + r: fetch those rows' factors from lanes li = 4*lg + r
-#pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const float ar = __int_as_float(
-            __builtin_amdgcn_ds_bpermute((4 * lg + r) << 2, __float_as_int(alpha)));
-#pragma unroll
-        for (int t = 0; t < 16; ++t) o[t][r] *= ar;
       }
-    }
-    // p = hi + lo, both bf16 (hardware round-to-nearest-even conversion); the
-    // row sum takes p itself (hi + lo equals p to ~2^-18 relative).
-    const float mref_safe = (m_ref == -INFINITY) ? 0.f : m_ref;
-    uint32_t phw[2][4], plw[2][4];  // packed bf16 A operands, k-step ks = ct / 2
+      // p = hi + lo, both bf16 (hardware round-to-nearest-even conversion); the
+      // row sum takes p itself (hi + lo equals p to ~2^-18 relative).
+      const float mref_safe = (m_ref == -INFINITY) ? 0.f : m_ref;
+      uint32_t phw[2][4], plw[2][4];  // packed bf16 A operands, k-step ks = ct / 2
 #pragma unroll
-    for (int ct = 0; ct < 4; ++ct) {
+      for (int ct = 0; ct < 4; ++ct) {
 #pragma unroll
-      for (int rp = 0; rp < 2; ++rp) {
-        const float pa = __builtin_amdgcn_exp2f(sv_[ct][2 * rp] - mref_safe);
-        const float pb = __builtin_amdgcn_exp2f(sv_[ct][2 * rp + 1] - mref_safe);
-        l_row += pa + pb;
-        const uint32_t hi = cvt_pk_bf16(pa, pb);
-        const uint32_t lo = cvt_pk_bf16(pa - bf16_lo(hi), pb - bf16_hi(hi));
-        phw[ct >> 1][(ct & 1) * 2 + rp] = hi;
-        plw[ct >> 1][(ct & 1) * 2 + rp] = lo;
+        for (int rp = 0; rp < 2; ++rp) {
+          const float pa = __builtin_amdgcn_exp2f(sv_[ct][2 * rp] - mref_safe);
+          const float pb = __builtin_amdgcn_exp2f(sv_[ct][2 * rp + 1] - mref_safe);
+          l_row += pa + pb;
+          const uint32_t hi = cvt_pk_bf16(pa, pb);
+          const uint32_t lo = cvt_pk_bf16(pa - bf16_lo(hi), pb - bf16_hi(hi));
+          phw[ct >> 1][(ct & 1) * 2 + rp] = hi;
+          plw[ct >> 1][(ct & 1) * 2 + rp] = lo;
+        }
       }
-    }
 
-    // ---- O += P V  (B operand through the LDS transpose read) ---------------
-    // The V fragments of the next group of four column tiles are requested
-    // before the current group's MFMAs are issued.
+      // ---- O += P V  (B operand through the LDS transpose read) ---------------
+      // The V fragments of the next group of four column tiles are requested
+      // before the current group's MFMAs are issued.
 #pragma unroll
-    for (int ks = 0; ks < 2; ++ks) {
-      const bf16x8 ph = as_bf16x8(make_uint4(phw[ks][0], phw[ks][1], phw[ks][2], phw[ks][3]));
-      const bf16x8 pl = as_bf16x8(make_uint4(plw[ks][0], plw[ks][1], plw[ks][2], plw[ks][3]));
-      // k-slots 0..3: keys 32ks + 4lg + 0..3; k-slots 4..7: keys 32ks + 16 + 4lg + 0..3
-      const uint16_t* v0 = &tb.v[(32 * ks + 4 * lg + (li >> 2)) * kVRow + 4 * (li & 3)];
-      const uint16_t* v1 = v0 + 16 * kVRow;
-      bf16x8 vf[2][4];
+      for (int ks = 0; ks < 2; ++ks) {
+        const bf16x8 ph = as_bf16x8(make_uint4(phw[ks][0], phw[ks][1], phw[ks][2], phw[ks][3]));
+        const bf16x8 pl = as_bf16x8(make_uint4(plw[ks][0], plw[ks][1], plw[ks][2], plw[ks][3]));
+        // k-slots 0..3: keys 32ks + 4lg + 0..3; k-slots 4..7: keys 32ks + 16 + 4lg + 0..3
+        const uint16_t* v0 = &tb.v[(32 * ks + 4 * lg + (li >> 2)) * kVRow + 4 * (li & 3)];
+        const uint16_t* v1 = v0 + 16 * kVRow;
+        bf16x8 vf[2][4];
 #pragma unroll
-      for (int u = 0; u < 4; ++u) {
-        const uint2 a0 = tr_read(v0 + 16 * u);
-        const uint2 a1 = tr_read(v1 + 16 * u);
-        vf[0][u] = as_bf16x8(make_uint4(a0.x, a0.y, a1.x, a1.y));
-      }
-#pragma unroll
-      for (int tg = 0; tg < 4; ++tg) {
-        if (tg + 1 < 4) {
-#pragma unroll
-          for (int u = 0; u < 4; ++u) {
-            const int t = 4 * (tg + 1) + u;
-            const uint2 a0 = tr_read(v0 + 16 * t);
-            const uint2 a1 = tr_read(v1 + 16 * t);
-            vf[(tg + 1) & 1][u] = as_bf16x8(make_uint4(a0.x, a0.y, a1.x, a1.y));
-          }
+        for (int u = 0; u < 4; ++u) {
+          const uint2 a0 = tr_read(v0 + 16 * u);
+          const uint2 a1 = tr_read(v1 + 16 * u);
+          vf[0][u] = as_bf16x8(make_uint4(a0.x, a0.y, a1.x, a1.y));
         }
 #pragma unroll
-        for (int u = 0; u < 4; ++u)
-          o[4 * tg + u] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ph, vf[tg & 1][u], o[4 * tg + u], 0, 0, 0);
+        for (int tg = 0; tg < 4; ++tg) {
+          if (tg + 1 < 4) {
 #pragma unroll
-        for (int u = 0; u < 4; ++u)
-          o[4 * tg + u] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(pl, vf[tg & 1][u], o[4 * tg + u], 0, 0, 0);
+            for (int u = 0; u < 4; ++u) {
+              const int t = 4 * (tg + 1) + u;
+              const uint2 a0 = tr_read(v0 + 16 * t);
+              const uint2 a1 = tr_read(v1 + 16 * t);
+              vf[(tg + 1) & 1][u] = as_bf16x8(make_uint4(a0.x, a0.y, a1.x, a1.y));
+            }
+          }
+#pragma unroll
+          for (int u = 0; u < 4; ++u)
+            o[4 * tg + u] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ph, vf[tg & 1][u], o[4 * tg + u], 0, 0, 0);
+#pragma unroll
+          for (int u = 0; u < 4; ++u)
+            o[4 * tg + u] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(pl, vf[tg & 1][u], o[4 * tg + u], 0, 0, 0);
+        }
       }
     }
 
@@ -349,6 +357,7 @@ __global__ __launch_bounds__(kThreads) void prefill_gate_kernel(PrefillArgs a) {
   }
 
   // ---- epilogue: O / l -> bf16, gate, store ------------------------------------
+  if (!active) return;
   l_row += shfl_xor(l_row, 16);  // the row's four lanes hold disjoint keys
   l_row += shfl_xor(l_row, 32);
 #pragma unroll
@@ -377,10 +386,14 @@ hipError_t launch_prefill(const PrefillLaunch& p, hipStream_t stream) {
   a.scale_log2 = p.scale * kLog2e;
   a.causal = p.causal;
   a.seq_len = p.seq_len;
+  a.num_q_heads = p.num_q_heads;
   a.num_kv_heads = p.num_kv_heads;
+  const int group = p.num_q_heads / p.num_kv_heads;
+  a.parts = head_parts(group);
+  a.heads_per_part = group / a.parts;
   a.batch = p.batch;
   a.num_m_tiles = (p.seq_len + kBM - 1) / kBM;
-  dim3 grid(grid_size(p.batch * p.num_kv_heads, a.num_m_tiles));
+  dim3 grid(grid_size(p.batch * p.num_kv_heads * a.parts, a.num_m_tiles));
   hipLaunchKernelGGL(prefill_gate_kernel, grid, dim3(kThreads), 0, stream, a);
   return hipGetLastError();
 }

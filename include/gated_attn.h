@@ -47,11 +47,20 @@ typedef enum ga_status {
     GA_ERR_HIP = 4                  /* the HIP runtime reported an error; see gated_attn_last_hip_error() */
 } ga_status;
 
+/* GQA groups (both entry points).  Query head h attends with kv head
+ * h / G, G = H_q / H_kv (contiguous groups: cuDNN "Gated Attention Block",
+ * Overview, stage (4), GQA H_q / H_kv).  Served: G = 1..8, and even G up to
+ * 16 -- among them the h_q = 32, h_kv = 2 geometry of that page's Performance
+ * section and the non-power-of-two groups the FreeToken PR #781 tests
+ * (Correctness and actual execution).  G = 10..16 runs as two workgroups per
+ * kv head, each streaming that head's K/V.  Other G: GA_ERR_UNSUPPORTED;
+ * H_q not a multiple of H_kv: GA_ERR_INVALID_ARGUMENT. */
+
 /* Shape of a paged decode call. */
 typedef struct ga_decode_dims {
     int32_t batch;             /* B >= 0 sequences, one query token each */
     int32_t num_q_heads;       /* H_q */
-    int32_t num_kv_heads;      /* H_kv; H_q / H_kv must be 8 */
+    int32_t num_kv_heads;      /* H_kv, dividing H_q; see GQA groups below */
     int32_t head_dim;          /* D; must be 256 */
     int32_t page_size;         /* tokens per page; must be 16 */
     int32_t max_pages_per_seq; /* W: columns of block_table (the allocated capacity) */
@@ -69,7 +78,9 @@ typedef struct ga_decode_plan {
 } ga_decode_plan;
 
 /* Fill *plan for dims.  GA_ERR_INVALID_ARGUMENT / GA_ERR_UNSUPPORTED as
- * gated_attn_decode would return for these dims. */
+ * gated_attn_decode would return for these dims (GA_ERR_UNSUPPORTED also when
+ * the split grid would exceed one launch: more than 2^22 stage-1 workgroups,
+ * or B * H_q > 2^26). */
 ga_status gated_attn_decode_plan(const ga_decode_dims *dims, ga_decode_plan *plan);
 
 /* Bytes of device workspace gated_attn_decode needs for dims (0 if dims are
@@ -120,7 +131,7 @@ typedef struct ga_prefill_dims {
     int32_t batch;        /* B >= 0 */
     int32_t seq_len;      /* S >= 0 */
     int32_t num_q_heads;  /* H_q */
-    int32_t num_kv_heads; /* H_kv; H_q / H_kv must be 8 */
+    int32_t num_kv_heads; /* H_kv, dividing H_q; see GQA groups below */
     int32_t head_dim;     /* D; must be 256 */
 } ga_prefill_dims;
 

@@ -58,6 +58,28 @@ def test_plan_covers_capacity(B, W):
     assert ga.decode_workspace_size(_dims(batch=B, max_pages_per_seq=W)) == p.workspace_bytes
 
 
+@pytest.mark.parametrize("G", [1, 2, 3, 4, 5, 6, 7, 8, 10, 12, 14, 16])
+def test_supported_groups_plan(G):
+    """Groups up to 8 use one workgroup per (sequence, kv head, split); even
+    groups of 10..16 use two, which the split plan counts."""
+    d = _dims(batch=64, num_q_heads=2 * G, num_kv_heads=2, max_pages_per_seq=256)
+    p = ga.decode_plan(d)
+    parts = 2 if G > 8 else 1
+    units = 64 * 2 * parts
+    t = -(-(4096 * units) // 256)
+    t = min(max(-(-t // 64) * 64, 64), 2048)
+    assert p.tokens_per_split == t
+    assert p.workspace_bytes >= 64 * 2 * G * p.num_splits * 258 * 4
+
+
+def test_oversize_stage1_grid_is_declined():
+    """B * H_kv * splits beyond one launch's grid: declined before any launch."""
+    d = _dims(batch=65535, num_q_heads=64, num_kv_heads=8, max_pages_per_seq=2048)
+    p = ga.DecodePlan()
+    assert ga.lib.gated_attn_decode_plan(ctypes.byref(d), ctypes.byref(p)) == ga.GA_ERR_UNSUPPORTED
+    assert ga.decode_workspace_size(d) == 0
+
+
 def test_plan_depends_on_capacity_not_lengths():
     a = ga.decode_plan(_dims(batch=64, max_pages_per_seq=256))
     b = ga.decode_plan(_dims(batch=64, max_pages_per_seq=256, num_pages=1 << 30))
@@ -66,8 +88,10 @@ def test_plan_depends_on_capacity_not_lengths():
 
 @pytest.mark.parametrize("kw,status", [
     (dict(head_dim=128), ga.GA_ERR_UNSUPPORTED),
-    (dict(num_q_heads=8), ga.GA_ERR_UNSUPPORTED),          # group of 4
-    (dict(num_q_heads=32), ga.GA_ERR_UNSUPPORTED),         # group of 16
+    (dict(num_q_heads=18), ga.GA_ERR_UNSUPPORTED),         # group of 9 (odd, > 8)
+    (dict(num_q_heads=30), ga.GA_ERR_UNSUPPORTED),         # group of 15
+    (dict(num_q_heads=34), ga.GA_ERR_UNSUPPORTED),         # group of 17
+    (dict(num_q_heads=64, num_kv_heads=2), ga.GA_ERR_UNSUPPORTED),  # group of 32
     (dict(num_q_heads=15), ga.GA_ERR_INVALID_ARGUMENT),    # not a multiple of H_kv
     (dict(page_size=32), ga.GA_ERR_UNSUPPORTED),
     (dict(page_size=0), ga.GA_ERR_INVALID_ARGUMENT),
@@ -136,7 +160,8 @@ def test_empty_batch_is_a_no_op():
 
 @pytest.mark.parametrize("dims,status", [
     ((2, 128, 16, 2, 128), ga.GA_ERR_UNSUPPORTED),
-    ((2, 128, 16, 4, 256), ga.GA_ERR_UNSUPPORTED),
+    ((2, 128, 18, 2, 256), ga.GA_ERR_UNSUPPORTED),
+    ((2, 128, 66, 2, 256), ga.GA_ERR_UNSUPPORTED),
     ((2, 128, 15, 2, 256), ga.GA_ERR_INVALID_ARGUMENT),
     ((-1, 128, 16, 2, 256), ga.GA_ERR_INVALID_ARGUMENT),
     ((2, -5, 16, 2, 256), ga.GA_ERR_INVALID_ARGUMENT),

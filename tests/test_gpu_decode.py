@@ -29,6 +29,26 @@ def test_workload_parity(wl):
         assert pad.sum() == 11
 
 
+@pytest.mark.parametrize("Hq,Hkv", [(32, 2), (24, 2), (20, 2), (12, 2), (14, 2), (8, 2),
+                                     (2, 2), (7, 1), (6, 3), (40, 8), (3, 1), (16, 1)])
+def test_gqa_group_sizes(Hq, Hkv):
+    """Groups 1..8 (idle head slots) and even groups 10..16 (two workgroups
+    per kv head), over ragged lengths, several splits and a dead row."""
+    lens = [700, 1, 2049, 0, 64, 333]
+    c = workloads.make_decode(f"gqa_{Hq}_{Hkv}", lens, seed=70 + Hq + Hkv, num_q_heads=Hq,
+                              num_kv_heads=Hkv, max_pages_per_seq=160)
+    res = decode_parity(c)
+    assert res["ok"], res
+
+
+def test_group16_full_size():
+    """H_q = 32, H_kv = 2 at B = 64, L = 4096, every output element."""
+    c = workloads.make_decode("decode_b64_l4096_hq32", [4096] * 64, seed=72, num_q_heads=32,
+                              num_kv_heads=2, max_pages_per_seq=256)
+    res = decode_parity(c)
+    assert res["ok"], res
+
+
 def test_ragged_lengths_across_steps_pages_and_splits():
     lens = [1, 2, 7, 8, 9, 15, 16, 17, 31, 32, 33, 63, 64, 65, 100, 257, 513, 640]
     c = workloads.make_decode("ragged", lens, seed=31, max_pages_per_seq=48, extra_pages=7)
