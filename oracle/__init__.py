@@ -60,6 +60,19 @@ def _load():
         ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int,
         ctypes.c_int64, _u16p, _f64p, _f64p, ctypes.c_int,
     ]
+    lib.oracle_decode_ex.restype = ctypes.c_int
+    lib.oracle_decode_ex.argtypes = [
+        _u16p, _u16p, _u16p, _u16p, _i32p, _i32p, ctypes.c_double,
+        ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int,
+        ctypes.c_int64, _f64p, ctypes.c_int, _u16p, _f64p, _f64p, _f64p, ctypes.c_int,
+    ]
+    lib.oracle_prefill_ex.restype = ctypes.c_int
+    lib.oracle_prefill_ex.argtypes = [
+        _u16p, _u16p, _u16p, _u16p, ctypes.c_double, ctypes.c_int,
+        ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int,
+        _i32p, _f64p, ctypes.c_int,
+        _i32p, ctypes.c_int, _u16p, _f64p, _f64p, _f64p, ctypes.c_int,
+    ]
     lib.oracle_prefill.restype = ctypes.c_int
     lib.oracle_prefill.argtypes = [
         _u16p, _u16p, _u16p, _u16p, ctypes.c_double, ctypes.c_int,
@@ -132,12 +145,24 @@ class OracleError(RuntimeError):
     pass
 
 
-def decode(q, gate, k_pool, v_pool, block_table, seq_lens, scale, nthreads=None):
+def _sinks(sinks, Hq):
+    if sinks is None:
+        return None, None
+    sk = np.ascontiguousarray(sinks, dtype=np.float64).reshape(-1)
+    assert sk.shape == (Hq,), "one sink logit per query head"
+    return sk, _ptr(sk, ctypes.c_double)
+
+
+def decode(q, gate, k_pool, v_pool, block_table, seq_lens, scale, nthreads=None, *,
+           sinks=None, window=0, return_lse=False):
     """Gated GQA decode over a paged pool.
 
     q, gate: [B, H_q, D] bf16 bits; k_pool, v_pool: [P, page, H_kv, D];
     block_table: [B, W] int32; seq_lens: [B] int32.
-    Returns (out bits [B,H_q,D], O fp64 [B,H_q,D], Mref fp64 [B,H_q,D]).
+    sinks: optional [H_q] sink logits; window > 0 keeps the last `window` keys.
+    Returns (out bits [B,H_q,D], O fp64 [B,H_q,D], Mref fp64 [B,H_q,D]) and,
+    with return_lse, also lse fp64 [B, H_q] (natural log of the softmax
+    denominator, -inf for a row with no visible key and no sink).
     """
     lib = _load()
     q, gate, k_pool, v_pool = (_u16(a) for a in (q, gate, k_pool, v_pool))
@@ -150,23 +175,31 @@ def decode(q, gate, k_pool, v_pool, block_table, seq_lens, scale, nthreads=None)
     out = np.zeros((B, Hq, D), dtype=np.uint16)
     o = np.zeros((B, Hq, D), dtype=np.float64)
     mref = np.zeros((B, Hq, D), dtype=np.float64)
-    st = lib.oracle_decode(
+    lse = np.zeros((B, Hq), dtype=np.float64)
+    sk, sk_p = _sinks(sinks, Hq)
+    st = lib.oracle_decode_ex(
         _ptr(q, ctypes.c_uint16), _ptr(gate, ctypes.c_uint16),
         _ptr(k_pool, ctypes.c_uint16), _ptr(v_pool, ctypes.c_uint16),
         _ptr(block_table, ctypes.c_int32), _ptr(seq_lens, ctypes.c_int32),
-        float(scale), B, Hq, Hkv, D, page, W, P,
+        float(scale), B, Hq, Hkv, D, page, W, P, sk_p, int(window),
         _ptr(out, ctypes.c_uint16), _ptr(o, ctypes.c_double), _ptr(mref, ctypes.c_double),
-        nthreads or default_threads())
+        _ptr(lse, ctypes.c_double), nthreads or default_threads())
     if st != 0:
         raise OracleError(f"oracle_decode failed with status {st}")
+    if return_lse:
+        return out, o, mref, lse
     return out, o, mref
 
 
-def prefill(q, gate, k, v, scale, causal=True, rows=None, nthreads=None):
+def prefill(q, gate, k, v, scale, causal=True, rows=None, nthreads=None, *, seq_lens=None,
+            sinks=None, window=0, return_lse=False):
     """Gated dense prefill.  q, gate: [B,S,H_q,D]; k, v: [B,S,H_kv,D].
 
     rows: optional int array [n, 2] of (b, i) query positions; results are
     then [n, H_q, D].  Without rows, results are [B, S, H_q, D].
+    seq_lens: optional [B] key lengths (keys j >= seq_lens[b] are masked);
+    sinks: optional [H_q] sink logits; window > 0: row i sees keys j > i - window.
+    With return_lse also returns lse fp64 ([n, H_q] or [B, S, H_q]).
     """
     lib = _load()
     q, gate, k, v = (_u16(a) for a in (q, gate, k, v))
@@ -185,12 +218,21 @@ def prefill(q, gate, k, v, scale, causal=True, rows=None, nthreads=None):
     out = np.zeros(shape, dtype=np.uint16)
     o = np.zeros(shape, dtype=np.float64)
     mref = np.zeros(shape, dtype=np.float64)
-    st = lib.oracle_prefill(
+    lse = np.zeros(shape[:-1], dtype=np.float64)
+    sl_p = None
+    if seq_lens is not None:
+        seq_lens = np.ascontiguousarray(seq_lens, dtype=np.int32).reshape(-1)
+        assert seq_lens.shape == (B,)
+        sl_p = _ptr(seq_lens, ctypes.c_int32)
+    sk, sk_p = _sinks(sinks, Hq)
+    st = lib.oracle_prefill_ex(
         _ptr(q, ctypes.c_uint16), _ptr(gate, ctypes.c_uint16),
         _ptr(k, ctypes.c_uint16), _ptr(v, ctypes.c_uint16),
-        float(scale), int(bool(causal)), B, S, Hq, Hkv, D, rows_p, n,
+        float(scale), int(bool(causal)), B, S, Hq, Hkv, D, sl_p, sk_p, int(window), rows_p, n,
         _ptr(out, ctypes.c_uint16), _ptr(o, ctypes.c_double), _ptr(mref, ctypes.c_double),
-        nthreads or default_threads())
+        _ptr(lse, ctypes.c_double), nthreads or default_threads())
     if st != 0:
         raise OracleError(f"oracle_prefill failed with status {st}")
+    if return_lse:
+        return out, o, mref, lse
     return out, o, mref

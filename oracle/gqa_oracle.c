@@ -18,6 +18,16 @@
  *                                                           bf16 values is exact)
  *   A row with L <= 0 (padded slot / dead row) gives out = +0.
  *
+ * Attention-spec options (the _ex entry points; the plain ones pass none):
+ *   visible keys   j < L, and with a window w > 0 only the last w of them
+ *                  (decode: j >= L - w; prefill row i: j > i - w), and in
+ *                  prefill with per-sequence key lengths also j < len[b]
+ *   sink           a per-head logit that joins the softmax denominator only:
+ *                  Z = sum_visible exp(s_j) + exp(sink_h)
+ *   O              sum_visible exp(s_j) V_j / Z      (0 when Z = 0)
+ *   lse            ln Z  (-inf when Z = 0), the softmax statistic of the row
+ *   A row with no visible key is dead: out = +0 (its lse is the sink, or -inf).
+ *
  * Sources (page title, then the part of the page):
  *  - cuDNN FE-OSS "Gated Attention Block (SM107)", Overview, stage (4) SDPA
  *    (softmax(Q K^T * scale + mask) V with GQA H_q / H_kv) and stage (5) gate
@@ -39,6 +49,13 @@
  *  - Paged pool layout [num_pages][page_size][H_kv][D]; token j of sequence b is
  *    slot j % page_size of page block_table[b][j / page_size].
  *  - Causal prefill with S_q == S_kv: key j is visible to query i iff j <= i.
+ *  - Window, sinks, lse and per-sequence key lengths: the pages name them (the
+ *    FreeToken PR's dispatch excludes windows and sinks; the cuDNN page's
+ *    Forward offers return_lse, "softmax stats [B, H_q, S] fp32", and
+ *    seq_lens_present, per-batch KV lengths) without defining them; the
+ *    definitions above are the plain ones: a window keeps the w most recent
+ *    keys, a sink is an extra logit with a zero value row, lse = ln Z in
+ *    natural-log units, and key lengths mask keys only.
  */
 #include <math.h>
 #include <pthread.h>
@@ -137,15 +154,18 @@ uint16_t oracle_gate_output(uint16_t ob, uint16_t sigma_b)
 
 /* ---------------------------------------------------------------------------
  * One attention row (cuDNN Gated Attention Block page, Overview stage (4)).
- * krows[j] / vrows[j] point at the D bf16 values of key / value j.
- * o[d] receives O in fp64; mref[d] receives sum_j p_j |V_j[d]| / sum_j p_j,
- * the magnitude the fp64 sum was formed from (used to size the tolerance).
+ * krows[j] / vrows[j] point at the D bf16 values of the L visible keys /
+ * values (L may be 0).  sink: NULL, or the row's sink logit.
+ * o[d] receives O in fp64; mref[d] receives sum_j p_j |V_j[d]| / Z, the
+ * magnitude the fp64 sum was formed from (used to size the tolerance);
+ * *lse receives ln Z.  Returns 0 for a row with Z = 0 (no visible key and no
+ * sink, or a sink of -inf), else 1.
  * ------------------------------------------------------------------------- */
-static void attend_row(const uint16_t *qrow, const uint16_t *const *krows,
-                       const uint16_t *const *vrows, int L, int D, double scale,
-                       double *scores, double *o, double *mref)
+static int attend_row(const uint16_t *qrow, const uint16_t *const *krows,
+                      const uint16_t *const *vrows, int L, int D, double scale,
+                      const double *sink, double *scores, double *o, double *mref, double *lse)
 {
-    double m = -INFINITY;
+    double m = sink ? *sink : -INFINITY;
     for (int j = 0; j < L; ++j) {
         double dot = 0.0;
         for (int d = 0; d < D; ++d)
@@ -154,7 +174,13 @@ static void attend_row(const uint16_t *qrow, const uint16_t *const *krows,
         if (scores[j] > m)
             m = scores[j];
     }
-    double den = 0.0;
+    if (m == -INFINITY) { /* Z = 0: no visible key, and no sink (or a sink of -inf) */
+        for (int d = 0; d < D; ++d)
+            o[d] = mref[d] = 0.0;
+        *lse = -INFINITY;
+        return 0;
+    }
+    double den = sink ? exp(*sink - m) : 0.0;
     for (int j = 0; j < L; ++j) {
         scores[j] = exp(scores[j] - m); /* now p_j */
         den += scores[j];
@@ -169,6 +195,8 @@ static void attend_row(const uint16_t *qrow, const uint16_t *const *krows,
         o[d] = num / den;
         mref[d] = mag / den;
     }
+    *lse = m + log(den);
+    return 1;
 }
 
 /* Gate epilogue for one row (stage (5) of the cuDNN page with the bf16
@@ -198,6 +226,9 @@ typedef struct {
     int64_t num_pages;
     uint16_t *out;
     double *o_f64, *mref;
+    const double *sinks; /* [H_q] or NULL */
+    int window;          /* > 0: only the last `window` keys are visible */
+    double *lse;         /* [B][H_q] or NULL */
     int nthreads, tid;
     int status;
 } decode_job;
@@ -221,30 +252,35 @@ static void *decode_worker(void *arg)
         int b = row / Hq, h = row % Hq, g = h / group;
         size_t rbase = ((size_t)b * Hq + h) * D;
         int L = job->seq_lens[b];
-        if (L <= 0) {
-            for (int d = 0; d < D; ++d) {
-                job->out[rbase + d] = 0;
-                o[d] = 0.0;
-                mref[d] = 0.0;
-            }
-        } else {
-            if (L > maxL) {
-                job->status = ORACLE_EBADARG;
+        if (L > maxL) {
+            job->status = ORACLE_EBADARG;
+            goto done;
+        }
+        int j0 = 0; /* first visible key */
+        if (job->window > 0 && L - job->window > 0)
+            j0 = L - job->window;
+        int nvis = L > j0 ? L - j0 : 0;
+        for (int j = j0; j < L; ++j) {
+            int32_t page = job->block_table[(size_t)b * job->max_pages + j / ps];
+            if (page < 0 || page >= job->num_pages) {
+                job->status = ORACLE_EPAGE;
                 goto done;
             }
-            for (int j = 0; j < L; ++j) {
-                int32_t page = job->block_table[(size_t)b * job->max_pages + j / ps];
-                if (page < 0 || page >= job->num_pages) {
-                    job->status = ORACLE_EPAGE;
-                    goto done;
-                }
-                size_t off = (((size_t)page * ps + (size_t)(j % ps)) * Hkv + g) * D;
-                krows[j] = job->k_pool + off;
-                vrows[j] = job->v_pool + off;
-            }
-            attend_row(job->q + rbase, krows, vrows, L, D, job->scale, scores, o, mref);
+            size_t off = (((size_t)page * ps + (size_t)(j % ps)) * Hkv + g) * D;
+            krows[j - j0] = job->k_pool + off;
+            vrows[j - j0] = job->v_pool + off;
+        }
+        double lse;
+        attend_row(job->q + rbase, krows, vrows, nvis, D, job->scale,
+                   job->sinks ? &job->sinks[h] : NULL, scores, o, mref, &lse);
+        if (nvis == 0) { /* dead row (padded slot): the dead-row select gives +0 */
+            for (int d = 0; d < D; ++d)
+                job->out[rbase + d] = 0;
+        } else {
             gate_row(o, job->gate + rbase, D, job->out + rbase);
         }
+        if (job->lse)
+            job->lse[(size_t)b * Hq + h] = lse;
         if (job->o_f64)
             memcpy(job->o_f64 + rbase, o, sizeof(double) * (size_t)D);
         if (job->mref)
@@ -280,10 +316,11 @@ static int run_jobs(void *jobs, size_t job_size, int nthreads, void *(*fn)(void 
     return ORACLE_OK;
 }
 
-int oracle_decode(const uint16_t *q, const uint16_t *gate, const uint16_t *k_pool,
-                  const uint16_t *v_pool, const int32_t *block_table, const int32_t *seq_lens,
-                  double scale, int B, int Hq, int Hkv, int D, int page_size, int max_pages,
-                  int64_t num_pages, uint16_t *out, double *o_f64, double *mref, int nthreads)
+int oracle_decode_ex(const uint16_t *q, const uint16_t *gate, const uint16_t *k_pool,
+                     const uint16_t *v_pool, const int32_t *block_table, const int32_t *seq_lens,
+                     double scale, int B, int Hq, int Hkv, int D, int page_size, int max_pages,
+                     int64_t num_pages, const double *sinks, int window, uint16_t *out,
+                     double *o_f64, double *mref, double *lse, int nthreads)
 {
     if (B < 0 || Hq <= 0 || Hkv <= 0 || D <= 0 || page_size <= 0 || max_pages < 0 ||
         num_pages < 0 || Hq % Hkv != 0)
@@ -300,7 +337,7 @@ int oracle_decode(const uint16_t *q, const uint16_t *gate, const uint16_t *k_poo
     for (int t = 0; t < nthreads; ++t) {
         decode_job j = {q, gate, k_pool, v_pool, block_table, seq_lens, scale,
                         B, Hq, Hkv, D, page_size, max_pages, num_pages,
-                        out, o_f64, mref, nthreads, t, ORACLE_OK};
+                        out, o_f64, mref, sinks, window, lse, nthreads, t, ORACLE_OK};
         jobs[t] = j;
     }
     int st = run_jobs(jobs, sizeof(decode_job), nthreads, decode_worker);
@@ -309,6 +346,16 @@ int oracle_decode(const uint16_t *q, const uint16_t *gate, const uint16_t *k_poo
             st = jobs[t].status;
     free(jobs);
     return st;
+}
+
+int oracle_decode(const uint16_t *q, const uint16_t *gate, const uint16_t *k_pool,
+                  const uint16_t *v_pool, const int32_t *block_table, const int32_t *seq_lens,
+                  double scale, int B, int Hq, int Hkv, int D, int page_size, int max_pages,
+                  int64_t num_pages, uint16_t *out, double *o_f64, double *mref, int nthreads)
+{
+    return oracle_decode_ex(q, gate, k_pool, v_pool, block_table, seq_lens, scale, B, Hq, Hkv,
+                            D, page_size, max_pages, num_pages, NULL, 0, out, o_f64, mref,
+                            NULL, nthreads);
 }
 
 /* ---------------------------------------------------------------------------
@@ -326,6 +373,10 @@ typedef struct {
     int nrows;
     uint16_t *out;
     double *o_f64, *mref;
+    const int32_t *seq_lens; /* [B] key lengths or NULL (all S) */
+    const double *sinks;     /* [H_q] or NULL */
+    int window;              /* > 0: row i sees keys j > i - window */
+    double *lse;             /* [nrows][H_q] or NULL */
     int nthreads, tid;
     int status;
 } prefill_job;
@@ -358,16 +409,36 @@ static void *prefill_worker(void *arg)
             job->status = ORACLE_EBADARG;
             goto done;
         }
-        int L = job->causal ? i + 1 : S; /* keys j <= i are visible under the causal mask */
-        for (int j = 0; j < L; ++j) {
+        /* visible keys: [j0, j1) -- key length, causal mask, window */
+        int j1 = S;
+        if (job->seq_lens) {
+            int len = job->seq_lens[b];
+            j1 = len < 0 ? 0 : (len < S ? len : S);
+        }
+        if (job->causal && i + 1 < j1)
+            j1 = i + 1; /* keys j <= i are visible under the causal mask */
+        int j0 = 0;
+        if (job->window > 0 && i - job->window + 1 > 0)
+            j0 = i - job->window + 1;
+        int nvis = j1 > j0 ? j1 - j0 : 0;
+        for (int j = j0; j < j1; ++j) {
             size_t off = (((size_t)b * S + j) * Hkv + g) * D;
-            krows[j] = job->k + off;
-            vrows[j] = job->v + off;
+            krows[j - j0] = job->k + off;
+            vrows[j - j0] = job->v + off;
         }
         size_t qbase = (((size_t)b * S + i) * Hq + h) * D;
         size_t obase = ((size_t)r * Hq + h) * D;
-        attend_row(job->q + qbase, krows, vrows, L, D, job->scale, scores, o, mref);
-        gate_row(o, job->gate + qbase, D, job->out + obase);
+        double lse;
+        attend_row(job->q + qbase, krows, vrows, nvis, D, job->scale,
+                   job->sinks ? &job->sinks[h] : NULL, scores, o, mref, &lse);
+        if (nvis == 0) { /* dead row: +0 */
+            for (int d = 0; d < D; ++d)
+                job->out[obase + d] = 0;
+        } else {
+            gate_row(o, job->gate + qbase, D, job->out + obase);
+        }
+        if (job->lse)
+            job->lse[(size_t)r * Hq + h] = lse;
         if (job->o_f64)
             memcpy(job->o_f64 + obase, o, sizeof(double) * (size_t)D);
         if (job->mref)
@@ -382,10 +453,11 @@ done:
     return NULL;
 }
 
-int oracle_prefill(const uint16_t *q, const uint16_t *gate, const uint16_t *k, const uint16_t *v,
-                   double scale, int causal, int B, int S, int Hq, int Hkv, int D,
-                   const int32_t *rows, int nrows, uint16_t *out, double *o_f64, double *mref,
-                   int nthreads)
+int oracle_prefill_ex(const uint16_t *q, const uint16_t *gate, const uint16_t *k,
+                      const uint16_t *v, double scale, int causal, int B, int S, int Hq,
+                      int Hkv, int D, const int32_t *seq_lens, const double *sinks, int window,
+                      const int32_t *rows, int nrows, uint16_t *out, double *o_f64,
+                      double *mref, double *lse, int nthreads)
 {
     if (B < 0 || S < 0 || Hq <= 0 || Hkv <= 0 || D <= 0 || Hq % Hkv != 0 || nrows < 0)
         return ORACLE_EBADARG;
@@ -402,7 +474,8 @@ int oracle_prefill(const uint16_t *q, const uint16_t *gate, const uint16_t *k, c
         return ORACLE_ENOMEM;
     for (int t = 0; t < nthreads; ++t) {
         prefill_job j = {q, gate, k, v, scale, causal, B, S, Hq, Hkv, D, rows, nrows,
-                         out, o_f64, mref, nthreads, t, ORACLE_OK};
+                         out, o_f64, mref, seq_lens, sinks, window, lse, nthreads, t,
+                         ORACLE_OK};
         jobs[t] = j;
     }
     int st = run_jobs(jobs, sizeof(prefill_job), nthreads, prefill_worker);
@@ -411,4 +484,13 @@ int oracle_prefill(const uint16_t *q, const uint16_t *gate, const uint16_t *k, c
             st = jobs[t].status;
     free(jobs);
     return st;
+}
+
+int oracle_prefill(const uint16_t *q, const uint16_t *gate, const uint16_t *k, const uint16_t *v,
+                   double scale, int causal, int B, int S, int Hq, int Hkv, int D,
+                   const int32_t *rows, int nrows, uint16_t *out, double *o_f64, double *mref,
+                   int nthreads)
+{
+    return oracle_prefill_ex(q, gate, k, v, scale, causal, B, S, Hq, Hkv, D, NULL, NULL, 0,
+                             rows, nrows, out, o_f64, mref, NULL, nthreads);
 }
