@@ -112,7 +112,7 @@ def to_dev(a, dev):
 class DecodeCall:
     """Pre-marshalled arguments of one gated_attn_decode call (raw C entry)."""
 
-    def __init__(self, ga, case, dev):
+    def __init__(self, ga, case, dev, sinks=None, window=0, lse=False):
         import torch
 
         self.ga = ga
@@ -130,9 +130,22 @@ class DecodeCall:
         self.wsb = ctypes.c_size_t(self.ws.numel())
         self.dref = ctypes.byref(self.dims)
         self.fn = ga.lib.gated_attn_decode
+        self.extra = ()
+        if sinks is not None or window or lse:
+            # attention-spec options through gated_attn_decode_ex
+            B, Hq = case.q.shape[:2]
+            self.sinks = None if sinks is None else torch.tensor(sinks, dtype=torch.float32,
+                                                                 device=dev)
+            self.lse = torch.empty((B, Hq), dtype=torch.float32, device=dev) if lse else None
+            self.opts = ga.AttnOptions(
+                sinks=None if self.sinks is None else self.sinks.data_ptr(),
+                lse=None if self.lse is None else self.lse.data_ptr(), window=int(window))
+            self.fn = ga.lib.gated_attn_decode_ex
+            self.extra = (ctypes.byref(self.opts),)
 
     def __call__(self):
-        st = self.fn(*self.args, self.scale, self.outp, self.stream, self.dref, self.wsp, self.wsb)
+        st = self.fn(*self.args, self.scale, self.outp, self.stream, self.dref, self.wsp, self.wsb,
+                     *self.extra)
         if st != 0:
             self.ga.check(st, "gated_attn_decode")
 
@@ -173,11 +186,18 @@ def time_prefill(ga, p, dev, n_calls: int, settle_s: float = 0.0) -> dict:
                     "the algorithmic MFMA work"}
 
 
-def time_decode(ga, case, dev, n_calls: int) -> dict:
-    """Back-to-back decode calls on case: us/call and K/V bytes per second."""
+def time_decode(ga, case, dev, n_calls: int, settle_s: float = 0.1, **opts) -> dict:
+    """Back-to-back decode calls on case: us/call and K/V bytes per second
+    (the bytes of the visible keys: a window reads only those)."""
+    import numpy as np
     import torch
 
-    call = DecodeCall(ga, case, dev)
+    call = DecodeCall(ga, case, dev, **opts)
+    t0 = time.perf_counter()
+    while time.perf_counter() - t0 < settle_s:  # clock settling, untimed
+        for _ in range(20):
+            call()
+        torch.cuda.synchronize()
     for _ in range(10):
         call()
     torch.cuda.synchronize()
@@ -191,9 +211,14 @@ def time_decode(ga, case, dev, n_calls: int) -> dict:
     ms = a.elapsed_time(b) / n_calls
     B, Hq, D = case.q.shape
     Hkv = case.k_pool.shape[2]
-    gbs = case.kv_bytes() / (ms * 1e-3) / 1e9
+    lens = np.clip(case.seq_lens.astype(np.int64), 0, None)
+    if opts.get("window"):
+        lens = np.minimum(lens, int(opts["window"]))
+    kv = int(lens.sum()) * Hkv * D * 2 * 2
+    gbs = kv / (ms * 1e-3) / 1e9
+    desc = ", ".join(f"{k}={'yes' if k == 'sinks' else v}" for k, v in opts.items() if v is not None)
     return {"workload": f"gated GQA decode B={B} L={int(case.seq_lens.max())} H_q={Hq} "
-                        f"H_kv={Hkv} D={D}, paged",
+                        f"H_kv={Hkv} D={D}, paged" + (f", {desc}" if desc else ""),
             "us_per_call": round(ms * 1e3, 3), "calls": n_calls,
             "kv_gbs": round(gbs, 2), "hbm_frac": round(gbs / HBM_PEAK_GBS, 4),
             "tokens_per_split": call.plan.tokens_per_split, "num_splits": call.plan.num_splits}
@@ -385,17 +410,25 @@ def main() -> int:
                              "samples_us": [round(x, 3) for x in samples]}
         del g
 
-        result["prefill"] = time_prefill(ga, workloads.workload(4), dev, 20)
+        result["prefill"] = time_prefill(ga, workloads.workload(4), dev, 20, settle_s=0.1)
 
         # ---- the h_q = 32, h_kv = 2 geometry (GQA group 16) -----------------
         c32 = workloads.make_decode("decode_b64_l4096_hq32", [4096] * 64, seed=2,
                                     num_q_heads=32, num_kv_heads=2, poison=False,
                                     max_pages_per_seq=256)
         result["decode_hq32"] = time_decode(ga, c32, dev, 100)
+        # attention-spec options on the headline workload
+        result["decode_sinks_lse"] = time_decode(ga, case, dev, 100, sinks=[0.5] * 16, lse=True)
+        result["decode_window1024"] = time_decode(ga, case, dev, 100, window=1024, lse=True)
+        # sequences far shorter than the capacity the call was planned for
+        short = workloads.make_decode("decode_b64_l1024_cap32768", [1024] * 64, seed=2,
+                                      poison=False, max_pages_per_seq=2048, extra_pages=0)
+        result["decode_l1024_cap32768"] = time_decode(ga, short, dev, 100)
+        del short
         del c32
         p32 = workloads.make_prefill("prefill_b2_s2048_hq32", 2, 2048, seed=4, causal=True,
                                      num_q_heads=32, num_kv_heads=2)
-        result["prefill_hq32"] = time_prefill(ga, p32, dev, 10)
+        result["prefill_hq32"] = time_prefill(ga, p32, dev, 10, settle_s=0.1)
         del p32
 
     if not args.no_cpu_baseline and not args.no_extras:

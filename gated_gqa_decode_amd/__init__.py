@@ -33,8 +33,10 @@ EXPORTED_SYMBOLS = (
     "gated_attn_decode_plan",
     "gated_attn_decode_workspace_size",
     "gated_attn_decode",
+    "gated_attn_decode_ex",
     "gated_attn_decode_time_stage1",
     "gated_attn_prefill",
+    "gated_attn_prefill_ex",
     "gated_attn_status_string",
     "gated_attn_last_hip_error",
 )
@@ -70,6 +72,17 @@ class PrefillDims(ctypes.Structure):
     ]
 
 
+class AttnOptions(ctypes.Structure):
+    """ga_attn_options: sinks, lse output, prefill key lengths, window."""
+    _fields_ = [
+        ("sinks", ctypes.c_void_p),
+        ("lse", ctypes.c_void_p),
+        ("kv_lens", ctypes.c_void_p),
+        ("window", ctypes.c_int32),
+        ("flags", ctypes.c_int32),
+    ]
+
+
 def _load_library() -> ctypes.CDLL:
     # torch ships its own HIP runtime (same SONAME, libamdhip64.so.7).  Loading
     # torch first makes the library bind to that runtime instead of pulling a
@@ -90,6 +103,14 @@ def _load_library() -> ctypes.CDLL:
     lib.gated_attn_decode.restype = ctypes.c_int
     lib.gated_attn_decode.argtypes = [vp, vp, vp, vp, vp, vp, ctypes.c_float, vp, vp,
                                       ctypes.POINTER(DecodeDims), vp, sz]
+    lib.gated_attn_decode_ex.restype = ctypes.c_int
+    lib.gated_attn_decode_ex.argtypes = [vp, vp, vp, vp, vp, vp, ctypes.c_float, vp, vp,
+                                         ctypes.POINTER(DecodeDims), vp, sz,
+                                         ctypes.POINTER(AttnOptions)]
+    lib.gated_attn_prefill_ex.restype = ctypes.c_int
+    lib.gated_attn_prefill_ex.argtypes = [vp, vp, vp, vp, ctypes.c_float, ctypes.c_int, vp, vp,
+                                          ctypes.POINTER(PrefillDims),
+                                          ctypes.POINTER(AttnOptions)]
     lib.gated_attn_prefill.restype = ctypes.c_int
     lib.gated_attn_prefill.argtypes = [vp, vp, vp, vp, ctypes.c_float, ctypes.c_int, vp, vp,
                                        ctypes.POINTER(PrefillDims)]
@@ -196,8 +217,27 @@ def decode_dims_for(q, k_pool, block_table) -> DecodeDims:
     return decode_dims(B, Hq, Hkv, D, ps, block_table.shape[1], P)
 
 
+def _options(sinks, window, lse, kv_lens, Hq, dev):
+    """AttnOptions for the _ex entry points, or None for plain attention."""
+    torch = _torch()
+    if sinks is None and lse is None and kv_lens is None and not window:
+        return None
+    o = AttnOptions()
+    if sinks is not None:
+        _need(sinks, "sinks", torch.float32, 1, dev)
+        if sinks.shape[0] != Hq:
+            raise ValueError("sinks must hold one logit per query head")
+        o.sinks = sinks.data_ptr()
+    if lse is not None:
+        o.lse = lse.data_ptr()
+    if kv_lens is not None:
+        o.kv_lens = kv_lens.data_ptr()
+    o.window = int(window) if window and window > 0 else 0
+    return o
+
+
 def decode(q, gate, k_pool, v_pool, block_table, seq_lens, scale, *, out=None, workspace=None,
-           stream=None):
+           stream=None, sinks=None, window=0, lse=None, return_lse=False):
     """Gated GQA decode over a paged pool; returns ``out`` [B, H_q, D] bf16.
 
     q, gate: [B, H_q, D] bf16; k_pool, v_pool: [P, 16, H_kv, D] bf16;
@@ -205,6 +245,10 @@ def decode(q, gate, k_pool, v_pool, block_table, seq_lens, scale, *, out=None, w
     ``workspace`` (uint8, >= decode_workspace_size bytes) is allocated when
     not given; pass one to keep the call allocation-free (e.g. under graph
     capture).  Work is enqueued on ``stream`` (default: torch's current stream).
+    Options (gated_attn_decode_ex): ``sinks`` fp32 [H_q] sink logits,
+    ``window`` > 0 keeps the last ``window`` keys, ``lse`` fp32 [B, H_q] to
+    receive the natural-log log-sum-exp (or ``return_lse=True`` to allocate
+    it; the call then returns ``(out, lse)``).
     """
     torch = _torch()
     dev = q.device
@@ -231,16 +275,32 @@ def decode(q, gate, k_pool, v_pool, block_table, seq_lens, scale, *, out=None, w
         workspace = torch.empty(max(need, 16), dtype=torch.uint8, device=dev)
     else:
         _need(workspace, "workspace", torch.uint8, 1, dev)
-    st = lib.gated_attn_decode(
-        q.data_ptr(), gate.data_ptr(), k_pool.data_ptr(), v_pool.data_ptr(),
-        block_table.data_ptr(), seq_lens.data_ptr(), float(scale), out.data_ptr(),
-        _stream_handle(stream, dev), ctypes.byref(dims), workspace.data_ptr(), workspace.numel())
-    check(st, "gated_attn_decode")
-    return out
+    if return_lse and lse is None:
+        lse = torch.empty((B, Hq), dtype=torch.float32, device=dev)
+    if lse is not None:
+        _need(lse, "lse", torch.float32, 2, dev)
+        if lse.shape != (B, Hq):
+            raise ValueError("lse must be [B, H_q]")
+    opts = _options(sinks, window, lse, None, Hq, dev)
+    args = (q.data_ptr(), gate.data_ptr(), k_pool.data_ptr(), v_pool.data_ptr(),
+            block_table.data_ptr(), seq_lens.data_ptr(), float(scale), out.data_ptr(),
+            _stream_handle(stream, dev), ctypes.byref(dims), workspace.data_ptr(),
+            workspace.numel())
+    if opts is None:
+        check(lib.gated_attn_decode(*args), "gated_attn_decode")
+    else:
+        check(lib.gated_attn_decode_ex(*args, ctypes.byref(opts)), "gated_attn_decode_ex")
+    return (out, lse) if return_lse else out
 
 
-def prefill(q, gate, k, v, scale, causal=True, *, out=None, stream=None):
-    """Gated dense prefill; q, gate: [B, S, H_q, D]; k, v: [B, S, H_kv, D] bf16."""
+def prefill(q, gate, k, v, scale, causal=True, *, out=None, stream=None, kv_lens=None,
+            sinks=None, window=0, lse=None, return_lse=False):
+    """Gated dense prefill; q, gate: [B, S, H_q, D]; k, v: [B, S, H_kv, D] bf16.
+
+    Options (gated_attn_prefill_ex): ``kv_lens`` int32 [B] key lengths,
+    ``sinks`` fp32 [H_q], ``window`` > 0 (row i sees keys j > i - window),
+    ``lse`` fp32 [B, S, H_q] (or ``return_lse=True``; returns ``(out, lse)``).
+    """
     torch = _torch()
     dev = q.device
     _need(q, "q", torch.bfloat16, 4, dev)
@@ -258,8 +318,21 @@ def prefill(q, gate, k, v, scale, causal=True, *, out=None, stream=None):
         if out.shape != q.shape:
             raise ValueError("out must match q")
     dims = PrefillDims(B, S, Hq, Hkv, D)
-    st = lib.gated_attn_prefill(q.data_ptr(), gate.data_ptr(), k.data_ptr(), v.data_ptr(),
-                                float(scale), int(bool(causal)), out.data_ptr(),
-                                _stream_handle(stream, dev), ctypes.byref(dims))
-    check(st, "gated_attn_prefill")
-    return out
+    if kv_lens is not None:
+        _need(kv_lens, "kv_lens", torch.int32, 1, dev)
+        if kv_lens.shape[0] != B:
+            raise ValueError("kv_lens must be [B]")
+    if return_lse and lse is None:
+        lse = torch.empty((B, S, Hq), dtype=torch.float32, device=dev)
+    if lse is not None:
+        _need(lse, "lse", torch.float32, 3, dev)
+        if lse.shape != (B, S, Hq):
+            raise ValueError("lse must be [B, S, H_q]")
+    opts = _options(sinks, window, lse, kv_lens, Hq, dev)
+    args = (q.data_ptr(), gate.data_ptr(), k.data_ptr(), v.data_ptr(), float(scale),
+            int(bool(causal)), out.data_ptr(), _stream_handle(stream, dev), ctypes.byref(dims))
+    if opts is None:
+        check(lib.gated_attn_prefill(*args), "gated_attn_prefill")
+    else:
+        check(lib.gated_attn_prefill_ex(*args, ctypes.byref(opts)), "gated_attn_prefill_ex")
+    return (out, lse) if return_lse else out

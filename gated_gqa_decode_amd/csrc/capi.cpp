@@ -97,6 +97,17 @@ ga_status check_decode_dims(const ga_decode_dims* d) {
   return GA_OK;
 }
 
+// Attention-spec options: pointers fp32 / int32 aligned, reserved flags zero,
+// key lengths only for prefill (decode has its seq_lens argument).
+ga_status check_options(const ga_attn_options* o, bool prefill) {
+  if (o == nullptr) return GA_OK;
+  if (o->flags != 0) return GA_ERR_INVALID_ARGUMENT;
+  if (!aligned(o->sinks, 4) || !aligned(o->lse, 4) || !aligned(o->kv_lens, 4))
+    return GA_ERR_INVALID_ARGUMENT;
+  if (!prefill && o->kv_lens != nullptr) return GA_ERR_INVALID_ARGUMENT;
+  return GA_OK;
+}
+
 // Split plan from the dims alone (allocated capacity, not current lengths).
 // GA_ERR_UNSUPPORTED when the stage-1 grid would not fit one launch.
 ga_status make_plan(const ga_decode_dims* d, ga_decode_plan* p) {
@@ -138,13 +149,16 @@ size_t gated_attn_decode_workspace_size(const ga_decode_dims* dims) {
   return p.workspace_bytes;
 }
 
-ga_status gated_attn_decode(const uint16_t* q, const uint16_t* gate, const uint16_t* k_pool,
-                            const uint16_t* v_pool, const int32_t* block_table,
-                            const int32_t* seq_lens, float scale, uint16_t* out, void* stream,
-                            const ga_decode_dims* dims, void* workspace, size_t workspace_bytes) {
+ga_status gated_attn_decode_ex(const uint16_t* q, const uint16_t* gate, const uint16_t* k_pool,
+                               const uint16_t* v_pool, const int32_t* block_table,
+                               const int32_t* seq_lens, float scale, uint16_t* out, void* stream,
+                               const ga_decode_dims* dims, void* workspace,
+                               size_t workspace_bytes, const ga_attn_options* opts) {
   ga_status st = check_decode_dims(dims);
   if (st != GA_OK) return st;
   if (!(std::isfinite(scale) && scale > 0.f)) return GA_ERR_INVALID_ARGUMENT;
+  st = check_options(opts, /*prefill=*/false);
+  if (st != GA_OK) return st;
   if (dims->batch == 0) return GA_OK;
   const void* ptr16[] = {q, gate, k_pool, v_pool, out, workspace};
   for (const void* p : ptr16)
@@ -178,6 +192,10 @@ ga_status gated_attn_decode(const uint16_t* q, const uint16_t* gate, const uint1
   L.num_pages = dims->num_pages;
   L.tokens_per_split = plan.tokens_per_split;
   L.num_splits = plan.num_splits;
+  L.split_target = GA_DECODE_TARGET_BLOCKS;
+  L.sinks = opts != nullptr ? opts->sinks : nullptr;
+  L.lse = opts != nullptr ? opts->lse : nullptr;
+  L.window = opts != nullptr && opts->window > 0 ? opts->window : 0;
   L.stage1_start = nullptr;
   L.stage1_stop = nullptr;
   if (g_timing.next < g_timing.n) {
@@ -190,14 +208,25 @@ ga_status gated_attn_decode(const uint16_t* q, const uint16_t* gate, const uint1
   return GA_OK;
 }
 
-ga_status gated_attn_prefill(const uint16_t* q, const uint16_t* gate, const uint16_t* k,
-                             const uint16_t* v, float scale, int causal, uint16_t* out,
-                             void* stream, const ga_prefill_dims* dims) {
+ga_status gated_attn_decode(const uint16_t* q, const uint16_t* gate, const uint16_t* k_pool,
+                            const uint16_t* v_pool, const int32_t* block_table,
+                            const int32_t* seq_lens, float scale, uint16_t* out, void* stream,
+                            const ga_decode_dims* dims, void* workspace, size_t workspace_bytes) {
+  return gated_attn_decode_ex(q, gate, k_pool, v_pool, block_table, seq_lens, scale, out, stream,
+                              dims, workspace, workspace_bytes, nullptr);
+}
+
+ga_status gated_attn_prefill_ex(const uint16_t* q, const uint16_t* gate, const uint16_t* k,
+                                const uint16_t* v, float scale, int causal, uint16_t* out,
+                                void* stream, const ga_prefill_dims* dims,
+                                const ga_attn_options* opts) {
   if (dims == nullptr) return GA_ERR_INVALID_ARGUMENT;
   if (dims->batch < 0 || dims->seq_len < 0) return GA_ERR_INVALID_ARGUMENT;
   ga_status st = check_heads(dims->num_q_heads, dims->num_kv_heads, dims->head_dim);
   if (st != GA_OK) return st;
   if (!(std::isfinite(scale) && scale > 0.f)) return GA_ERR_INVALID_ARGUMENT;
+  st = check_options(opts, /*prefill=*/true);
+  if (st != GA_OK) return st;
   if (dims->batch > kMaxGridYZ) return GA_ERR_UNSUPPORTED;
   if (dims->batch == 0 || dims->seq_len == 0) return GA_OK;
   // q/gate/out hold B*S*H_q*D elements; keep every element index in int32 range.
@@ -221,9 +250,19 @@ ga_status gated_attn_prefill(const uint16_t* q, const uint16_t* gate, const uint
   P.seq_len = dims->seq_len;
   P.num_q_heads = dims->num_q_heads;
   P.num_kv_heads = dims->num_kv_heads;
+  P.kv_lens = opts != nullptr ? opts->kv_lens : nullptr;
+  P.sinks = opts != nullptr ? opts->sinks : nullptr;
+  P.lse = opts != nullptr ? opts->lse : nullptr;
+  P.window = opts != nullptr && opts->window > 0 ? opts->window : 0;
   hipError_t e = ga::launch_prefill(P, static_cast<hipStream_t>(stream));
   if (e != hipSuccess) return hip_fail(e);
   return GA_OK;
+}
+
+ga_status gated_attn_prefill(const uint16_t* q, const uint16_t* gate, const uint16_t* k,
+                             const uint16_t* v, float scale, int causal, uint16_t* out,
+                             void* stream, const ga_prefill_dims* dims) {
+  return gated_attn_prefill_ex(q, gate, k, v, scale, causal, out, stream, dims, nullptr);
 }
 
 ga_status gated_attn_decode_time_stage1(void* const* starts, void* const* stops, int n) {

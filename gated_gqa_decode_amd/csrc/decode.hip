@@ -44,6 +44,7 @@ constexpr int kStep = 8;         // tokens per wave step
 constexpr int kWaves = 8;        // waves per stage-1 workgroup (one workgroup per CU)
 constexpr int kPageRegs = 2;     // page ids per lane: a split spans at most 128 pages
 constexpr float kLog2e = 1.4426950408889634f;
+constexpr float kLn2 = 0.6931471805599453f;
 constexpr float kSlack = 8.f;    // lazy-rescale threshold, log2 units
 
 struct Stage1Args {
@@ -62,8 +63,11 @@ struct Stage1Args {
   int num_units;       // B * H_kv * num_splits
   int max_pages;     // W
   long long num_pages;
-  int tokens_per_split;
+  int tokens_per_split;  // the most tokens of one split
   int num_splits;
+  int window;  // > 0: only the last `window` tokens of a sequence are visible
+  int split_units;   // B * H_kv * head parts (the split sizing rule's units)
+  int split_target;  // the workgroups the sizing rule aims for
 };
 
 struct alignas(16) WaveSlot {
@@ -98,6 +102,41 @@ __device__ __forceinline__ uint2 ldg8_stream(const char* p) {
   return make_uint2(v[0], v[1]);
 }
 
+// How one sequence is split.  The grid and the workspace come from the
+// capacity (num_splits splits of at most max_tokens tokens), so a call
+// captured once serves every length.  Inside that, the sequence's visible
+// keys [base, L) -- base is the window start rounded down to a page -- get
+// the same sizing rule the capacity got (about target_blocks workgroups for
+// `units` (sequence, kv head, head part) triples, at least 64 tokens, one
+// step per wave), cut into equal page-aligned parts: short sequences and
+// windows spread over several splits, and no split is a sliver.
+struct SplitRange {
+  int base;    // first token of split 0
+  int tokens;  // tokens per split (0 for an empty sequence)
+  int count;   // non-empty splits (<= num_splits)
+};
+
+__device__ __forceinline__ SplitRange split_range(int L, int window, int num_splits,
+                                                  int max_tokens, int units, int target_blocks) {
+  SplitRange r;
+  const int tok_lo = window > 0 ? max(0, L - window) : 0;
+  r.base = tok_lo & ~(kPage - 1);
+  const int n = L - r.base;
+  if (n <= 0) {
+    r.tokens = 0;
+    r.count = 0;
+    return r;
+  }
+  long long t = ((long long)n * units + target_blocks - 1) / target_blocks;
+  t = max(t, (long long)(kWaves * kStep));
+  t = max(t, (long long)((n + num_splits - 1) / num_splits));  // at most num_splits splits
+  t = min(t, (long long)max_tokens);
+  const int count = (int)((n + t - 1) / t);
+  r.tokens = (((n + count - 1) / count) + kPage - 1) & ~(kPage - 1);
+  r.count = (n + r.tokens - 1) / r.tokens;
+  return r;
+}
+
 }  // namespace
 
 __global__ __launch_bounds__(512, 1) void decode_stage1_kernel(Stage1Args a) {
@@ -106,18 +145,21 @@ __global__ __launch_bounds__(512, 1) void decode_stage1_kernel(Stage1Args a) {
   __shared__ int progress[kWaves];  // last step each wave started
 
   // Workgroup id -> (split s, kv head g, head part, sequence b).  Ids are
-  // dispatched round-robin over the 8 XCDs; the parts of one (s, g, b) unit
-  // get ids 8 apart, i.e. the same XCD and consecutive there, so the second
-  // part finds the unit's K/V rows in that XCD's L2.
+  // dispatched in order, round-robin over the 8 XCDs.  Units are split-major
+  // (every sequence's split 0, then split 1, ...): the splits a short
+  // sequence leaves empty come last and the busy ones spread over all XCDs.
+  // The parts of one unit get ids 8 apart, i.e. the same XCD and consecutive
+  // there, so the second part finds the unit's K/V rows in that XCD's L2.
   const int id = blockIdx.x;
   const int xcd = id & 7;
   const int r = id >> 3;
   const int part = r % a.parts;
-  const int unit = (r / a.parts) * 8 + xcd;  // (b * H_kv + g) * num_splits + s
+  const int unit = (r / a.parts) * 8 + xcd;  // (s * B + b) * H_kv + g
   if (unit >= a.num_units) return;
-  const int s = unit % a.num_splits;
-  const int g = (unit / a.num_splits) % a.num_kv_heads;
-  const int b = unit / (a.num_splits * a.num_kv_heads);
+  const int seq_heads = a.num_units / a.num_splits;  // B * H_kv
+  const int s = unit / seq_heads;
+  const int g = (unit - s * seq_heads) % a.num_kv_heads;
+  const int b = (unit - s * seq_heads) / a.num_kv_heads;
   const int lane = __lane_id();
   // wave-uniform by construction; readfirstlane lets the compiler keep the
   // step bookkeeping and the load base addresses in scalar registers
@@ -126,17 +168,22 @@ __global__ __launch_bounds__(512, 1) void decode_stage1_kernel(Stage1Args a) {
   const int Hq = a.num_q_heads;
   const int nh = a.heads_per_part;  // head slots 0..nh-1 are real, the rest idle
   const int h0 = g * (Hq / Hkv) + part * nh;  // first query head of this workgroup
-  const int tok_begin = s * a.tokens_per_split;  // < capacity, since s < num_splits
 
-  // Issued together, before the length is known: the page ids of the whole
-  // split (page j in lane j % 64 of register j / 64; ids past the sequence's
-  // end are never used), the length, and q.
-  const int first_page = tok_begin / kPage;
-  const int split_pages = min(a.tokens_per_split / kPage, a.max_pages - first_page);
-  const int32_t* bt = a.block_table + (size_t)b * a.max_pages + first_page;
-  int my_page[kPageRegs];
+  // Issued together, before the length is known: the page ids of split s as
+  // it is when the sequence fills its capacity (page j of the split in lane
+  // j % 64 of register j / 64; ids past the sequence's end are never used),
+  // the length, and q.  Other lengths reload the page ids below.
+  const int32_t* bt_row = a.block_table + (size_t)b * a.max_pages;
+  auto load_pages = [&](int tok_first, int ntok, int (&pages)[kPageRegs]) {
+    const int fp = tok_first / kPage;
+    const int np = min(ntok / kPage, a.max_pages - fp);
 #pragma unroll
-  for (int r = 0; r < kPageRegs; ++r) my_page[r] = lane + 64 * r < split_pages ? bt[lane + 64 * r] : 0;
+    for (int r = 0; r < kPageRegs; ++r)
+      pages[r] = lane + 64 * r < np ? bt_row[fp + lane + 64 * r] : 0;
+  };
+  int my_page[kPageRegs];
+  const int full_begin = s * a.tokens_per_split;  // < capacity, since s < num_splits
+  load_pages(full_begin, a.tokens_per_split, my_page);
 
   // score-lane coordinates
   const int tq = lane >> 4;    // token within a pass
@@ -163,8 +210,15 @@ __global__ __launch_bounds__(512, 1) void decode_stage1_kernel(Stage1Args a) {
   // documented preconditions; both are clamped so such input yields garbage
   // in its own row instead of an access outside the buffers.
   const int L = min(a.seq_lens[b], a.max_pages * kPage);
-  if (tok_begin >= L) return;  // empty split: stage 2 never reads its slot
-  const int tok_end = min(L, tok_begin + a.tokens_per_split);
+  // First visible token: the sliding window keeps the last `window` tokens.
+  const int tok_lo = a.window > 0 ? max(0, L - a.window) : 0;
+  const SplitRange sr = split_range(L, a.window, a.num_splits, a.tokens_per_split,
+                                    a.split_units, a.split_target);
+  if (s >= sr.count) return;  // empty split: stage 2 never reads its slot
+  const int tok_begin = sr.base + s * sr.tokens;
+  const int tok_end = min(L, tok_begin + sr.tokens);
+  const int first_page = tok_begin / kPage;
+  if (tok_begin != full_begin) load_pages(tok_begin, sr.tokens, my_page);
 #pragma unroll
   for (int r = 0; r < kPageRegs; ++r) my_page[r] = (int)min((long long)max(my_page[r], 0), a.num_pages - 1);
   if (threadIdx.x < kWaves) progress[threadIdx.x] = 0;
@@ -254,7 +308,7 @@ __global__ __launch_bounds__(512, 1) void decode_stage1_kernel(Stage1Args a) {
       }
       const float mine = reduce_scatter8(part, c16);
       const int t = t0 + pass * 4 + tq;
-      sc[pass] = (t < tok_end) ? mine * a.scale_log2 : -INFINITY;
+      sc[pass] = (t < tok_end && t >= tok_lo) ? mine * a.scale_log2 : -INFINITY;
     }
     // Lazy rescaling: probabilities are taken relative to a reference max
     // m_run that is only raised (with a rescale of l and acc) when some score
@@ -299,10 +353,12 @@ __global__ __launch_bounds__(512, 1) void decode_stage1_kernel(Stage1Args a) {
     uint2 vv[kStep];
 #pragma unroll
     for (int t = 0; t < kStep; ++t) vv[t] = r.v[t];
-    if (t0 + kStep > tok_end) {  // last step of the sequence: tail slots may hold anything
+    if (t0 + kStep > tok_end || t0 < tok_lo) {
+      // last step of the sequence (tail slots may hold anything) or the step
+      // the window starts in: invisible rows take no part, whatever they hold
 #pragma unroll
       for (int t = 0; t < kStep; ++t)
-        if (t0 + t >= tok_end) vv[t] = make_uint2(0, 0);
+        if (t0 + t >= tok_end || t0 + t < tok_lo) vv[t] = make_uint2(0, 0);
     }
 #pragma unroll
     for (int t = 0; t < kStep; ++t) {
@@ -342,7 +398,8 @@ __global__ __launch_bounds__(512, 1) void decode_stage1_kernel(Stage1Args a) {
     else
       __builtin_amdgcn_s_setprio(0);
   };
-  int c0 = wave;
+  const int first_step = (max(tok_begin, tok_lo) - tok_begin) / kStep;
+  int c0 = first_step + wave;
   if (c0 < n_steps) {
     const int last = n_steps - 1;
     int c1 = c0 + kWaves;
@@ -437,12 +494,17 @@ struct Stage2Args {
   const int32_t* seq_lens;
   const float* part_acc;
   const float* part_ml;
+  const float* sinks;  // [H_q] sink logits (natural-log units) or null
   uint16_t* out;
+  float* lse;          // [B][H_q] or null
   int num_q_heads;
   int tokens_per_split;
   int num_splits;
   int batch;
   int capacity;  // max_pages * page size
+  int window;
+  int split_units;
+  int split_target;
 };
 
 // One wave per (b, h); lane owns d = 4*lane .. 4*lane+3.  4 waves per block.
@@ -468,16 +530,22 @@ __global__ __launch_bounds__(256) void decode_stage2_gate_kernel(Stage2Args a) {
       x0[u] = *reinterpret_cast<const float4*>(pa + (size_t)u * kD);
       ml0[u] = *reinterpret_cast<const float2*>(ml + 2 * u);
     }
+  const int h = row - b * a.num_q_heads;
+  // A sink joins the denominator as one more term exp(sink) (in log2 units
+  // here, like the partials' maxima); it takes no part in the numerator.
+  const float sink2 = a.sinks != nullptr ? a.sinks[h] * kLog2e : -INFINITY;
   const int L = min(a.seq_lens[b], a.capacity);  // same clamp as stage 1
   uint16_t o16[4] = {0, 0, 0, 0};
+  float lse = sink2 * kLn2;  // a dead row: ln(exp(sink)), or -inf
   if (L > 0) {  // L <= 0: padded slot, output +0
-    const int ns = (L + a.tokens_per_split - 1) / a.tokens_per_split;
-    float M = -INFINITY;
+    const int ns = split_range(L, a.window, a.num_splits, a.tokens_per_split, a.split_units,
+                               a.split_target).count;  // >= 1 here
+    float M = sink2;
 #pragma unroll
     for (int u = 0; u < 8; ++u)
       if (u < ns) M = fmaxf(M, ml0[u].x);
     for (int s = 8; s < ns; ++s) M = fmaxf(M, ml[2 * s]);
-    float lam = 0.f;
+    float lam = a.sinks != nullptr ? __builtin_amdgcn_exp2f(sink2 - M) : 0.f;
     float o[4] = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int u = 0; u < 8; ++u)
@@ -513,7 +581,9 @@ __global__ __launch_bounds__(256) void decode_stage2_gate_kernel(Stage2Args a) {
       const uint16_t ob = bf16_rne_f32(o[e] / lam);
       o16[e] = gate_output(ob, gt[e]);
     }
+    lse = (M + log2f(lam)) * kLn2;
   }
+  if (a.lse != nullptr && lane == 0) a.lse[row] = lse;
   uint2 w;
   w.x = (uint32_t)o16[0] | ((uint32_t)o16[1] << 16);
   w.y = (uint32_t)o16[2] | ((uint32_t)o16[3] << 16);
@@ -539,6 +609,9 @@ hipError_t launch_decode(const DecodeLaunch& d, hipStream_t stream) {
   a1.num_pages = d.num_pages;
   a1.tokens_per_split = d.tokens_per_split;
   a1.num_splits = d.num_splits;
+  a1.window = d.window;
+  a1.split_units = d.batch * d.num_kv_heads * a1.parts;
+  a1.split_target = d.split_target;
   a1.num_units = d.batch * d.num_kv_heads * d.num_splits;
   dim3 grid1(((a1.num_units + 7) / 8) * 8 * a1.parts);
   hipError_t err;
@@ -559,9 +632,14 @@ hipError_t launch_decode(const DecodeLaunch& d, hipStream_t stream) {
   a2.seq_lens = d.seq_lens;
   a2.part_acc = d.part_acc;
   a2.part_ml = d.part_ml;
+  a2.sinks = d.sinks;
   a2.out = d.out;
-  a2.num_q_heads = d.num_q_heads;
+  a2.lse = d.lse;
+  a2.window = d.window;
   a2.tokens_per_split = d.tokens_per_split;
+  a2.split_units = a1.split_units;
+  a2.split_target = d.split_target;
+  a2.num_q_heads = d.num_q_heads;
   a2.num_splits = d.num_splits;
   a2.batch = d.batch;
   a2.capacity = d.max_pages * kPage;

@@ -35,6 +35,11 @@ struct DecodeLaunch {
   long long num_pages;
   int tokens_per_split;
   int num_splits;
+  int split_target;  // workgroups the split sizing rule aims for
+  // attention-spec options (null / 0: plain attention)
+  const float* sinks;  // [H_q] sink logits
+  float* lse;          // [B][H_q] log-sum-exp output
+  int window;          // > 0: sliding window of that many keys
   hipEvent_t stage1_start;  // recorded around stage 1 when non-null
   hipEvent_t stage1_stop;
 };
@@ -51,6 +56,11 @@ struct PrefillLaunch {
   int seq_len;
   int num_q_heads;
   int num_kv_heads;
+  // attention-spec options (null / 0: plain attention)
+  const int32_t* kv_lens;  // [B] key lengths
+  const float* sinks;      // [H_q] sink logits
+  float* lse;              // [B][S][H_q] log-sum-exp output
+  int window;              // > 0: row i sees keys j > i - window
 };
 
 hipError_t launch_decode(const DecodeLaunch& d, hipStream_t stream);

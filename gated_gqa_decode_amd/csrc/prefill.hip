@@ -46,6 +46,7 @@ constexpr int kKRow = kD + 8;    // K row stride in LDS (bf16 elements): +16 B
 constexpr int kVRow = kD + 16;   // V row stride in LDS (bf16 elements): +32 B
 constexpr int kThreads = 512;
 constexpr float kLog2e = 1.4426950408889634f;
+constexpr float kLn2 = 0.6931471805599453f;
 constexpr float kSlack = 8.f;  // lazy-rescale threshold, log2 units
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
@@ -68,6 +69,11 @@ struct PrefillArgs {
   int heads_per_part;  // query heads of a workgroup: G or G / 2 (<= 8)
   int batch;
   int num_m_tiles;
+  // attention-spec options (null / 0: plain attention)
+  const int32_t* kv_lens;  // [B] key lengths: keys j >= kv_lens[b] are masked
+  const float* sinks;      // [H_q] sink logits (natural-log units)
+  float* lse;              // [B][S][H_q] natural-log log-sum-exp
+  int window;              // > 0: row i sees keys j > i - window
 };
 
 // Workgroup order.  Workgroups are dispatched round-robin over the 8 XCDs of
@@ -174,8 +180,14 @@ __global__ __launch_bounds__(kThreads) void prefill_gate_kernel(PrefillArgs a) {
   float l_row = 0.f;        // this lane's share of the sum of row li
 
   const int qi = p0 + li;
-  const int kv_end = a.causal ? min(S, p0 + kBM) : S;
-  const int n_tiles = (kv_end + kBN - 1) / kBN;
+  // Keys this query tile can see: [kv_lo, kv_end).  The key length masks keys
+  // only; the causal mask ends at the tile's last row; the window starts at
+  // the first row's window.
+  const int len = a.kv_lens != nullptr ? min(max(a.kv_lens[b], 0), S) : S;
+  const int kv_end = a.causal ? min(len, p0 + kBM) : len;
+  const int kv_lo = a.window > 0 ? max(0, p0 - a.window + 1) : 0;
+  const int kt_lo = kv_lo / kBN;
+  const int n_tiles = (kv_end + kBN - 1) / kBN;  // key tiles kt_lo .. n_tiles - 1
   const size_t kv_row_stride = (size_t)Hkv * kD;
   const uint16_t* kbase = a.k + ((size_t)b * S * Hkv + g) * kD;
   const uint16_t* vbase = a.v + ((size_t)b * S * Hkv + g) * kD;
@@ -195,7 +207,8 @@ __global__ __launch_bounds__(kThreads) void prefill_gate_kernel(PrefillArgs a) {
       const unsigned off = g_off + (unsigned)(it * 16 * (int)kv_row_stride);
       sk[it] = make_uint4(0, 0, 0, 0);
       sv[it] = make_uint4(0, 0, 0, 0);
-      if (j0 + it * 16 + st_key < kv_end) {
+      const int j = j0 + it * 16 + st_key;
+      if (j < kv_end && j >= kv_lo) {  // keys no row of the tile sees stay zero
         sk[it] = *reinterpret_cast<const uint4*>(kb + off);
         sv[it] = *reinterpret_cast<const uint4*>(vb + off);
       }
@@ -210,13 +223,15 @@ __global__ __launch_bounds__(kThreads) void prefill_gate_kernel(PrefillArgs a) {
     }
   };
 
-  load_tile(0);
-  store_tile(buf[0]);
-  if (n_tiles > 1) load_tile(1);
+  if (kt_lo < n_tiles) {
+    load_tile(kt_lo);
+    store_tile(buf[0]);
+    if (kt_lo + 1 < n_tiles) load_tile(kt_lo + 1);
+  }
   __syncthreads();
 
-  for (int kt = 0; kt < n_tiles; ++kt) {
-    const TileBuf& tb = buf[kt & 1];
+  for (int kt = kt_lo; kt < n_tiles; ++kt) {
+    const TileBuf& tb = buf[(kt - kt_lo) & 1];
     const int j0 = kt * kBN;
 
     if (active) {
@@ -249,7 +264,8 @@ __global__ __launch_bounds__(kThreads) void prefill_gate_kernel(PrefillArgs a) {
       // ---- mask, lazy online softmax (row li), split P ------------------------
       // Only a tile that reaches past the first row of the query tile (causal)
       // or past the last key needs the mask; the test is uniform.
-      const bool need_mask = (j0 + kBN > kv_end) || (a.causal && j0 + kBN - 1 > p0);
+      const bool need_mask = (j0 + kBN > kv_end) || (a.causal && j0 + kBN - 1 > p0) ||
+                             (a.window > 0 && j0 < p0 + kBM - a.window);
       float sv_[4][4];
       bool raise = false;
 #pragma unroll
@@ -262,7 +278,8 @@ __global__ __launch_bounds__(kThreads) void prefill_gate_kernel(PrefillArgs a) {
 #pragma unroll
           for (int r = 0; r < 4; ++r) {
             const int kj = j0 + ct * 16 + 4 * lg + r;
-            const bool ok = (kj < kv_end) && (!a.causal || kj <= qi);
+            const bool ok = (kj < kv_end) && (!a.causal || kj <= qi) &&
+                            (a.window <= 0 || kj > qi - a.window);
             sv_[ct][r] = ok ? sv_[ct][r] : -INFINITY;
           }
       }
@@ -350,7 +367,7 @@ __global__ __launch_bounds__(kThreads) void prefill_gate_kernel(PrefillArgs a) {
 
     // ---- next tile: staged registers -> the other buffer ---------------------
     if (kt + 1 < n_tiles) {
-      store_tile(buf[(kt + 1) & 1]);
+      store_tile(buf[(kt + 1 - kt_lo) & 1]);
       if (kt + 2 < n_tiles) load_tile(kt + 2);
     }
     __syncthreads();
@@ -360,19 +377,37 @@ __global__ __launch_bounds__(kThreads) void prefill_gate_kernel(PrefillArgs a) {
   if (!active) return;
   l_row += shfl_xor(l_row, 16);  // the row's four lanes hold disjoint keys
   l_row += shfl_xor(l_row, 32);
+  // A sink joins the denominator as one more term exp(sink) (log2 units here,
+  // like m_ref); a row with no visible key (l = 0) is dead: out = +0.
+  const float sink2 = a.sinks != nullptr ? a.sinks[h] * kLog2e : -INFINITY;
 #pragma unroll
   for (int r = 0; r < 4; ++r) {
     const int row = 4 * lg + r;
     const float lr = __int_as_float(__builtin_amdgcn_ds_bpermute(row << 2, __float_as_int(l_row)));
+    const float mr = __int_as_float(__builtin_amdgcn_ds_bpermute(row << 2, __float_as_int(m_ref)));
     const int qr = p0 + row;
     if (qr >= S) continue;
+    const bool dead = lr == 0.f;
+    float mtot = mr, f = 1.f, den = lr;
+    if (a.sinks != nullptr) {
+      mtot = fmaxf(mr, sink2);
+      f = __builtin_amdgcn_exp2f(mr - mtot);  // 0 for a dead row
+      den = fmaf(lr, f, __builtin_amdgcn_exp2f(sink2 - mtot));
+    }
     const size_t rowoff = (((size_t)b * S + qr) * Hq + h) * kD;
 #pragma unroll
     for (int t = 0; t < 16; ++t) {
       const int d = t * 16 + li;
-      const uint16_t ob = bf16_rne_f32(o[t][r] / lr);
-      a.out[rowoff + d] = gate_output(ob, a.gate[rowoff + d]);
+      uint16_t res = 0;
+      if (!dead) {
+        const uint16_t ob = bf16_rne_f32(o[t][r] * f / den);
+        res = gate_output(ob, a.gate[rowoff + d]);
+      }
+      a.out[rowoff + d] = res;
     }
+    if (a.lse != nullptr && li == 0)
+      a.lse[((size_t)b * S + qr) * Hq + h] =
+          (den > 0.f) ? (mtot + log2f(den)) * kLn2 : -INFINITY;
   }
 }
 
@@ -393,6 +428,10 @@ hipError_t launch_prefill(const PrefillLaunch& p, hipStream_t stream) {
   a.heads_per_part = group / a.parts;
   a.batch = p.batch;
   a.num_m_tiles = (p.seq_len + kBM - 1) / kBM;
+  a.kv_lens = p.kv_lens;
+  a.sinks = p.sinks;
+  a.lse = p.lse;
+  a.window = p.window;
   dim3 grid(grid_size(p.batch * p.num_kv_heads * a.parts, a.num_m_tiles));
   hipLaunchKernelGGL(prefill_gate_kernel, grid, dim3(kThreads), 0, stream, a);
   return hipGetLastError();

@@ -67,13 +67,17 @@ typedef struct ga_decode_dims {
     int64_t num_pages;         /* P: pages in each of k_pool / v_pool */
 } ga_decode_dims;
 
-/* How a decode call splits each sequence (chosen from the dims alone, i.e. from
- * the allocated capacity W * page_size and not from the current lengths, so one
- * captured graph serves every length up to the capacity -- FreeToken PR #781,
- * Automatic dispatch: "capacity refers to the allocated buffer"). */
+/* How a decode call splits each sequence.  The grid, NS and the workspace are
+ * chosen from the dims alone, i.e. from the allocated capacity W * page_size
+ * and not from the current lengths, so one captured graph serves every length
+ * up to the capacity (FreeToken PR #781, Automatic dispatch, ties its
+ * dispatch to the allocated capacity).  On the device, each sequence's visible
+ * keys (from the window start, rounded down to a page, to its length) are cut
+ * into NS equal page-aligned parts of at least 64 tokens, so a sequence far
+ * shorter than the capacity still spreads over its NS blocks. */
 typedef struct ga_decode_plan {
-    int32_t tokens_per_split;  /* T: each (sequence, kv head, split) block covers T tokens */
-    int32_t num_splits;        /* ceil(W * page_size / T) */
+    int32_t tokens_per_split;  /* T: the most tokens one (sequence, kv head, split) block covers */
+    int32_t num_splits;        /* NS = ceil(W * page_size / T) blocks per (sequence, kv head) */
     size_t workspace_bytes;    /* fp32 partials: B * H_q * num_splits * (D + 2) * 4, rounded up */
 } ga_decode_plan;
 
@@ -147,6 +151,51 @@ typedef struct ga_prefill_dims {
 ga_status gated_attn_prefill(const uint16_t *q, const uint16_t *gate, const uint16_t *k,
                              const uint16_t *v, float scale, int causal, uint16_t *out,
                              void *stream, const ga_prefill_dims *dims);
+
+/*
+ * Attention-spec options of the _ex entry points.  The pages name these
+ * options without defining them: the FreeToken PR #781 keeps windows and sinks
+ * off its fused path (Automatic dispatch) and tests them (Correctness and
+ * actual execution); the cuDNN "Gated Attention Block" page's Forward offers
+ * return_lse (softmax statistics [B, H_q, S] fp32) and seq_lens_present
+ * (per-batch KV lengths).  This library reads them as follows, per query row:
+ *   visible keys  decode: j < L; prefill row i: j < kv_lens[b], j <= i if
+ *                 causal; and with window w > 0 only the w most recent of
+ *                 them (decode: j >= L - w; prefill: j > i - w)
+ *   Z             sum over visible j of exp(s_j), plus exp(sinks[h]) if sinks
+ *   O             sum over visible j of exp(s_j) V_j / Z   (s_j = scale q.k_j)
+ *   lse           ln Z, natural log; -inf when Z = 0
+ *   A row with no visible key is dead and gets out = +0 (its lse is the sink
+ *   logit, or -inf).  A zeroed struct (or NULL) is plain attention.
+ * All pointers are device pointers, 4-byte aligned, owned by the caller.
+ */
+typedef struct ga_attn_options {
+    const float *sinks;     /* [H_q] fp32 sink logits (natural-log units, not scaled), or NULL */
+    float *lse;             /* written: decode [B][H_q], prefill [B][S][H_q] fp32; or NULL */
+    const int32_t *kv_lens; /* prefill only, [B] int32 key lengths (clamped to [0, S]);
+                               NULL = S for every sequence; must be NULL for decode */
+    int32_t window;         /* > 0: sliding window of that many keys; <= 0: none */
+    int32_t flags;          /* reserved; must be 0 */
+} ga_attn_options;
+
+/* gated_attn_decode with options appended (the cuDNN page's Forward appends
+ * new arguments at the end).  opts == NULL is gated_attn_decode.  Extra
+ * errors: GA_ERR_INVALID_ARGUMENT for flags != 0, a misaligned pointer, or
+ * kv_lens set.  The workspace size does not depend on the options. */
+ga_status gated_attn_decode_ex(const uint16_t *q, const uint16_t *gate, const uint16_t *k_pool,
+                               const uint16_t *v_pool, const int32_t *block_table,
+                               const int32_t *seq_lens, float scale, uint16_t *out, void *stream,
+                               const ga_decode_dims *dims, void *workspace,
+                               size_t workspace_bytes, const ga_attn_options *opts);
+
+/* gated_attn_prefill with options appended.  opts == NULL is
+ * gated_attn_prefill.  GA_ERR_INVALID_ARGUMENT for flags != 0 or a misaligned
+ * pointer.  Key lengths mask keys only: a row past its sequence's length
+ * still attends to the sequence's keys (causal rows see all of them). */
+ga_status gated_attn_prefill_ex(const uint16_t *q, const uint16_t *gate, const uint16_t *k,
+                                const uint16_t *v, float scale, int causal, uint16_t *out,
+                                void *stream, const ga_prefill_dims *dims,
+                                const ga_attn_options *opts);
 
 /* Static, human-readable name of a status. */
 const char *gated_attn_status_string(ga_status status);

@@ -140,6 +140,42 @@ def test_small_workspace_is_rejected():
     assert _call(wsb=need - 1) == ga.GA_ERR_WORKSPACE_TOO_SMALL
 
 
+def _call_ex(opts, dims=None, batch=None):
+    d = dims or _dims(**({} if batch is None else dict(batch=batch)))
+    return ga.lib.gated_attn_decode_ex(FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 0.0625, FAKE, None,
+                                       ctypes.byref(d), FAKE, 1 << 40, opts)
+
+
+@pytest.mark.parametrize("kw", [dict(flags=1), dict(sinks=FAKE + 2), dict(lse=FAKE + 1),
+                                dict(kv_lens=FAKE)])
+def test_decode_ex_bad_options_are_rejected(kw):
+    """Reserved flags, misaligned option pointers, and prefill-only key lengths."""
+    o = ga.AttnOptions(**kw)
+    assert _call_ex(ctypes.byref(o)) == ga.GA_ERR_INVALID_ARGUMENT
+    assert _call_ex(ctypes.byref(o), batch=0) == ga.GA_ERR_INVALID_ARGUMENT
+
+
+def test_decode_ex_null_or_zero_options_behave_like_plain_decode():
+    """No device here: the plain and _ex calls fail the same way, after the
+    same argument checks, and a batch of 0 succeeds for both."""
+    plain = _call()
+    assert _call_ex(None) == plain
+    assert _call_ex(ctypes.byref(ga.AttnOptions())) == plain
+    assert _call_ex(ctypes.byref(ga.AttnOptions(window=-5))) == plain
+    assert _call_ex(ctypes.byref(ga.AttnOptions(window=7, sinks=FAKE, lse=FAKE)), batch=0) == \
+        ga.GA_OK
+
+
+@pytest.mark.parametrize("kw,status", [(dict(flags=2), ga.GA_ERR_INVALID_ARGUMENT),
+                                       (dict(kv_lens=FAKE + 2), ga.GA_ERR_INVALID_ARGUMENT),
+                                       (dict(kv_lens=FAKE, window=3), ga.GA_OK)])
+def test_prefill_ex_options(kw, status):
+    d = ga.PrefillDims(0, 128, 16, 2, 256)  # batch 0: validated, then nothing to do
+    o = ga.AttnOptions(**kw)
+    assert ga.lib.gated_attn_prefill_ex(FAKE, FAKE, FAKE, FAKE, 0.0625, 1, FAKE, None,
+                                        ctypes.byref(d), ctypes.byref(o)) == status
+
+
 def test_null_dims_rejected():
     assert ga.lib.gated_attn_decode(FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 0.0625, FAKE, None,
                                     None, FAKE, 1 << 40) == ga.GA_ERR_INVALID_ARGUMENT
