@@ -124,7 +124,9 @@ ga_status gated_attn_decode(const uint16_t *q, const uint16_t *gate, const uint1
 /* Measurement hook for benchmarks and profilers.  Arms the calling thread's
  * next n gated_attn_decode calls: the i-th of them records starts[i] on its
  * stream immediately before its stage-1 kernel and stops[i] immediately after
- * it, so hipEventElapsedTime(starts[i], stops[i]) is that kernel's duration.
+ * it, so hipEventElapsedTime(starts[i], stops[i]) bounds that kernel's
+ * duration from above (the interval also holds the event packets and the
+ * kernel's dispatch: a few microseconds on MI355X).
  * The events (hipEvent_t) are created, owned and destroyed by the caller and
  * must stay valid until recorded.  n == 0 disarms.  Results are unaffected.
  * GA_ERR_INVALID_ARGUMENT for n < 0, or n > 0 with a NULL array. */
