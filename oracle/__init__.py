@@ -66,6 +66,15 @@ def _load():
         ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int,
         ctypes.c_int64, _f64p, ctypes.c_int, _u16p, _f64p, _f64p, _f64p, ctypes.c_int,
     ]
+    lib.oracle_e4m3_value.restype = ctypes.c_double
+    lib.oracle_e4m3_value.argtypes = [ctypes.c_uint8]
+    lib.oracle_decode_fp8.restype = ctypes.c_int
+    lib.oracle_decode_fp8.argtypes = [
+        _u16p, _u16p, ctypes.POINTER(ctypes.c_uint8), ctypes.POINTER(ctypes.c_uint8), _i32p, _i32p,
+        ctypes.c_double, ctypes.c_double, ctypes.c_double,
+        ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int,
+        ctypes.c_int64, _f64p, ctypes.c_int, _u16p, _f64p, _f64p, _f64p, ctypes.c_int,
+    ]
     lib.oracle_prefill_ex.restype = ctypes.c_int
     lib.oracle_prefill_ex.argtypes = [
         _u16p, _u16p, _u16p, _u16p, ctypes.c_double, ctypes.c_int,
@@ -138,6 +147,11 @@ def gate_output(ob_bits: int, sigma_bits: int) -> int:
     return int(_load().oracle_gate_output(int(ob_bits), int(sigma_bits)))
 
 
+def e4m3_value(code: int) -> float:
+    """fp64 value of an OCP float8 e4m3 code (NaN for 0x7F / 0xFF)."""
+    return float(_load().oracle_e4m3_value(int(code) & 0xFF))
+
+
 # --------------------------------------------------------------------------
 # Attention
 # --------------------------------------------------------------------------
@@ -154,7 +168,7 @@ def _sinks(sinks, Hq):
 
 
 def decode(q, gate, k_pool, v_pool, block_table, seq_lens, scale, nthreads=None, *,
-           sinks=None, window=0, return_lse=False):
+           sinks=None, window=0, return_lse=False, k_descale=1.0, v_descale=1.0):
     """Gated GQA decode over a paged pool.
 
     q, gate: [B, H_q, D] bf16 bits; k_pool, v_pool: [P, page, H_kv, D];
@@ -163,9 +177,16 @@ def decode(q, gate, k_pool, v_pool, block_table, seq_lens, scale, nthreads=None,
     Returns (out bits [B,H_q,D], O fp64 [B,H_q,D], Mref fp64 [B,H_q,D]) and,
     with return_lse, also lse fp64 [B, H_q] (natural log of the softmax
     denominator, -inf for a row with no visible key and no sink).
+    uint8 pools hold e4m3 codes: K = k_descale * e4m3(code), V likewise.
     """
     lib = _load()
-    q, gate, k_pool, v_pool = (_u16(a) for a in (q, gate, k_pool, v_pool))
+    fp8 = np.asarray(k_pool).dtype == np.uint8
+    q, gate = _u16(q), _u16(gate)
+    if fp8:
+        k_pool = np.ascontiguousarray(k_pool, dtype=np.uint8)
+        v_pool = np.ascontiguousarray(v_pool, dtype=np.uint8)
+    else:
+        k_pool, v_pool = _u16(k_pool), _u16(v_pool)
     block_table = np.ascontiguousarray(block_table, dtype=np.int32)
     seq_lens = np.ascontiguousarray(seq_lens, dtype=np.int32)
     B, Hq, D = q.shape
@@ -177,13 +198,21 @@ def decode(q, gate, k_pool, v_pool, block_table, seq_lens, scale, nthreads=None,
     mref = np.zeros((B, Hq, D), dtype=np.float64)
     lse = np.zeros((B, Hq), dtype=np.float64)
     sk, sk_p = _sinks(sinks, Hq)
-    st = lib.oracle_decode_ex(
-        _ptr(q, ctypes.c_uint16), _ptr(gate, ctypes.c_uint16),
-        _ptr(k_pool, ctypes.c_uint16), _ptr(v_pool, ctypes.c_uint16),
-        _ptr(block_table, ctypes.c_int32), _ptr(seq_lens, ctypes.c_int32),
-        float(scale), B, Hq, Hkv, D, page, W, P, sk_p, int(window),
-        _ptr(out, ctypes.c_uint16), _ptr(o, ctypes.c_double), _ptr(mref, ctypes.c_double),
-        _ptr(lse, ctypes.c_double), nthreads or default_threads())
+    tail = (B, Hq, Hkv, D, page, W, P, sk_p, int(window),
+            _ptr(out, ctypes.c_uint16), _ptr(o, ctypes.c_double), _ptr(mref, ctypes.c_double),
+            _ptr(lse, ctypes.c_double), nthreads or default_threads())
+    if fp8:
+        st = lib.oracle_decode_fp8(
+            _ptr(q, ctypes.c_uint16), _ptr(gate, ctypes.c_uint16),
+            _ptr(k_pool, ctypes.c_uint8), _ptr(v_pool, ctypes.c_uint8),
+            _ptr(block_table, ctypes.c_int32), _ptr(seq_lens, ctypes.c_int32),
+            float(scale), float(k_descale), float(v_descale), *tail)
+    else:
+        st = lib.oracle_decode_ex(
+            _ptr(q, ctypes.c_uint16), _ptr(gate, ctypes.c_uint16),
+            _ptr(k_pool, ctypes.c_uint16), _ptr(v_pool, ctypes.c_uint16),
+            _ptr(block_table, ctypes.c_int32), _ptr(seq_lens, ctypes.c_int32),
+            float(scale), *tail)
     if st != 0:
         raise OracleError(f"oracle_decode failed with status {st}")
     if return_lse:

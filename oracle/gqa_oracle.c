@@ -28,6 +28,12 @@
  *   lse            ln Z  (-inf when Z = 0), the softmax statistic of the row
  *   A row with no visible key is dead: out = +0 (its lse is the sink, or -inf).
  *
+ * FP8 KV pool (oracle_decode_fp8): K and V are stored as OCP float8 e4m3
+ * codes with one dequantisation factor per tensor (cuDNN Gated Attention
+ * Block page, Quantization specs: static per-tensor scales):
+ *   K_j[d] = k_descale * e4m3(code),  V_j[d] = v_descale * e4m3(code)
+ * and attention proceeds as above on those values (exact in fp64).
+ *
  * Sources (page title, then the part of the page):
  *  - cuDNN FE-OSS "Gated Attention Block (SM107)", Overview, stage (4) SDPA
  *    (softmax(Q K^T * scale + mask) V with GQA H_q / H_kv) and stage (5) gate
@@ -130,6 +136,19 @@ void oracle_bf16_rne_array(const double *x, uint16_t *out, int64_t n)
         out[i] = oracle_bf16_rne(x[i]);
 }
 
+/* OCP float8 e4m3 (the "fn" variant: no infinities): 1 sign bit, 4 exponent
+ * bits (bias 7), 3 fraction bits.  Exponent field 0 holds the subnormals
+ * m * 2^-9; all-ones exponent and fraction (0x7F / 0xFF) is NaN; the largest
+ * finite magnitude is 1.75 * 2^8 = 448. */
+double oracle_e4m3_value(uint8_t c)
+{
+    int sign = (c >> 7) & 1, e = (c >> 3) & 15, m = c & 7;
+    if (e == 15 && m == 7)
+        return NAN;
+    double mag = (e == 0) ? ldexp((double)m, -9) : ldexp(8.0 + m, e - 10);
+    return sign ? -mag : mag;
+}
+
 /* sigma_b = bf16_rne(1 / (1 + exp(-g))) evaluated in fp64 (FreeToken PR #781,
  * Summary: the sigmoid of each bf16 gate is itself a bf16 value). */
 uint16_t oracle_sigmoid_bf16(uint16_t gate)
@@ -161,15 +180,31 @@ uint16_t oracle_gate_output(uint16_t ob, uint16_t sigma_b)
  * *lse receives ln Z.  Returns 0 for a row with Z = 0 (no visible key and no
  * sink, or a sink of -inf), else 1.
  * ------------------------------------------------------------------------- */
-static int attend_row(const uint16_t *qrow, const uint16_t *const *krows,
-                      const uint16_t *const *vrows, int L, int D, double scale,
-                      const double *sink, double *scores, double *o, double *mref, double *lse)
+/* K / V element d of a row: a bf16 pattern, or an e4m3 code times its
+ * per-tensor dequantisation factor (exact in fp64). */
+typedef struct {
+    int fp8;
+    double k_descale, v_descale;
+} kv_format;
+
+static double kv_elem(const void *row, int d, const kv_format *f, double descale)
 {
+    if (f && f->fp8)
+        return descale * oracle_e4m3_value(((const uint8_t *)row)[d]);
+    return oracle_bf16_value(((const uint16_t *)row)[d]);
+}
+
+static int attend_row(const uint16_t *qrow, const void *const *krows,
+                      const void *const *vrows, int L, int D, double scale,
+                      const double *sink, const kv_format *f, double *scores, double *o,
+                      double *mref, double *lse)
+{
+    const double kd = f ? f->k_descale : 1.0, vd = f ? f->v_descale : 1.0;
     double m = sink ? *sink : -INFINITY;
     for (int j = 0; j < L; ++j) {
         double dot = 0.0;
         for (int d = 0; d < D; ++d)
-            dot += oracle_bf16_value(qrow[d]) * oracle_bf16_value(krows[j][d]);
+            dot += oracle_bf16_value(qrow[d]) * kv_elem(krows[j], d, f, kd);
         scores[j] = scale * dot;
         if (scores[j] > m)
             m = scores[j];
@@ -188,7 +223,7 @@ static int attend_row(const uint16_t *qrow, const uint16_t *const *krows,
     for (int d = 0; d < D; ++d) {
         double num = 0.0, mag = 0.0;
         for (int j = 0; j < L; ++j) {
-            double v = oracle_bf16_value(vrows[j][d]);
+            double v = kv_elem(vrows[j], d, f, vd);
             num += scores[j] * v;
             mag += scores[j] * fabs(v);
         }
@@ -219,7 +254,8 @@ static void gate_row(const double *o, const uint16_t *gate_row, int D, uint16_t 
  * o_f64, mref  : [B][H_q][D] or NULL
  * ------------------------------------------------------------------------- */
 typedef struct {
-    const uint16_t *q, *gate, *k_pool, *v_pool;
+    const uint16_t *q, *gate;
+    const void *k_pool, *v_pool;
     const int32_t *block_table, *seq_lens;
     double scale;
     int B, Hq, Hkv, D, page_size, max_pages;
@@ -229,6 +265,7 @@ typedef struct {
     const double *sinks; /* [H_q] or NULL */
     int window;          /* > 0: only the last `window` keys are visible */
     double *lse;         /* [B][H_q] or NULL */
+    kv_format fmt;       /* bf16 pools, or e4m3 pools with their factors */
     int nthreads, tid;
     int status;
 } decode_job;
@@ -239,9 +276,10 @@ static void *decode_worker(void *arg)
     const int D = job->D, Hq = job->Hq, Hkv = job->Hkv, ps = job->page_size;
     const int group = Hq / Hkv;
     int maxL = job->max_pages * ps;
-    const uint16_t **krows = malloc(sizeof(*krows) * (size_t)(maxL > 0 ? maxL : 1));
-    const uint16_t **vrows = malloc(sizeof(*vrows) * (size_t)(maxL > 0 ? maxL : 1));
+    const void **krows = malloc(sizeof(*krows) * (size_t)(maxL > 0 ? maxL : 1));
+    const void **vrows = malloc(sizeof(*vrows) * (size_t)(maxL > 0 ? maxL : 1));
     double *scores = malloc(sizeof(double) * (size_t)(maxL > 0 ? maxL : 1));
+    const size_t esize = job->fmt.fp8 ? 1 : 2; /* bytes per pool element */
     double *o = malloc(sizeof(double) * (size_t)D);
     double *mref = malloc(sizeof(double) * (size_t)D);
     if (!krows || !vrows || !scores || !o || !mref) {
@@ -266,13 +304,13 @@ static void *decode_worker(void *arg)
                 job->status = ORACLE_EPAGE;
                 goto done;
             }
-            size_t off = (((size_t)page * ps + (size_t)(j % ps)) * Hkv + g) * D;
-            krows[j - j0] = job->k_pool + off;
-            vrows[j - j0] = job->v_pool + off;
+            size_t off = (((size_t)page * ps + (size_t)(j % ps)) * Hkv + g) * D * esize;
+            krows[j - j0] = (const char *)job->k_pool + off;
+            vrows[j - j0] = (const char *)job->v_pool + off;
         }
         double lse;
         attend_row(job->q + rbase, krows, vrows, nvis, D, job->scale,
-                   job->sinks ? &job->sinks[h] : NULL, scores, o, mref, &lse);
+                   job->sinks ? &job->sinks[h] : NULL, &job->fmt, scores, o, mref, &lse);
         if (nvis == 0) { /* dead row (padded slot): the dead-row select gives +0 */
             for (int d = 0; d < D; ++d)
                 job->out[rbase + d] = 0;
@@ -316,11 +354,11 @@ static int run_jobs(void *jobs, size_t job_size, int nthreads, void *(*fn)(void 
     return ORACLE_OK;
 }
 
-int oracle_decode_ex(const uint16_t *q, const uint16_t *gate, const uint16_t *k_pool,
-                     const uint16_t *v_pool, const int32_t *block_table, const int32_t *seq_lens,
-                     double scale, int B, int Hq, int Hkv, int D, int page_size, int max_pages,
-                     int64_t num_pages, const double *sinks, int window, uint16_t *out,
-                     double *o_f64, double *mref, double *lse, int nthreads)
+static int decode_any(const uint16_t *q, const uint16_t *gate, const void *k_pool,
+                      const void *v_pool, const int32_t *block_table, const int32_t *seq_lens,
+                      double scale, kv_format fmt, int B, int Hq, int Hkv, int D, int page_size,
+                      int max_pages, int64_t num_pages, const double *sinks, int window,
+                      uint16_t *out, double *o_f64, double *mref, double *lse, int nthreads)
 {
     if (B < 0 || Hq <= 0 || Hkv <= 0 || D <= 0 || page_size <= 0 || max_pages < 0 ||
         num_pages < 0 || Hq % Hkv != 0)
@@ -337,7 +375,7 @@ int oracle_decode_ex(const uint16_t *q, const uint16_t *gate, const uint16_t *k_
     for (int t = 0; t < nthreads; ++t) {
         decode_job j = {q, gate, k_pool, v_pool, block_table, seq_lens, scale,
                         B, Hq, Hkv, D, page_size, max_pages, num_pages,
-                        out, o_f64, mref, sinks, window, lse, nthreads, t, ORACLE_OK};
+                        out, o_f64, mref, sinks, window, lse, fmt, nthreads, t, ORACLE_OK};
         jobs[t] = j;
     }
     int st = run_jobs(jobs, sizeof(decode_job), nthreads, decode_worker);
@@ -346,6 +384,33 @@ int oracle_decode_ex(const uint16_t *q, const uint16_t *gate, const uint16_t *k_
             st = jobs[t].status;
     free(jobs);
     return st;
+}
+
+int oracle_decode_ex(const uint16_t *q, const uint16_t *gate, const uint16_t *k_pool,
+                     const uint16_t *v_pool, const int32_t *block_table, const int32_t *seq_lens,
+                     double scale, int B, int Hq, int Hkv, int D, int page_size, int max_pages,
+                     int64_t num_pages, const double *sinks, int window, uint16_t *out,
+                     double *o_f64, double *mref, double *lse, int nthreads)
+{
+    kv_format fmt = {0, 1.0, 1.0};
+    return decode_any(q, gate, k_pool, v_pool, block_table, seq_lens, scale, fmt, B, Hq, Hkv, D,
+                      page_size, max_pages, num_pages, sinks, window, out, o_f64, mref, lse,
+                      nthreads);
+}
+
+/* Decode over e4m3 K / V pools ([num_pages][page_size][H_kv][D] bytes) with
+ * per-tensor dequantisation factors; otherwise as oracle_decode_ex. */
+int oracle_decode_fp8(const uint16_t *q, const uint16_t *gate, const uint8_t *k_pool,
+                      const uint8_t *v_pool, const int32_t *block_table, const int32_t *seq_lens,
+                      double scale, double k_descale, double v_descale, int B, int Hq, int Hkv,
+                      int D, int page_size, int max_pages, int64_t num_pages,
+                      const double *sinks, int window, uint16_t *out, double *o_f64,
+                      double *mref, double *lse, int nthreads)
+{
+    kv_format fmt = {1, k_descale, v_descale};
+    return decode_any(q, gate, k_pool, v_pool, block_table, seq_lens, scale, fmt, B, Hq, Hkv, D,
+                      page_size, max_pages, num_pages, sinks, window, out, o_f64, mref, lse,
+                      nthreads);
 }
 
 int oracle_decode(const uint16_t *q, const uint16_t *gate, const uint16_t *k_pool,
@@ -386,8 +451,8 @@ static void *prefill_worker(void *arg)
     prefill_job *job = (prefill_job *)arg;
     const int D = job->D, Hq = job->Hq, Hkv = job->Hkv, S = job->S;
     const int group = Hq / Hkv;
-    const uint16_t **krows = malloc(sizeof(*krows) * (size_t)S);
-    const uint16_t **vrows = malloc(sizeof(*vrows) * (size_t)S);
+    const void **krows = malloc(sizeof(*krows) * (size_t)S);
+    const void **vrows = malloc(sizeof(*vrows) * (size_t)S);
     double *scores = malloc(sizeof(double) * (size_t)S);
     double *o = malloc(sizeof(double) * (size_t)D);
     double *mref = malloc(sizeof(double) * (size_t)D);
@@ -430,7 +495,7 @@ static void *prefill_worker(void *arg)
         size_t obase = ((size_t)r * Hq + h) * D;
         double lse;
         attend_row(job->q + qbase, krows, vrows, nvis, D, job->scale,
-                   job->sinks ? &job->sinks[h] : NULL, scores, o, mref, &lse);
+                   job->sinks ? &job->sinks[h] : NULL, NULL, scores, o, mref, &lse);
         if (nvis == 0) { /* dead row: +0 */
             for (int d = 0; d < D; ++d)
                 job->out[obase + d] = 0;

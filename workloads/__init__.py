@@ -28,6 +28,11 @@ import numpy as np
 
 PAGE_SIZE = 16
 NAN_BF16 = 0x7FC0
+NAN_E4M3 = 0x7F
+E4M3_MAX = 448.0
+# default per-tensor dequantisation factor of FP8 pools: N(0, 1) values up to
+# 6.5 map onto the whole e4m3 range
+E4M3_DESCALE = float(np.float32(6.5 / E4M3_MAX))
 
 # Stream ids for SeedSequence([seed, stream]).
 _S_Q, _S_GATE, _S_K, _S_V, _S_LEN, _S_PERM, _S_PAD = range(1, 8)
@@ -74,6 +79,36 @@ def normal_bf16(seed: int, stream: int, shape, std: float = 1.0, chunk: int = 1 
     return out.reshape(shape)
 
 
+def normal_e4m3(seed: int, stream: int, shape, descale: float, chunk: int = 1 << 22) -> np.ndarray:
+    """e4m3 codes (uint8) of N(0, 1) draws divided by ``descale``, clipped to
+    the finite range, encoded by torch's float32 -> float8_e4m3fn conversion.
+    Same chunked, thread-count independent streams as normal_bf16."""
+    import torch
+
+    n = int(np.prod(shape)) if len(shape) else 1
+    out = np.empty(n, dtype=np.uint8)
+    inv = np.float32(1.0 / descale)
+
+    def fill(i: int) -> None:
+        s, e = i * chunk, min(n, (i + 1) * chunk)
+        rng = np.random.Generator(np.random.PCG64(np.random.SeedSequence([int(seed), int(stream), i])))
+        x = np.clip(rng.standard_normal(e - s, dtype=np.float32) * inv, -E4M3_MAX, E4M3_MAX)
+        t = torch.from_numpy(x).to(torch.float8_e4m3fn).view(torch.uint8)
+        out[s:e] = t.numpy()
+
+    nchunks = (n + chunk - 1) // chunk
+    if nchunks <= 1:
+        for i in range(nchunks):
+            fill(i)
+    else:
+        from concurrent.futures import ThreadPoolExecutor
+
+        workers = max(1, min(16, len(os.sched_getaffinity(0))))
+        with ThreadPoolExecutor(workers) as ex:
+            list(ex.map(fill, range(nchunks)))
+    return out.reshape(shape)
+
+
 @dataclasses.dataclass
 class DecodeCase:
     name: str
@@ -84,6 +119,12 @@ class DecodeCase:
     block_table: np.ndarray  # [B, W] int32, -1 where unused
     seq_lens: np.ndarray     # [B] int32, 0 for padded slots
     scale: float
+    k_descale: float = 1.0   # FP8 pools (uint8 e4m3 codes): K = k_descale * e4m3(code)
+    v_descale: float = 1.0
+
+    @property
+    def fp8(self) -> bool:
+        return self.k_pool.dtype == np.uint8
 
     @property
     def dims(self):
@@ -93,9 +134,11 @@ class DecodeCase:
                     max_pages_per_seq=self.block_table.shape[1], num_pages=P)
 
     def kv_bytes(self) -> int:
-        """Algorithmic K+V bytes a decode call reads: sum_b L_b * H_kv * D * 2 B * 2."""
+        """Algorithmic K+V bytes a decode call reads: sum_b L_b * H_kv * D * elem * 2
+        (elem = 2 bytes for bf16 pools, 1 for e4m3)."""
         _, _, Hkv, D = self.k_pool.shape
-        return int(np.clip(self.seq_lens, 0, None).astype(np.int64).sum()) * Hkv * D * 2 * 2
+        elem = self.k_pool.dtype.itemsize
+        return int(np.clip(self.seq_lens, 0, None).astype(np.int64).sum()) * Hkv * D * elem * 2
 
 
 @dataclasses.dataclass
@@ -112,7 +155,9 @@ class PrefillCase:
 def make_decode(name: str, seq_lens: Sequence[int], *, seed: int, num_q_heads: int = 16,
                 num_kv_heads: int = 2, head_dim: int = 256, max_pages_per_seq: Optional[int] = None,
                 shuffle: bool = True, poison: bool = True, extra_pages: int = 0,
-                scale: Optional[float] = None, gate_std: float = 2.0) -> DecodeCase:
+                scale: Optional[float] = None, gate_std: float = 2.0, kv_dtype: str = "bf16",
+                kv_descale: float = E4M3_DESCALE) -> DecodeCase:
+    """kv_dtype "fp8": K and V pools of e4m3 codes with per-tensor factor kv_descale."""
     lens = np.asarray(seq_lens, dtype=np.int32)
     B = lens.shape[0]
     npages = (np.clip(lens, 0, None).astype(np.int64) + PAGE_SIZE - 1) // PAGE_SIZE
@@ -133,22 +178,33 @@ def make_decode(name: str, seq_lens: Sequence[int], *, seed: int, num_q_heads: i
     Hq, Hkv, D = num_q_heads, num_kv_heads, head_dim
     q = normal_bf16(seed, _S_Q, (B, Hq, D))
     gate = normal_bf16(seed, _S_GATE, (B, Hq, D), std=gate_std)
-    k_pool = normal_bf16(seed, _S_K, (max(P, 1), PAGE_SIZE, Hkv, D))
-    v_pool = normal_bf16(seed, _S_V, (max(P, 1), PAGE_SIZE, Hkv, D))
+    pool_shape = (max(P, 1), PAGE_SIZE, Hkv, D)
+    if kv_dtype == "fp8":
+        k_pool = normal_e4m3(seed, _S_K, pool_shape, kv_descale)
+        v_pool = normal_e4m3(seed, _S_V, pool_shape, kv_descale)
+        nan = NAN_E4M3
+    else:
+        assert kv_dtype == "bf16", kv_dtype
+        k_pool = normal_bf16(seed, _S_K, pool_shape)
+        v_pool = normal_bf16(seed, _S_V, pool_shape)
+        nan = NAN_BF16
     if poison:
         for b in range(B):
             n = int(npages[b])
             tail = int(lens[b]) - (n - 1) * PAGE_SIZE if n > 0 else PAGE_SIZE
             if n > 0 and tail < PAGE_SIZE:
                 last = block_table[b, n - 1]
-                k_pool[last, tail:] = NAN_BF16
-                v_pool[last, tail:] = NAN_BF16
+                k_pool[last, tail:] = nan
+                v_pool[last, tail:] = nan
         if extra_pages or P == 0:
             unused = ids[used:] if P else np.array([0])
-            k_pool[unused] = NAN_BF16
-            v_pool[unused] = NAN_BF16
+            k_pool[unused] = nan
+            v_pool[unused] = nan
+    fp8 = kv_dtype == "fp8"
     return DecodeCase(name, q, gate, k_pool, v_pool, block_table, lens,
-                      float(scale if scale is not None else 1.0 / np.sqrt(D)))
+                      float(scale if scale is not None else 1.0 / np.sqrt(D)),
+                      k_descale=float(kv_descale) if fp8 else 1.0,
+                      v_descale=float(kv_descale) if fp8 else 1.0)
 
 
 def make_prefill(name: str, batch: int, seq_len: int, *, seed: int, num_q_heads: int = 16,
