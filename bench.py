@@ -143,9 +143,17 @@ class DecodeCall:
             self.fn = ga.lib.gated_attn_decode_ex
             self.extra = (ctypes.byref(self.opts),)
 
+        self.descales = ()
+        if getattr(case, "fp8", False):
+            # e4m3 pools through gated_attn_decode_fp8kv (options pointer last, may be NULL)
+            self.fn = ga.lib.gated_attn_decode_fp8kv
+            self.descales = (ctypes.c_float(case.k_descale), ctypes.c_float(case.v_descale))
+            if not self.extra:
+                self.extra = (None,)
+
     def __call__(self):
-        st = self.fn(*self.args, self.scale, self.outp, self.stream, self.dref, self.wsp, self.wsb,
-                     *self.extra)
+        st = self.fn(*self.args, self.scale, *self.descales, self.outp, self.stream, self.dref,
+                     self.wsp, self.wsb, *self.extra)
         if st != 0:
             self.ga.check(st, "gated_attn_decode")
 
@@ -214,7 +222,7 @@ def time_decode(ga, case, dev, n_calls: int, settle_s: float = 0.1, **opts) -> d
     lens = np.clip(case.seq_lens.astype(np.int64), 0, None)
     if opts.get("window"):
         lens = np.minimum(lens, int(opts["window"]))
-    kv = int(lens.sum()) * Hkv * D * 2 * 2
+    kv = int(lens.sum()) * Hkv * D * case.k_pool.dtype.itemsize * 2
     gbs = kv / (ms * 1e-3) / 1e9
     desc = ", ".join(f"{k}={'yes' if k == 'sinks' else v}" for k, v in opts.items() if v is not None)
     return {"workload": f"gated GQA decode B={B} L={int(case.seq_lens.max())} H_q={Hq} "
@@ -425,6 +433,11 @@ def main() -> int:
                                       poison=False, max_pages_per_seq=2048, extra_pages=0)
         result["decode_l1024_cap32768"] = time_decode(ga, short, dev, 100)
         del short
+        # FP8 (e4m3) K / V pools, same shape as the headline
+        c8 = workloads.make_decode("decode_b64_l4096_fp8", [4096] * 64, seed=2, poison=False,
+                                   max_pages_per_seq=256, kv_dtype="fp8")
+        result["decode_fp8kv"] = time_decode(ga, c8, dev, 200)
+        del c8
         del c32
         p32 = workloads.make_prefill("prefill_b2_s2048_hq32", 2, 2048, seed=4, causal=True,
                                      num_q_heads=32, num_kv_heads=2)

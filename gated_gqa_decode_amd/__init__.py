@@ -34,6 +34,7 @@ EXPORTED_SYMBOLS = (
     "gated_attn_decode_workspace_size",
     "gated_attn_decode",
     "gated_attn_decode_ex",
+    "gated_attn_decode_fp8kv",
     "gated_attn_decode_time_stage1",
     "gated_attn_prefill",
     "gated_attn_prefill_ex",
@@ -107,6 +108,10 @@ def _load_library() -> ctypes.CDLL:
     lib.gated_attn_decode_ex.argtypes = [vp, vp, vp, vp, vp, vp, ctypes.c_float, vp, vp,
                                          ctypes.POINTER(DecodeDims), vp, sz,
                                          ctypes.POINTER(AttnOptions)]
+    lib.gated_attn_decode_fp8kv.restype = ctypes.c_int
+    lib.gated_attn_decode_fp8kv.argtypes = [vp, vp, vp, vp, vp, vp, ctypes.c_float, ctypes.c_float,
+                                            ctypes.c_float, vp, vp, ctypes.POINTER(DecodeDims),
+                                            vp, sz, ctypes.POINTER(AttnOptions)]
     lib.gated_attn_prefill_ex.restype = ctypes.c_int
     lib.gated_attn_prefill_ex.argtypes = [vp, vp, vp, vp, ctypes.c_float, ctypes.c_int, vp, vp,
                                           ctypes.POINTER(PrefillDims),
@@ -237,7 +242,8 @@ def _options(sinks, window, lse, kv_lens, Hq, dev):
 
 
 def decode(q, gate, k_pool, v_pool, block_table, seq_lens, scale, *, out=None, workspace=None,
-           stream=None, sinks=None, window=0, lse=None, return_lse=False):
+           stream=None, sinks=None, window=0, lse=None, return_lse=False, k_descale=None,
+           v_descale=None):
     """Gated GQA decode over a paged pool; returns ``out`` [B, H_q, D] bf16.
 
     q, gate: [B, H_q, D] bf16; k_pool, v_pool: [P, 16, H_kv, D] bf16;
@@ -249,13 +255,22 @@ def decode(q, gate, k_pool, v_pool, block_table, seq_lens, scale, *, out=None, w
     ``window`` > 0 keeps the last ``window`` keys, ``lse`` fp32 [B, H_q] to
     receive the natural-log log-sum-exp (or ``return_lse=True`` to allocate
     it; the call then returns ``(out, lse)``).
+    FP8 pools (gated_attn_decode_fp8kv): ``k_pool`` / ``v_pool`` of dtype
+    float8_e4m3fn (or uint8 holding e4m3 codes) with per-tensor factors
+    ``k_descale`` / ``v_descale`` (K = k_descale * code value).
     """
     torch = _torch()
     dev = q.device
     _need(q, "q", torch.bfloat16, 3, dev)
     _need(gate, "gate", torch.bfloat16, 3, dev)
-    _need(k_pool, "k_pool", torch.bfloat16, 4, dev)
-    _need(v_pool, "v_pool", torch.bfloat16, 4, dev)
+    fp8 = k_pool.dtype in (torch.uint8, torch.float8_e4m3fn)
+    pool_dtype = k_pool.dtype if fp8 else torch.bfloat16
+    _need(k_pool, "k_pool", pool_dtype, 4, dev)
+    _need(v_pool, "v_pool", pool_dtype, 4, dev)
+    if fp8 and (k_descale is None or v_descale is None):
+        raise ValueError("FP8 pools need k_descale and v_descale")
+    if not fp8 and (k_descale is not None or v_descale is not None):
+        raise ValueError("k_descale / v_descale apply to FP8 pools only")
     _need(block_table, "block_table", torch.int32, 2, dev)
     _need(seq_lens, "seq_lens", torch.int32, 1, dev)
     if gate.shape != q.shape or v_pool.shape != k_pool.shape:
@@ -286,7 +301,11 @@ def decode(q, gate, k_pool, v_pool, block_table, seq_lens, scale, *, out=None, w
             block_table.data_ptr(), seq_lens.data_ptr(), float(scale), out.data_ptr(),
             _stream_handle(stream, dev), ctypes.byref(dims), workspace.data_ptr(),
             workspace.numel())
-    if opts is None:
+    if fp8:
+        args = args[:7] + (float(k_descale), float(v_descale)) + args[7:]
+        check(lib.gated_attn_decode_fp8kv(*args, None if opts is None else ctypes.byref(opts)),
+              "gated_attn_decode_fp8kv")
+    elif opts is None:
         check(lib.gated_attn_decode(*args), "gated_attn_decode")
     else:
         check(lib.gated_attn_decode_ex(*args, ctypes.byref(opts)), "gated_attn_decode_ex")

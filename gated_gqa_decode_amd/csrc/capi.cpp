@@ -149,14 +149,22 @@ size_t gated_attn_decode_workspace_size(const ga_decode_dims* dims) {
   return p.workspace_bytes;
 }
 
-ga_status gated_attn_decode_ex(const uint16_t* q, const uint16_t* gate, const uint16_t* k_pool,
-                               const uint16_t* v_pool, const int32_t* block_table,
-                               const int32_t* seq_lens, float scale, uint16_t* out, void* stream,
-                               const ga_decode_dims* dims, void* workspace,
-                               size_t workspace_bytes, const ga_attn_options* opts) {
+}  // extern "C"
+
+namespace {
+
+// Shared by the bf16 and e4m3 decode entry points.
+ga_status decode_impl(const uint16_t* q, const uint16_t* gate, const void* k_pool,
+                      const void* v_pool, const int32_t* block_table, const int32_t* seq_lens,
+                      float scale, int kv_fp8, float k_descale, float v_descale, uint16_t* out,
+                      void* stream, const ga_decode_dims* dims, void* workspace,
+                      size_t workspace_bytes, const ga_attn_options* opts) {
   ga_status st = check_decode_dims(dims);
   if (st != GA_OK) return st;
   if (!(std::isfinite(scale) && scale > 0.f)) return GA_ERR_INVALID_ARGUMENT;
+  if (!(std::isfinite(k_descale) && k_descale > 0.f && std::isfinite(v_descale) &&
+        v_descale > 0.f))
+    return GA_ERR_INVALID_ARGUMENT;
   st = check_options(opts, /*prefill=*/false);
   if (st != GA_OK) return st;
   if (dims->batch == 0) return GA_OK;
@@ -185,6 +193,9 @@ ga_status gated_attn_decode_ex(const uint16_t* q, const uint16_t* gate, const ui
   L.part_acc = static_cast<float*>(workspace);
   L.part_ml = L.part_acc + rows * kHeadDim;
   L.scale = scale;
+  L.kv_fp8 = kv_fp8;
+  L.k_descale = k_descale;
+  L.v_descale = v_descale;
   L.batch = dims->batch;
   L.num_q_heads = dims->num_q_heads;
   L.num_kv_heads = dims->num_kv_heads;
@@ -206,6 +217,29 @@ ga_status gated_attn_decode_ex(const uint16_t* q, const uint16_t* gate, const ui
   hipError_t e = ga::launch_decode(L, static_cast<hipStream_t>(stream));
   if (e != hipSuccess) return hip_fail(e);
   return GA_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+ga_status gated_attn_decode_ex(const uint16_t* q, const uint16_t* gate, const uint16_t* k_pool,
+                               const uint16_t* v_pool, const int32_t* block_table,
+                               const int32_t* seq_lens, float scale, uint16_t* out, void* stream,
+                               const ga_decode_dims* dims, void* workspace,
+                               size_t workspace_bytes, const ga_attn_options* opts) {
+  return decode_impl(q, gate, k_pool, v_pool, block_table, seq_lens, scale, 0, 1.f, 1.f, out,
+                     stream, dims, workspace, workspace_bytes, opts);
+}
+
+ga_status gated_attn_decode_fp8kv(const uint16_t* q, const uint16_t* gate, const uint8_t* k_pool,
+                                  const uint8_t* v_pool, const int32_t* block_table,
+                                  const int32_t* seq_lens, float scale, float k_descale,
+                                  float v_descale, uint16_t* out, void* stream,
+                                  const ga_decode_dims* dims, void* workspace,
+                                  size_t workspace_bytes, const ga_attn_options* opts) {
+  return decode_impl(q, gate, k_pool, v_pool, block_table, seq_lens, scale, 1, k_descale,
+                     v_descale, out, stream, dims, workspace, workspace_bytes, opts);
 }
 
 ga_status gated_attn_decode(const uint16_t* q, const uint16_t* gate, const uint16_t* k_pool,

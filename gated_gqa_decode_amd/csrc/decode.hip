@@ -30,6 +30,8 @@
 #include <math.h>
 #include <stdint.h>
 
+#include <type_traits>
+
 #include "ga_device.h"
 #include "ga_internal.h"
 
@@ -49,8 +51,8 @@ constexpr float kSlack = 8.f;    // lazy-rescale threshold, log2 units
 
 struct Stage1Args {
   const uint16_t* q;
-  const uint16_t* k_pool;
-  const uint16_t* v_pool;
+  const char* k_pool;  // bf16 or e4m3 elements, [P][16][H_kv][D]
+  const char* v_pool;
   const int32_t* block_table;
   const int32_t* seq_lens;
   float* part_acc;   // [B][H_q][NS][D]
@@ -102,6 +104,25 @@ __device__ __forceinline__ uint2 ldg8_stream(const char* p) {
   return make_uint2(v[0], v[1]);
 }
 
+__device__ __forceinline__ uint32_t ldg4_stream(const char* p) {
+  return __builtin_nontemporal_load(reinterpret_cast<const uint32_t*>(p));
+}
+
+// e4m3 codes -> numbers.  gfx950's conversions decode the OCP e4m3 format
+// exactly (checked on all 256 codes against an independent decoder); every
+// e4m3 value is a bf16 value, so the bf16 form feeds the dot2 instructions
+// unchanged.  `hi` selects the codes in bytes 2-3 instead of 0-1.
+typedef __attribute__((ext_vector_type(2))) float f32x2_t;
+
+template <bool hi>
+__device__ __forceinline__ uint32_t e4m3x2_to_bf16x2(uint32_t codes) {
+  return __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(codes, 1.0f, hi));
+}
+template <bool hi>
+__device__ __forceinline__ f32x2_t e4m3x2_to_f32x2(uint32_t codes) {
+  return __builtin_amdgcn_cvt_pk_f32_fp8(codes, hi);
+}
+
 // How one sequence is split.  The grid and the workspace come from the
 // capacity (num_splits splits of at most max_tokens tokens), so a call
 // captured once serves every length.  Inside that, the sequence's visible
@@ -139,7 +160,9 @@ __device__ __forceinline__ SplitRange split_range(int L, int window, int num_spl
 
 }  // namespace
 
-__global__ __launch_bounds__(512, 1) void decode_stage1_kernel(Stage1Args a) {
+// The stage-1 body for bf16 pools (kFp8 = false) and e4m3 pools (true).
+template <bool kFp8>
+__device__ __forceinline__ void stage1_body(const Stage1Args& a) {
   __shared__ WaveSlot wslot[kWaves][2];
   __shared__ MergeSlot merge;
   __shared__ int progress[kWaves];  // last step each wave started
@@ -190,16 +213,21 @@ __global__ __launch_bounds__(512, 1) void decode_stage1_kernel(Stage1Args a) {
   const int c16 = lane & 15;   // 16-byte chunk (and chunk + 16)
   const int hs = c16 >> 1;     // head whose score this lane keeps (see reduce_scatter8)
 
-  // q chunks c16 and c16 + 16 of the workgroup's heads (bf16 pairs); idle
-  // head slots get q = 0 (their scores and sums are computed and dropped).
+  // q of the workgroup's heads over the dims this lane's K pieces hold (bf16
+  // pairs): bf16 pools, d = 8 c16 .. +7 and 8 (c16 + 16) .. +7 (two 16-byte
+  // pieces of the 512-byte row); e4m3 pools, d = 16 c16 .. +15 (one 16-byte
+  // piece of the 256-byte row).  Idle head slots get q = 0 (their scores and
+  // sums are computed and dropped).
   uint4 qa[kGroup], qb[kGroup];
   {
     const uint16_t* qbase = a.q + ((size_t)b * Hq + (size_t)h0) * kD;
+    const int da = kFp8 ? 16 * c16 : 8 * c16;
+    const int db = kFp8 ? 16 * c16 + 8 : 8 * (c16 + 16);
 #pragma unroll
     for (int h = 0; h < kGroup; ++h) {
       const int hh = min(h, nh - 1);
-      qa[h] = ldg16(qbase + hh * kD + c16 * 8);
-      qb[h] = ldg16(qbase + hh * kD + (c16 + 16) * 8);
+      qa[h] = ldg16(qbase + hh * kD + da);
+      qb[h] = ldg16(qbase + hh * kD + db);
     }
 #pragma unroll
     for (int h = 0; h < kGroup; ++h)
@@ -234,47 +262,56 @@ __global__ __launch_bounds__(512, 1) void decode_stage1_kernel(Stage1Args a) {
   float l_run = 0.f;        // this lane's share of the running sum of head hs
 
   const int n_steps = (tok_end - tok_begin + kStep - 1) / kStep;
-  const size_t row_stride = (size_t)Hkv * kD;            // elements between tokens
-  const size_t page_stride = (size_t)kPage * row_stride; // elements between pages
+  constexpr int kElem = kFp8 ? 1 : 2;                      // bytes per K / V element
+  const size_t row_bytes = (size_t)Hkv * kD * kElem;        // between tokens
+  const size_t page_bytes = (size_t)kPage * row_bytes;      // between pages
 
-  // Element offsets of this lane's pieces inside one 8-token step (the same
-  // for every step); the step's base address is wave-uniform.
-  unsigned k_off[2];  // bytes
+  // Byte offsets of this lane's pieces inside one 8-token step (the same for
+  // every step); the step's base address is wave-uniform.
+  unsigned k_off[2];
 #pragma unroll
   for (int pass = 0; pass < 2; ++pass)
-    k_off[pass] = (unsigned)(((pass * 4 + tq) * (int)row_stride + c16 * 8) * 2);
-  unsigned v_off[kStep];  // bytes
+    k_off[pass] = (unsigned)((pass * 4 + tq) * (int)row_bytes + c16 * 16);
+  unsigned v_off[kStep];
 #pragma unroll
-  for (int t = 0; t < kStep; ++t) v_off[t] = (unsigned)((t * (int)row_stride + lane * 4) * 2);
+  for (int t = 0; t < kStep; ++t) v_off[t] = (unsigned)(t * (int)row_bytes + lane * 4 * kElem);
 
-  auto step_base = [&](int step, const uint16_t* pool) -> const uint16_t* {
+  auto step_base = [&](int step, const char* pool) -> const char* {
     const int t0 = tok_begin + step * kStep;
     const int j = t0 / kPage - first_page;  // wave-uniform
     const int pg = j < 64 ? __builtin_amdgcn_readlane(my_page[0], j)
                           : __builtin_amdgcn_readlane(my_page[1], j - 64);
-    return pool + (size_t)pg * page_stride + (size_t)(t0 % kPage) * row_stride + (size_t)g * kD;
+    return pool + (size_t)pg * page_bytes + (size_t)(t0 % kPage) * row_bytes +
+           (size_t)g * kD * kElem;
   };
 
-  // One step's data: K as 4 x 16 bytes (two passes of 4 tokens), V as 8 x 8
-  // bytes (one per token, a whole 512-byte row per wave instruction).
+  // One step's data.  K: per pass of 4 tokens, 32 bytes per lane (bf16) or 16
+  // (e4m3).  V: per token, 8 bytes per lane (bf16) or 4 (e4m3) -- a whole row
+  // segment per wave instruction either way.
+  typedef typename std::conditional<kFp8, uint32_t, uint2>::type VElem;
   struct KRegs {
-    uint4 k[2][2];
+    uint4 k[2][kFp8 ? 1 : 2];
   };
   struct VRegs {
-    uint2 v[kStep];
+    VElem v[kStep];
   };
   auto load_k = [&](int step, KRegs& r) {
-    const char* kb = reinterpret_cast<const char*>(step_base(step, a.k_pool));
+    const char* kb = step_base(step, a.k_pool);
 #pragma unroll
     for (int pass = 0; pass < 2; ++pass) {
       r.k[pass][0] = ldg16_stream(kb + k_off[pass]);
-      r.k[pass][1] = ldg16_stream(kb + (k_off[pass] + 256u));
+      if constexpr (!kFp8) r.k[pass][1] = ldg16_stream(kb + (k_off[pass] + 256u));
     }
   };
   auto load_v = [&](int step, VRegs& r) {
-    const char* vb = reinterpret_cast<const char*>(step_base(step, a.v_pool));
+    const char* vb = step_base(step, a.v_pool);
 #pragma unroll
-    for (int t = 0; t < kStep; ++t) r.v[t] = ldg8_stream(vb + v_off[t]);
+    for (int t = 0; t < kStep; ++t) {
+      if constexpr (kFp8)
+        r.v[t] = ldg4_stream(vb + v_off[t]);
+      else
+        r.v[t] = ldg8_stream(vb + v_off[t]);
+    }
   };
 
   // Two probability slots per wave: the scores of step i+1 are computed into
@@ -292,18 +329,40 @@ __global__ __launch_bounds__(512, 1) void decode_stage1_kernel(Stage1Args a) {
     float sc[2];
 #pragma unroll
     for (int pass = 0; pass < 2; ++pass) {
+      // this lane's 16 K values as 8 bf16 pairs, in q's pair order
+      uint32_t kp[8];
+      if constexpr (kFp8) {
+        const uint4 c = r.k[pass][0];
+        kp[0] = e4m3x2_to_bf16x2<false>(c.x);
+        kp[1] = e4m3x2_to_bf16x2<true>(c.x);
+        kp[2] = e4m3x2_to_bf16x2<false>(c.y);
+        kp[3] = e4m3x2_to_bf16x2<true>(c.y);
+        kp[4] = e4m3x2_to_bf16x2<false>(c.z);
+        kp[5] = e4m3x2_to_bf16x2<true>(c.z);
+        kp[6] = e4m3x2_to_bf16x2<false>(c.w);
+        kp[7] = e4m3x2_to_bf16x2<true>(c.w);
+      } else {
+        kp[0] = r.k[pass][0].x;
+        kp[1] = r.k[pass][0].y;
+        kp[2] = r.k[pass][0].z;
+        kp[3] = r.k[pass][0].w;
+        kp[4] = r.k[pass][kFp8 ? 0 : 1].x;
+        kp[5] = r.k[pass][kFp8 ? 0 : 1].y;
+        kp[6] = r.k[pass][kFp8 ? 0 : 1].z;
+        kp[7] = r.k[pass][kFp8 ? 0 : 1].w;
+      }
       float part[kGroup];
 #pragma unroll
       for (int h = 0; h < kGroup; ++h) {
         float x = 0.f;
-        x = dot2_bf16(qa[h].x, r.k[pass][0].x, x);
-        x = dot2_bf16(qa[h].y, r.k[pass][0].y, x);
-        x = dot2_bf16(qa[h].z, r.k[pass][0].z, x);
-        x = dot2_bf16(qa[h].w, r.k[pass][0].w, x);
-        x = dot2_bf16(qb[h].x, r.k[pass][1].x, x);
-        x = dot2_bf16(qb[h].y, r.k[pass][1].y, x);
-        x = dot2_bf16(qb[h].z, r.k[pass][1].z, x);
-        x = dot2_bf16(qb[h].w, r.k[pass][1].w, x);
+        x = dot2_bf16(qa[h].x, kp[0], x);
+        x = dot2_bf16(qa[h].y, kp[1], x);
+        x = dot2_bf16(qa[h].z, kp[2], x);
+        x = dot2_bf16(qa[h].w, kp[3], x);
+        x = dot2_bf16(qb[h].x, kp[4], x);
+        x = dot2_bf16(qb[h].y, kp[5], x);
+        x = dot2_bf16(qb[h].z, kp[6], x);
+        x = dot2_bf16(qb[h].w, kp[7], x);
         part[h] = x;
       }
       const float mine = reduce_scatter8(part, c16);
@@ -350,7 +409,7 @@ __global__ __launch_bounds__(512, 1) void decode_stage1_kernel(Stage1Args a) {
 #pragma unroll
         for (int e = 0; e < 4; ++e) acc[h][e] *= al[h];
     }
-    uint2 vv[kStep];
+    VElem vv[kStep];
 #pragma unroll
     for (int t = 0; t < kStep; ++t) vv[t] = r.v[t];
     if (t0 + kStep > tok_end || t0 < tok_lo) {
@@ -358,12 +417,24 @@ __global__ __launch_bounds__(512, 1) void decode_stage1_kernel(Stage1Args a) {
       // the window starts in: invisible rows take no part, whatever they hold
 #pragma unroll
       for (int t = 0; t < kStep; ++t)
-        if (t0 + t >= tok_end || t0 + t < tok_lo) vv[t] = make_uint2(0, 0);
+        if (t0 + t >= tok_end || t0 + t < tok_lo) vv[t] = VElem{};
     }
 #pragma unroll
     for (int t = 0; t < kStep; ++t) {
-      const uint2 v = vv[t];
-      const float vf[4] = {bf16_lo(v.x), bf16_hi(v.x), bf16_lo(v.y), bf16_hi(v.y)};
+      float vf[4];
+      if constexpr (kFp8) {
+        const f32x2_t lo = e4m3x2_to_f32x2<false>(vv[t]);
+        const f32x2_t hi = e4m3x2_to_f32x2<true>(vv[t]);
+        vf[0] = lo[0];
+        vf[1] = lo[1];
+        vf[2] = hi[0];
+        vf[3] = hi[1];
+      } else {
+        vf[0] = bf16_lo(vv[t].x);
+        vf[1] = bf16_hi(vv[t].x);
+        vf[2] = bf16_lo(vv[t].y);
+        vf[3] = bf16_hi(vv[t].y);
+      }
       const float4 pa = *reinterpret_cast<const float4*>(&ws.p[t][0]);
       const float4 pb = *reinterpret_cast<const float4*>(&ws.p[t][4]);
       const float pr[kGroup] = {pa.x, pa.y, pa.z, pa.w, pb.x, pb.y, pb.z, pb.w};
@@ -489,6 +560,14 @@ __global__ __launch_bounds__(512, 1) void decode_stage1_kernel(Stage1Args a) {
   }
 }
 
+__global__ __launch_bounds__(512, 1) void decode_stage1_kernel(Stage1Args a) {
+  stage1_body<false>(a);
+}
+
+__global__ __launch_bounds__(512, 1) void decode_stage1_fp8_kernel(Stage1Args a) {
+  stage1_body<true>(a);
+}
+
 struct Stage2Args {
   const uint16_t* gate;
   const int32_t* seq_lens;
@@ -497,6 +576,7 @@ struct Stage2Args {
   const float* sinks;  // [H_q] sink logits (natural-log units) or null
   uint16_t* out;
   float* lse;          // [B][H_q] or null
+  float v_descale;     // e4m3 pools: V = v_descale * code value (1 for bf16)
   int num_q_heads;
   int tokens_per_split;
   int num_splits;
@@ -578,7 +658,7 @@ __global__ __launch_bounds__(256) void decode_stage2_gate_kernel(Stage2Args a) {
                             (uint16_t)(graw.y & 0xffff), (uint16_t)(graw.y >> 16)};
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
-      const uint16_t ob = bf16_rne_f32(o[e] / lam);
+      const uint16_t ob = bf16_rne_f32(o[e] * a.v_descale / lam);
       o16[e] = gate_output(ob, gt[e]);
     }
     lse = (M + log2f(lam)) * kLn2;
@@ -593,13 +673,13 @@ __global__ __launch_bounds__(256) void decode_stage2_gate_kernel(Stage2Args a) {
 hipError_t launch_decode(const DecodeLaunch& d, hipStream_t stream) {
   Stage1Args a1;
   a1.q = d.q;
-  a1.k_pool = d.k_pool;
-  a1.v_pool = d.v_pool;
+  a1.k_pool = static_cast<const char*>(d.k_pool);
+  a1.v_pool = static_cast<const char*>(d.v_pool);
   a1.block_table = d.block_table;
   a1.seq_lens = d.seq_lens;
   a1.part_acc = d.part_acc;
   a1.part_ml = d.part_ml;
-  a1.scale_log2 = d.scale * kLog2e;
+  a1.scale_log2 = d.scale * d.k_descale * kLog2e;  // the K factor folds into the scores
   a1.num_q_heads = d.num_q_heads;
   a1.num_kv_heads = d.num_kv_heads;
   const int group = d.num_q_heads / d.num_kv_heads;
@@ -619,7 +699,10 @@ hipError_t launch_decode(const DecodeLaunch& d, hipStream_t stream) {
     err = hipEventRecord(d.stage1_start, stream);
     if (err != hipSuccess) return err;
   }
-  hipLaunchKernelGGL(decode_stage1_kernel, grid1, dim3(kWaves * 64), 0, stream, a1);
+  if (d.kv_fp8)
+    hipLaunchKernelGGL(decode_stage1_fp8_kernel, grid1, dim3(kWaves * 64), 0, stream, a1);
+  else
+    hipLaunchKernelGGL(decode_stage1_kernel, grid1, dim3(kWaves * 64), 0, stream, a1);
   err = hipGetLastError();
   if (err != hipSuccess) return err;
   if (d.stage1_stop != nullptr) {
@@ -635,6 +718,7 @@ hipError_t launch_decode(const DecodeLaunch& d, hipStream_t stream) {
   a2.sinks = d.sinks;
   a2.out = d.out;
   a2.lse = d.lse;
+  a2.v_descale = d.v_descale;
   a2.window = d.window;
   a2.tokens_per_split = d.tokens_per_split;
   a2.split_units = a1.split_units;

@@ -20,14 +20,17 @@ inline bool group_supported(int group) {
 struct DecodeLaunch {
   const uint16_t* q;
   const uint16_t* gate;
-  const uint16_t* k_pool;
-  const uint16_t* v_pool;
+  const void* k_pool;  // bf16, or e4m3 codes when kv_fp8
+  const void* v_pool;
   const int32_t* block_table;
   const int32_t* seq_lens;
   uint16_t* out;
   float* part_acc;  // workspace: [B][H_q][num_splits][D] fp32
   float* part_ml;   // workspace: [B][H_q][num_splits][2] fp32
   float scale;
+  int kv_fp8;        // pools hold e4m3 codes: K = k_descale * code, V = v_descale * code
+  float k_descale;   // 1 for bf16 pools
+  float v_descale;
   int batch;
   int num_q_heads;
   int num_kv_heads;

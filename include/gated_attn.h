@@ -190,6 +190,25 @@ ga_status gated_attn_decode_ex(const uint16_t *q, const uint16_t *gate, const ui
                                const ga_decode_dims *dims, void *workspace,
                                size_t workspace_bytes, const ga_attn_options *opts);
 
+/*
+ * Gated GQA decode over FP8 K / V pools: each element is an OCP float8 e4m3
+ * code (1 sign, 4 exponent bits biased by 7, 3 fraction bits, no infinities)
+ * and K = k_descale * value(code), V = v_descale * value(code) with one factor
+ * per tensor (the cuDNN "Gated Attention Block" page's FP8 pipeline takes
+ * static per-tensor scales, Forward: Quantization specs).  Everything else --
+ * layouts ([num_pages][page_size][H_kv][D], one byte per element), q, gate,
+ * out, dims, plan, workspace, options, errors -- is as gated_attn_decode_ex.
+ * The factors must be finite and > 0 (else GA_ERR_INVALID_ARGUMENT).  The K
+ * factor is folded into the score scale and the V factor into O before its
+ * bf16 rounding; the codes themselves are decoded exactly.
+ */
+ga_status gated_attn_decode_fp8kv(const uint16_t *q, const uint16_t *gate, const uint8_t *k_pool,
+                                  const uint8_t *v_pool, const int32_t *block_table,
+                                  const int32_t *seq_lens, float scale, float k_descale,
+                                  float v_descale, uint16_t *out, void *stream,
+                                  const ga_decode_dims *dims, void *workspace,
+                                  size_t workspace_bytes, const ga_attn_options *opts);
+
 /* gated_attn_prefill with options appended.  opts == NULL is
  * gated_attn_prefill.  GA_ERR_INVALID_ARGUMENT for flags != 0 or a misaligned
  * pointer.  Key lengths mask keys only: a row past its sequence's length

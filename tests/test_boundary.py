@@ -176,6 +176,26 @@ def test_prefill_ex_options(kw, status):
                                         ctypes.byref(d), ctypes.byref(o)) == status
 
 
+@pytest.mark.parametrize("kd,vd", [(0.0, 1.0), (1.0, -2.0), (float("inf"), 1.0),
+                                   (1.0, float("nan"))])
+def test_fp8kv_bad_factors_are_rejected(kd, vd):
+    d = _dims()
+    assert ga.lib.gated_attn_decode_fp8kv(FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 0.0625, kd, vd, FAKE,
+                                          None, ctypes.byref(d), FAKE, 1 << 40,
+                                          None) == ga.GA_ERR_INVALID_ARGUMENT
+
+
+def test_fp8kv_shares_the_decode_checks():
+    d = _dims(head_dim=128)
+    assert ga.lib.gated_attn_decode_fp8kv(FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 0.0625, 0.01, 0.01,
+                                          FAKE, None, ctypes.byref(d), FAKE, 1 << 40,
+                                          None) == ga.GA_ERR_UNSUPPORTED
+    d = _dims(batch=0)
+    assert ga.lib.gated_attn_decode_fp8kv(FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 0.0625, 0.01, 0.01,
+                                          FAKE, None, ctypes.byref(d), FAKE, 1 << 40,
+                                          None) == ga.GA_OK
+
+
 def test_null_dims_rejected():
     assert ga.lib.gated_attn_decode(FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 0.0625, FAKE, None,
                                     None, FAKE, 1 << 40) == ga.GA_ERR_INVALID_ARGUMENT
