@@ -265,3 +265,60 @@ def prefill(q, gate, k, v, scale, causal=True, rows=None, nthreads=None, *, seq_
     if return_lse:
         return out, o, mref, lse
     return out, o, mref
+
+
+# --------------------------------------------------------------------------
+# QK-RMSNorm + partial RoPE + K/V slot write
+# --------------------------------------------------------------------------
+def qk_norm_rope(q, k, v, w_q, w_k, eps, cos, sin, slot_mapping=None, k_pool=None,
+                 v_pool=None):
+    """q [T,H_q,D], k, v [T,H_kv,D] bf16 bits; w_q, w_k [D] or None; cos, sin [T,R].
+
+    Without slot_mapping returns (q_out, k_out, v_out, qz, qmag, kz, kmag) with
+    dense k_out / v_out [T,H_kv,D]; with slot_mapping [T] (int64, < 0 skips),
+    k_pool / v_pool ([P, page, H_kv, D]) are copied, written and returned in
+    place of the dense outputs.  qz / kz: fp64 values before the rounding;
+    qmag / kmag: the magnitudes they were formed from.
+    """
+    lib = _load()
+    if not hasattr(lib, "_qknr"):
+        lib.oracle_qk_norm_rope.restype = ctypes.c_int
+        lib.oracle_qk_norm_rope.argtypes = [
+            _u16p, _u16p, _u16p, _u16p, _u16p, ctypes.c_double, _u16p, _u16p,
+            ctypes.POINTER(ctypes.c_int64), ctypes.c_int64, ctypes.c_int, ctypes.c_int,
+            ctypes.c_int, ctypes.c_int, ctypes.c_int64, _u16p, _u16p, _u16p,
+            _f64p, _f64p, _f64p, _f64p]
+        lib._qknr = True
+    q, k, v = (_u16(a) for a in (q, k, v))
+    T, Hq, D = q.shape
+    Hkv = k.shape[1]
+    cos, sin = _u16(cos), _u16(sin)
+    R = cos.shape[1] if cos.ndim == 2 else 0
+    wq = None if w_q is None else _u16(w_q)
+    wk = None if w_k is None else _u16(w_k)
+    q_out = np.zeros_like(q)
+    qz = np.zeros(q.shape, np.float64)
+    qmag = np.zeros(q.shape, np.float64)
+    kz = np.zeros(k.shape, np.float64)
+    kmag = np.zeros(k.shape, np.float64)
+    if slot_mapping is None:
+        k_out = np.zeros_like(k)
+        v_out = np.zeros_like(v)
+        sm, nslots = None, 0
+    else:
+        sm = np.ascontiguousarray(slot_mapping, dtype=np.int64)
+        k_out = _u16(k_pool).copy()
+        v_out = _u16(v_pool).copy()
+        nslots = k_out.shape[0] * k_out.shape[1]
+    st = lib.oracle_qk_norm_rope(
+        _ptr(q, ctypes.c_uint16), _ptr(k, ctypes.c_uint16), _ptr(v, ctypes.c_uint16),
+        None if wq is None else _ptr(wq, ctypes.c_uint16),
+        None if wk is None else _ptr(wk, ctypes.c_uint16), float(eps),
+        _ptr(cos, ctypes.c_uint16) if R else None, _ptr(sin, ctypes.c_uint16) if R else None,
+        None if sm is None else _ptr(sm, ctypes.c_int64), T, Hq, Hkv, D, R, nslots,
+        _ptr(q_out, ctypes.c_uint16), _ptr(k_out, ctypes.c_uint16), _ptr(v_out, ctypes.c_uint16),
+        _ptr(qz, ctypes.c_double), _ptr(qmag, ctypes.c_double), _ptr(kz, ctypes.c_double),
+        _ptr(kmag, ctypes.c_double))
+    if st != 0:
+        raise OracleError(f"oracle_qk_norm_rope failed with status {st}")
+    return q_out, k_out, v_out, qz, qmag, kz, kmag

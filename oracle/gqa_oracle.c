@@ -559,3 +559,105 @@ int oracle_prefill(const uint16_t *q, const uint16_t *gate, const uint16_t *k, c
     return oracle_prefill_ex(q, gate, k, v, scale, causal, B, S, Hq, Hkv, D, NULL, NULL, 0,
                              rows, nrows, out, o_f64, mref, NULL, nthreads);
 }
+
+/* ---------------------------------------------------------------------------
+ * The step before attention: per-head QK-RMSNorm and partial RoPE on q and k,
+ * with the token's K / V written to its pool slot (cuDNN Gated Attention
+ * Block page, Overview stages (2)+(3): "QK-RMSNorm per head (optional) +
+ * partial RoPE on the first rope_dim", one kernel for Q and K; Weights and
+ * tables: cos, sin [.., rope_dim] rotary tables in the activation dtype,
+ * rotate-half convention on the first rope_dim dims of every head; w_q_norm,
+ * w_k_norm [D]; Fusion knobs: normed and rotated on fp32 values and written
+ * once).
+ *
+ * For one head row x[D] of token t (bf16), in fp64:
+ *   y_d   = x_d / sqrt(mean_d' x_d'^2 + eps) * w_d          (w == NULL: y = x)
+ *   for i < R/2, p = i + R/2  (R = rope_dim, rotate-half):
+ *     z_i = y_i cos[t][i] - y_p sin[t][i],   z_p = y_p cos[t][p] + y_i sin[t][p]
+ *   z_d = y_d for d >= R;  out_d = bf16_rne(z_d)
+ * and, for the magnitude a rotated value is formed from (tolerance sizing),
+ *   mag_i = |y_i cos[t][i]| + |y_p sin[t][i]|, mag_p likewise, mag_d = |y_d|.
+ * Readings (the pages are silent): eps is a parameter; the norm weight
+ * multiplies the normalised value (no offset); a table entry is used as given
+ * (the two halves' cos / sin are not assumed equal).
+ * ------------------------------------------------------------------------- */
+static void norm_rope_row(const uint16_t *x, const uint16_t *w, double eps, const uint16_t *cos_t,
+                          const uint16_t *sin_t, int D, int R, uint16_t *out, double *z_out,
+                          double *mag_out)
+{
+    double y[1024];
+    double ss = 0.0;
+    for (int d = 0; d < D; ++d) {
+        y[d] = oracle_bf16_value(x[d]);
+        ss += y[d] * y[d];
+    }
+    if (w) {
+        double r = 1.0 / sqrt(ss / D + eps);
+        for (int d = 0; d < D; ++d)
+            y[d] = y[d] * r * oracle_bf16_value(w[d]);
+    }
+    for (int d = 0; d < D; ++d) {
+        double z = y[d], mag = fabs(y[d]);
+        if (d < R) {
+            int half = R / 2;
+            int i = d < half ? d : d - half; /* first-half index of the pair */
+            double c = oracle_bf16_value(cos_t[d]), s = oracle_bf16_value(sin_t[d]);
+            if (d < half) { /* z_i = y_i cos - y_p sin */
+                z = y[i] * c - y[i + half] * s;
+                mag = fabs(y[i] * c) + fabs(y[i + half] * s);
+            } else {        /* z_p = y_p cos + y_i sin */
+                z = y[d] * c + y[i] * s;
+                mag = fabs(y[d] * c) + fabs(y[i] * s);
+            }
+        }
+        out[d] = oracle_bf16_rne(z);
+        if (z_out)
+            z_out[d] = z;
+        if (mag_out)
+            mag_out[d] = mag;
+    }
+}
+
+/* T tokens: q [T][H_q][D], k and v [T][H_kv][D]; cos, sin [T][R].
+ * q_out [T][H_q][D] always.  With slot_mapping: K / V of token t go to slot
+ * s = slot_mapping[t] of the pools k_out / v_out ([num_pages * page_size]
+ * [H_kv][D]); s < 0 writes nothing.  Without: k_out / v_out are dense
+ * [T][H_kv][D] (v_out may be NULL).  qz / qmag, kz / kmag (optional, the
+ * shapes of q and k) receive the fp64 values before rounding and their
+ * magnitudes.  Returns -1 for bad arguments or a slot outside the pools. */
+int oracle_qk_norm_rope(const uint16_t *q, const uint16_t *k, const uint16_t *v,
+                        const uint16_t *w_q, const uint16_t *w_k, double eps,
+                        const uint16_t *cos_tab, const uint16_t *sin_tab, const int64_t *slot_mapping,
+                        int64_t T, int Hq, int Hkv, int D, int R, int64_t num_slots,
+                        uint16_t *q_out, uint16_t *k_out, uint16_t *v_out,
+                        double *qz, double *qmag, double *kz, double *kmag)
+{
+    if (T < 0 || Hq <= 0 || Hkv <= 0 || D <= 0 || D > 1024 || R < 0 || R > D || R % 2 != 0)
+        return ORACLE_EBADARG;
+    if ((w_q == NULL) != (w_k == NULL))
+        return ORACLE_EBADARG;
+    for (int64_t t = 0; t < T; ++t) {
+        const uint16_t *ct = R ? cos_tab + t * R : NULL, *st = R ? sin_tab + t * R : NULL;
+        for (int h = 0; h < Hq; ++h) {
+            size_t off = ((size_t)t * Hq + h) * D;
+            norm_rope_row(q + off, w_q, eps, ct, st, D, R, q_out + off, qz ? qz + off : NULL,
+                          qmag ? qmag + off : NULL);
+        }
+        int64_t slot = slot_mapping ? slot_mapping[t] : t;
+        if (slot_mapping && slot >= num_slots)
+            return ORACLE_EBADARG;
+        for (int h = 0; h < Hkv; ++h) {
+            size_t in_off = ((size_t)t * Hkv + h) * D;
+            uint16_t krow[1024];
+            norm_rope_row(k + in_off, w_k, eps, ct, st, D, R, krow, kz ? kz + in_off : NULL,
+                          kmag ? kmag + in_off : NULL);
+            if (slot < 0)
+                continue;
+            size_t out_off = ((size_t)slot * Hkv + h) * D;
+            memcpy(k_out + out_off, krow, sizeof(uint16_t) * (size_t)D);
+            if (v_out)
+                memcpy(v_out + out_off, v + in_off, sizeof(uint16_t) * (size_t)D);
+        }
+    }
+    return ORACLE_OK;
+}

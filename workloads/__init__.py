@@ -260,3 +260,50 @@ def workload(i: int, *, poison: bool = True):
     if i == 4:
         return make_prefill("prefill_b2_s2048_causal", 2, 2048, seed=4, causal=True)
     raise ValueError(f"no workload {i}")
+
+
+@dataclasses.dataclass
+class RopeCase:
+    """Inputs of the QK-RMSNorm + partial-RoPE + K/V-write step for T tokens."""
+    name: str
+    q: np.ndarray       # [T, H_q, D] bf16 bits
+    k: np.ndarray       # [T, H_kv, D]
+    v: np.ndarray       # [T, H_kv, D]
+    w_q: np.ndarray     # [D] norm weights
+    w_k: np.ndarray     # [D]
+    cos: np.ndarray     # [T, R] bf16 bits, rotate-half (both halves hold the same angles)
+    sin: np.ndarray     # [T, R]
+    positions: np.ndarray  # [T] int64
+    eps: float
+
+
+def rope_tables(positions: np.ndarray, rope_dim: int, base: float = 1.0e7):
+    """bf16 cos / sin tables [T, rope_dim] for the given positions: angle
+    pos * base^(-2i / rope_dim) for i < rope_dim / 2, repeated for the second
+    half (rotate-half layout), computed in fp64 and rounded by torch."""
+    import torch
+
+    half = rope_dim // 2
+    inv = base ** (-np.arange(half, dtype=np.float64) * 2.0 / rope_dim)
+    ang = np.asarray(positions, dtype=np.float64)[:, None] * inv[None, :]
+    ang = np.concatenate([ang, ang], axis=1)
+    to16 = lambda a: torch.from_numpy(a.astype(np.float32)).to(torch.bfloat16).view(
+        torch.int16).numpy().view(np.uint16).copy()
+    return to16(np.cos(ang)), to16(np.sin(ang))
+
+
+def make_rope(name: str, num_tokens: int, *, seed: int, num_q_heads: int = 16,
+              num_kv_heads: int = 2, head_dim: int = 256, rope_dim: int = 64,
+              max_position: int = 8192, eps: float = 1e-6) -> RopeCase:
+    """q, k, v ~ N(0, 1); norm weights 1 + 0.1 N(0, 1); random positions."""
+    import torch
+
+    T, Hq, Hkv, D = num_tokens, num_q_heads, num_kv_heads, head_dim
+    pos = _rng(seed, _S_LEN).integers(0, max_position, size=T).astype(np.int64)
+    w = _rng(seed, _S_PAD).standard_normal((2, D)).astype(np.float32) * np.float32(0.1) + 1
+    w16 = torch.from_numpy(w).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+    cos, sin = rope_tables(pos, rope_dim) if rope_dim else (np.zeros((T, 0), np.uint16),) * 2
+    return RopeCase(name, normal_bf16(seed, _S_Q, (T, Hq, D)), normal_bf16(seed, _S_K, (T, Hkv, D)),
+                    normal_bf16(seed, _S_V, (T, Hkv, D)), w16[0].copy(), w16[1].copy(), cos, sin,
+                    pos, float(eps))
+
