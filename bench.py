@@ -232,6 +232,56 @@ def time_decode(ga, case, dev, n_calls: int, settle_s: float = 0.1, **opts) -> d
             "tokens_per_split": call.plan.tokens_per_split, "num_splits": call.plan.num_splits}
 
 
+def time_qk_norm_rope(ga, workloads, dev, T: int, slots: bool, n_calls: int = 200) -> dict:
+    """QK-RMSNorm + RoPE (+ K/V slot write) over T tokens, H_q=16, H_kv=2,
+    rope_dim 64: us/call and bytes moved per second."""
+    import numpy as np
+    import torch
+
+    r = workloads.make_rope(f"rope_t{T}", T, seed=5, rope_dim=64)
+    t = {n: to_dev(getattr(r, n), dev) for n in ("q", "k", "v", "w_q", "w_k", "cos", "sin")}
+    kw = {}
+    if slots:
+        P = (T + 15) // 16
+        kw = dict(slot_mapping=torch.arange(T, dtype=torch.int64, device=dev),
+                  k_pool=torch.zeros((P, 16, 2, 256), dtype=torch.bfloat16, device=dev),
+                  v_pool=torch.zeros((P, 16, 2, 256), dtype=torch.bfloat16, device=dev))
+    q_out = torch.empty_like(t["q"])
+    if slots:
+        k_out, v_out = kw["k_pool"], kw["v_pool"]
+    else:
+        k_out, v_out = torch.empty_like(t["k"]), torch.empty_like(t["v"])
+    # pre-marshalled raw C call, so the timing is the GPU's and not the wrapper's
+    dims = ga.QkNormRopeDims(T, 16, 2, 256, 64, 16, 0, k_out.shape[0] if slots else 0)
+    args = [ctypes.c_void_p(x.data_ptr()) for x in
+            (t["q"], t["k"], t["v"], t["w_q"], t["w_k"])] + [ctypes.c_float(r.eps)] + \
+        [ctypes.c_void_p(x.data_ptr()) for x in (t["cos"], t["sin"])] + \
+        [ctypes.c_void_p(kw["slot_mapping"].data_ptr()) if slots else None] + \
+        [ctypes.c_void_p(x.data_ptr()) for x in (q_out, k_out, v_out)] + \
+        [ctypes.c_void_p(torch.cuda.current_stream(dev).cuda_stream), ctypes.byref(dims)]
+    fn = ga.lib.gated_attn_qk_norm_rope
+
+    def call():
+        st = fn(*args)
+        if st != 0:
+            ga.check(st, "gated_attn_qk_norm_rope")
+    for _ in range(20):
+        call()
+    torch.cuda.synchronize()
+    a = torch.cuda.Event(enable_timing=True)
+    b = torch.cuda.Event(enable_timing=True)
+    a.record()
+    for _ in range(n_calls):
+        call()
+    b.record()
+    torch.cuda.synchronize()
+    us = a.elapsed_time(b) * 1e3 / n_calls
+    moved = 2 * T * (16 + 2 + 2) * 256 * 2 + T * 64 * 2 * 2  # rows in + out, tables in
+    return {"workload": f"QK-RMSNorm + RoPE (rope_dim 64) + K/V {'slot writes' if slots else 'dense'}, "
+                        f"T={T}, H_q=16 H_kv=2 D=256",
+            "us_per_call": round(us, 3), "gbs": round(moved / (us * 1e-6) / 1e9, 2)}
+
+
 def main() -> int:
     args = parse_args()
     world = int(os.environ.get("WORLD_SIZE", "1"))
@@ -433,6 +483,8 @@ def main() -> int:
                                       poison=False, max_pages_per_seq=2048, extra_pages=0)
         result["decode_l1024_cap32768"] = time_decode(ga, short, dev, 100)
         del short
+        result["qk_norm_rope_decode_t64"] = time_qk_norm_rope(ga, workloads, dev, 64, True)
+        result["qk_norm_rope_prefill_t4096"] = time_qk_norm_rope(ga, workloads, dev, 4096, False)
         # FP8 (e4m3) K / V pools, same shape as the headline
         c8 = workloads.make_decode("decode_b64_l4096_fp8", [4096] * 64, seed=2, poison=False,
                                    max_pages_per_seq=256, kv_dtype="fp8")

@@ -38,6 +38,7 @@ EXPORTED_SYMBOLS = (
     "gated_attn_decode_time_stage1",
     "gated_attn_prefill",
     "gated_attn_prefill_ex",
+    "gated_attn_qk_norm_rope",
     "gated_attn_status_string",
     "gated_attn_last_hip_error",
 )
@@ -70,6 +71,19 @@ class PrefillDims(ctypes.Structure):
         ("num_q_heads", ctypes.c_int32),
         ("num_kv_heads", ctypes.c_int32),
         ("head_dim", ctypes.c_int32),
+    ]
+
+
+class QkNormRopeDims(ctypes.Structure):
+    _fields_ = [
+        ("num_tokens", ctypes.c_int64),
+        ("num_q_heads", ctypes.c_int32),
+        ("num_kv_heads", ctypes.c_int32),
+        ("head_dim", ctypes.c_int32),
+        ("rope_dim", ctypes.c_int32),
+        ("page_size", ctypes.c_int32),
+        ("reserved", ctypes.c_int32),
+        ("num_pages", ctypes.c_int64),
     ]
 
 
@@ -112,6 +126,9 @@ def _load_library() -> ctypes.CDLL:
     lib.gated_attn_decode_fp8kv.argtypes = [vp, vp, vp, vp, vp, vp, ctypes.c_float, ctypes.c_float,
                                             ctypes.c_float, vp, vp, ctypes.POINTER(DecodeDims),
                                             vp, sz, ctypes.POINTER(AttnOptions)]
+    lib.gated_attn_qk_norm_rope.restype = ctypes.c_int
+    lib.gated_attn_qk_norm_rope.argtypes = [vp, vp, vp, vp, vp, ctypes.c_float, vp, vp, vp, vp, vp,
+                                            vp, vp, ctypes.POINTER(QkNormRopeDims)]
     lib.gated_attn_prefill_ex.restype = ctypes.c_int
     lib.gated_attn_prefill_ex.argtypes = [vp, vp, vp, vp, ctypes.c_float, ctypes.c_int, vp, vp,
                                           ctypes.POINTER(PrefillDims),
@@ -355,3 +372,57 @@ def prefill(q, gate, k, v, scale, causal=True, *, out=None, stream=None, kv_lens
     else:
         check(lib.gated_attn_prefill_ex(*args, ctypes.byref(opts)), "gated_attn_prefill_ex")
     return (out, lse) if return_lse else out
+
+
+def qk_norm_rope(q, k, v, *, w_q=None, w_k=None, eps=1e-6, cos=None, sin=None,
+                 slot_mapping=None, k_pool=None, v_pool=None, q_out=None, stream=None):
+    """QK-RMSNorm + partial rotate-half RoPE on q [T, H_q, D] and k [T, H_kv, D]
+    (bf16), one kernel launch (gated_attn_qk_norm_rope).
+
+    ``w_q`` / ``w_k``: bf16 [D] norm weights (both or neither); ``cos`` /
+    ``sin``: bf16 [T, R] tables (R = 0 without them).  With ``slot_mapping``
+    (int64 [T], < 0 skips) K and V are written into ``k_pool`` / ``v_pool``
+    ([P, 16, H_kv, D], in place) and ``(q_out, k_pool, v_pool)`` is returned;
+    otherwise ``(q_out, k_out, v_out)`` with dense K / V outputs.
+    """
+    torch = _torch()
+    dev = q.device
+    _need(q, "q", torch.bfloat16, 3, dev)
+    _need(k, "k", torch.bfloat16, 3, dev)
+    _need(v, "v", torch.bfloat16, 3, dev)
+    T, Hq, D = q.shape
+    Hkv = k.shape[1]
+    if k.shape != (T, Hkv, D) or v.shape != k.shape:
+        raise ValueError("inconsistent shapes")
+    if (w_q is None) != (w_k is None):
+        raise ValueError("give both norm weights or neither")
+    for name, w in (("w_q", w_q), ("w_k", w_k)):
+        if w is not None:
+            _need(w, name, torch.bfloat16, 1, dev)
+    R = 0
+    if cos is not None or sin is not None:
+        _need(cos, "cos", torch.bfloat16, 2, dev)
+        _need(sin, "sin", torch.bfloat16, 2, dev)
+        if cos.shape[0] != T or sin.shape != cos.shape:
+            raise ValueError("cos / sin must be [T, rope_dim]")
+        R = cos.shape[1]
+    if q_out is None:
+        q_out = torch.empty_like(q)
+    P = 0
+    if slot_mapping is not None:
+        _need(slot_mapping, "slot_mapping", torch.int64, 1, dev)
+        _need(k_pool, "k_pool", torch.bfloat16, 4, dev)
+        _need(v_pool, "v_pool", torch.bfloat16, 4, dev)
+        P = k_pool.shape[0]
+        k_out, v_out = k_pool, v_pool
+    else:
+        k_out, v_out = torch.empty_like(k), torch.empty_like(v)
+    dims = QkNormRopeDims(T, Hq, Hkv, D, R, 16, 0, P)
+    ptr = lambda t: None if t is None else t.data_ptr()
+    st = lib.gated_attn_qk_norm_rope(
+        q.data_ptr(), k.data_ptr(), v.data_ptr(), ptr(w_q), ptr(w_k), float(eps), ptr(cos),
+        ptr(sin), ptr(slot_mapping), q_out.data_ptr(), k_out.data_ptr(), v_out.data_ptr(),
+        _stream_handle(stream, dev), ctypes.byref(dims))
+    check(st, "gated_attn_qk_norm_rope")
+    return q_out, k_out, v_out
+

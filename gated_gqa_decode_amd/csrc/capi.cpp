@@ -299,6 +299,64 @@ ga_status gated_attn_prefill(const uint16_t* q, const uint16_t* gate, const uint
   return gated_attn_prefill_ex(q, gate, k, v, scale, causal, out, stream, dims, nullptr);
 }
 
+ga_status gated_attn_qk_norm_rope(const uint16_t* q, const uint16_t* k, const uint16_t* v,
+                                  const uint16_t* w_q_norm, const uint16_t* w_k_norm, float eps,
+                                  const uint16_t* cos, const uint16_t* sin,
+                                  const int64_t* slot_mapping, uint16_t* q_out, uint16_t* k_out,
+                                  uint16_t* v_out, void* stream, const ga_qk_norm_rope_dims* dims) {
+  if (dims == nullptr) return GA_ERR_INVALID_ARGUMENT;
+  const int64_t T = dims->num_tokens;
+  if (T < 0 || dims->num_q_heads <= 0 || dims->num_kv_heads <= 0 || dims->head_dim <= 0 ||
+      dims->rope_dim < 0 || dims->rope_dim > dims->head_dim || (dims->rope_dim & 1))
+    return GA_ERR_INVALID_ARGUMENT;
+  if (dims->head_dim != kHeadDim || dims->rope_dim % 8 != 0) return GA_ERR_UNSUPPORTED;
+  if (!(std::isfinite(eps) && eps >= 0.f)) return GA_ERR_INVALID_ARGUMENT;
+  if ((w_q_norm == nullptr) != (w_k_norm == nullptr)) return GA_ERR_INVALID_ARGUMENT;
+  const int64_t rows = T * ((int64_t)dims->num_q_heads + dims->num_kv_heads);
+  if (rows > ((int64_t)1 << 30)) return GA_ERR_UNSUPPORTED;
+  int64_t num_slots = 0;
+  if (slot_mapping != nullptr) {
+    if (dims->page_size != kPageSize) return GA_ERR_UNSUPPORTED;
+    if (dims->num_pages <= 0) return GA_ERR_INVALID_ARGUMENT;
+    num_slots = dims->num_pages * kPageSize;
+  }
+  if (T == 0) return GA_OK;
+  const void* need8[] = {q, k, v, q_out, k_out};
+  for (const void* p : need8)
+    if (p == nullptr || !aligned(p, 8)) return GA_ERR_INVALID_ARGUMENT;
+  if (slot_mapping != nullptr && (v_out == nullptr || !aligned(slot_mapping, 8)))
+    return GA_ERR_INVALID_ARGUMENT;
+  if (!aligned(v_out, 8) || !aligned(w_q_norm, 8) || !aligned(w_k_norm, 8))
+    return GA_ERR_INVALID_ARGUMENT;
+  if (dims->rope_dim > 0 &&
+      (cos == nullptr || sin == nullptr || !aligned(cos, 8) || !aligned(sin, 8)))
+    return GA_ERR_INVALID_ARGUMENT;
+  ga_status st = check_device();
+  if (st != GA_OK) return st;
+
+  ga::RopeLaunch P;
+  P.q = q;
+  P.k = k;
+  P.v = v;
+  P.w_q = w_q_norm;
+  P.w_k = w_k_norm;
+  P.cos = cos;
+  P.sin = sin;
+  P.slot_mapping = slot_mapping;
+  P.q_out = q_out;
+  P.k_out = k_out;
+  P.v_out = v_out;
+  P.eps = eps;
+  P.num_tokens = T;
+  P.num_slots = num_slots;
+  P.num_q_heads = dims->num_q_heads;
+  P.num_kv_heads = dims->num_kv_heads;
+  P.rope_dim = dims->rope_dim;
+  hipError_t e = ga::launch_qk_norm_rope(P, static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return hip_fail(e);
+  return GA_OK;
+}
+
 ga_status gated_attn_decode_time_stage1(void* const* starts, void* const* stops, int n) {
   if (n < 0 || (n > 0 && (starts == nullptr || stops == nullptr))) return GA_ERR_INVALID_ARGUMENT;
   g_timing.starts = n > 0 ? starts : nullptr;

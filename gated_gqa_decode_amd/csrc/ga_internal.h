@@ -66,7 +66,28 @@ struct PrefillLaunch {
   int window;              // > 0: row i sees keys j > i - window
 };
 
+struct RopeLaunch {
+  const uint16_t* q;
+  const uint16_t* k;
+  const uint16_t* v;
+  const uint16_t* w_q;  // null: no norm (then w_k is null too)
+  const uint16_t* w_k;
+  const uint16_t* cos;  // [T][rope_dim]
+  const uint16_t* sin;
+  const int64_t* slot_mapping;  // null: dense K / V outputs
+  uint16_t* q_out;
+  uint16_t* k_out;
+  uint16_t* v_out;
+  float eps;
+  long long num_tokens;
+  long long num_slots;
+  int num_q_heads;
+  int num_kv_heads;
+  int rope_dim;
+};
+
 hipError_t launch_decode(const DecodeLaunch& d, hipStream_t stream);
+hipError_t launch_qk_norm_rope(const RopeLaunch& p, hipStream_t stream);
 hipError_t launch_prefill(const PrefillLaunch& p, hipStream_t stream);
 
 }  // namespace ga

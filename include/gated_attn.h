@@ -218,6 +218,48 @@ ga_status gated_attn_prefill_ex(const uint16_t *q, const uint16_t *gate, const u
                                 void *stream, const ga_prefill_dims *dims,
                                 const ga_attn_options *opts);
 
+/* Shape of a QK-norm / RoPE call over T tokens. */
+typedef struct ga_qk_norm_rope_dims {
+    int64_t num_tokens;    /* T >= 0 */
+    int32_t num_q_heads;   /* H_q */
+    int32_t num_kv_heads;  /* H_kv */
+    int32_t head_dim;      /* D; must be 256 */
+    int32_t rope_dim;      /* R: rotated leading dims of every head, 0..D, a multiple of 8 */
+    int32_t page_size;     /* pool page size (must be 16) when slot_mapping is given */
+    int32_t reserved;      /* ignored */
+    int64_t num_pages;     /* pages of k_out / v_out when slot_mapping is given */
+} ga_qk_norm_rope_dims;
+
+/*
+ * The step before attention (cuDNN "Gated Attention Block" page, Overview
+ * stages (2)+(3), one kernel for Q and K; Weights and tables: cos / sin
+ * rotary tables in the activation dtype, rotate-half on the first rope_dim
+ * dims of every head, norm weights [D]): for every head row x of q and k,
+ *   y = x / sqrt(mean(x^2) + eps) * w       (w_q_norm / w_k_norm; both NULL: y = x)
+ *   z_i = y_i cos[t][i] - y_{i+R/2} sin[t][i],  z_{i+R/2} = y_{i+R/2} cos[t][i+R/2]
+ *         + y_i sin[t][i+R/2]  for i < R/2;  z_d = y_d for d >= R
+ * computed in fp32 and rounded once to bf16 (the page's fused form normalises
+ * and rotates on fp32 values and writes once).  MRoPE and any other position
+ * scheme is expressed through the per-token tables.
+ *   q, q_out   [T][H_q][D] bf16      k, v  [T][H_kv][D] bf16     cos, sin [T][R] bf16
+ * With slot_mapping ([T] int64, device): token t's K (normed and rotated) and
+ * V go to slot s = slot_mapping[t] of the pools k_out / v_out
+ * ([num_pages][16][H_kv][D]; slot s is page s / 16, row s % 16); s < 0 or
+ * s >= num_pages * 16 writes nothing.  Without it: k_out is dense [T][H_kv][D]
+ * and v_out is a dense copy of v, or NULL (not written).
+ * Errors: GA_ERR_INVALID_ARGUMENT for null / misaligned (8-byte) pointers,
+ * one norm weight without the other, eps < 0 or not finite, odd R, missing
+ * tables with R > 0; GA_ERR_UNSUPPORTED for D != 256, R not a multiple of 8,
+ * page size != 16, T * (H_q + H_kv) > 2^30, or a non-gfx950 device.  One
+ * kernel launch on `stream`; nothing allocated.  Inputs are not written
+ * (q_out may not alias q, nor the pools k / v).
+ */
+ga_status gated_attn_qk_norm_rope(const uint16_t *q, const uint16_t *k, const uint16_t *v,
+                                  const uint16_t *w_q_norm, const uint16_t *w_k_norm, float eps,
+                                  const uint16_t *cos, const uint16_t *sin,
+                                  const int64_t *slot_mapping, uint16_t *q_out, uint16_t *k_out,
+                                  uint16_t *v_out, void *stream, const ga_qk_norm_rope_dims *dims);
+
 /* Static, human-readable name of a status. */
 const char *gated_attn_status_string(ga_status status);
 

@@ -196,6 +196,35 @@ def test_fp8kv_shares_the_decode_checks():
                                           None) == ga.GA_OK
 
 
+def _rope_call(dims, eps=1e-6, wq=FAKE, wk=FAKE, cos=FAKE, sin=FAKE, slots=None, v_out=FAKE,
+               q=FAKE):
+    return ga.lib.gated_attn_qk_norm_rope(q, FAKE, FAKE, wq, wk, eps, cos, sin, slots, FAKE,
+                                          FAKE, v_out, None, ctypes.byref(dims))
+
+
+@pytest.mark.parametrize("kw,call_kw,status", [
+    (dict(head_dim=128), {}, ga.GA_ERR_UNSUPPORTED),
+    (dict(rope_dim=12), {}, ga.GA_ERR_UNSUPPORTED),        # not a multiple of 8
+    (dict(rope_dim=7), {}, ga.GA_ERR_INVALID_ARGUMENT),    # odd
+    (dict(rope_dim=264), {}, ga.GA_ERR_INVALID_ARGUMENT),  # > D
+    (dict(num_tokens=-1), {}, ga.GA_ERR_INVALID_ARGUMENT),
+    ({}, dict(eps=-1.0), ga.GA_ERR_INVALID_ARGUMENT),
+    ({}, dict(eps=float("nan")), ga.GA_ERR_INVALID_ARGUMENT),
+    ({}, dict(wk=None), ga.GA_ERR_INVALID_ARGUMENT),        # one weight only
+    ({}, dict(cos=None), ga.GA_ERR_INVALID_ARGUMENT),       # R > 0 without tables
+    ({}, dict(q=FAKE + 4), ga.GA_ERR_INVALID_ARGUMENT),     # misaligned
+    ({}, dict(slots=FAKE, v_out=None), ga.GA_ERR_INVALID_ARGUMENT),  # pools need v_out
+    (dict(page_size=8), dict(slots=FAKE), ga.GA_ERR_UNSUPPORTED),
+    (dict(num_pages=0), dict(slots=FAKE), ga.GA_ERR_INVALID_ARGUMENT),
+    (dict(num_tokens=0), {}, ga.GA_OK),
+])
+def test_qk_norm_rope_argument_checks(kw, call_kw, status):
+    base = dict(num_tokens=4, num_q_heads=16, num_kv_heads=2, head_dim=256, rope_dim=64,
+                page_size=16, reserved=0, num_pages=10)
+    base.update(kw)
+    assert _rope_call(ga.QkNormRopeDims(**base), **call_kw) == status
+
+
 def test_null_dims_rejected():
     assert ga.lib.gated_attn_decode(FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 0.0625, FAKE, None,
                                     None, FAKE, 1 << 40) == ga.GA_ERR_INVALID_ARGUMENT
