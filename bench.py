@@ -232,6 +232,42 @@ def time_decode(ga, case, dev, n_calls: int, settle_s: float = 0.1, **opts) -> d
             "tokens_per_split": call.plan.tokens_per_split, "num_splits": call.plan.num_splits}
 
 
+def time_decode_csr(ga, workloads, case, dev, n_calls: int) -> dict:
+    """The headline workload's tokens at page size 1 (one pool row per token,
+    shuffled), addressed by CSR row pointers: back-to-back calls."""
+    import numpy as np
+    import torch
+
+    k1, v1, indptr, idx, _ = workloads.csr_layout(case, seed=2, poison=False)
+    cap = case.block_table.shape[1] * case.k_pool.shape[1]
+    t = [to_dev(x, dev) for x in (case.q, case.gate, k1, v1, indptr, idx)]
+    dims = ga.decode_dims(case.q.shape[0], case.q.shape[1], k1.shape[2], case.q.shape[2], 1, cap,
+                          k1.shape[0])
+    ws = torch.empty(max(ga.decode_plan(dims).workspace_bytes, 16), dtype=torch.uint8, device=dev)
+    out = torch.empty_like(t[0])
+    args = [ctypes.c_void_p(x.data_ptr()) for x in t] + [ctypes.c_int64(idx.size),
+            ctypes.c_float(case.scale), ctypes.c_void_p(out.data_ptr()),
+            ctypes.c_void_p(torch.cuda.current_stream(dev).cuda_stream), ctypes.byref(dims),
+            ctypes.c_void_p(ws.data_ptr()), ctypes.c_size_t(ws.numel()), None]
+    fn = ga.lib.gated_attn_decode_csr
+    for _ in range(30):
+        ga.check(fn(*args), "gated_attn_decode_csr")
+    torch.cuda.synchronize()
+    a = torch.cuda.Event(enable_timing=True)
+    b = torch.cuda.Event(enable_timing=True)
+    a.record()
+    for _ in range(n_calls):
+        fn(*args)
+    b.record()
+    torch.cuda.synchronize()
+    us = a.elapsed_time(b) * 1e3 / n_calls
+    gbs = case.kv_bytes() / (us * 1e-6) / 1e9
+    return {"workload": "gated GQA decode B=64 L=4096 H_q=16 H_kv=2 D=256, page size 1, "
+                        "CSR indexing, shuffled token slots",
+            "us_per_call": round(us, 3), "kv_gbs": round(gbs, 2),
+            "hbm_frac": round(gbs / HBM_PEAK_GBS, 4)}
+
+
 def time_qk_norm_rope(ga, workloads, dev, T: int, slots: bool, n_calls: int = 200) -> dict:
     """QK-RMSNorm + RoPE (+ K/V slot write) over T tokens, H_q=16, H_kv=2,
     rope_dim 64: us/call and bytes moved per second."""
@@ -485,6 +521,8 @@ def main() -> int:
         del short
         result["qk_norm_rope_decode_t64"] = time_qk_norm_rope(ga, workloads, dev, 64, True)
         result["qk_norm_rope_prefill_t4096"] = time_qk_norm_rope(ga, workloads, dev, 4096, False)
+        # page size 1 with CSR indexing (the FreeToken PR's serving layout)
+        result["decode_csr"] = time_decode_csr(ga, workloads, case, dev, 200)
         # FP8 (e4m3) K / V pools, same shape as the headline
         c8 = workloads.make_decode("decode_b64_l4096_fp8", [4096] * 64, seed=2, poison=False,
                                    max_pages_per_seq=256, kv_dtype="fp8")

@@ -35,6 +35,7 @@ EXPORTED_SYMBOLS = (
     "gated_attn_decode",
     "gated_attn_decode_ex",
     "gated_attn_decode_fp8kv",
+    "gated_attn_decode_csr",
     "gated_attn_decode_time_stage1",
     "gated_attn_prefill",
     "gated_attn_prefill_ex",
@@ -126,6 +127,10 @@ def _load_library() -> ctypes.CDLL:
     lib.gated_attn_decode_fp8kv.argtypes = [vp, vp, vp, vp, vp, vp, ctypes.c_float, ctypes.c_float,
                                             ctypes.c_float, vp, vp, ctypes.POINTER(DecodeDims),
                                             vp, sz, ctypes.POINTER(AttnOptions)]
+    lib.gated_attn_decode_csr.restype = ctypes.c_int
+    lib.gated_attn_decode_csr.argtypes = [vp, vp, vp, vp, vp, vp, ctypes.c_int64, ctypes.c_float,
+                                          vp, vp, ctypes.POINTER(DecodeDims), vp, sz,
+                                          ctypes.POINTER(AttnOptions)]
     lib.gated_attn_qk_norm_rope.restype = ctypes.c_int
     lib.gated_attn_qk_norm_rope.argtypes = [vp, vp, vp, vp, vp, ctypes.c_float, vp, vp, vp, vp, vp,
                                             vp, vp, ctypes.POINTER(QkNormRopeDims)]
@@ -425,4 +430,44 @@ def qk_norm_rope(q, k, v, *, w_q=None, w_k=None, eps=1e-6, cos=None, sin=None,
         _stream_handle(stream, dev), ctypes.byref(dims))
     check(st, "gated_attn_qk_norm_rope")
     return q_out, k_out, v_out
+
+
+def decode_csr(q, gate, k_pool, v_pool, kv_indptr, kv_indices, scale, *, max_seq_len,
+               out=None, workspace=None, stream=None, sinks=None, window=0, lse=None,
+               return_lse=False):
+    """Gated GQA decode with CSR token indexing (page size 1,
+    gated_attn_decode_csr): k_pool, v_pool [N, 1, H_kv, D] bf16 (or [N, H_kv, D]);
+    kv_indptr int32 [B + 1]; kv_indices int32 [capacity]; ``max_seq_len`` is
+    the per-sequence capacity in tokens that fixes the plan.  Options as
+    :func:`decode`."""
+    torch = _torch()
+    dev = q.device
+    _need(q, "q", torch.bfloat16, 3, dev)
+    _need(gate, "gate", torch.bfloat16, 3, dev)
+    if k_pool.dim() == 3:
+        k_pool, v_pool = k_pool.unsqueeze(1), v_pool.unsqueeze(1)
+    _need(k_pool, "k_pool", torch.bfloat16, 4, dev)
+    _need(v_pool, "v_pool", torch.bfloat16, 4, dev)
+    _need(kv_indptr, "kv_indptr", torch.int32, 1, dev)
+    _need(kv_indices, "kv_indices", torch.int32, 1, dev)
+    B, Hq, D = q.shape
+    N, one, Hkv, _ = k_pool.shape
+    if one != 1 or kv_indptr.shape[0] != B + 1 or gate.shape != q.shape:
+        raise ValueError("inconsistent shapes")
+    dims = decode_dims(B, Hq, Hkv, D, 1, int(max_seq_len), N)
+    if out is None:
+        out = torch.empty_like(q)
+    need = decode_workspace_size(dims)
+    if workspace is None:
+        workspace = torch.empty(max(need, 16), dtype=torch.uint8, device=dev)
+    if return_lse and lse is None:
+        lse = torch.empty((B, Hq), dtype=torch.float32, device=dev)
+    opts = _options(sinks, window, lse, None, Hq, dev)
+    st = lib.gated_attn_decode_csr(
+        q.data_ptr(), gate.data_ptr(), k_pool.data_ptr(), v_pool.data_ptr(), kv_indptr.data_ptr(),
+        kv_indices.data_ptr(), kv_indices.numel(), float(scale), out.data_ptr(),
+        _stream_handle(stream, dev), ctypes.byref(dims), workspace.data_ptr(), workspace.numel(),
+        None if opts is None else ctypes.byref(opts))
+    check(st, "gated_attn_decode_csr")
+    return (out, lse) if return_lse else out
 

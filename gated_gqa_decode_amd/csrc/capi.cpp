@@ -89,11 +89,11 @@ ga_status check_decode_dims(const ga_decode_dims* d) {
     return GA_ERR_INVALID_ARGUMENT;
   ga_status st = check_heads(d->num_q_heads, d->num_kv_heads, d->head_dim);
   if (st != GA_OK) return st;
-  if (d->page_size != kPageSize) return GA_ERR_UNSUPPORTED;
+  if (d->page_size != kPageSize && d->page_size != 1) return GA_ERR_UNSUPPORTED;
   if (d->batch > kMaxGridYZ) return GA_ERR_UNSUPPORTED;
   if ((int64_t)d->batch * d->num_q_heads > kMaxDecodeRows) return GA_ERR_UNSUPPORTED;
   // capacity in tokens must fit an int32
-  if ((int64_t)d->max_pages_per_seq * kPageSize > INT32_MAX / 2) return GA_ERR_UNSUPPORTED;
+  if ((int64_t)d->max_pages_per_seq * d->page_size > INT32_MAX / 2) return GA_ERR_UNSUPPORTED;
   return GA_OK;
 }
 
@@ -111,7 +111,7 @@ ga_status check_options(const ga_attn_options* o, bool prefill) {
 // Split plan from the dims alone (allocated capacity, not current lengths).
 // GA_ERR_UNSUPPORTED when the stage-1 grid would not fit one launch.
 ga_status make_plan(const ga_decode_dims* d, ga_decode_plan* p) {
-  const int64_t cap = (int64_t)d->max_pages_per_seq * kPageSize;
+  const int64_t cap = (int64_t)d->max_pages_per_seq * d->page_size;
   // stage-1 workgroups per split: one per (sequence, kv head, head part)
   const int64_t bkv = (int64_t)d->batch * d->num_kv_heads *
                       ga::head_parts(d->num_q_heads / d->num_kv_heads);
@@ -154,13 +154,26 @@ size_t gated_attn_decode_workspace_size(const ga_decode_dims* dims) {
 namespace {
 
 // Shared by the bf16 and e4m3 decode entry points.
+// Token / page addressing of a decode call: a block table with seq_lens, or
+// CSR row pointers and token slots (page size 1).
+struct Indexing {
+  const int32_t* block_table;
+  const int32_t* seq_lens;
+  const int32_t* kv_indptr;
+  const int32_t* kv_indices;
+  int64_t index_capacity;
+};
+
 ga_status decode_impl(const uint16_t* q, const uint16_t* gate, const void* k_pool,
-                      const void* v_pool, const int32_t* block_table, const int32_t* seq_lens,
-                      float scale, int kv_fp8, float k_descale, float v_descale, uint16_t* out,
-                      void* stream, const ga_decode_dims* dims, void* workspace,
-                      size_t workspace_bytes, const ga_attn_options* opts) {
+                      const void* v_pool, const Indexing& ix, float scale, int kv_fp8,
+                      float k_descale, float v_descale, uint16_t* out, void* stream,
+                      const ga_decode_dims* dims, void* workspace, size_t workspace_bytes,
+                      const ga_attn_options* opts) {
   ga_status st = check_decode_dims(dims);
   if (st != GA_OK) return st;
+  const bool csr = ix.kv_indptr != nullptr || ix.kv_indices != nullptr;
+  if (csr && dims->page_size != 1) return GA_ERR_UNSUPPORTED;
+  if (kv_fp8 && dims->page_size != kPageSize) return GA_ERR_UNSUPPORTED;
   if (!(std::isfinite(scale) && scale > 0.f)) return GA_ERR_INVALID_ARGUMENT;
   if (!(std::isfinite(k_descale) && k_descale > 0.f && std::isfinite(v_descale) &&
         v_descale > 0.f))
@@ -171,9 +184,14 @@ ga_status decode_impl(const uint16_t* q, const uint16_t* gate, const void* k_poo
   const void* ptr16[] = {q, gate, k_pool, v_pool, out, workspace};
   for (const void* p : ptr16)
     if (p == nullptr || !aligned(p, 16)) return GA_ERR_INVALID_ARGUMENT;
-  if (block_table == nullptr || seq_lens == nullptr || !aligned(block_table, 4) ||
-      !aligned(seq_lens, 4))
+  if (csr) {
+    if (ix.kv_indptr == nullptr || ix.kv_indices == nullptr || !aligned(ix.kv_indptr, 4) ||
+        !aligned(ix.kv_indices, 4) || ix.index_capacity < 0)
+      return GA_ERR_INVALID_ARGUMENT;
+  } else if (ix.block_table == nullptr || ix.seq_lens == nullptr ||
+             !aligned(ix.block_table, 4) || !aligned(ix.seq_lens, 4)) {
     return GA_ERR_INVALID_ARGUMENT;
+  }
   ga_decode_plan plan;
   st = make_plan(dims, &plan);
   if (st != GA_OK) return st;
@@ -186,8 +204,12 @@ ga_status decode_impl(const uint16_t* q, const uint16_t* gate, const void* k_poo
   L.gate = gate;
   L.k_pool = k_pool;
   L.v_pool = v_pool;
-  L.block_table = block_table;
-  L.seq_lens = seq_lens;
+  L.block_table = csr ? nullptr : ix.block_table;
+  L.seq_lens = csr ? nullptr : ix.seq_lens;
+  L.kv_indptr = csr ? ix.kv_indptr : nullptr;
+  L.kv_indices = csr ? ix.kv_indices : nullptr;
+  L.index_capacity = csr ? ix.index_capacity : 0;
+  L.page_size = dims->page_size;
   L.out = out;
   const size_t rows = (size_t)dims->batch * dims->num_q_heads * plan.num_splits;
   L.part_acc = static_cast<float*>(workspace);
@@ -228,8 +250,21 @@ ga_status gated_attn_decode_ex(const uint16_t* q, const uint16_t* gate, const ui
                                const int32_t* seq_lens, float scale, uint16_t* out, void* stream,
                                const ga_decode_dims* dims, void* workspace,
                                size_t workspace_bytes, const ga_attn_options* opts) {
-  return decode_impl(q, gate, k_pool, v_pool, block_table, seq_lens, scale, 0, 1.f, 1.f, out,
-                     stream, dims, workspace, workspace_bytes, opts);
+  const Indexing ix = {block_table, seq_lens, nullptr, nullptr, 0};
+  return decode_impl(q, gate, k_pool, v_pool, ix, scale, 0, 1.f, 1.f, out, stream, dims,
+                     workspace, workspace_bytes, opts);
+}
+
+ga_status gated_attn_decode_csr(const uint16_t* q, const uint16_t* gate, const uint16_t* k_pool,
+                                const uint16_t* v_pool, const int32_t* kv_indptr,
+                                const int32_t* kv_indices, int64_t index_capacity, float scale,
+                                uint16_t* out, void* stream, const ga_decode_dims* dims,
+                                void* workspace, size_t workspace_bytes,
+                                const ga_attn_options* opts) {
+  if (kv_indptr == nullptr || kv_indices == nullptr) return GA_ERR_INVALID_ARGUMENT;
+  const Indexing ix = {nullptr, nullptr, kv_indptr, kv_indices, index_capacity};
+  return decode_impl(q, gate, k_pool, v_pool, ix, scale, 0, 1.f, 1.f, out, stream, dims,
+                     workspace, workspace_bytes, opts);
 }
 
 ga_status gated_attn_decode_fp8kv(const uint16_t* q, const uint16_t* gate, const uint8_t* k_pool,
@@ -238,8 +273,9 @@ ga_status gated_attn_decode_fp8kv(const uint16_t* q, const uint16_t* gate, const
                                   float v_descale, uint16_t* out, void* stream,
                                   const ga_decode_dims* dims, void* workspace,
                                   size_t workspace_bytes, const ga_attn_options* opts) {
-  return decode_impl(q, gate, k_pool, v_pool, block_table, seq_lens, scale, 1, k_descale,
-                     v_descale, out, stream, dims, workspace, workspace_bytes, opts);
+  const Indexing ix = {block_table, seq_lens, nullptr, nullptr, 0};
+  return decode_impl(q, gate, k_pool, v_pool, ix, scale, 1, k_descale, v_descale, out, stream,
+                     dims, workspace, workspace_bytes, opts);
 }
 
 ga_status gated_attn_decode(const uint16_t* q, const uint16_t* gate, const uint16_t* k_pool,

@@ -45,6 +45,7 @@ constexpr int kPage = 16;        // tokens per page
 constexpr int kStep = 8;         // tokens per wave step
 constexpr int kWaves = 8;        // waves per stage-1 workgroup (one workgroup per CU)
 constexpr int kPageRegs = 2;     // page ids per lane: a split spans at most 128 pages
+constexpr int kMaxSplit = 2048;  // tokens of the largest split
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
 constexpr float kSlack = 8.f;    // lazy-rescale threshold, log2 units
@@ -55,6 +56,9 @@ struct Stage1Args {
   const char* v_pool;
   const int32_t* block_table;
   const int32_t* seq_lens;
+  const int32_t* kv_indptr;   // CSR (page size 1): [B + 1], or null for a block table
+  const int32_t* kv_indices;  // CSR token slots
+  long long index_capacity;   // entries of kv_indices
   float* part_acc;   // [B][H_q][NS][D]
   float* part_ml;    // [B][H_q][NS][2]  (m in log2 units, l)
   float scale_log2;  // scale * log2(e)
@@ -63,7 +67,7 @@ struct Stage1Args {
   int heads_per_part;  // query heads of this workgroup: G or G / 2 (<= 8)
   int parts;           // workgroups per (sequence, kv head, split): 1 or 2
   int num_units;       // B * H_kv * num_splits
-  int max_pages;     // W
+  int max_pages;     // W: block-table columns (pages, or tokens at page size 1)
   long long num_pages;
   int tokens_per_split;  // the most tokens of one split
   int num_splits;
@@ -160,12 +164,31 @@ __device__ __forceinline__ SplitRange split_range(int L, int window, int num_spl
 
 }  // namespace
 
-// The stage-1 body for bf16 pools (kFp8 = false) and e4m3 pools (true).
-template <bool kFp8>
+// The length of sequence b and where its token / page ids start: from the
+// CSR row pointers, or seq_lens and the block-table row.  Clamped so that a
+// violated precondition cannot lead outside the buffers.
+__device__ __forceinline__ int seq_length(const int32_t* seq_lens, const int32_t* indptr,
+                                          long long index_capacity, int b, int capacity,
+                                          long long* first_index) {
+  if (indptr != nullptr) {
+    const long long lo = min(max((long long)indptr[b], 0LL), index_capacity);
+    const long long hi = min(max((long long)indptr[b + 1], lo), index_capacity);
+    *first_index = lo;
+    return (int)min(hi - lo, (long long)capacity);
+  }
+  *first_index = 0;
+  return min(seq_lens[b], capacity);
+}
+
+// The stage-1 body for bf16 pools (kFp8 = false) or e4m3 pools (true), with
+// 16-token pages (kTok = false) or one token per page (true: block-table
+// entries or CSR indices are token slots).
+template <bool kFp8, bool kTok>
 __device__ __forceinline__ void stage1_body(const Stage1Args& a) {
   __shared__ WaveSlot wslot[kWaves][2];
   __shared__ MergeSlot merge;
   __shared__ int progress[kWaves];  // last step each wave started
+  __shared__ __align__(16) int tok_ids[kTok ? kMaxSplit : 4];  // page size 1: the split's token slots
 
   // Workgroup id -> (split s, kv head g, head part, sequence b).  Ids are
   // dispatched in order, round-robin over the 8 XCDs.  Units are split-major
@@ -204,9 +227,9 @@ __device__ __forceinline__ void stage1_body(const Stage1Args& a) {
     for (int r = 0; r < kPageRegs; ++r)
       pages[r] = lane + 64 * r < np ? bt_row[fp + lane + 64 * r] : 0;
   };
-  int my_page[kPageRegs];
+  int my_page[kPageRegs] = {0, 0};
   const int full_begin = s * a.tokens_per_split;  // < capacity, since s < num_splits
-  load_pages(full_begin, a.tokens_per_split, my_page);
+  if constexpr (!kTok) load_pages(full_begin, a.tokens_per_split, my_page);
 
   // score-lane coordinates
   const int tq = lane >> 4;    // token within a pass
@@ -237,7 +260,9 @@ __device__ __forceinline__ void stage1_body(const Stage1Args& a) {
   // Lengths past the capacity and page ids outside the pool break the
   // documented preconditions; both are clamped so such input yields garbage
   // in its own row instead of an access outside the buffers.
-  const int L = min(a.seq_lens[b], a.max_pages * kPage);
+  const int capacity = kTok ? a.max_pages : a.max_pages * kPage;
+  long long first_index = 0;
+  const int L = seq_length(a.seq_lens, a.kv_indptr, a.index_capacity, b, capacity, &first_index);
   // First visible token: the sliding window keeps the last `window` tokens.
   const int tok_lo = a.window > 0 ? max(0, L - a.window) : 0;
   const SplitRange sr = split_range(L, a.window, a.num_splits, a.tokens_per_split,
@@ -246,9 +271,20 @@ __device__ __forceinline__ void stage1_body(const Stage1Args& a) {
   const int tok_begin = sr.base + s * sr.tokens;
   const int tok_end = min(L, tok_begin + sr.tokens);
   const int first_page = tok_begin / kPage;
-  if (tok_begin != full_begin) load_pages(tok_begin, sr.tokens, my_page);
+  if constexpr (kTok) {
+    // one slot per token: the split's slots go to LDS (at most kMaxSplit)
+    const int32_t* ids = a.kv_indptr != nullptr ? a.kv_indices + first_index : bt_row;
+    for (int i = threadIdx.x; i < sr.tokens; i += kWaves * 64) {
+      const int tok = tok_begin + i;
+      const int id = tok < tok_end ? ids[tok] : 0;
+      tok_ids[i] = (int)min((long long)max(id, 0), a.num_pages - 1);
+    }
+  } else {
+    if (tok_begin != full_begin) load_pages(tok_begin, sr.tokens, my_page);
 #pragma unroll
-  for (int r = 0; r < kPageRegs; ++r) my_page[r] = (int)min((long long)max(my_page[r], 0), a.num_pages - 1);
+    for (int r = 0; r < kPageRegs; ++r)
+      my_page[r] = (int)min((long long)max(my_page[r], 0), a.num_pages - 1);
+  }
   if (threadIdx.x < kWaves) progress[threadIdx.x] = 0;
   __syncthreads();
 
@@ -295,22 +331,47 @@ __device__ __forceinline__ void stage1_body(const Stage1Args& a) {
   struct VRegs {
     VElem v[kStep];
   };
+  // Page size 1: every token has its own slot, so K takes a per-lane address
+  // (the lane's token of the pass) and V one scalar base per token, both from
+  // the slots in LDS.
+  const size_t head_bytes = (size_t)g * kD * kElem;
   auto load_k = [&](int step, KRegs& r) {
-    const char* kb = step_base(step, a.k_pool);
 #pragma unroll
     for (int pass = 0; pass < 2; ++pass) {
-      r.k[pass][0] = ldg16_stream(kb + k_off[pass]);
-      if constexpr (!kFp8) r.k[pass][1] = ldg16_stream(kb + (k_off[pass] + 256u));
+      const char* kb;
+      unsigned off;
+      if constexpr (kTok) {
+        kb = a.k_pool + (size_t)tok_ids[step * kStep + pass * 4 + tq] * row_bytes + head_bytes;
+        off = (unsigned)(c16 * 16);
+      } else {
+        kb = step_base(step, a.k_pool);
+        off = k_off[pass];
+      }
+      r.k[pass][0] = ldg16_stream(kb + off);
+      if constexpr (!kFp8) r.k[pass][1] = ldg16_stream(kb + (off + 256u));
     }
   };
   auto load_v = [&](int step, VRegs& r) {
-    const char* vb = step_base(step, a.v_pool);
+    int4 ids_lo = make_int4(0, 0, 0, 0), ids_hi = make_int4(0, 0, 0, 0);
+    if constexpr (kTok) {
+      ids_lo = *reinterpret_cast<const int4*>(&tok_ids[step * kStep]);
+      ids_hi = *reinterpret_cast<const int4*>(&tok_ids[step * kStep + 4]);
+    }
+    const int ids[kStep] = {ids_lo.x, ids_lo.y, ids_lo.z, ids_lo.w,
+                            ids_hi.x, ids_hi.y, ids_hi.z, ids_hi.w};
+    const char* vb = kTok ? nullptr : step_base(step, a.v_pool);
 #pragma unroll
     for (int t = 0; t < kStep; ++t) {
-      if constexpr (kFp8)
-        r.v[t] = ldg4_stream(vb + v_off[t]);
+      const char* p;
+      if constexpr (kTok)
+        p = a.v_pool + (size_t)__builtin_amdgcn_readfirstlane(ids[t]) * row_bytes + head_bytes +
+            lane * 4 * kElem;
       else
-        r.v[t] = ldg8_stream(vb + v_off[t]);
+        p = vb + v_off[t];
+      if constexpr (kFp8)
+        r.v[t] = ldg4_stream(p);
+      else
+        r.v[t] = ldg8_stream(p);
     }
   };
 
@@ -561,11 +622,15 @@ __device__ __forceinline__ void stage1_body(const Stage1Args& a) {
 }
 
 __global__ __launch_bounds__(512, 1) void decode_stage1_kernel(Stage1Args a) {
-  stage1_body<false>(a);
+  stage1_body<false, false>(a);
 }
 
 __global__ __launch_bounds__(512, 1) void decode_stage1_fp8_kernel(Stage1Args a) {
-  stage1_body<true>(a);
+  stage1_body<true, false>(a);
+}
+
+__global__ __launch_bounds__(512, 1) void decode_stage1_tok_kernel(Stage1Args a) {
+  stage1_body<false, true>(a);
 }
 
 struct Stage2Args {
@@ -574,6 +639,8 @@ struct Stage2Args {
   const float* part_acc;
   const float* part_ml;
   const float* sinks;  // [H_q] sink logits (natural-log units) or null
+  const int32_t* kv_indptr;  // CSR row pointers or null (then seq_lens)
+  long long index_capacity;
   uint16_t* out;
   float* lse;          // [B][H_q] or null
   float v_descale;     // e4m3 pools: V = v_descale * code value (1 for bf16)
@@ -614,7 +681,9 @@ __global__ __launch_bounds__(256) void decode_stage2_gate_kernel(Stage2Args a) {
   // A sink joins the denominator as one more term exp(sink) (in log2 units
   // here, like the partials' maxima); it takes no part in the numerator.
   const float sink2 = a.sinks != nullptr ? a.sinks[h] * kLog2e : -INFINITY;
-  const int L = min(a.seq_lens[b], a.capacity);  // same clamp as stage 1
+  long long first_index;
+  const int L = seq_length(a.seq_lens, a.kv_indptr, a.index_capacity, b, a.capacity,
+                           &first_index);  // as in stage 1
   uint16_t o16[4] = {0, 0, 0, 0};
   float lse = sink2 * kLn2;  // a dead row: ln(exp(sink)), or -inf
   if (L > 0) {  // L <= 0: padded slot, output +0
@@ -677,6 +746,9 @@ hipError_t launch_decode(const DecodeLaunch& d, hipStream_t stream) {
   a1.v_pool = static_cast<const char*>(d.v_pool);
   a1.block_table = d.block_table;
   a1.seq_lens = d.seq_lens;
+  a1.kv_indptr = d.kv_indptr;
+  a1.kv_indices = d.kv_indices;
+  a1.index_capacity = d.index_capacity;
   a1.part_acc = d.part_acc;
   a1.part_ml = d.part_ml;
   a1.scale_log2 = d.scale * d.k_descale * kLog2e;  // the K factor folds into the scores
@@ -699,7 +771,9 @@ hipError_t launch_decode(const DecodeLaunch& d, hipStream_t stream) {
     err = hipEventRecord(d.stage1_start, stream);
     if (err != hipSuccess) return err;
   }
-  if (d.kv_fp8)
+  if (d.page_size == 1)
+    hipLaunchKernelGGL(decode_stage1_tok_kernel, grid1, dim3(kWaves * 64), 0, stream, a1);
+  else if (d.kv_fp8)
     hipLaunchKernelGGL(decode_stage1_fp8_kernel, grid1, dim3(kWaves * 64), 0, stream, a1);
   else
     hipLaunchKernelGGL(decode_stage1_kernel, grid1, dim3(kWaves * 64), 0, stream, a1);
@@ -713,6 +787,8 @@ hipError_t launch_decode(const DecodeLaunch& d, hipStream_t stream) {
   Stage2Args a2;
   a2.gate = d.gate;
   a2.seq_lens = d.seq_lens;
+  a2.kv_indptr = d.kv_indptr;
+  a2.index_capacity = d.index_capacity;
   a2.part_acc = d.part_acc;
   a2.part_ml = d.part_ml;
   a2.sinks = d.sinks;
@@ -726,7 +802,7 @@ hipError_t launch_decode(const DecodeLaunch& d, hipStream_t stream) {
   a2.num_q_heads = d.num_q_heads;
   a2.num_splits = d.num_splits;
   a2.batch = d.batch;
-  a2.capacity = d.max_pages * kPage;
+  a2.capacity = d.max_pages * d.page_size;
   const int rows = d.batch * a2.num_q_heads;
   hipLaunchKernelGGL(decode_stage2_gate_kernel, dim3((rows + 3) / 4), dim3(256), 0, stream, a2);
   return hipGetLastError();

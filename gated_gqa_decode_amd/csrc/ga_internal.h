@@ -24,6 +24,10 @@ struct DecodeLaunch {
   const void* v_pool;
   const int32_t* block_table;
   const int32_t* seq_lens;
+  const int32_t* kv_indptr;   // CSR row pointers [B + 1] (page size 1) or null
+  const int32_t* kv_indices;  // CSR token slots
+  long long index_capacity;   // entries of kv_indices
+  int page_size;              // 16, or 1 (token slots)
   uint16_t* out;
   float* part_acc;  // workspace: [B][H_q][num_splits][D] fp32
   float* part_ml;   // workspace: [B][H_q][num_splits][2] fp32

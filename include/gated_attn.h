@@ -62,7 +62,7 @@ typedef struct ga_decode_dims {
     int32_t num_q_heads;       /* H_q */
     int32_t num_kv_heads;      /* H_kv, dividing H_q; see GQA groups below */
     int32_t head_dim;          /* D; must be 256 */
-    int32_t page_size;         /* tokens per page; must be 16 */
+    int32_t page_size;         /* tokens per page: 16, or 1 (every table entry is a token slot) */
     int32_t max_pages_per_seq; /* W: columns of block_table (the allocated capacity) */
     int64_t num_pages;         /* P: pages in each of k_pool / v_pool */
 } ga_decode_dims;
@@ -208,6 +208,30 @@ ga_status gated_attn_decode_fp8kv(const uint16_t *q, const uint16_t *gate, const
                                   float v_descale, uint16_t *out, void *stream,
                                   const ga_decode_dims *dims, void *workspace,
                                   size_t workspace_bytes, const ga_attn_options *opts);
+
+/*
+ * Gated GQA decode with CSR token indexing at page size 1, the serving layout
+ * of the FreeToken PR #781 (Automatic dispatch: a CSR index of allocated
+ * capacity; the server runs with page size 1): sequence b's tokens are
+ * kv_indices[kv_indptr[b]] .. kv_indices[kv_indptr[b + 1] - 1], each a row of
+ * the pools k_pool / v_pool [num_pages][1][H_kv][D] (num_pages = pool rows).
+ * Its length is kv_indptr[b + 1] - kv_indptr[b] (no seq_lens).
+ *   kv_indptr      [B + 1] int32, device, non-decreasing
+ *   kv_indices     [index_capacity] int32, device
+ *   dims           page_size must be 1; max_pages_per_seq is the per-sequence
+ *                  capacity in tokens, which alone fixes the plan and workspace
+ * Everything else as gated_attn_decode_ex.  Row pointers outside
+ * [0, index_capacity], lengths past the capacity and slots outside the pools
+ * are clamped (an unspecified row, never an access outside the buffers).
+ * GA_ERR_INVALID_ARGUMENT for null or misaligned index arrays or a negative
+ * capacity; GA_ERR_UNSUPPORTED for page_size != 1.
+ */
+ga_status gated_attn_decode_csr(const uint16_t *q, const uint16_t *gate, const uint16_t *k_pool,
+                                const uint16_t *v_pool, const int32_t *kv_indptr,
+                                const int32_t *kv_indices, int64_t index_capacity, float scale,
+                                uint16_t *out, void *stream, const ga_decode_dims *dims,
+                                void *workspace, size_t workspace_bytes,
+                                const ga_attn_options *opts);
 
 /* gated_attn_prefill with options appended.  opts == NULL is
  * gated_attn_prefill.  GA_ERR_INVALID_ARGUMENT for flags != 0 or a misaligned

@@ -307,3 +307,34 @@ def make_rope(name: str, num_tokens: int, *, seed: int, num_q_heads: int = 16,
                     normal_bf16(seed, _S_V, (T, Hkv, D)), w16[0].copy(), w16[1].copy(), cos, sin,
                     pos, float(eps))
 
+
+def csr_layout(case: DecodeCase, seed: int, extra_slots: int = 7, poison: bool = True):
+    """The same tokens at page size 1: every token of every sequence gets its
+    own pool row, at a seeded random slot, addressed by CSR row pointers and
+    indices (sequence b's tokens are indices[indptr[b] : indptr[b + 1]]).
+    Also returns the equivalent page-size-1 block table [B, capacity] (-1
+    where unused).  Unused slots hold NaN when ``poison``.
+
+    Returns (k_pool [N, 1, H_kv, D], v_pool, indptr [B + 1], indices, table)."""
+    lens = np.clip(case.seq_lens.astype(np.int64), 0, None)
+    B = lens.shape[0]
+    cap = case.block_table.shape[1] * case.k_pool.shape[1]
+    total = int(lens.sum())
+    N = total + int(extra_slots)
+    slots = _rng(seed, _S_PERM + 16).permutation(N)[:total].astype(np.int32)
+    _, _, Hkv, D = case.k_pool.shape
+    nan = NAN_E4M3 if case.fp8 else NAN_BF16
+    k1 = np.full((max(N, 1), 1, Hkv, D), nan if poison else 0, dtype=case.k_pool.dtype)
+    v1 = np.full_like(k1, nan if poison else 0)
+    indptr = np.zeros(B + 1, dtype=np.int32)
+    indptr[1:] = np.cumsum(lens)
+    table = np.full((B, cap), -1, dtype=np.int32)
+    ps = case.k_pool.shape[1]
+    seq = np.repeat(np.arange(B), lens)                  # sequence of each token
+    j = np.arange(total) - np.repeat(indptr[:-1], lens)  # position in its sequence
+    page = case.block_table[seq, j // ps]
+    k1[slots, 0] = case.k_pool[page, j % ps]
+    v1[slots, 0] = case.v_pool[page, j % ps]
+    table[seq, j] = slots
+    return k1, v1, indptr, slots.copy(), table
+
