@@ -112,17 +112,17 @@ ga_status check_options(const ga_attn_options* o, bool prefill) {
 // GA_ERR_UNSUPPORTED when the stage-1 grid would not fit one launch.
 ga_status make_plan(const ga_decode_dims* d, ga_decode_plan* p) {
   const int64_t cap = (int64_t)d->max_pages_per_seq * d->page_size;
-  // stage-1 workgroups per split: one per (sequence, kv head, head part)
-  const int64_t bkv = (int64_t)d->batch * d->num_kv_heads *
-                      ga::head_parts(d->num_q_heads / d->num_kv_heads);
+  // stage-1 workgroups per split: one per (sequence, kv head); a workgroup
+  // serves all the group's query heads
+  const int64_t bkv = (int64_t)d->batch * d->num_kv_heads;
   int64_t t = (cap * (bkv > 0 ? bkv : 1) + GA_DECODE_TARGET_BLOCKS - 1) / GA_DECODE_TARGET_BLOCKS;
   t = ((t + kSplitQuantum - 1) / kSplitQuantum) * kSplitQuantum;
   if (t < kSplitQuantum) t = kSplitQuantum;
   if (t > kMaxSplitTokens) t = kMaxSplitTokens;
   const int64_t ns = (cap + t - 1) / t;
-  // stage-1 grid: (B * H_kv * NS) units rounded up to 8, times the head parts
+  // stage-1 grid: one workgroup per (split, sequence, kv head)
   const int64_t units = (int64_t)d->batch * d->num_kv_heads * ns;
-  const int64_t wgs = (units + 7) / 8 * 8 * ga::head_parts(d->num_q_heads / d->num_kv_heads);
+  const int64_t wgs = units;
   if (units > INT32_MAX / 2 || wgs > kMaxStage1Workgroups) return GA_ERR_UNSUPPORTED;
   p->tokens_per_split = (int32_t)t;
   p->num_splits = (int32_t)ns;

@@ -7,10 +7,11 @@
 
 namespace ga {
 
-// Query heads per kv head (the GQA group G = H_q / H_kv) that the kernels
-// handle in one workgroup: at most 8.  Groups of up to 8 run whole (missing
-// head slots are idle); even groups of 10..16 run as two halves of G/2 heads,
-// each half streaming the kv head's K/V.
+// GQA groups (G = H_q / H_kv) the kernels take: 1..8, and even groups up to
+// 16.  Decode serves a whole group of up to 16 heads in one workgroup (idle
+// MFMA columns past G).  Prefill runs up to 8 heads per workgroup (one wave
+// each); even groups of 10..16 run as two halves of G/2 heads, each half
+// streaming the kv head's K/V.
 constexpr int kMaxHeadsPerPart = 8;
 inline int head_parts(int group) { return group > kMaxHeadsPerPart ? 2 : 1; }
 inline bool group_supported(int group) {
