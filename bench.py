@@ -4,7 +4,9 @@
 A step is one gated_attn_decode call -- stage 1 and stage 2 with the fused
 gate, the whole decode path -- over the B=64, L=4096 paged workload (512 MiB of
 K/V), inputs resident in HBM.  ``value`` is K/V bytes per second over the timed
-steps.  The same JSON line also carries:
+steps.  Decode measurements rotate over copies of their inputs (two for this
+workload) so that no call can read K/V the previous one left in the 256 MB
+Infinity Cache.  The same JSON line also carries:
   * roofline   -- the stage-1 kernel's achieved HBM rate, from HIP events
                   recorded around each of its launches in a second pass of K
                   calls (the headline steps run without them);
@@ -194,13 +196,49 @@ def time_prefill(ga, p, dev, n_calls: int, settle_s: float = 0.0) -> dict:
                     "the algorithmic MFMA work"}
 
 
+# The MI355X's 256 MB Infinity Cache (MALL) sits between L2 and HBM.  Back-to-
+# back calls on one set of inputs could read part of a call's K/V from what the
+# previous call left there, which would overstate HBM bandwidth.  Every decode
+# measurement therefore rotates over copies of its inputs (all resident in
+# HBM) whose visible K/V add up to at least 768 MiB per rotation, so no call
+# finds its rows in the cache.
+MALL_DEFEAT_BYTES = 768 << 20
+
+
+def rotation_sets(visible_bytes: int) -> int:
+    return max(2, min(8, -(-MALL_DEFEAT_BYTES // max(int(visible_bytes), 1))))
+
+
+class Rotation:
+    """Calls of one decode configuration over n resident input copies, in turn."""
+
+    def __init__(self, make, n: int):
+        self.calls = [make() for _ in range(n)]
+        self.i = 0
+
+    def __call__(self):
+        self.calls[self.i]()
+        self.i = (self.i + 1) % len(self.calls)
+
+    @property
+    def plan(self):
+        return self.calls[0].plan
+
+
 def time_decode(ga, case, dev, n_calls: int, settle_s: float = 0.1, **opts) -> dict:
     """Back-to-back decode calls on case: us/call and K/V bytes per second
     (the bytes of the visible keys: a window reads only those)."""
     import numpy as np
     import torch
 
-    call = DecodeCall(ga, case, dev, **opts)
+    import numpy as np
+
+    lens_v = np.clip(case.seq_lens.astype(np.int64), 0, None)
+    if opts.get("window"):
+        lens_v = np.minimum(lens_v, int(opts["window"]))
+    visible = int(lens_v.sum()) * case.k_pool.shape[2] * case.k_pool.shape[3] * case.k_pool.dtype.itemsize * 2
+    n_sets = rotation_sets(visible)
+    call = Rotation(lambda: DecodeCall(ga, case, dev, **opts), n_sets)
     t0 = time.perf_counter()
     while time.perf_counter() - t0 < settle_s:  # clock settling, untimed
         for _ in range(20):
@@ -229,7 +267,8 @@ def time_decode(ga, case, dev, n_calls: int, settle_s: float = 0.1, **opts) -> d
                         f"H_kv={Hkv} D={D}, paged" + (f", {desc}" if desc else ""),
             "us_per_call": round(ms * 1e3, 3), "calls": n_calls,
             "kv_gbs": round(gbs, 2), "hbm_frac": round(gbs / HBM_PEAK_GBS, 4),
-            "tokens_per_split": call.plan.tokens_per_split, "num_splits": call.plan.num_splits}
+            "tokens_per_split": call.plan.tokens_per_split, "num_splits": call.plan.num_splits,
+            "input_sets": n_sets}
 
 
 def time_decode_csr(ga, workloads, case, dev, n_calls: int) -> dict:
@@ -240,24 +279,29 @@ def time_decode_csr(ga, workloads, case, dev, n_calls: int) -> dict:
 
     k1, v1, indptr, idx, _ = workloads.csr_layout(case, seed=2, poison=False)
     cap = case.block_table.shape[1] * case.k_pool.shape[1]
-    t = [to_dev(x, dev) for x in (case.q, case.gate, k1, v1, indptr, idx)]
     dims = ga.decode_dims(case.q.shape[0], case.q.shape[1], k1.shape[2], case.q.shape[2], 1, cap,
                           k1.shape[0])
-    ws = torch.empty(max(ga.decode_plan(dims).workspace_bytes, 16), dtype=torch.uint8, device=dev)
-    out = torch.empty_like(t[0])
-    args = [ctypes.c_void_p(x.data_ptr()) for x in t] + [ctypes.c_int64(idx.size),
-            ctypes.c_float(case.scale), ctypes.c_void_p(out.data_ptr()),
+    n_sets = rotation_sets(case.kv_bytes())
+    keep, arg_sets = [], []
+    for _ in range(n_sets):  # resident copies used in turn (see MALL_DEFEAT_BYTES)
+        t = [to_dev(x, dev) for x in (case.q, case.gate, k1, v1, indptr, idx)]
+        ws = torch.empty(max(ga.decode_plan(dims).workspace_bytes, 16), dtype=torch.uint8,
+                         device=dev)
+        out = torch.empty_like(t[0])
+        keep.append((t, ws, out))
+        arg_sets.append([ctypes.c_void_p(x.data_ptr()) for x in t] + [
+            ctypes.c_int64(idx.size), ctypes.c_float(case.scale), ctypes.c_void_p(out.data_ptr()),
             ctypes.c_void_p(torch.cuda.current_stream(dev).cuda_stream), ctypes.byref(dims),
-            ctypes.c_void_p(ws.data_ptr()), ctypes.c_size_t(ws.numel()), None]
+            ctypes.c_void_p(ws.data_ptr()), ctypes.c_size_t(ws.numel()), None])
     fn = ga.lib.gated_attn_decode_csr
-    for _ in range(30):
-        ga.check(fn(*args), "gated_attn_decode_csr")
+    for i in range(30):
+        ga.check(fn(*arg_sets[i % n_sets]), "gated_attn_decode_csr")
     torch.cuda.synchronize()
     a = torch.cuda.Event(enable_timing=True)
     b = torch.cuda.Event(enable_timing=True)
     a.record()
-    for _ in range(n_calls):
-        fn(*args)
+    for i in range(n_calls):
+        fn(*arg_sets[i % n_sets])
     b.record()
     torch.cuda.synchronize()
     us = a.elapsed_time(b) * 1e3 / n_calls
@@ -265,7 +309,7 @@ def time_decode_csr(ga, workloads, case, dev, n_calls: int) -> dict:
     return {"workload": "gated GQA decode B=64 L=4096 H_q=16 H_kv=2 D=256, page size 1, "
                         "CSR indexing, shuffled token slots",
             "us_per_call": round(us, 3), "kv_gbs": round(gbs, 2),
-            "hbm_frac": round(gbs / HBM_PEAK_GBS, 4)}
+            "hbm_frac": round(gbs / HBM_PEAK_GBS, 4), "input_sets": n_sets}
 
 
 def time_qk_norm_rope(ga, workloads, dev, T: int, slots: bool, n_calls: int = 200) -> dict:
@@ -275,30 +319,38 @@ def time_qk_norm_rope(ga, workloads, dev, T: int, slots: bool, n_calls: int = 20
     import torch
 
     r = workloads.make_rope(f"rope_t{T}", T, seed=5, rope_dim=64)
-    t = {n: to_dev(getattr(r, n), dev) for n in ("q", "k", "v", "w_q", "w_k", "cos", "sin")}
-    kw = {}
-    if slots:
-        P = (T + 15) // 16
-        kw = dict(slot_mapping=torch.arange(T, dtype=torch.int64, device=dev),
-                  k_pool=torch.zeros((P, 16, 2, 256), dtype=torch.bfloat16, device=dev),
-                  v_pool=torch.zeros((P, 16, 2, 256), dtype=torch.bfloat16, device=dev))
-    q_out = torch.empty_like(t["q"])
-    if slots:
-        k_out, v_out = kw["k_pool"], kw["v_pool"]
-    else:
-        k_out, v_out = torch.empty_like(t["k"]), torch.empty_like(t["v"])
-    # pre-marshalled raw C call, so the timing is the GPU's and not the wrapper's
-    dims = ga.QkNormRopeDims(T, 16, 2, 256, 64, 16, 0, k_out.shape[0] if slots else 0)
-    args = [ctypes.c_void_p(x.data_ptr()) for x in
-            (t["q"], t["k"], t["v"], t["w_q"], t["w_k"])] + [ctypes.c_float(r.eps)] + \
-        [ctypes.c_void_p(x.data_ptr()) for x in (t["cos"], t["sin"])] + \
-        [ctypes.c_void_p(kw["slot_mapping"].data_ptr()) if slots else None] + \
-        [ctypes.c_void_p(x.data_ptr()) for x in (q_out, k_out, v_out)] + \
-        [ctypes.c_void_p(torch.cuda.current_stream(dev).cuda_stream), ctypes.byref(dims)]
+    moved = 2 * T * (16 + 2 + 2) * 256 * 2 + T * 64 * 2 * 2  # rows in + out, tables in
+    n_sets = rotation_sets(moved)
     fn = ga.lib.gated_attn_qk_norm_rope
+    keep, arg_sets = [], []
+    for _ in range(n_sets):  # resident copies used in turn (see MALL_DEFEAT_BYTES)
+        t = {n: to_dev(getattr(r, n), dev) for n in ("q", "k", "v", "w_q", "w_k", "cos", "sin")}
+        kw = {}
+        if slots:
+            P = (T + 15) // 16
+            kw = dict(slot_mapping=torch.arange(T, dtype=torch.int64, device=dev),
+                      k_pool=torch.zeros((P, 16, 2, 256), dtype=torch.bfloat16, device=dev),
+                      v_pool=torch.zeros((P, 16, 2, 256), dtype=torch.bfloat16, device=dev))
+        q_out = torch.empty_like(t["q"])
+        if slots:
+            k_out, v_out = kw["k_pool"], kw["v_pool"]
+        else:
+            k_out, v_out = torch.empty_like(t["k"]), torch.empty_like(t["v"])
+        # pre-marshalled raw C call, so the timing is the GPU's and not the wrapper's
+        dims = ga.QkNormRopeDims(T, 16, 2, 256, 64, 16, 0, k_out.shape[0] if slots else 0)
+        keep.append((t, kw, q_out, k_out, v_out, dims))
+        arg_sets.append(
+            [ctypes.c_void_p(x.data_ptr()) for x in (t["q"], t["k"], t["v"], t["w_q"], t["w_k"])]
+            + [ctypes.c_float(r.eps)]
+            + [ctypes.c_void_p(x.data_ptr()) for x in (t["cos"], t["sin"])]
+            + [ctypes.c_void_p(kw["slot_mapping"].data_ptr()) if slots else None]
+            + [ctypes.c_void_p(x.data_ptr()) for x in (q_out, k_out, v_out)]
+            + [ctypes.c_void_p(torch.cuda.current_stream(dev).cuda_stream), ctypes.byref(dims)])
+    turn = [0]
 
     def call():
-        st = fn(*args)
+        st = fn(*arg_sets[turn[0]])
+        turn[0] = (turn[0] + 1) % n_sets
         if st != 0:
             ga.check(st, "gated_attn_qk_norm_rope")
     for _ in range(20):
@@ -312,10 +364,10 @@ def time_qk_norm_rope(ga, workloads, dev, T: int, slots: bool, n_calls: int = 20
     b.record()
     torch.cuda.synchronize()
     us = a.elapsed_time(b) * 1e3 / n_calls
-    moved = 2 * T * (16 + 2 + 2) * 256 * 2 + T * 64 * 2 * 2  # rows in + out, tables in
     return {"workload": f"QK-RMSNorm + RoPE (rope_dim 64) + K/V {'slot writes' if slots else 'dense'}, "
                         f"T={T}, H_q=16 H_kv=2 D=256",
-            "us_per_call": round(us, 3), "gbs": round(moved / (us * 1e-6) / 1e9, 2)}
+            "us_per_call": round(us, 3), "gbs": round(moved / (us * 1e-6) / 1e9, 2),
+            "input_sets": n_sets}
 
 
 def main() -> int:
@@ -347,7 +399,8 @@ def main() -> int:
     case = workloads.workload(2, poison=False)
     gen_s = time.time() - t_gen
     kv_bytes = case.kv_bytes()
-    call = DecodeCall(ga, case, dev)
+    n_sets = rotation_sets(kv_bytes)
+    call = Rotation(lambda: DecodeCall(ga, case, dev), n_sets)
     torch.cuda.synchronize()
 
     if args.calibration_copy:
@@ -429,7 +482,7 @@ def main() -> int:
                         "H_q=16 H_kv=2 D=256",
             "batch": 64, "kv_len": 4096, "num_q_heads": 16, "num_kv_heads": 2, "head_dim": 256,
             "page_size": 16, "tokens_per_split": call.plan.tokens_per_split,
-            "num_splits": call.plan.num_splits,
+            "num_splits": call.plan.num_splits, "input_sets": n_sets,
         },
         "us_per_call": round(ms_per_step * 1e3, 3),
         "kv_bytes_per_call": kv_bytes,

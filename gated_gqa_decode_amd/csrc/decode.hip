@@ -40,6 +40,9 @@
 #include <math.h>
 #include <stdint.h>
 
+#include <cstdlib>
+#include <cstring>
+
 #include "ga_device.h"
 #include "ga_internal.h"
 
@@ -48,7 +51,9 @@ namespace ga {
 namespace {
 
 constexpr int kD = 256;          // head dim
-constexpr int kHeads = 16;       // query-head columns of a stage-1 workgroup
+constexpr int kHeads = 16;       // query-head columns of an MFMA stage-1 workgroup
+constexpr int kGroup = 8;        // query-head slots of a VALU stage-1 workgroup
+constexpr int kStep = 8;         // tokens per VALU wave step
 constexpr int kPage = 16;        // tokens per page = keys per tile
 constexpr int kWaves = 8;        // waves per stage-1 workgroup (one workgroup per CU)
 constexpr int kPageRegs = 2;     // page ids per lane: a split spans at most 128 pages
@@ -95,8 +100,10 @@ __device__ __forceinline__ uint4 ldg16(const uint16_t* p) {
   return *reinterpret_cast<const uint4*>(p);
 }
 
-// K rows are read exactly once per call: non-temporal loads keep them from
-// displacing reusable lines in L2 / MALL.
+// K/V rows are read exactly once per call: non-temporal loads keep them from
+// displacing reusable lines in L2 and the Infinity Cache (MALL).  kNt is the
+// same policy for the direct global-to-LDS copies (cache-policy bit "nt").
+constexpr int kNt = 2;
 __device__ __forceinline__ uint4 ldg16_stream(const char* p) {
   const u32x4 v = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p));
   return make_uint4(v[0], v[1], v[2], v[3]);
@@ -122,6 +129,24 @@ __device__ __forceinline__ uint32_t pk_bf16(float x, float y) {
 __device__ __forceinline__ s16x4_t lds_tr_read(const char* p) {
   return __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4_t*)(p));
 }
+
+typedef unsigned u32x2 __attribute__((ext_vector_type(2)));
+
+__device__ __forceinline__ uint2 ldg8_stream(const char* p) {
+  const u32x2 v = __builtin_nontemporal_load(reinterpret_cast<const u32x2*>(p));
+  return make_uint2(v[0], v[1]);
+}
+
+struct alignas(16) WaveSlot {
+  float p[kStep][kGroup];  // probabilities of the step's 8 tokens x 8 heads
+  float alpha[kGroup];     // rescale factor of the running state per head
+};
+
+struct alignas(16) MergeSlot {
+  float acc[kWaves][kGroup][kD];
+  float m[kWaves][kGroup];
+  float l[kWaves][kGroup];
+};
 
 // How one sequence is split.  The grid and the workspace come from the
 // capacity (num_splits splits of at most max_tokens tokens), so a call
@@ -176,11 +201,419 @@ __device__ __forceinline__ int seq_length(const int32_t* seq_lens, const int32_t
   return min(seq_lens[b], capacity);
 }
 
-// The stage-1 body for bf16 pools (kFp8 = false) or e4m3 pools (true), with
-// 16-token pages (kTok = false) or one token per page (true: block-table
-// entries or CSR indices are token slots).
+// The VALU stage-1 body (bf16 pools, groups of up to 8 heads), with 16-token
+// pages (kTok = false) or one token per page (true: block-table entries or
+// CSR indices are token slots).  Work layout inside a wave, per step of 8
+// tokens, which all lie in one half of one 16-token page:
+//   scores : lane = (token tq in 0..3) x (16-byte chunk c16 in 0..15).  A pass
+//            covers 4 tokens; each lane holds q chunks c16 and c16+16 of all 8
+//            heads (64 VGPRs) and forms 8 partial dot products with bf16 dot2
+//            instructions; a 16-lane DPP reduce-scatter completes them (each
+//            head's score lands in two lanes).  Two passes per step.
+//   values : lane owns d = 4*lane .. 4*lane+3 of all 8 heads (32 fp32
+//            accumulators) and takes every token of the step.
+//   softmax: probabilities go through a 288-byte per-wave LDS slot from the
+//            score lanes to the value lanes.
+// Every K and V load instruction of a wave reads whole 256/512-byte row
+// segments, and two steps' loads are in flight while a step is computed.
+template <bool kTok>
+__device__ __forceinline__ void stage1_valu_body(const Stage1Args& a) {
+  __shared__ WaveSlot wslot[kWaves][2];
+  __shared__ MergeSlot merge;
+  __shared__ int progress[kWaves];  // last step each wave started
+  __shared__ __align__(16) int tok_ids[kTok ? kMaxSplit : 4];  // page size 1: the split's token slots
+
+  // Workgroup id -> (split s, sequence b, kv head g), split-major as in the
+  // MFMA body.
+  const int unit = blockIdx.x;  // (s * B + b) * H_kv + g
+  if (unit >= a.num_units) return;
+  const int seq_heads = a.num_units / a.num_splits;  // B * H_kv
+  const int s = unit / seq_heads;
+  const int g = (unit - s * seq_heads) % a.num_kv_heads;
+  const int b = (unit - s * seq_heads) / a.num_kv_heads;
+  const int lane = __lane_id();
+  // wave-uniform by construction; readfirstlane lets the compiler keep the
+  // step bookkeeping and the load base addresses in scalar registers
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int Hkv = a.num_kv_heads;
+  const int Hq = a.num_q_heads;
+  const int nh = Hq / Hkv;  // <= kGroup: head slots 0..nh-1 are real, the rest idle
+  const int h0 = g * nh;    // first query head of this workgroup
+
+  // Issued together, before the length is known: the page ids of split s as
+  // it is when the sequence fills its capacity (page j of the split in lane
+  // j % 64 of register j / 64; ids past the sequence's end are never used),
+  // the length, and q.  Other lengths reload the page ids below.
+  const int32_t* bt_row = a.block_table + (size_t)b * a.max_pages;
+  auto load_pages = [&](int tok_first, int ntok, int (&pages)[kPageRegs]) {
+    const int fp = tok_first / kPage;
+    const int np = min(ntok / kPage, a.max_pages - fp);
+#pragma unroll
+    for (int r = 0; r < kPageRegs; ++r)
+      pages[r] = lane + 64 * r < np ? bt_row[fp + lane + 64 * r] : 0;
+  };
+  int my_page[kPageRegs] = {0, 0};
+  const int full_begin = s * a.tokens_per_split;  // < capacity, since s < num_splits
+  if constexpr (!kTok) load_pages(full_begin, a.tokens_per_split, my_page);
+
+  // score-lane coordinates
+  const int tq = lane >> 4;    // token within a pass
+  const int c16 = lane & 15;   // 16-byte chunk (and chunk + 16)
+  const int hs = c16 >> 1;     // head whose score this lane keeps (see reduce_scatter8)
+
+  // q of the workgroup's heads over the dims this lane's K pieces hold (bf16
+  // pairs): d = 8 c16 .. +7 and 8 (c16 + 16) .. +7 (two 16-byte pieces of the
+  // 512-byte row).  Idle head slots get q = 0 (their scores and sums are
+  // computed and dropped).
+  uint4 qa[kGroup], qb[kGroup];
+  {
+    const uint16_t* qbase = a.q + ((size_t)b * Hq + (size_t)h0) * kD;
+    const int da = 8 * c16;
+    const int db = 8 * (c16 + 16);
+#pragma unroll
+    for (int h = 0; h < kGroup; ++h) {
+      const int hh = min(h, nh - 1);
+      qa[h] = ldg16(qbase + hh * kD + da);
+      qb[h] = ldg16(qbase + hh * kD + db);
+    }
+#pragma unroll
+    for (int h = 0; h < kGroup; ++h)
+      if (h >= nh) qa[h] = qb[h] = make_uint4(0, 0, 0, 0);
+  }
+
+  // Lengths past the capacity and page ids outside the pool break the
+  // documented preconditions; both are clamped so such input yields garbage
+  // in its own row instead of an access outside the buffers.
+  const int capacity = kTok ? a.max_pages : a.max_pages * kPage;
+  long long first_index = 0;
+  const int L = seq_length(a.seq_lens, a.kv_indptr, a.index_capacity, b, capacity, &first_index);
+  // First visible token: the sliding window keeps the last `window` tokens.
+  const int tok_lo = a.window > 0 ? max(0, L - a.window) : 0;
+  const SplitRange sr = split_range(L, a.window, a.num_splits, a.tokens_per_split,
+                                    a.split_units, a.split_target);
+  if (s >= sr.count) return;  // empty split: stage 2 never reads its slot
+  const int tok_begin = sr.base + s * sr.tokens;
+  const int tok_end = min(L, tok_begin + sr.tokens);
+  const int first_page = tok_begin / kPage;
+  if constexpr (kTok) {
+    // one slot per token: the split's slots go to LDS (at most kMaxSplit)
+    const int32_t* ids = a.kv_indptr != nullptr ? a.kv_indices + first_index : bt_row;
+    for (int i = threadIdx.x; i < sr.tokens; i += kWaves * 64) {
+      const int tok = tok_begin + i;
+      const int id = tok < tok_end ? ids[tok] : 0;
+      tok_ids[i] = (int)min((long long)max(id, 0), a.num_pages - 1);
+    }
+  } else {
+    if (tok_begin != full_begin) load_pages(tok_begin, sr.tokens, my_page);
+#pragma unroll
+    for (int r = 0; r < kPageRegs; ++r)
+      my_page[r] = (int)min((long long)max(my_page[r], 0), a.num_pages - 1);
+  }
+  if (threadIdx.x < kWaves) progress[threadIdx.x] = 0;
+  __syncthreads();
+
+  // value lanes: lane owns d = 4*lane .. 4*lane+3 of all 8 heads
+  float acc[kGroup][4];
+#pragma unroll
+  for (int h = 0; h < kGroup; ++h)
+#pragma unroll
+    for (int e = 0; e < 4; ++e) acc[h][e] = 0.f;
+  float m_run = -INFINITY;  // reference max (log2 units) of head hs
+  float l_run = 0.f;        // this lane's share of the running sum of head hs
+
+  const int n_steps = (tok_end - tok_begin + kStep - 1) / kStep;
+  constexpr int kElem = 2;                                  // bytes per K / V element
+  const size_t row_bytes = (size_t)Hkv * kD * kElem;        // between tokens
+  const size_t page_bytes = (size_t)kPage * row_bytes;      // between pages
+
+  // Byte offsets of this lane's pieces inside one 8-token step (the same for
+  // every step); the step's base address is wave-uniform.
+  unsigned k_off[2];
+#pragma unroll
+  for (int pass = 0; pass < 2; ++pass)
+    k_off[pass] = (unsigned)((pass * 4 + tq) * (int)row_bytes + c16 * 16);
+  unsigned v_off[kStep];
+#pragma unroll
+  for (int t = 0; t < kStep; ++t) v_off[t] = (unsigned)(t * (int)row_bytes + lane * 4 * kElem);
+
+  auto step_base = [&](int step, const char* pool) -> const char* {
+    const int t0 = tok_begin + step * kStep;
+    const int j = t0 / kPage - first_page;  // wave-uniform
+    const int pg = j < 64 ? __builtin_amdgcn_readlane(my_page[0], j)
+                          : __builtin_amdgcn_readlane(my_page[1], j - 64);
+    return pool + (size_t)pg * page_bytes + (size_t)(t0 % kPage) * row_bytes +
+           (size_t)g * kD * kElem;
+  };
+
+  // One step's data.  K: per pass of 4 tokens, 32 bytes per lane.  V: per
+  // token, 8 bytes per lane -- a whole row segment per wave instruction.
+  typedef uint2 VElem;
+  struct KRegs {
+    uint4 k[2][2];
+  };
+  struct VRegs {
+    VElem v[kStep];
+  };
+  // Page size 1: every token has its own slot, so K takes a per-lane address
+  // (the lane's token of the pass) and V one scalar base per token, both from
+  // the slots in LDS.
+  const size_t head_bytes = (size_t)g * kD * kElem;
+  auto load_k = [&](int step, KRegs& r) {
+#pragma unroll
+    for (int pass = 0; pass < 2; ++pass) {
+      const char* kb;
+      unsigned off;
+      if constexpr (kTok) {
+        kb = a.k_pool + (size_t)tok_ids[step * kStep + pass * 4 + tq] * row_bytes + head_bytes;
+        off = (unsigned)(c16 * 16);
+      } else {
+        kb = step_base(step, a.k_pool);
+        off = k_off[pass];
+      }
+      r.k[pass][0] = ldg16_stream(kb + off);
+      r.k[pass][1] = ldg16_stream(kb + (off + 256u));
+    }
+  };
+  auto load_v = [&](int step, VRegs& r) {
+    int4 ids_lo = make_int4(0, 0, 0, 0), ids_hi = make_int4(0, 0, 0, 0);
+    if constexpr (kTok) {
+      ids_lo = *reinterpret_cast<const int4*>(&tok_ids[step * kStep]);
+      ids_hi = *reinterpret_cast<const int4*>(&tok_ids[step * kStep + 4]);
+    }
+    const int ids[kStep] = {ids_lo.x, ids_lo.y, ids_lo.z, ids_lo.w,
+                            ids_hi.x, ids_hi.y, ids_hi.z, ids_hi.w};
+    const char* vb = kTok ? nullptr : step_base(step, a.v_pool);
+#pragma unroll
+    for (int t = 0; t < kStep; ++t) {
+      const char* p;
+      if constexpr (kTok)
+        p = a.v_pool + (size_t)__builtin_amdgcn_readfirstlane(ids[t]) * row_bytes + head_bytes +
+            lane * 4 * kElem;
+      else
+        p = vb + v_off[t];
+      r.v[t] = ldg8_stream(p);
+    }
+  };
+
+  // Two probability slots per wave: the scores of step i+1 are computed into
+  // one while the values of step i are accumulated from the other, so the two
+  // dependency chains can be interleaved; one fence per step separates a
+  // slot's writes from its reads.
+  WaveSlot* slots = wslot[wave];
+
+  // Scores of one step -> probabilities in the step's slot.  Returns (wave-
+  // uniform) whether the reference max was raised, in which case the slot's
+  // alpha[] holds the factors the value accumulators must take before this
+  // step's probabilities are added (l_run is rescaled here).
+  auto score_step = [&](int step, const KRegs& r, WaveSlot& ws) -> bool {
+    const int t0 = tok_begin + step * kStep;
+    float sc[2];
+#pragma unroll
+    for (int pass = 0; pass < 2; ++pass) {
+      // this lane's 16 K values as 8 bf16 pairs, in q's pair order
+      const uint32_t kp[8] = {r.k[pass][0].x, r.k[pass][0].y, r.k[pass][0].z, r.k[pass][0].w,
+                              r.k[pass][1].x, r.k[pass][1].y, r.k[pass][1].z, r.k[pass][1].w};
+      float part[kGroup];
+#pragma unroll
+      for (int h = 0; h < kGroup; ++h) {
+        float x = 0.f;
+        x = dot2_bf16(qa[h].x, kp[0], x);
+        x = dot2_bf16(qa[h].y, kp[1], x);
+        x = dot2_bf16(qa[h].z, kp[2], x);
+        x = dot2_bf16(qa[h].w, kp[3], x);
+        x = dot2_bf16(qb[h].x, kp[4], x);
+        x = dot2_bf16(qb[h].y, kp[5], x);
+        x = dot2_bf16(qb[h].z, kp[6], x);
+        x = dot2_bf16(qb[h].w, kp[7], x);
+        part[h] = x;
+      }
+      const float mine = reduce_scatter8(part, c16);
+      const int t = t0 + pass * 4 + tq;
+      sc[pass] = (t < tok_end && t >= tok_lo) ? mine * a.scale_log2 : -INFINITY;
+    }
+    // Lazy rescaling: probabilities are taken relative to a reference max
+    // m_run that is only raised (with a rescale of l and acc) when some score
+    // of the step exceeds it by more than kSlack (log2 units), i.e. when a
+    // probability would exceed 2^kSlack.  On the common path there is then no
+    // cross-lane max and no rescale; any reference gives the same O, and
+    // probabilities stay in [0, 2^kSlack].
+    const bool raise = (sc[0] > m_run + kSlack) || (sc[1] > m_run + kSlack);
+    const bool raised = __builtin_amdgcn_ballot_w64(raise) != 0;  // wave-uniform
+    if (raised) {
+      float mx = fmaxf(sc[0], sc[1]);
+      mx = fmaxf(mx, shfl_xor(mx, 16));
+      mx = fmaxf(mx, shfl_xor(mx, 32));
+      const float m_new = fmaxf(m_run, mx);
+      const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
+      l_run *= alpha;
+      m_run = m_new;
+      if ((c16 & 1) == 0 && tq == 0) ws.alpha[hs] = alpha;
+    }
+    const float p0 = __builtin_amdgcn_exp2f(sc[0] - m_run);
+    const float p1 = __builtin_amdgcn_exp2f(sc[1] - m_run);
+    l_run += p0 + p1;
+    if ((c16 & 1) == 0) {  // odd lanes hold the same (token, head) as their even neighbour
+      ws.p[tq][hs] = p0;
+      ws.p[4 + tq][hs] = p1;
+    }
+    return raised;
+  };
+
+  // Values of one step from its slot (after the rescale its scores asked for).
+  auto value_step = [&](int step, const VRegs& r, const WaveSlot& ws, bool rescale) {
+    const int t0 = tok_begin + step * kStep;
+    if (rescale) {
+      const float4 al0 = *reinterpret_cast<const float4*>(&ws.alpha[0]);
+      const float4 al1 = *reinterpret_cast<const float4*>(&ws.alpha[4]);
+      const float al[kGroup] = {al0.x, al0.y, al0.z, al0.w, al1.x, al1.y, al1.z, al1.w};
+#pragma unroll
+      for (int h = 0; h < kGroup; ++h)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) acc[h][e] *= al[h];
+    }
+    VElem vv[kStep];
+#pragma unroll
+    for (int t = 0; t < kStep; ++t) vv[t] = r.v[t];
+    if (t0 + kStep > tok_end || t0 < tok_lo) {
+      // last step of the sequence (tail slots may hold anything) or the step
+      // the window starts in: invisible rows take no part, whatever they hold
+#pragma unroll
+      for (int t = 0; t < kStep; ++t)
+        if (t0 + t >= tok_end || t0 + t < tok_lo) vv[t] = VElem{};
+    }
+#pragma unroll
+    for (int t = 0; t < kStep; ++t) {
+      const float vf[4] = {bf16_lo(vv[t].x), bf16_hi(vv[t].x), bf16_lo(vv[t].y),
+                           bf16_hi(vv[t].y)};
+      const float4 pa = *reinterpret_cast<const float4*>(&ws.p[t][0]);
+      const float4 pb = *reinterpret_cast<const float4*>(&ws.p[t][4]);
+      const float pr[kGroup] = {pa.x, pa.y, pa.z, pa.w, pb.x, pb.y, pb.z, pb.w};
+#pragma unroll
+      for (int h = 0; h < kGroup; ++h)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) acc[h][e] = fmaf(pr[h], vf[e], acc[h][e]);
+    }
+  };
+
+  // Steps of this wave: wave, wave + 8, ...; the assignment is static, so
+  // the result does not depend on timing.  Each iteration scores step c1 and
+  // accumulates the values of step c0; the K rows of a step are loaded one
+  // iteration before its scores and its V rows one iteration before its
+  // values, into two K and two V register sets used in turn (the loop is
+  // unrolled twice, so no set is copied).  Loads are issued unconditionally
+  // (past the end a wave re-reads the last step), so the wait before a step's
+  // arithmetic covers only that step's own loads.
+  //
+  // A CU issues instructions of older waves first, which on its own lets the
+  // first waves of the workgroup run well ahead of the last ones, and the
+  // workgroup ends with its slowest wave.  So at every step a wave compares
+  // its position with the other waves' and, while at least half of them are
+  // ahead of it, runs at a raised issue priority (measured at B=64, L=4096:
+  // stage 1 takes 89.4 us with this and 92.2 us without).
+  auto balance = [&](int c) {
+    if (lane == 0) progress[wave] = c;
+    const int other = lane < kWaves ? progress[lane] : 0;
+    const unsigned long long ahead = __builtin_amdgcn_ballot_w64(other > c);
+    if (__builtin_popcountll(ahead) >= kWaves / 2)
+      __builtin_amdgcn_s_setprio(2);
+    else
+      __builtin_amdgcn_s_setprio(0);
+  };
+  const int first_step = (max(tok_begin, tok_lo) - tok_begin) / kStep;
+  int c0 = first_step + wave;
+  if (c0 < n_steps) {
+    const int last = n_steps - 1;
+    int c1 = c0 + kWaves;
+    int c2 = c0 + 2 * kWaves;
+    KRegs kA, kB;
+    VRegs vA, vB;
+    load_k(c0, kA);
+    load_v(c0, vA);
+    load_k(min(c1, last), kB);
+    bool resc = score_step(c0, kA, slots[0]);
+    wave_lds_sync();
+    for (;;) {
+      // kB: K of c1; vA: V of c0 (scored, slot 0)
+      balance(c0);
+      load_k(min(c2, last), kA);
+      load_v(min(c1, last), vB);
+      bool resc_next = false;
+      if (c1 < n_steps) resc_next = score_step(c1, kB, slots[1]);
+      value_step(c0, vA, slots[0], resc);
+      wave_lds_sync();
+      c0 = c1;
+      c1 = c2;
+      c2 += kWaves;
+      resc = resc_next;
+      if (c0 >= n_steps) break;
+
+      // kA: K of c1; vB: V of c0 (scored, slot 1)
+      balance(c0);
+      load_k(min(c2, last), kB);
+      load_v(min(c1, last), vA);
+      resc_next = false;
+      if (c1 < n_steps) resc_next = score_step(c1, kA, slots[0]);
+      value_step(c0, vB, slots[1], resc);
+      wave_lds_sync();
+      c0 = c1;
+      c1 = c2;
+      c2 += kWaves;
+      resc = resc_next;
+      if (c0 >= n_steps) break;
+    }
+    __builtin_amdgcn_s_setprio(0);
+  }
+
+  // ---- merge the waves' states and write the split's partial ---------------
+  l_run += shfl_xor(l_run, 16);
+  l_run += shfl_xor(l_run, 32);
+  if (lane < 2 * kGroup && (lane & 1) == 0) {  // tq == 0, c16 == 2h: one lane per head
+    merge.m[wave][lane >> 1] = m_run;
+    merge.l[wave][lane >> 1] = l_run;
+  }
+#pragma unroll
+  for (int h = 0; h < kGroup; ++h)
+    *reinterpret_cast<float4*>(&merge.acc[wave][h][lane * 4]) =
+        make_float4(acc[h][0], acc[h][1], acc[h][2], acc[h][3]);
+  __syncthreads();
+  {
+    const int h = threadIdx.x >> 6;   // 0..7
+    const int c = threadIdx.x & 63;   // 4 values each
+    float M = -INFINITY;
+#pragma unroll
+    for (int w = 0; w < kWaves; ++w) M = fmaxf(M, merge.m[w][h]);
+    float wgt[kWaves];
+    float lam = 0.f;
+#pragma unroll
+    for (int w = 0; w < kWaves; ++w) {
+      wgt[w] = __builtin_amdgcn_exp2f(merge.m[w][h] - M);  // 0 for a wave without tokens
+      lam += merge.l[w][h] * wgt[w];
+    }
+    float out[4] = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int w = 0; w < kWaves; ++w) {
+      const float4 x = *reinterpret_cast<const float4*>(&merge.acc[w][h][c * 4]);
+      out[0] = fmaf(x.x, wgt[w], out[0]);
+      out[1] = fmaf(x.y, wgt[w], out[1]);
+      out[2] = fmaf(x.z, wgt[w], out[2]);
+      out[3] = fmaf(x.w, wgt[w], out[3]);
+    }
+    if (h < nh) {
+      const size_t row = ((size_t)b * Hq + (size_t)(h0 + h)) * a.num_splits + s;
+      *reinterpret_cast<float4*>(a.part_acc + row * kD + c * 4) =
+          make_float4(out[0], out[1], out[2], out[3]);
+      if (c == 0) {
+        a.part_ml[row * 2 + 0] = M;
+        a.part_ml[row * 2 + 1] = lam;
+      }
+    }
+  }
+}
+
+// The MFMA stage-1 body for bf16 pools (kFp8 = false) or e4m3 pools (true),
+// with 16-token pages (kTok = false) or one token per page (true).
 template <bool kFp8, bool kTok>
-__device__ __forceinline__ void stage1_body(const Stage1Args& a) {
+__device__ __forceinline__ void stage1_mma_body(const Stage1Args& a) {
   // Per-wave LDS tiles.  bf16 pools: vA / vB = two V tiles, used in turn.
   // e4m3 pools: vA = the converted bf16 tile, vB / vC = two raw e4m3 tiles.
   // Separate objects, so the compiler can see that a copy into one does not
@@ -327,7 +760,7 @@ __device__ __forceinline__ void stage1_body(const Stage1Args& a) {
       const int rc = min(max(r, lo), hi - 1);
       const int p = lane & 31;
       const char* src = row_ptr(a.v_pool, i, rc) + 16 * (p ^ ((r & 7) << 1));
-      __builtin_amdgcn_global_load_lds(src, (lds_void_t*)(buf + 2 * d * 512), 16, 0, 0);
+      __builtin_amdgcn_global_load_lds(src, (lds_void_t*)(buf + 2 * d * 512), 16, 0, kNt);
     }
   };
   // e4m3 V tile i -> LDS raw (copy d: rows 4d .. 4d + 3, 16 lanes per row).
@@ -339,7 +772,7 @@ __device__ __forceinline__ void stage1_body(const Stage1Args& a) {
       const int r = 4 * d + (lane >> 4);
       const int rc = min(max(r, lo), hi - 1);
       const char* src = row_ptr(a.v_pool, i, rc) + 16 * (lane & 15);
-      __builtin_amdgcn_global_load_lds(src, (lds_void_t*)(raw + d * 1024), 16, 0, 0);
+      __builtin_amdgcn_global_load_lds(src, (lds_void_t*)(raw + d * 1024), 16, 0, kNt);
     }
   };
   // raw e4m3 tile -> the swizzled bf16 tile: lane l converts bytes
@@ -583,15 +1016,23 @@ __device__ __forceinline__ void stage1_body(const Stage1Args& a) {
 }
 
 __global__ __launch_bounds__(512, 1) void decode_stage1_kernel(Stage1Args a) {
-  stage1_body<false, false>(a);
-}
-
-__global__ __launch_bounds__(512, 1) void decode_stage1_fp8_kernel(Stage1Args a) {
-  stage1_body<true, false>(a);
+  stage1_valu_body<false>(a);
 }
 
 __global__ __launch_bounds__(512, 1) void decode_stage1_tok_kernel(Stage1Args a) {
-  stage1_body<false, true>(a);
+  stage1_valu_body<true>(a);
+}
+
+__global__ __launch_bounds__(512, 1) void decode_stage1_mma_kernel(Stage1Args a) {
+  stage1_mma_body<false, false>(a);
+}
+
+__global__ __launch_bounds__(512, 1) void decode_stage1_mma_fp8_kernel(Stage1Args a) {
+  stage1_mma_body<true, false>(a);
+}
+
+__global__ __launch_bounds__(512, 1) void decode_stage1_mma_tok_kernel(Stage1Args a) {
+  stage1_mma_body<false, true>(a);
 }
 
 struct Stage2Args {
@@ -700,6 +1141,25 @@ __global__ __launch_bounds__(256) void decode_stage2_gate_kernel(Stage2Args a) {
   *reinterpret_cast<uint2*>(a.out + (size_t)row * kD + lane * 4) = w;
 }
 
+// Which stage 1 runs.  The MFMA body serves e4m3 pools (its conversions cost
+// a fraction of the VALU body's), groups of more than 8 heads (one workgroup
+// reads the K/V once for all 16 MFMA columns), and short capacities (splits
+// under 1,024 tokens: latency-bound, where its shorter per-tile chain wins).
+// The VALU body streams long bf16 sequences of groups up to 8 about 3% faster
+// (measured at B=64, L=4096 with inputs rotated so no call finds the previous
+// one's rows in the Infinity Cache: 91.9 vs 95.1 us per call).
+// The environment variable GATED_ATTN_DECODE_STAGE1 = "mma" or "valu" forces
+// one body where both apply (tests run every case through each).
+bool use_mma_stage1(const DecodeLaunch& d) {
+  const int group = d.num_q_heads / d.num_kv_heads;
+  if (d.kv_fp8 || group > kGroup) return true;  // the VALU body takes neither
+  if (const char* e = std::getenv("GATED_ATTN_DECODE_STAGE1")) {
+    if (std::strcmp(e, "mma") == 0) return true;
+    if (std::strcmp(e, "valu") == 0) return false;
+  }
+  return d.tokens_per_split < 1024;
+}
+
 hipError_t launch_decode(const DecodeLaunch& d, hipStream_t stream) {
   Stage1Args a1;
   a1.q = d.q;
@@ -729,12 +1189,19 @@ hipError_t launch_decode(const DecodeLaunch& d, hipStream_t stream) {
     err = hipEventRecord(d.stage1_start, stream);
     if (err != hipSuccess) return err;
   }
-  if (d.page_size == 1)
-    hipLaunchKernelGGL(decode_stage1_tok_kernel, grid1, dim3(kWaves * 64), 0, stream, a1);
-  else if (d.kv_fp8)
-    hipLaunchKernelGGL(decode_stage1_fp8_kernel, grid1, dim3(kWaves * 64), 0, stream, a1);
-  else
-    hipLaunchKernelGGL(decode_stage1_kernel, grid1, dim3(kWaves * 64), 0, stream, a1);
+  const dim3 block(kWaves * 64);
+  if (use_mma_stage1(d)) {
+    if (d.kv_fp8)
+      hipLaunchKernelGGL(decode_stage1_mma_fp8_kernel, grid1, block, 0, stream, a1);
+    else if (d.page_size == 1)
+      hipLaunchKernelGGL(decode_stage1_mma_tok_kernel, grid1, block, 0, stream, a1);
+    else
+      hipLaunchKernelGGL(decode_stage1_mma_kernel, grid1, block, 0, stream, a1);
+  } else if (d.page_size == 1) {
+    hipLaunchKernelGGL(decode_stage1_tok_kernel, grid1, block, 0, stream, a1);
+  } else {
+    hipLaunchKernelGGL(decode_stage1_kernel, grid1, block, 0, stream, a1);
+  }
   err = hipGetLastError();
   if (err != hipSuccess) return err;
   if (d.stage1_stop != nullptr) {
