@@ -63,6 +63,8 @@ def parse_args():
                     help="only the timed decode steps (cold, B1, prefill, CPU legs skipped)")
     ap.add_argument("--prefill-only", action="store_true",
                     help="time only the B=2, S=2048 causal prefill (for profiling)")
+    ap.add_argument("--only", choices=["decode_fp8kv", "decode_hq32"], default=None,
+                    help="time only this decode variant at B=64, L=4096 (for profiling its kernel)")
     ap.add_argument("--calibration-copy", action="store_true",
                     help="also run one plain 1 GiB device copy (counter calibration)")
     ap.add_argument("--json-out", default=None)
@@ -271,6 +273,18 @@ def time_decode(ga, case, dev, n_calls: int, settle_s: float = 0.1, **opts) -> d
             "input_sets": n_sets}
 
 
+def only_case(workloads, name: str):
+    """The B=64, L=4096 decode variants that run the MFMA stage 1."""
+    if name == "decode_hq32":  # GQA group 16
+        return workloads.make_decode("decode_b64_l4096_hq32", [4096] * 64, seed=2,
+                                     num_q_heads=32, num_kv_heads=2, poison=False,
+                                     max_pages_per_seq=256)
+    if name == "decode_fp8kv":  # e4m3 K / V pools, same shape as the headline
+        return workloads.make_decode("decode_b64_l4096_fp8", [4096] * 64, seed=2, poison=False,
+                                     max_pages_per_seq=256, kv_dtype="fp8")
+    raise ValueError(name)
+
+
 def time_decode_csr(ga, workloads, case, dev, n_calls: int) -> dict:
     """The headline workload's tokens at page size 1 (one pool row per token,
     shuffled), addressed by CSR row pointers: back-to-back calls."""
@@ -392,6 +406,11 @@ def main() -> int:
     if args.prefill_only:
         print(json.dumps({"prefill": time_prefill(ga, workloads.workload(4), dev, K,
                                                   settle_s=args.settle_s)}), flush=True)
+        return 0
+    if args.only:
+        extra = only_case(workloads, args.only)
+        print(json.dumps({args.only: time_decode(ga, extra, dev, K, settle_s=args.settle_s)}),
+              flush=True)
         return 0
 
     # ---------------- headline: B=64, L=4096 paged decode --------------------
@@ -560,9 +579,7 @@ def main() -> int:
         result["prefill"] = time_prefill(ga, workloads.workload(4), dev, 20, settle_s=0.1)
 
         # ---- the h_q = 32, h_kv = 2 geometry (GQA group 16) -----------------
-        c32 = workloads.make_decode("decode_b64_l4096_hq32", [4096] * 64, seed=2,
-                                    num_q_heads=32, num_kv_heads=2, poison=False,
-                                    max_pages_per_seq=256)
+        c32 = only_case(workloads, "decode_hq32")
         result["decode_hq32"] = time_decode(ga, c32, dev, 100)
         # attention-spec options on the headline workload
         result["decode_sinks_lse"] = time_decode(ga, case, dev, 100, sinks=[0.5] * 16, lse=True)
@@ -577,8 +594,7 @@ def main() -> int:
         # page size 1 with CSR indexing (the FreeToken PR's serving layout)
         result["decode_csr"] = time_decode_csr(ga, workloads, case, dev, 200)
         # FP8 (e4m3) K / V pools, same shape as the headline
-        c8 = workloads.make_decode("decode_b64_l4096_fp8", [4096] * 64, seed=2, poison=False,
-                                   max_pages_per_seq=256, kv_dtype="fp8")
+        c8 = only_case(workloads, "decode_fp8kv")
         result["decode_fp8kv"] = time_decode(ga, c8, dev, 200)
         del c8
         del c32
