@@ -273,6 +273,33 @@ def time_decode(ga, case, dev, n_calls: int, settle_s: float = 0.1, **opts) -> d
             "input_sets": n_sets}
 
 
+def stream_read_ceiling(ga, dev, n_calls: int = 20) -> dict:
+    """GB/s of a plain read of 1 GiB with the decode's non-temporal 16-byte
+    loads (gated_attn_stream_read; two buffers used in turn, so neither is
+    served from the Infinity Cache): the streaming-read rate of the device."""
+    import torch
+
+    bufs = [torch.ones(1 << 28, dtype=torch.float32, device=dev) for _ in range(2)]
+    sink = torch.zeros(1, dtype=torch.int32, device=dev)
+    stream = ctypes.c_void_p(torch.cuda.current_stream(dev).cuda_stream)
+    args = [(ctypes.c_void_p(x.data_ptr()), ctypes.c_size_t(1 << 30),
+             ctypes.c_void_p(sink.data_ptr()), stream) for x in bufs]
+    for i in range(6):
+        ga.check(ga.lib.gated_attn_stream_read(*args[i % 2]), "gated_attn_stream_read")
+    torch.cuda.synchronize()
+    a = torch.cuda.Event(enable_timing=True)
+    b = torch.cuda.Event(enable_timing=True)
+    a.record()
+    for i in range(n_calls):
+        ga.lib.gated_attn_stream_read(*args[i % 2])
+    b.record()
+    torch.cuda.synchronize()
+    us = a.elapsed_time(b) * 1e3 / n_calls
+    return {"method": "gated_attn_stream_read over 1 GiB, two buffers in turn",
+            "us_per_call": round(us, 3), "gbs": round((1 << 30) / (us * 1e-6) / 1e9, 2),
+            "hbm_frac": round((1 << 30) / (us * 1e-6) / 1e9 / HBM_PEAK_GBS, 4)}
+
+
 def only_case(workloads, name: str):
     """The B=64, L=4096 decode variants that run the MFMA stage 1."""
     if name == "decode_hq32":  # GQA group 16
@@ -579,6 +606,13 @@ def main() -> int:
         result["prefill"] = time_prefill(ga, workloads.workload(4), dev, 20, settle_s=0.1)
 
         # ---- the h_q = 32, h_kv = 2 geometry (GQA group 16) -----------------
+        # the serving shape: B=224, L ~ U{4094..6142}, 11 padded slots (HBM-bound)
+        c224 = workloads.workload(3, poison=False)
+        result["decode_b224"] = time_decode(ga, c224, dev, 50)
+        del c224
+        # a plain device-wide read of 1 GiB (a reduction, two buffers in turn):
+        # the streaming-read rate the decode's KV GB/s can be set beside
+        result["stream_read_ceiling"] = stream_read_ceiling(ga, dev)
         c32 = only_case(workloads, "decode_hq32")
         result["decode_hq32"] = time_decode(ga, c32, dev, 100)
         # attention-spec options on the headline workload

@@ -40,6 +40,7 @@ EXPORTED_SYMBOLS = (
     "gated_attn_prefill",
     "gated_attn_prefill_ex",
     "gated_attn_qk_norm_rope",
+    "gated_attn_stream_read",
     "gated_attn_status_string",
     "gated_attn_last_hip_error",
 )
@@ -141,6 +142,8 @@ def _load_library() -> ctypes.CDLL:
     lib.gated_attn_prefill.restype = ctypes.c_int
     lib.gated_attn_prefill.argtypes = [vp, vp, vp, vp, ctypes.c_float, ctypes.c_int, vp, vp,
                                        ctypes.POINTER(PrefillDims)]
+    lib.gated_attn_stream_read.restype = ctypes.c_int
+    lib.gated_attn_stream_read.argtypes = [vp, sz, vp, vp]
     lib.gated_attn_decode_time_stage1.restype = ctypes.c_int
     lib.gated_attn_decode_time_stage1.argtypes = [ctypes.POINTER(ctypes.c_void_p),
                                                   ctypes.POINTER(ctypes.c_void_p), ctypes.c_int]

@@ -12,7 +12,7 @@ ROOT = os.path.dirname(HERE)
 CSRC = os.path.join(HERE, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(HERE, "libgated_attn.so")
-SOURCES = ["capi.cpp", "decode.hip", "prefill.hip", "qk_norm_rope.hip"]
+SOURCES = ["capi.cpp", "decode.hip", "prefill.hip", "qk_norm_rope.hip", "stream_read.hip"]
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 

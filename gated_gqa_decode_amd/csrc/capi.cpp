@@ -402,6 +402,17 @@ ga_status gated_attn_decode_time_stage1(void* const* starts, void* const* stops,
   return GA_OK;
 }
 
+ga_status gated_attn_stream_read(const void* src, size_t bytes, uint32_t* sink, void* stream) {
+  if (src == nullptr || sink == nullptr || !aligned(src, 16) || !aligned(sink, 4) || bytes % 16 != 0)
+    return GA_ERR_INVALID_ARGUMENT;
+  ga_status st = check_device();
+  if (st != GA_OK) return st;
+  if (bytes == 0) return GA_OK;
+  hipError_t e = ga::launch_stream_read(src, bytes, sink, static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return hip_fail(e);
+  return GA_OK;
+}
+
 const char* gated_attn_status_string(ga_status status) {
   switch (status) {
     case GA_OK: return "GA_OK";

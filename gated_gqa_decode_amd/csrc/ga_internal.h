@@ -93,6 +93,7 @@ struct RopeLaunch {
 
 hipError_t launch_decode(const DecodeLaunch& d, hipStream_t stream);
 hipError_t launch_qk_norm_rope(const RopeLaunch& p, hipStream_t stream);
+hipError_t launch_stream_read(const void* src, size_t bytes, uint32_t* sink, hipStream_t stream);
 hipError_t launch_prefill(const PrefillLaunch& p, hipStream_t stream);
 
 }  // namespace ga

@@ -135,6 +135,18 @@ ga_status gated_attn_decode(const uint16_t *q, const uint16_t *gate, const uint1
  * GA_ERR_INVALID_ARGUMENT for n < 0, or n > 0 with a NULL array. */
 ga_status gated_attn_decode_time_stage1(void *const *starts, void *const *stops, int n);
 
+/* Measurement hook for benchmarks: reads `bytes` of device memory at `src`
+ * once, with the non-temporal 16-byte loads the decode's K/V stream uses, in
+ * one kernel launch on `stream`, so a caller can time the device's streaming-
+ * read rate beside the decode's KV bandwidth.  Not part of the attention path.
+ *   src    device buffer, 16-byte aligned, read
+ *   bytes  a multiple of 16 (0: nothing is launched)
+ *   sink   device uint32[1], 4-byte aligned; written only if the XOR of all
+ *          words read equals 0x9e3779b9 (it keeps the loads from being removed)
+ * GA_ERR_INVALID_ARGUMENT for a NULL or misaligned pointer or a size not a
+ * multiple of 16; GA_ERR_UNSUPPORTED off gfx950; GA_ERR_HIP on a launch error. */
+ga_status gated_attn_stream_read(const void *src, size_t bytes, uint32_t *sink, void *stream);
+
 /* Shape of a dense prefill call: S_q = S_kv = seq_len. */
 typedef struct ga_prefill_dims {
     int32_t batch;        /* B >= 0 */

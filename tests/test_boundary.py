@@ -272,3 +272,12 @@ def test_prefill_bad_scale():
     d = ga.PrefillDims(2, 128, 16, 2, 256)
     assert ga.lib.gated_attn_prefill(FAKE, FAKE, FAKE, FAKE, float("nan"), 1, FAKE, None,
                                      ctypes.byref(d)) == ga.GA_ERR_INVALID_ARGUMENT
+
+
+@pytest.mark.parametrize("src,nbytes,sink", [
+    (None, 1 << 20, FAKE), (FAKE + 8, 1 << 20, FAKE), (FAKE, (1 << 20) + 4, FAKE),
+    (FAKE, 1 << 20, None), (FAKE, 1 << 20, FAKE + 2)])
+def test_stream_read_argument_checks(src, nbytes, sink):
+    """The measurement hook rejects NULL / misaligned pointers and sizes that
+    are not whole 16-byte loads before any HIP call."""
+    assert ga.lib.gated_attn_stream_read(src, nbytes, sink, None) == ga.GA_ERR_INVALID_ARGUMENT
