@@ -63,7 +63,7 @@ def parse_args():
                     help="only the timed decode steps (cold, B1, prefill, CPU legs skipped)")
     ap.add_argument("--prefill-only", action="store_true",
                     help="time only the B=2, S=2048 causal prefill (for profiling)")
-    ap.add_argument("--only", choices=["decode_fp8kv", "decode_hq32"], default=None,
+    ap.add_argument("--only", choices=["decode_fp8kv", "decode_hq32", "decode_b224"], default=None,
                     help="time only this decode variant at B=64, L=4096 (for profiling its kernel)")
     ap.add_argument("--calibration-copy", action="store_true",
                     help="also run one plain 1 GiB device copy (counter calibration)")
@@ -301,7 +301,8 @@ def stream_read_ceiling(ga, dev, n_calls: int = 20) -> dict:
 
 
 def only_case(workloads, name: str):
-    """The B=64, L=4096 decode variants that run the MFMA stage 1."""
+    """Decode variants timed on their own with --only: the B=64, L=4096
+    variants that run the MFMA stage 1, and the B=224 serving shape."""
     if name == "decode_hq32":  # GQA group 16
         return workloads.make_decode("decode_b64_l4096_hq32", [4096] * 64, seed=2,
                                      num_q_heads=32, num_kv_heads=2, poison=False,
@@ -309,6 +310,8 @@ def only_case(workloads, name: str):
     if name == "decode_fp8kv":  # e4m3 K / V pools, same shape as the headline
         return workloads.make_decode("decode_b64_l4096_fp8", [4096] * 64, seed=2, poison=False,
                                      max_pages_per_seq=256, kv_dtype="fp8")
+    if name == "decode_b224":  # the serving shape: B=224, L ~ U{4094..6142}
+        return workloads.workload(3, poison=False)
     raise ValueError(name)
 
 
@@ -607,7 +610,7 @@ def main() -> int:
 
         # ---- the h_q = 32, h_kv = 2 geometry (GQA group 16) -----------------
         # the serving shape: B=224, L ~ U{4094..6142}, 11 padded slots (HBM-bound)
-        c224 = workloads.workload(3, poison=False)
+        c224 = only_case(workloads, "decode_b224")
         result["decode_b224"] = time_decode(ga, c224, dev, 50)
         del c224
         # a plain device-wide read of 1 GiB (a reduction, two buffers in turn):

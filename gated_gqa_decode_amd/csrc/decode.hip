@@ -18,24 +18,25 @@
 // = lane % 16, k = 8(lane / 16) + 0..7, B column = lane % 16, same k;
 // v_mfma_f32_16x16x16_bf16 the same with k = 4(lane / 16) + 0..3; C row =
 // 4(lane / 16) + r, column = lane % 16.  Per tile:
-//   S^T (16 keys x 16 head columns) = K Q^T, 8 MFMAs 16x16x32.  A = K read
-//       from HBM straight into registers (lane (li, lg): key li, 8 dims per
-//       k-step), B = q (column = head; idle columns are zero).  Each lane then
-//       holds head li's scores of keys 4lg .. 4lg+3 -- already the A layout of
-//       P for the 16x16x16 product below.
+//   S^T (16 keys x 16 head columns) = K Q^T, 8 MFMAs 16x16x32.  A = K
+//       fragments (lane (li, lg): key li, 8 dims per k-step), B = q (column =
+//       head; idle columns are zero).  Each lane then holds head li's scores
+//       of keys 4lg .. 4lg+3 -- already the A layout of P for P V.
 //   online softmax per head in fp32 (lazy rescaling against a reference max);
 //   P = Phi + Plo, two bf16 terms (~16 significant bits of the fp32 weight);
 //   O (16 heads x 256) += P V, 16 column tiles x 2 MFMAs 16x16x16.  V needs
-//       keys along k, but rows are stored dims-first, so it passes through a
-//       per-wave LDS tile (rows of 512 B, 16-byte chunk c of row r stored at
-//       c ^ 2(r & 7): conflict-free) and comes back transposed by the gfx950
-//       read ds_read_b64_tr_b16 (within 16 lanes, lane i of the result gets
-//       element i % 4 of source lane 4k + i / 4 in slot k; source lane s
-//       points at V[key0 + s/4][d0 + 4(s%4)]).
-// bf16 V is copied HBM -> LDS by direct global-to-LDS loads (no registers),
-// alternating between two tiles; e4m3 K is converted to bf16 in registers
-// before the score MFMAs, and e4m3 V is copied raw to LDS and converted into
-// the bf16 tile just before its P V.  About two tiles per wave are in flight.
+//       keys along k while rows are stored dims-first: gfx950's transposing
+//       LDS reads (ds_read_b64_tr_b16, ds_read_b64_tr_b8) deliver it.
+// Both K and V reach LDS by direct copies that read whole rows (every copy
+// instruction covers whole 128-byte pieces of rows; K fragments read straight
+// from HBM would cover half pieces, which measured about 8% slower), through
+// buffer descriptors: the compiler tracks a buffer-form copy as a plain
+// vector-memory access, so its wait counts stay exact, whereas the
+// global-address form counts as a possible flat access and every wait after
+// it drains all outstanding requests.  bf16 tiles are single-buffered (the
+// next tile's K is requested as soon as this tile's fragments are in
+// registers, its V once P V has read this tile's); e4m3 tiles are half the
+// size and double-buffered.
 #include <hip/hip_runtime.h>
 #include <math.h>
 #include <stdint.h>
@@ -51,15 +52,13 @@ namespace ga {
 namespace {
 
 constexpr int kD = 256;          // head dim
-constexpr int kHeads = 16;       // query-head columns of an MFMA stage-1 workgroup
-constexpr int kGroup = 8;        // query-head slots of a VALU stage-1 workgroup
-constexpr int kStep = 8;         // tokens per VALU wave step
+constexpr int kHeads = 16;       // query-head columns of a stage-1 workgroup
 constexpr int kPage = 16;        // tokens per page = keys per tile
 constexpr int kWaves = 8;        // waves per stage-1 workgroup (one workgroup per CU)
 constexpr int kPageRegs = 2;     // page ids per lane: a split spans at most 128 pages
 constexpr int kMaxSplit = 2048;  // tokens of the largest split
 constexpr int kMinSplit = 64;    // tokens of the smallest split a sizing rule asks for
-constexpr int kTileBytes = kPage * kD * 2;  // one bf16 V tile in LDS
+constexpr int kTileBytes = kPage * kD * 2;  // one bf16 K or V tile in LDS
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
 constexpr float kSlack = 8.f;    // lazy-rescale threshold, log2 units
@@ -88,26 +87,43 @@ struct Stage1Args {
   int split_target;  // the workgroups the sizing rule aims for
 };
 
-typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
 typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
 typedef float f32x2_t __attribute__((ext_vector_type(2)));
 typedef float f32x4_t __attribute__((ext_vector_type(4)));
 typedef short s16x4_t __attribute__((ext_vector_type(4)));
 typedef s16x4_t __attribute__((address_space(3))) lds_s16x4_t;
+typedef int i32x2_t __attribute__((ext_vector_type(2)));
+typedef i32x2_t __attribute__((address_space(3))) lds_i32x2_t;
 typedef __attribute__((address_space(3))) void lds_void_t;
 
 __device__ __forceinline__ uint4 ldg16(const uint16_t* p) {
   return *reinterpret_cast<const uint4*>(p);
 }
 
-// K/V rows are read exactly once per call: non-temporal loads keep them from
-// displacing reusable lines in L2 and the Infinity Cache (MALL).  kNt is the
-// same policy for the direct global-to-LDS copies (cache-policy bit "nt").
+// K/V rows are read exactly once per call: the copies carry the non-temporal
+// cache policy (bit "nt"), which keeps them from displacing reusable lines in
+// L2 and the Infinity Cache (MALL).
 constexpr int kNt = 2;
-__device__ __forceinline__ uint4 ldg16_stream(const char* p) {
-  const u32x4 v = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p));
-  return make_uint4(v[0], v[1], v[2], v[3]);
+
+// One 16-byte-per-lane copy from global memory into LDS (the destination is
+// wave-uniform; lane l writes lds + 16 l).  kWide = false: through a buffer
+// descriptor at `base` with a 32-bit lane offset (reads past `extent` bytes
+// return zeros); true: the global-address form, for offsets that do not fit
+// 32 bits (its waits drain every outstanding request, see the file comment).
+template <bool kWide>
+__device__ __forceinline__ void copy16(const char* base, uint32_t extent, size_t off, char* lds) {
+  if constexpr (kWide) {
+    __builtin_amdgcn_global_load_lds(base + off, (lds_void_t*)lds, 16, 0, kNt);
+  } else {
+    const __amdgpu_buffer_rsrc_t rs =
+        __builtin_amdgcn_make_buffer_rsrc(const_cast<char*>(base), 0, (int)extent, 0x00020000);
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_void_t*)lds, 16, (uint32_t)off, 0, 0, kNt);
+  }
 }
+
+// Wait until this wave's LDS reads have returned, before a copy overwrites
+// the tile they read.
+__device__ __forceinline__ void lds_reads_done() { asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory"); }
 
 // e4m3 codes -> bf16.  gfx950's conversion decodes the OCP e4m3 format
 // exactly (checked on all 256 codes against an independent decoder); every
@@ -124,29 +140,6 @@ __device__ __forceinline__ uint32_t pk_bf16(float x, float y) {
   const f32x2_t v = {x, y};
   return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, bf16x2_t));
 }
-
-// p must point into LDS (8-byte aligned).
-__device__ __forceinline__ s16x4_t lds_tr_read(const char* p) {
-  return __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4_t*)(p));
-}
-
-typedef unsigned u32x2 __attribute__((ext_vector_type(2)));
-
-__device__ __forceinline__ uint2 ldg8_stream(const char* p) {
-  const u32x2 v = __builtin_nontemporal_load(reinterpret_cast<const u32x2*>(p));
-  return make_uint2(v[0], v[1]);
-}
-
-struct alignas(16) WaveSlot {
-  float p[kStep][kGroup];  // probabilities of the step's 8 tokens x 8 heads
-  float alpha[kGroup];     // rescale factor of the running state per head
-};
-
-struct alignas(16) MergeSlot {
-  float acc[kWaves][kGroup][kD];
-  float m[kWaves][kGroup];
-  float l[kWaves][kGroup];
-};
 
 // How one sequence is split.  The grid and the workspace come from the
 // capacity (num_splits splits of at most max_tokens tokens), so a call
@@ -201,426 +194,22 @@ __device__ __forceinline__ int seq_length(const int32_t* seq_lens, const int32_t
   return min(seq_lens[b], capacity);
 }
 
-// The VALU stage-1 body (bf16 pools, groups of up to 8 heads), with 16-token
-// pages (kTok = false) or one token per page (true: block-table entries or
-// CSR indices are token slots).  Work layout inside a wave, per step of 8
-// tokens, which all lie in one half of one 16-token page:
-//   scores : lane = (token tq in 0..3) x (16-byte chunk c16 in 0..15).  A pass
-//            covers 4 tokens; each lane holds q chunks c16 and c16+16 of all 8
-//            heads (64 VGPRs) and forms 8 partial dot products with bf16 dot2
-//            instructions; a 16-lane DPP reduce-scatter completes them (each
-//            head's score lands in two lanes).  Two passes per step.
-//   values : lane owns d = 4*lane .. 4*lane+3 of all 8 heads (32 fp32
-//            accumulators) and takes every token of the step.
-//   softmax: probabilities go through a 288-byte per-wave LDS slot from the
-//            score lanes to the value lanes.
-// Every K and V load instruction of a wave reads whole 256/512-byte row
-// segments, and two steps' loads are in flight while a step is computed.
-template <bool kTok>
-__device__ __forceinline__ void stage1_valu_body(const Stage1Args& a) {
-  __shared__ WaveSlot wslot[kWaves][2];
-  __shared__ MergeSlot merge;
-  __shared__ int progress[kWaves];  // last step each wave started
-  __shared__ __align__(16) int tok_ids[kTok ? kMaxSplit : 4];  // page size 1: the split's token slots
-
-  // Workgroup id -> (split s, sequence b, kv head g), split-major as in the
-  // MFMA body.
-  const int unit = blockIdx.x;  // (s * B + b) * H_kv + g
-  if (unit >= a.num_units) return;
-  const int seq_heads = a.num_units / a.num_splits;  // B * H_kv
-  const int s = unit / seq_heads;
-  const int g = (unit - s * seq_heads) % a.num_kv_heads;
-  const int b = (unit - s * seq_heads) / a.num_kv_heads;
-  const int lane = __lane_id();
-  // wave-uniform by construction; readfirstlane lets the compiler keep the
-  // step bookkeeping and the load base addresses in scalar registers
-  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  const int Hkv = a.num_kv_heads;
-  const int Hq = a.num_q_heads;
-  const int nh = Hq / Hkv;  // <= kGroup: head slots 0..nh-1 are real, the rest idle
-  const int h0 = g * nh;    // first query head of this workgroup
-
-  // Issued together, before the length is known: the page ids of split s as
-  // it is when the sequence fills its capacity (page j of the split in lane
-  // j % 64 of register j / 64; ids past the sequence's end are never used),
-  // the length, and q.  Other lengths reload the page ids below.
-  const int32_t* bt_row = a.block_table + (size_t)b * a.max_pages;
-  auto load_pages = [&](int tok_first, int ntok, int (&pages)[kPageRegs]) {
-    const int fp = tok_first / kPage;
-    const int np = min(ntok / kPage, a.max_pages - fp);
-#pragma unroll
-    for (int r = 0; r < kPageRegs; ++r)
-      pages[r] = lane + 64 * r < np ? bt_row[fp + lane + 64 * r] : 0;
-  };
-  int my_page[kPageRegs] = {0, 0};
-  const int full_begin = s * a.tokens_per_split;  // < capacity, since s < num_splits
-  if constexpr (!kTok) load_pages(full_begin, a.tokens_per_split, my_page);
-
-  // score-lane coordinates
-  const int tq = lane >> 4;    // token within a pass
-  const int c16 = lane & 15;   // 16-byte chunk (and chunk + 16)
-  const int hs = c16 >> 1;     // head whose score this lane keeps (see reduce_scatter8)
-
-  // q of the workgroup's heads over the dims this lane's K pieces hold (bf16
-  // pairs): d = 8 c16 .. +7 and 8 (c16 + 16) .. +7 (two 16-byte pieces of the
-  // 512-byte row).  Idle head slots get q = 0 (their scores and sums are
-  // computed and dropped).
-  uint4 qa[kGroup], qb[kGroup];
-  {
-    const uint16_t* qbase = a.q + ((size_t)b * Hq + (size_t)h0) * kD;
-    const int da = 8 * c16;
-    const int db = 8 * (c16 + 16);
-#pragma unroll
-    for (int h = 0; h < kGroup; ++h) {
-      const int hh = min(h, nh - 1);
-      qa[h] = ldg16(qbase + hh * kD + da);
-      qb[h] = ldg16(qbase + hh * kD + db);
-    }
-#pragma unroll
-    for (int h = 0; h < kGroup; ++h)
-      if (h >= nh) qa[h] = qb[h] = make_uint4(0, 0, 0, 0);
-  }
-
-  // Lengths past the capacity and page ids outside the pool break the
-  // documented preconditions; both are clamped so such input yields garbage
-  // in its own row instead of an access outside the buffers.
-  const int capacity = kTok ? a.max_pages : a.max_pages * kPage;
-  long long first_index = 0;
-  const int L = seq_length(a.seq_lens, a.kv_indptr, a.index_capacity, b, capacity, &first_index);
-  // First visible token: the sliding window keeps the last `window` tokens.
-  const int tok_lo = a.window > 0 ? max(0, L - a.window) : 0;
-  const SplitRange sr = split_range(L, a.window, a.num_splits, a.tokens_per_split,
-                                    a.split_units, a.split_target);
-  if (s >= sr.count) return;  // empty split: stage 2 never reads its slot
-  const int tok_begin = sr.base + s * sr.tokens;
-  const int tok_end = min(L, tok_begin + sr.tokens);
-  const int first_page = tok_begin / kPage;
-  if constexpr (kTok) {
-    // one slot per token: the split's slots go to LDS (at most kMaxSplit)
-    const int32_t* ids = a.kv_indptr != nullptr ? a.kv_indices + first_index : bt_row;
-    for (int i = threadIdx.x; i < sr.tokens; i += kWaves * 64) {
-      const int tok = tok_begin + i;
-      const int id = tok < tok_end ? ids[tok] : 0;
-      tok_ids[i] = (int)min((long long)max(id, 0), a.num_pages - 1);
-    }
-  } else {
-    if (tok_begin != full_begin) load_pages(tok_begin, sr.tokens, my_page);
-#pragma unroll
-    for (int r = 0; r < kPageRegs; ++r)
-      my_page[r] = (int)min((long long)max(my_page[r], 0), a.num_pages - 1);
-  }
-  if (threadIdx.x < kWaves) progress[threadIdx.x] = 0;
-  __syncthreads();
-
-  // value lanes: lane owns d = 4*lane .. 4*lane+3 of all 8 heads
-  float acc[kGroup][4];
-#pragma unroll
-  for (int h = 0; h < kGroup; ++h)
-#pragma unroll
-    for (int e = 0; e < 4; ++e) acc[h][e] = 0.f;
-  float m_run = -INFINITY;  // reference max (log2 units) of head hs
-  float l_run = 0.f;        // this lane's share of the running sum of head hs
-
-  const int n_steps = (tok_end - tok_begin + kStep - 1) / kStep;
-  constexpr int kElem = 2;                                  // bytes per K / V element
-  const size_t row_bytes = (size_t)Hkv * kD * kElem;        // between tokens
-  const size_t page_bytes = (size_t)kPage * row_bytes;      // between pages
-
-  // Byte offsets of this lane's pieces inside one 8-token step (the same for
-  // every step); the step's base address is wave-uniform.
-  unsigned k_off[2];
-#pragma unroll
-  for (int pass = 0; pass < 2; ++pass)
-    k_off[pass] = (unsigned)((pass * 4 + tq) * (int)row_bytes + c16 * 16);
-  unsigned v_off[kStep];
-#pragma unroll
-  for (int t = 0; t < kStep; ++t) v_off[t] = (unsigned)(t * (int)row_bytes + lane * 4 * kElem);
-
-  auto step_base = [&](int step, const char* pool) -> const char* {
-    const int t0 = tok_begin + step * kStep;
-    const int j = t0 / kPage - first_page;  // wave-uniform
-    const int pg = j < 64 ? __builtin_amdgcn_readlane(my_page[0], j)
-                          : __builtin_amdgcn_readlane(my_page[1], j - 64);
-    return pool + (size_t)pg * page_bytes + (size_t)(t0 % kPage) * row_bytes +
-           (size_t)g * kD * kElem;
-  };
-
-  // One step's data.  K: per pass of 4 tokens, 32 bytes per lane.  V: per
-  // token, 8 bytes per lane -- a whole row segment per wave instruction.
-  typedef uint2 VElem;
-  struct KRegs {
-    uint4 k[2][2];
-  };
-  struct VRegs {
-    VElem v[kStep];
-  };
-  // Page size 1: every token has its own slot, so K takes a per-lane address
-  // (the lane's token of the pass) and V one scalar base per token, both from
-  // the slots in LDS.
-  const size_t head_bytes = (size_t)g * kD * kElem;
-  auto load_k = [&](int step, KRegs& r) {
-#pragma unroll
-    for (int pass = 0; pass < 2; ++pass) {
-      const char* kb;
-      unsigned off;
-      if constexpr (kTok) {
-        kb = a.k_pool + (size_t)tok_ids[step * kStep + pass * 4 + tq] * row_bytes + head_bytes;
-        off = (unsigned)(c16 * 16);
-      } else {
-        kb = step_base(step, a.k_pool);
-        off = k_off[pass];
-      }
-      r.k[pass][0] = ldg16_stream(kb + off);
-      r.k[pass][1] = ldg16_stream(kb + (off + 256u));
-    }
-  };
-  auto load_v = [&](int step, VRegs& r) {
-    int4 ids_lo = make_int4(0, 0, 0, 0), ids_hi = make_int4(0, 0, 0, 0);
-    if constexpr (kTok) {
-      ids_lo = *reinterpret_cast<const int4*>(&tok_ids[step * kStep]);
-      ids_hi = *reinterpret_cast<const int4*>(&tok_ids[step * kStep + 4]);
-    }
-    const int ids[kStep] = {ids_lo.x, ids_lo.y, ids_lo.z, ids_lo.w,
-                            ids_hi.x, ids_hi.y, ids_hi.z, ids_hi.w};
-    const char* vb = kTok ? nullptr : step_base(step, a.v_pool);
-#pragma unroll
-    for (int t = 0; t < kStep; ++t) {
-      const char* p;
-      if constexpr (kTok)
-        p = a.v_pool + (size_t)__builtin_amdgcn_readfirstlane(ids[t]) * row_bytes + head_bytes +
-            lane * 4 * kElem;
-      else
-        p = vb + v_off[t];
-      r.v[t] = ldg8_stream(p);
-    }
-  };
-
-  // Two probability slots per wave: the scores of step i+1 are computed into
-  // one while the values of step i are accumulated from the other, so the two
-  // dependency chains can be interleaved; one fence per step separates a
-  // slot's writes from its reads.
-  WaveSlot* slots = wslot[wave];
-
-  // Scores of one step -> probabilities in the step's slot.  Returns (wave-
-  // uniform) whether the reference max was raised, in which case the slot's
-  // alpha[] holds the factors the value accumulators must take before this
-  // step's probabilities are added (l_run is rescaled here).
-  auto score_step = [&](int step, const KRegs& r, WaveSlot& ws) -> bool {
-    const int t0 = tok_begin + step * kStep;
-    float sc[2];
-#pragma unroll
-    for (int pass = 0; pass < 2; ++pass) {
-      // this lane's 16 K values as 8 bf16 pairs, in q's pair order
-      const uint32_t kp[8] = {r.k[pass][0].x, r.k[pass][0].y, r.k[pass][0].z, r.k[pass][0].w,
-                              r.k[pass][1].x, r.k[pass][1].y, r.k[pass][1].z, r.k[pass][1].w};
-      float part[kGroup];
-#pragma unroll
-      for (int h = 0; h < kGroup; ++h) {
-        float x = 0.f;
-        x = dot2_bf16(qa[h].x, kp[0], x);
-        x = dot2_bf16(qa[h].y, kp[1], x);
-        x = dot2_bf16(qa[h].z, kp[2], x);
-        x = dot2_bf16(qa[h].w, kp[3], x);
-        x = dot2_bf16(qb[h].x, kp[4], x);
-        x = dot2_bf16(qb[h].y, kp[5], x);
-        x = dot2_bf16(qb[h].z, kp[6], x);
-        x = dot2_bf16(qb[h].w, kp[7], x);
-        part[h] = x;
-      }
-      const float mine = reduce_scatter8(part, c16);
-      const int t = t0 + pass * 4 + tq;
-      sc[pass] = (t < tok_end && t >= tok_lo) ? mine * a.scale_log2 : -INFINITY;
-    }
-    // Lazy rescaling: probabilities are taken relative to a reference max
-    // m_run that is only raised (with a rescale of l and acc) when some score
-    // of the step exceeds it by more than kSlack (log2 units), i.e. when a
-    // probability would exceed 2^kSlack.  On the common path there is then no
-    // cross-lane max and no rescale; any reference gives the same O, and
-    // probabilities stay in [0, 2^kSlack].
-    const bool raise = (sc[0] > m_run + kSlack) || (sc[1] > m_run + kSlack);
-    const bool raised = __builtin_amdgcn_ballot_w64(raise) != 0;  // wave-uniform
-    if (raised) {
-      float mx = fmaxf(sc[0], sc[1]);
-      mx = fmaxf(mx, shfl_xor(mx, 16));
-      mx = fmaxf(mx, shfl_xor(mx, 32));
-      const float m_new = fmaxf(m_run, mx);
-      const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
-      l_run *= alpha;
-      m_run = m_new;
-      if ((c16 & 1) == 0 && tq == 0) ws.alpha[hs] = alpha;
-    }
-    const float p0 = __builtin_amdgcn_exp2f(sc[0] - m_run);
-    const float p1 = __builtin_amdgcn_exp2f(sc[1] - m_run);
-    l_run += p0 + p1;
-    if ((c16 & 1) == 0) {  // odd lanes hold the same (token, head) as their even neighbour
-      ws.p[tq][hs] = p0;
-      ws.p[4 + tq][hs] = p1;
-    }
-    return raised;
-  };
-
-  // Values of one step from its slot (after the rescale its scores asked for).
-  auto value_step = [&](int step, const VRegs& r, const WaveSlot& ws, bool rescale) {
-    const int t0 = tok_begin + step * kStep;
-    if (rescale) {
-      const float4 al0 = *reinterpret_cast<const float4*>(&ws.alpha[0]);
-      const float4 al1 = *reinterpret_cast<const float4*>(&ws.alpha[4]);
-      const float al[kGroup] = {al0.x, al0.y, al0.z, al0.w, al1.x, al1.y, al1.z, al1.w};
-#pragma unroll
-      for (int h = 0; h < kGroup; ++h)
-#pragma unroll
-        for (int e = 0; e < 4; ++e) acc[h][e] *= al[h];
-    }
-    VElem vv[kStep];
-#pragma unroll
-    for (int t = 0; t < kStep; ++t) vv[t] = r.v[t];
-    if (t0 + kStep > tok_end || t0 < tok_lo) {
-      // last step of the sequence (tail slots may hold anything) or the step
-      // the window starts in: invisible rows take no part, whatever they hold
-#pragma unroll
-      for (int t = 0; t < kStep; ++t)
-        if (t0 + t >= tok_end || t0 + t < tok_lo) vv[t] = VElem{};
-    }
-#pragma unroll
-    for (int t = 0; t < kStep; ++t) {
-      const float vf[4] = {bf16_lo(vv[t].x), bf16_hi(vv[t].x), bf16_lo(vv[t].y),
-                           bf16_hi(vv[t].y)};
-      const float4 pa = *reinterpret_cast<const float4*>(&ws.p[t][0]);
-      const float4 pb = *reinterpret_cast<const float4*>(&ws.p[t][4]);
-      const float pr[kGroup] = {pa.x, pa.y, pa.z, pa.w, pb.x, pb.y, pb.z, pb.w};
-#pragma unroll
-      for (int h = 0; h < kGroup; ++h)
-#pragma unroll
-        for (int e = 0; e < 4; ++e) acc[h][e] = fmaf(pr[h], vf[e], acc[h][e]);
-    }
-  };
-
-  // Steps of this wave: wave, wave + 8, ...; the assignment is static, so
-  // the result does not depend on timing.  Each iteration scores step c1 and
-  // accumulates the values of step c0; the K rows of a step are loaded one
-  // iteration before its scores and its V rows one iteration before its
-  // values, into two K and two V register sets used in turn (the loop is
-  // unrolled twice, so no set is copied).  Loads are issued unconditionally
-  // (past the end a wave re-reads the last step), so the wait before a step's
-  // arithmetic covers only that step's own loads.
-  //
-  // A CU issues instructions of older waves first, which on its own lets the
-  // first waves of the workgroup run well ahead of the last ones, and the
-  // workgroup ends with its slowest wave.  So at every step a wave compares
-  // its position with the other waves' and, while at least half of them are
-  // ahead of it, runs at a raised issue priority (measured at B=64, L=4096:
-  // stage 1 takes 89.4 us with this and 92.2 us without).
-  auto balance = [&](int c) {
-    if (lane == 0) progress[wave] = c;
-    const int other = lane < kWaves ? progress[lane] : 0;
-    const unsigned long long ahead = __builtin_amdgcn_ballot_w64(other > c);
-    if (__builtin_popcountll(ahead) >= kWaves / 2)
-      __builtin_amdgcn_s_setprio(2);
-    else
-      __builtin_amdgcn_s_setprio(0);
-  };
-  const int first_step = (max(tok_begin, tok_lo) - tok_begin) / kStep;
-  int c0 = first_step + wave;
-  if (c0 < n_steps) {
-    const int last = n_steps - 1;
-    int c1 = c0 + kWaves;
-    int c2 = c0 + 2 * kWaves;
-    KRegs kA, kB;
-    VRegs vA, vB;
-    load_k(c0, kA);
-    load_v(c0, vA);
-    load_k(min(c1, last), kB);
-    bool resc = score_step(c0, kA, slots[0]);
-    wave_lds_sync();
-    for (;;) {
-      // kB: K of c1; vA: V of c0 (scored, slot 0)
-      balance(c0);
-      load_k(min(c2, last), kA);
-      load_v(min(c1, last), vB);
-      bool resc_next = false;
-      if (c1 < n_steps) resc_next = score_step(c1, kB, slots[1]);
-      value_step(c0, vA, slots[0], resc);
-      wave_lds_sync();
-      c0 = c1;
-      c1 = c2;
-      c2 += kWaves;
-      resc = resc_next;
-      if (c0 >= n_steps) break;
-
-      // kA: K of c1; vB: V of c0 (scored, slot 1)
-      balance(c0);
-      load_k(min(c2, last), kB);
-      load_v(min(c1, last), vA);
-      resc_next = false;
-      if (c1 < n_steps) resc_next = score_step(c1, kA, slots[0]);
-      value_step(c0, vB, slots[1], resc);
-      wave_lds_sync();
-      c0 = c1;
-      c1 = c2;
-      c2 += kWaves;
-      resc = resc_next;
-      if (c0 >= n_steps) break;
-    }
-    __builtin_amdgcn_s_setprio(0);
-  }
-
-  // ---- merge the waves' states and write the split's partial ---------------
-  l_run += shfl_xor(l_run, 16);
-  l_run += shfl_xor(l_run, 32);
-  if (lane < 2 * kGroup && (lane & 1) == 0) {  // tq == 0, c16 == 2h: one lane per head
-    merge.m[wave][lane >> 1] = m_run;
-    merge.l[wave][lane >> 1] = l_run;
-  }
-#pragma unroll
-  for (int h = 0; h < kGroup; ++h)
-    *reinterpret_cast<float4*>(&merge.acc[wave][h][lane * 4]) =
-        make_float4(acc[h][0], acc[h][1], acc[h][2], acc[h][3]);
-  __syncthreads();
-  {
-    const int h = threadIdx.x >> 6;   // 0..7
-    const int c = threadIdx.x & 63;   // 4 values each
-    float M = -INFINITY;
-#pragma unroll
-    for (int w = 0; w < kWaves; ++w) M = fmaxf(M, merge.m[w][h]);
-    float wgt[kWaves];
-    float lam = 0.f;
-#pragma unroll
-    for (int w = 0; w < kWaves; ++w) {
-      wgt[w] = __builtin_amdgcn_exp2f(merge.m[w][h] - M);  // 0 for a wave without tokens
-      lam += merge.l[w][h] * wgt[w];
-    }
-    float out[4] = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-    for (int w = 0; w < kWaves; ++w) {
-      const float4 x = *reinterpret_cast<const float4*>(&merge.acc[w][h][c * 4]);
-      out[0] = fmaf(x.x, wgt[w], out[0]);
-      out[1] = fmaf(x.y, wgt[w], out[1]);
-      out[2] = fmaf(x.z, wgt[w], out[2]);
-      out[3] = fmaf(x.w, wgt[w], out[3]);
-    }
-    if (h < nh) {
-      const size_t row = ((size_t)b * Hq + (size_t)(h0 + h)) * a.num_splits + s;
-      *reinterpret_cast<float4*>(a.part_acc + row * kD + c * 4) =
-          make_float4(out[0], out[1], out[2], out[3]);
-      if (c == 0) {
-        a.part_ml[row * 2 + 0] = M;
-        a.part_ml[row * 2 + 1] = lam;
-      }
-    }
-  }
-}
-
-// The MFMA stage-1 body for bf16 pools (kFp8 = false) or e4m3 pools (true),
-// with 16-token pages (kTok = false) or one token per page (true).
-template <bool kFp8, bool kTok>
-__device__ __forceinline__ void stage1_mma_body(const Stage1Args& a) {
-  // Per-wave LDS tiles.  bf16 pools: vA / vB = two V tiles, used in turn.
-  // e4m3 pools: vA = the converted bf16 tile, vB / vC = two raw e4m3 tiles.
-  // Separate objects, so the compiler can see that a copy into one does not
-  // touch the others.  After the loop they hold the waves' O for the merge.
-  __shared__ __align__(16) char vA[kWaves][kTileBytes];
-  __shared__ __align__(16) char vB[kWaves][kFp8 ? kTileBytes / 2 : kTileBytes];
-  __shared__ __align__(16) char vC[kWaves][kFp8 ? kTileBytes / 2 : 16];
+// The stage-1 body: kFp8 = e4m3 pools (16-token pages); kTok = one token per
+// page (block-table entries or CSR indices are token slots); kWide = a
+// page-size-1 pool whose byte offsets do not fit 32 bits.
+template <bool kFp8, bool kTok, bool kWide>
+__device__ __forceinline__ void stage1_body(const Stage1Args& a) {
+  // Per-wave LDS tiles, separate objects so the compiler can tell a copy into
+  // one from a read of another (its wait before a read then covers only the
+  // copy that read needs).  bf16 pools: tA = the V tile, tB = the K tile.
+  // e4m3 pools: tA / tB = V tiles and tC / tD = K tiles, used in turn.  After
+  // the loop they hold the wave's O (16 heads x 256 fp32 = 16 KiB) for the
+  // merge.
+  constexpr int kTile = kFp8 ? kTileBytes / 2 : kTileBytes;
+  __shared__ __align__(16) char tA[kWaves][kTile];
+  __shared__ __align__(16) char tB[kWaves][kTile];
+  __shared__ __align__(16) char tC[kWaves][kFp8 ? kTile : 16];
+  __shared__ __align__(16) char tD[kWaves][kFp8 ? kTile : 16];
   __shared__ float m_w[kWaves][kHeads], l_w[kWaves][kHeads];
   __shared__ __align__(16) int tok_ids[kTok ? kMaxSplit : 4];  // page size 1: the split's token slots
 
@@ -661,7 +250,7 @@ __device__ __forceinline__ void stage1_mma_body(const Stage1Args& a) {
 
   // q, the B operand of K Q^T: lane (li, lg) holds head li's dims of k-step k
   // -- bf16 pools: 32k + 8lg .. +7; e4m3 pools: k = 2m + e covers
-  // 16(lg + 4m) + 8e .. +7, matching the 16-byte K pieces loaded there.
+  // 16(lg + 4m) + 8e .. +7, matching the 16-byte K pieces read there.
   bf16x8_t qf[8];
   {
     const uint16_t* qrow = a.q + ((size_t)b * Hq + (size_t)(h0 + min(li, nh - 1))) * kD;
@@ -704,21 +293,133 @@ __device__ __forceinline__ void stage1_mma_body(const Stage1Args& a) {
       my_page[r] = (int)min((long long)max(my_page[r], 0), a.num_pages - 1);
   }
 
+  const int n_tiles = (tok_end - tok_begin + kPage - 1) / kPage;
+  const int vis_lo = max(tok_begin, tok_lo);  // first visible token of the split
+  const int first_tile = (vis_lo - tok_begin) / kPage;
+
   constexpr int kElem = kFp8 ? 1 : 2;  // bytes per pool element
-  const size_t row_bytes = (size_t)Hkv * kD * kElem;    // between tokens
+  constexpr int kRow = kD * kElem;     // bytes of one head's row
+  const size_t row_bytes = (size_t)Hkv * kRow;          // between tokens
   const size_t page_bytes = (size_t)kPage * row_bytes;  // between pages
-  const size_t head_bytes = (size_t)g * kD * kElem;
-  // this head's row of token (tile i, row r) in a pool
-  auto row_ptr = [&](const char* pool, int i, int r) -> const char* {
+  const size_t head_bytes = (size_t)g * kRow;
+  // Bytes a copy may read from its tile base: the rest of the page, or of
+  // the pool at page size 1 (the launch picks kWide when that exceeds 32 bits).
+  const uint32_t extent = kTok ? (uint32_t)min((size_t)a.num_pages * row_bytes - head_bytes,
+                                               (size_t)0xffffffffu)
+                               : (uint32_t)(page_bytes - head_bytes);
+  // Tile i's rows in a pool.  The loops request the next tile unconditionally
+  // (so the compiler's wait counts stay exact); for a tile past the split's
+  // last one every lane reads the first 16 bytes of the last tile instead.
+  auto tile_base = [&](const char* pool, int i) -> const char* {
     if constexpr (kTok) {
-      return pool + (size_t)tok_ids[i * kPage + r] * row_bytes + head_bytes;
+      return pool + head_bytes;
     } else {
-      const int j = (tok_begin / kPage + i) - first_page;  // wave-uniform
-      const int pg = j < 64 ? __builtin_amdgcn_readlane(my_page[0], j)
-                            : __builtin_amdgcn_readlane(my_page[1], j - 64);
-      return pool + (size_t)pg * page_bytes + (size_t)r * row_bytes + head_bytes;
+      const int j = (tok_begin / kPage + min(i, n_tiles - 1)) - first_page;  // wave-uniform, < 128
+      const int pg = __builtin_amdgcn_readlane(j < 64 ? my_page[0] : my_page[1], j & 63);
+      return pool + (size_t)pg * page_bytes + head_bytes;
     }
   };
+  // byte offset of row r of tile i from tile_base (0 for tiles past the end)
+  auto row_off = [&](int i, int r) -> size_t {
+    size_t off;
+    if constexpr (kTok) {
+      off = (size_t)tok_ids[min(i, n_tiles - 1) * kPage + r] * row_bytes;
+    } else {
+      off = (size_t)r * row_bytes;
+    }
+    return i < n_tiles ? off : 0;
+  };
+  // Rows outside the visible range [lo, hi) of a tile copy the nearest
+  // visible row of V instead (finite data whose probability is exactly 0).
+  // K rows need no such care: their scores are replaced by -inf.
+  auto visible_rows = [&](int i, int& lo, int& hi) {
+    const int t0 = tok_begin + i * kPage;
+    lo = max(vis_lo, t0) - t0;
+    hi = min(tok_end, t0 + kPage) - t0;
+  };
+
+  // ---- HBM -> LDS copies of one tile (kRow / 16 chunks of 16 bytes per row) --
+  // K: copy d fills whole rows; chunk c of row r is stored at c ^ (r & 15), so
+  // a fragment read of 16 rows at one chunk touches 16 different bank groups.
+  auto stage_k = [&](int i, char* buf) {
+    constexpr int kChunks = kRow / 16;       // 32 (bf16) or 16 (e4m3)
+    constexpr int kRowsPerCopy = 64 / kChunks;
+    const char* base = tile_base(a.k_pool, i);
+    const int live = i < n_tiles ? 1 : 0;
+#pragma unroll
+    for (int d = 0; d < kPage / kRowsPerCopy; ++d) {
+      const int r = kRowsPerCopy * d + lane / kChunks;
+      const int p = lane % kChunks;
+      copy16<kWide>(base, extent, row_off(i, r) + live * 16 * (p ^ (r & 15)), buf + d * 1024);
+    }
+  };
+  // bf16 V: copy d fills rows 2d, 2d + 1; chunk c of row r is stored at
+  // c ^ 2(r & 7), which keeps the transposing reads below conflict-free.
+  auto stage_v = [&](int i, char* buf) {
+    int lo, hi;
+    visible_rows(i, lo, hi);
+    const char* base = tile_base(a.v_pool, i);
+    const int live = i < n_tiles ? 1 : 0;
+#pragma unroll
+    for (int d = 0; d < 8; ++d) {
+      const int r = 2 * d + (lane >> 5);
+      const int rc = min(max(r, lo), hi - 1);
+      const int p = lane & 31;
+      copy16<kWide>(base, extent, row_off(i, rc) + live * 16 * (p ^ ((r & 7) << 1)), buf + d * 1024);
+    }
+  };
+  // e4m3 V: 32-dim granule G of row r is stored at 2048(r / 8) + 256 G +
+  // 32(r % 8).  Copy d fills rows 8(d / 2) .. +7, granules 4(d % 2) .. +3:
+  // lane l takes 16 bytes of row 8(d / 2) + (l / 2) % 8 at byte
+  // 128(d % 2) + 32(l / 16) + 16(l % 2) -- a whole 128-byte piece per row.
+  auto stage_v8 = [&](int i, char* buf) {
+    int lo, hi;
+    visible_rows(i, lo, hi);
+    const char* base = tile_base(a.v_pool, i);
+    const int live = i < n_tiles ? 1 : 0;
+#pragma unroll
+    for (int d = 0; d < 4; ++d) {
+      const int r = 8 * (d >> 1) + ((lane >> 1) & 7);
+      const int rc = min(max(r, lo), hi - 1);
+      copy16<kWide>(base, extent,
+                    row_off(i, rc) + live * (128 * (d & 1) + 32 * (lane >> 4) + 16 * (lane & 1)),
+                    buf + d * 1024);
+    }
+  };
+
+  // ---- LDS -> registers ------------------------------------------------------
+  // K fragments, 16 bytes per piece: bf16, k-step s <- key li, chunk 4s + lg
+  // (dims 32s + 8lg .. +7); e4m3, piece m <- key li, chunk lg + 4m (the dims
+  // of k-steps 2m and 2m + 1, as q is laid out above).
+  struct KFrag {
+    uint4 w[kFp8 ? 4 : 8];
+  };
+  auto read_k = [&](const char* buf, KFrag& kf) {
+#pragma unroll
+    for (int m = 0; m < (kFp8 ? 4 : 8); ++m) {
+      const int c = kFp8 ? lg + 4 * m : 4 * m + lg;
+      kf.w[m] = *reinterpret_cast<const uint4*>(buf + li * kRow + 16 * (c ^ li));
+    }
+  };
+  // bf16 V through ds_read_b64_tr_b16 (within 16 lanes, lane i of the result
+  // gets element i % 4 of source lane 4k + i / 4 in slot k).  Source lane
+  // (li, lg) points at key 4lg + li / 4, dims 16t + 4(li % 4) .. +3: result
+  // lane (li, lg) then holds keys 4lg .. 4lg+3 of dim 16t + li, the B operand
+  // of column tile t.  Offsets of tiles t and t + 8 differ by 256 bytes.
+  const int vrow = 4 * lg + (li >> 2);
+  int voff[8];
+#pragma unroll
+  for (int t8 = 0; t8 < 8; ++t8) voff[t8] = vrow * 512 + 32 * (t8 ^ (vrow & 7)) + 8 * (li & 3);
+  // e4m3 V through ds_read_b64_tr_b8 (within 16 lanes, lane i of the result
+  // gets byte i % 8 of source lane 2k + i / 8 in byte k).  Source lane
+  // (li, lg) points at key 4lg + (li / 2) % 4, 8 bytes at dims
+  // 32p + 16(li / 8) + 8(li % 2): result lane (li, lg) then holds keys
+  // 4lg .. 4lg+3 of dim 32p + li in bytes 0-3 (column tile 2p) and of dim
+  // 32p + 16 + li in bytes 4-7 (tile 2p + 1).  With the staging layout the
+  // eight 32-byte pieces a half wave reads fall in eight different bank
+  // groups, and p only moves the address by 256 p.
+  const int v8row = 4 * lg + ((li >> 1) & 3);
+  const int v8base = 2048 * (v8row >> 3) + 32 * (v8row & 7) + 16 * (li >> 3) + 8 * (li & 1);
 
   f32x4_t o[16];  // O[head 4lg + r][d = 16t + li]
 #pragma unroll
@@ -726,88 +427,8 @@ __device__ __forceinline__ void stage1_mma_body(const Stage1Args& a) {
   float m_ref = -INFINITY;  // reference max (log2 units) of head li
   float l_row = 0.f;        // this lane's share of head li's running sum
 
-  const int n_tiles = (tok_end - tok_begin + kPage - 1) / kPage;
-  const int vis_lo = max(tok_begin, tok_lo);  // first visible token of the split
-  const int first_tile = (vis_lo - tok_begin) / kPage;
-
-  // K of tile i.  bf16: key li, dims 32k + 8lg .. +7 for k-step k (8 x 16 B).
-  // e4m3: 4 x 16 B, bytes 16(lg + 4m) .. +15 of key li (k-steps 2m, 2m + 1).
-  struct KRaw {
-    uint4 w[kFp8 ? 4 : 8];
-  };
-  auto load_k = [&](int i, KRaw& kr) {
-    const char* p = row_ptr(a.k_pool, i, li);
-#pragma unroll
-    for (int k = 0; k < (kFp8 ? 4 : 8); ++k)
-      kr.w[k] = ldg16_stream(p + (kFp8 ? 16 * (lg + 4 * k) : 64 * k + 16 * lg));
-  };
-  // Rows outside the visible range [lo, hi) of a tile copy the nearest
-  // visible row instead (finite data whose probability is exactly 0), so the
-  // V copies need no branches and the compiler's wait counts stay exact.
-  auto visible_rows = [&](int i, int& lo, int& hi) {
-    const int t0 = tok_begin + i * kPage;
-    lo = max(vis_lo, t0) - t0;
-    hi = min(tok_end, t0 + kPage) - t0;
-  };
-  // bf16 V tile i -> LDS: copy d fills rows 2d, 2d + 1 (lane l: row
-  // 2d + l/32, physical chunk l%32 <- logical chunk (l%32) ^ 2(row & 7)).
-  auto stage_v = [&](int i, char* buf) {
-    int lo, hi;
-    visible_rows(i, lo, hi);
-#pragma unroll
-    for (int d = 0; d < 8; ++d) {
-      const int r = 2 * d + (lane >> 5);
-      const int rc = min(max(r, lo), hi - 1);
-      const int p = lane & 31;
-      const char* src = row_ptr(a.v_pool, i, rc) + 16 * (p ^ ((r & 7) << 1));
-      __builtin_amdgcn_global_load_lds(src, (lds_void_t*)(buf + 2 * d * 512), 16, 0, kNt);
-    }
-  };
-  // e4m3 V tile i -> LDS raw (copy d: rows 4d .. 4d + 3, 16 lanes per row).
-  auto stage_v8 = [&](int i, char* raw) {
-    int lo, hi;
-    visible_rows(i, lo, hi);
-#pragma unroll
-    for (int d = 0; d < 4; ++d) {
-      const int r = 4 * d + (lane >> 4);
-      const int rc = min(max(r, lo), hi - 1);
-      const char* src = row_ptr(a.v_pool, i, rc) + 16 * (lane & 15);
-      __builtin_amdgcn_global_load_lds(src, (lds_void_t*)(raw + d * 1024), 16, 0, kNt);
-    }
-  };
-  // raw e4m3 tile -> the swizzled bf16 tile: lane l converts bytes
-  // 64(l%4) .. +63 of row l/4 (logical 16-byte chunks 8(l%4) .. +7)
-  auto convert_v8 = [&](const char* raw, char* buf) {
-    const int r = lane >> 2, q4 = lane & 3;
-    uint4 w[4];
-#pragma unroll
-    for (int k = 0; k < 4; ++k) w[k] = *reinterpret_cast<const uint4*>(raw + r * 256 + 64 * q4 + 16 * k);
-#pragma unroll
-    for (int k = 0; k < 4; ++k) {
-      const uint32_t w4[4] = {w[k].x, w[k].y, w[k].z, w[k].w};
-      uint32_t bf[8];
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        bf[2 * e] = e4m3x2_to_bf16x2<false>(w4[e]);
-        bf[2 * e + 1] = e4m3x2_to_bf16x2<true>(w4[e]);
-      }
-#pragma unroll
-      for (int hh = 0; hh < 2; ++hh) {
-        const int c = 8 * q4 + 2 * k + hh;
-        *reinterpret_cast<uint4*>(buf + r * 512 + 16 * (c ^ ((r & 7) << 1))) =
-            make_uint4(bf[4 * hh], bf[4 * hh + 1], bf[4 * hh + 2], bf[4 * hh + 3]);
-      }
-    }
-  };
-  // transpose-read offsets: source lane (li, lg) reads row 4lg + li/4, 8 bytes
-  // at logical byte 32t + 8(li&3) of the bf16 row -> chunk pair t ^ (row & 7)
-  const int vrow = 4 * lg + (li >> 2);
-  int voff[8];
-#pragma unroll
-  for (int t8 = 0; t8 < 8; ++t8) voff[t8] = vrow * 512 + 32 * (t8 ^ (vrow & 7)) + 8 * (li & 3);
-
   // ---- S^T = K Q^T of one tile ----------------------------------------------
-  auto scores = [&](const KRaw& kr) {
+  auto scores = [&](const KFrag& kr) {
     bf16x8_t kf[8];
     if constexpr (kFp8) {
 #pragma unroll
@@ -883,97 +504,117 @@ __device__ __forceinline__ void stage1_mma_body(const Stage1Args& a) {
     const uint32_t l23 = pk_bf16(p[2] - bf16_lo(h23), p[3] - bf16_hi(h23));
     const s16x4_t ph = __builtin_bit_cast(s16x4_t, make_uint2(h01, h23));
     const s16x4_t pl = __builtin_bit_cast(s16x4_t, make_uint2(l01, l23));
+    if constexpr (kFp8) {
 #pragma unroll
-    for (int tg = 0; tg < 4; ++tg) {
-      s16x4_t vf[4];
+      for (int half = 0; half < 2; ++half) {
+        uint2 w[4];
 #pragma unroll
-      for (int u = 0; u < 4; ++u) {
-        const int t = 4 * tg + u;
-        vf[u] = lds_tr_read(vbuf + voff[t & 7] + 256 * (t >> 3));
+        for (int u = 0; u < 4; ++u) {
+          const i32x2_t r = __builtin_amdgcn_ds_read_tr8_b64_v2i32(
+              (lds_i32x2_t*)(vbuf + v8base + 256 * (4 * half + u)));
+          w[u] = make_uint2((uint32_t)r[0], (uint32_t)r[1]);
+        }
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+          const int t = 2 * (4 * half + u);  // column tiles t, t + 1
+          const s16x4_t v0 = __builtin_bit_cast(
+              s16x4_t, make_uint2(e4m3x2_to_bf16x2<false>(w[u].x), e4m3x2_to_bf16x2<true>(w[u].x)));
+          const s16x4_t v1 = __builtin_bit_cast(
+              s16x4_t, make_uint2(e4m3x2_to_bf16x2<false>(w[u].y), e4m3x2_to_bf16x2<true>(w[u].y)));
+          o[t] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(ph, v0, o[t], 0, 0, 0);
+          o[t + 1] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(ph, v1, o[t + 1], 0, 0, 0);
+          o[t] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(pl, v0, o[t], 0, 0, 0);
+          o[t + 1] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(pl, v1, o[t + 1], 0, 0, 0);
+        }
       }
+    } else {
 #pragma unroll
-      for (int u = 0; u < 4; ++u)
-        o[4 * tg + u] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(ph, vf[u], o[4 * tg + u], 0, 0, 0);
+      for (int tg = 0; tg < 4; ++tg) {
+        s16x4_t vf[4];
 #pragma unroll
-      for (int u = 0; u < 4; ++u)
-        o[4 * tg + u] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(pl, vf[u], o[4 * tg + u], 0, 0, 0);
+        for (int u = 0; u < 4; ++u) {
+          const int t = 4 * tg + u;
+          vf[u] = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+              (lds_s16x4_t*)(vbuf + voff[t & 7] + 256 * (t >> 3)));
+        }
+#pragma unroll
+        for (int u = 0; u < 4; ++u)
+          o[4 * tg + u] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(ph, vf[u], o[4 * tg + u], 0, 0, 0);
+#pragma unroll
+        for (int u = 0; u < 4; ++u)
+          o[4 * tg + u] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(pl, vf[u], o[4 * tg + u], 0, 0, 0);
+      }
     }
   };
 
-  // One K register set per tile in flight: the next tile's K is requested as
-  // soon as this tile's score MFMAs have read its registers.  bf16 V tiles
-  // alternate between two buffers filled by direct copies (two tiles in
-  // flight); e4m3 tiles are half the bytes, so their loop keeps two K sets
-  // and two raw V tiles in flight and converts each raw tile just before its
-  // P V.  The loops are unrolled twice so every buffer is named statically.
-  char* bufA = vA[wave];
-  char* bufB = vB[wave];
-  char* bufC = vC[wave];
   int i = first_tile + wave;
   if (i < n_tiles) {
-    KRaw kr;
-    load_k(i, kr);
+    KFrag kf;
     if constexpr (kFp8) {
-      KRaw kr2;
-      stage_v8(i, bufB);
-      if (i + kWaves < n_tiles) {
-        load_k(i + kWaves, kr2);
-        stage_v8(i + kWaves, bufC);
-      }
+      // double-buffered: the next tile's K and V are requested before this
+      // tile's K fragments are read; unrolled twice so every tile is named
+      // statically
+      char* const kA = tC[wave];
+      char* const kB = tD[wave];
+      char* const vA = tA[wave];
+      char* const vB = tB[wave];
+      stage_k(i, kA);
+      stage_v8(i, vA);
       for (;;) {
-        f32x4_t st = scores(kr);
-        convert_v8(bufB, bufA);
+        lds_reads_done();
+        stage_k(i + kWaves, kB);
+        stage_v8(i + kWaves, vB);
+        read_k(kA, kf);
+        const f32x4_t st = scores(kf);
         __builtin_amdgcn_sched_barrier(0);
-        if (i + 2 * kWaves < n_tiles) {
-          load_k(i + 2 * kWaves, kr);
-          stage_v8(i + 2 * kWaves, bufB);
-        }
-        softmax_pv(i, st, bufA);
+        softmax_pv(i, st, vA);
         i += kWaves;
         if (i >= n_tiles) break;
-        st = scores(kr2);
-        convert_v8(bufC, bufA);
+        lds_reads_done();
+        stage_k(i + kWaves, kA);
+        stage_v8(i + kWaves, vA);
+        read_k(kB, kf);
+        const f32x4_t st2 = scores(kf);
         __builtin_amdgcn_sched_barrier(0);
-        if (i + 2 * kWaves < n_tiles) {
-          load_k(i + 2 * kWaves, kr2);
-          stage_v8(i + 2 * kWaves, bufC);
-        }
-        softmax_pv(i, st, bufA);
+        softmax_pv(i, st2, vB);
         i += kWaves;
         if (i >= n_tiles) break;
       }
     } else {
-      stage_v(i, bufA);
+      // single-buffered (two bf16 tiles per wave fill the LDS): the next K
+      // is requested once this tile's fragments are in registers, the next V
+      // once P V has read this tile's
+      char* const kbuf = tB[wave];
+      char* const vbuf = tA[wave];
+      stage_k(i, kbuf);
+      stage_v(i, vbuf);
       for (;;) {
-        f32x4_t st = scores(kr);
+        read_k(kbuf, kf);
+        lds_reads_done();
+        stage_k(i + kWaves, kbuf);
+        const f32x4_t st = scores(kf);
         __builtin_amdgcn_sched_barrier(0);
-        if (i + kWaves < n_tiles) {
-          load_k(i + kWaves, kr);
-          stage_v(i + kWaves, bufB);
-        }
-        softmax_pv(i, st, bufA);
-        i += kWaves;
-        if (i >= n_tiles) break;
-        st = scores(kr);
+        softmax_pv(i, st, vbuf);
         __builtin_amdgcn_sched_barrier(0);
-        if (i + kWaves < n_tiles) {
-          load_k(i + kWaves, kr);
-          stage_v(i + kWaves, bufA);
-        }
-        softmax_pv(i, st, bufB);
+        lds_reads_done();
+        stage_v(i + kWaves, vbuf);
         i += kWaves;
         if (i >= n_tiles) break;
       }
     }
+    // the last requests (past the end) may still be writing a tile
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
   }
 
   // ---- merge the waves' states and write the split's partial ---------------
   // Each wave's O goes to its own LDS tiles as fp32 [head][256]: heads 0-7 in
-  // vA, 8-15 in vB (bf16 pools) or 8-11 in vB and 12-15 in vC (e4m3 pools).
+  // tA and 8-15 in tB (bf16 pools), four heads in each of tA .. tD (e4m3).
   auto o_row = [&](int w, int hh) -> float* {
-    if (hh < 8) return reinterpret_cast<float*>(vA[w]) + hh * kD;
-    if (!kFp8 || hh < 12) return reinterpret_cast<float*>(vB[w]) + (hh - 8) * kD;
-    return reinterpret_cast<float*>(vC[w]) + (hh - 12) * kD;
+    if constexpr (kFp8) {
+      char* const t[4] = {tA[w], tB[w], tC[w], tD[w]};
+      return reinterpret_cast<float*>(t[hh >> 2]) + (hh & 3) * kD;
+    }
+    return reinterpret_cast<float*>(hh < 8 ? tA[w] : tB[w]) + (hh & 7) * kD;
   };
   l_row += shfl_xor(l_row, 16);  // the head's four lanes hold disjoint keys
   l_row += shfl_xor(l_row, 32);
@@ -1016,23 +657,19 @@ __device__ __forceinline__ void stage1_mma_body(const Stage1Args& a) {
 }
 
 __global__ __launch_bounds__(512, 1) void decode_stage1_kernel(Stage1Args a) {
-  stage1_valu_body<false>(a);
+  stage1_body<false, false, false>(a);
+}
+
+__global__ __launch_bounds__(512, 1) void decode_stage1_fp8_kernel(Stage1Args a) {
+  stage1_body<true, false, false>(a);
 }
 
 __global__ __launch_bounds__(512, 1) void decode_stage1_tok_kernel(Stage1Args a) {
-  stage1_valu_body<true>(a);
+  stage1_body<false, true, false>(a);
 }
 
-__global__ __launch_bounds__(512, 1) void decode_stage1_mma_kernel(Stage1Args a) {
-  stage1_mma_body<false, false>(a);
-}
-
-__global__ __launch_bounds__(512, 1) void decode_stage1_mma_fp8_kernel(Stage1Args a) {
-  stage1_mma_body<true, false>(a);
-}
-
-__global__ __launch_bounds__(512, 1) void decode_stage1_mma_tok_kernel(Stage1Args a) {
-  stage1_mma_body<false, true>(a);
+__global__ __launch_bounds__(512, 1) void decode_stage1_tok_wide_kernel(Stage1Args a) {
+  stage1_body<false, true, true>(a);
 }
 
 struct Stage2Args {
@@ -1141,23 +778,16 @@ __global__ __launch_bounds__(256) void decode_stage2_gate_kernel(Stage2Args a) {
   *reinterpret_cast<uint2*>(a.out + (size_t)row * kD + lane * 4) = w;
 }
 
-// Which stage 1 runs.  The MFMA body serves e4m3 pools (its conversions cost
-// a fraction of the VALU body's), groups of more than 8 heads (one workgroup
-// reads the K/V once for all 16 MFMA columns), and short capacities (splits
-// under 1,024 tokens: latency-bound, where its shorter per-tile chain wins).
-// The VALU body streams long bf16 sequences of groups up to 8 about 3% faster
-// (measured at B=64, L=4096 with inputs rotated so no call finds the previous
-// one's rows in the Infinity Cache: 91.9 vs 95.1 us per call).
-// The environment variable GATED_ATTN_DECODE_STAGE1 = "mma" or "valu" forces
-// one body where both apply (tests run every case through each).
-bool use_mma_stage1(const DecodeLaunch& d) {
-  const int group = d.num_q_heads / d.num_kv_heads;
-  if (d.kv_fp8 || group > kGroup) return true;  // the VALU body takes neither
-  if (const char* e = std::getenv("GATED_ATTN_DECODE_STAGE1")) {
-    if (std::strcmp(e, "mma") == 0) return true;
-    if (std::strcmp(e, "valu") == 0) return false;
-  }
-  return d.tokens_per_split < 1024;
+// Page size 1: the copies address a token's row by a 32-bit offset from the
+// pool's start unless the pool's rows span more bytes than that (or the
+// environment variable GATED_ATTN_DECODE_WIDE is "1", which forces the 64-bit
+// address form for testing it on small pools).
+bool wide_offsets(const DecodeLaunch& d) {
+  const unsigned long long bytes =
+      (unsigned long long)d.num_pages * d.num_kv_heads * kD * (d.kv_fp8 ? 1 : 2);
+  if (bytes > 0xffffffffull) return true;
+  const char* e = std::getenv("GATED_ATTN_DECODE_WIDE");
+  return e != nullptr && std::strcmp(e, "1") == 0;
 }
 
 hipError_t launch_decode(const DecodeLaunch& d, hipStream_t stream) {
@@ -1190,18 +820,14 @@ hipError_t launch_decode(const DecodeLaunch& d, hipStream_t stream) {
     if (err != hipSuccess) return err;
   }
   const dim3 block(kWaves * 64);
-  if (use_mma_stage1(d)) {
-    if (d.kv_fp8)
-      hipLaunchKernelGGL(decode_stage1_mma_fp8_kernel, grid1, block, 0, stream, a1);
-    else if (d.page_size == 1)
-      hipLaunchKernelGGL(decode_stage1_mma_tok_kernel, grid1, block, 0, stream, a1);
-    else
-      hipLaunchKernelGGL(decode_stage1_mma_kernel, grid1, block, 0, stream, a1);
-  } else if (d.page_size == 1) {
+  if (d.kv_fp8)
+    hipLaunchKernelGGL(decode_stage1_fp8_kernel, grid1, block, 0, stream, a1);
+  else if (d.page_size == 1 && wide_offsets(d))
+    hipLaunchKernelGGL(decode_stage1_tok_wide_kernel, grid1, block, 0, stream, a1);
+  else if (d.page_size == 1)
     hipLaunchKernelGGL(decode_stage1_tok_kernel, grid1, block, 0, stream, a1);
-  } else {
+  else
     hipLaunchKernelGGL(decode_stage1_kernel, grid1, block, 0, stream, a1);
-  }
   err = hipGetLastError();
   if (err != hipSuccess) return err;
   if (d.stage1_stop != nullptr) {

@@ -70,14 +70,8 @@ __device__ __forceinline__ uint16_t gate_output(uint16_t ob, uint16_t gate) {
 }
 
 // ---------------------------------------------------------------------------
-// dot products and reductions
+// wave-level reductions
 // ---------------------------------------------------------------------------
-// acc + a.lo*b.lo + a.hi*b.hi on packed bf16 pairs, fp32 accumulate.
-__device__ __forceinline__ float dot2_bf16(uint32_t a, uint32_t b, float acc) {
-  return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, a),
-                                         __builtin_bit_cast(bf16x2_t, b), acc, false);
-}
-
 template <int CTRL>
 __device__ __forceinline__ float dpp(float v) {
   return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), CTRL, 0xf, 0xf, true));
@@ -100,48 +94,9 @@ __device__ __forceinline__ float sum16(float v) {
   return v;
 }
 
-// Reduce-scatter of 8 per-lane partial sums over an aligned group of 16 lanes
-// (c16 = lane % 16): afterwards lane c16 holds the complete sum of entry
-// c16 >> 1 (the two lanes c16 = 2h, 2h + 1 both hold entry h).  Three halving
-// rounds pair lane i with 15 - i (row mirror: splits entries 0-3 / 4-7 by bit
-// 3), with 7 - i inside each half-row (bit 2) and with i ^ 3 inside each quad
-// (bit 1); each lane keeps the half it owns and adds the partner's copy of it.
-// A last round sums the two lanes of a pair.  22 VALU operations instead of
-// the 32 of eight separate all-reduces, and no select of the lane's entry.
-constexpr int kDppQuadReverse = 0x1b;  // quad_perm [3,2,1,0]
-
-__device__ __forceinline__ float reduce_scatter8(const float (&x)[8], int c16) {
-  const bool b3 = (c16 & 8) != 0, b2 = (c16 & 4) != 0, b1 = (c16 & 2) != 0;
-  float y[4];
-#pragma unroll
-  for (int k = 0; k < 4; ++k) {
-    const float keep = b3 ? x[k + 4] : x[k];
-    const float send = b3 ? x[k] : x[k + 4];
-    y[k] = keep + dpp<kDppMirror>(send);
-  }
-  float z[2];
-#pragma unroll
-  for (int k = 0; k < 2; ++k) {
-    const float keep = b2 ? y[k + 2] : y[k];
-    const float send = b2 ? y[k] : y[k + 2];
-    z[k] = keep + dpp<kDppHalfMirror>(send);
-  }
-  const float keep = b1 ? z[1] : z[0];
-  const float send = b1 ? z[0] : z[1];
-  float w = keep + dpp<kDppQuadReverse>(send);
-  return w + dpp<kDppXor1>(w);
-}
-
 __device__ __forceinline__ float shfl_xor(float v, int mask) {
   int lane = __lane_id();
   return __int_as_float(__builtin_amdgcn_ds_bpermute((lane ^ mask) << 2, __float_as_int(v)));
-}
-
-// Orders this wave's LDS writes before its later LDS reads of other lanes' data.
-__device__ __forceinline__ void wave_lds_sync() {
-  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-  __builtin_amdgcn_wave_barrier();
-  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
 }
 
 }  // namespace ga

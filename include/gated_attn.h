@@ -96,10 +96,11 @@ size_t gated_attn_decode_workspace_size(const ga_decode_dims *dims);
  * (FreeToken PR #781, Summary: stage1, then a stage2 fp32 reduction) followed,
  * in the same second kernel, by the bf16 rounding of O, the bf16 sigmoid of the
  * gate and the rounded product -- two kernel launches per call, none of them
- * for the gate.  The first launch runs one of two stage-1 kernels, chosen from
- * the dims (results agree to the documented tolerance either way); setting the
- * environment variable GATED_ATTN_DECODE_STAGE1 to "mma" or "valu" forces one
- * where both apply (testing and tuning).
+ * for the gate.  At page size 1 the first launch addresses token rows by
+ * 32-bit offsets from the pool's start, or by 64-bit addresses when the pool's
+ * rows span more than 4 GiB; setting the environment variable
+ * GATED_ATTN_DECODE_WIDE to "1" forces the 64-bit form (testing; the results
+ * are identical either way).
  *
  *   q, gate     [B][H_q][D]                       bf16, read
  *   k_pool,

@@ -14,15 +14,16 @@ def pytest_configure(config):
 import pytest  # noqa: E402
 
 
-@pytest.fixture(params=["mma", "valu"])
-def decode_stage1(request):
-    """Runs a decode test through each stage-1 body (the library reads
-    GATED_ATTN_DECODE_STAGE1 at every launch; e4m3 pools and groups above 8
-    always take the MFMA body)."""
-    old = os.environ.get("GATED_ATTN_DECODE_STAGE1")
-    os.environ["GATED_ATTN_DECODE_STAGE1"] = request.param
+@pytest.fixture(params=["offset32", "wide"])
+def page1_copies(request):
+    """Runs a page-size-1 decode test through both forms of the stage-1
+    copies: 32-bit offsets from the pool's start (what small pools get) and
+    64-bit addresses (what pools of more than 4 GiB of rows get; the library
+    reads GATED_ATTN_DECODE_WIDE at every launch)."""
+    old = os.environ.get("GATED_ATTN_DECODE_WIDE")
+    os.environ["GATED_ATTN_DECODE_WIDE"] = "1" if request.param == "wide" else "0"
     yield request.param
     if old is None:
-        os.environ.pop("GATED_ATTN_DECODE_STAGE1", None)
+        os.environ.pop("GATED_ATTN_DECODE_WIDE", None)
     else:
-        os.environ["GATED_ATTN_DECODE_STAGE1"] = old
+        os.environ["GATED_ATTN_DECODE_WIDE"] = old

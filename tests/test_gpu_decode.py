@@ -15,7 +15,7 @@ from gpu_helpers import DEV, decode_parity, gpu_decode, to_dev, to_np
 
 import gated_gqa_decode_amd as ga
 
-pytestmark = [pytest.mark.gpu, pytest.mark.usefixtures("decode_stage1")]
+pytestmark = pytest.mark.gpu
 
 
 @pytest.mark.parametrize("wl", [0, 1, 2, 3])

@@ -56,7 +56,6 @@ def _decode_case_parity(c, sinks=None, window=0):
 
 @pytest.mark.parametrize("window", [0, 1, 7, 16, 100, 1000, 2049])
 @pytest.mark.parametrize("with_sinks", [False, True])
-@pytest.mark.usefixtures("decode_stage1")
 def test_decode_window_sinks_lse(window, with_sinks):
     """Windows below, at and across step (8), page (16) and split boundaries,
     over ragged lengths (0 = padded slot) and a long row spanning splits."""
@@ -69,7 +68,6 @@ def test_decode_window_sinks_lse(window, with_sinks):
     _decode_case_parity(c, sinks, window)
 
 
-@pytest.mark.usefixtures("decode_stage1")
 def test_decode_sinks_dominating_and_negligible():
     """Sinks far above every score (O -> 0 but not underflowing to a wrong
     value) and far below (no effect)."""
@@ -79,7 +77,6 @@ def test_decode_sinks_dominating_and_negligible():
     _decode_case_parity(c, sinks, 0)
 
 
-@pytest.mark.usefixtures("decode_stage1")
 def test_decode_options_group16_and_group6():
     for hq in (32, 12):
         c = workloads.make_decode(f"spec_hq{hq}", [2000, 9, 0, 700], seed=96 + hq,
@@ -88,7 +85,6 @@ def test_decode_options_group16_and_group6():
         _decode_case_parity(c, sinks, 333)
 
 
-@pytest.mark.usefixtures("decode_stage1")
 def test_decode_options_full_size():
     """B = 64, L = 4096 with a 1000-token window, sinks and lse."""
     c = workloads.make_decode("decode_b64_l4096_spec", [4096] * 64, seed=97,
@@ -97,7 +93,6 @@ def test_decode_options_full_size():
     _decode_case_parity(c, sinks, 1000)
 
 
-@pytest.mark.usefixtures("decode_stage1")
 def test_decode_plain_entry_matches_ex_with_zero_options():
     c = workloads.make_decode("plain_vs_ex", [700, 33, 0], seed=98, max_pages_per_seq=64)
     args = [to_dev(x) for x in (c.q, c.gate, c.k_pool, c.v_pool, c.block_table, c.seq_lens)]
