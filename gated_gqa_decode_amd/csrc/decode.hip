@@ -23,8 +23,8 @@
 //       head; idle columns are zero).  Each lane then holds head li's scores
 //       of keys 4lg .. 4lg+3 -- already the A layout of P for P V.
 //   online softmax per head in fp32 (lazy rescaling against a reference max);
-//   P = Phi + Plo, two bf16 terms (~16 significant bits of the fp32 weight);
-//   O (16 heads x 256) += P V, 16 column tiles x 2 MFMAs 16x16x16.  V needs
+//   P = Phi + Pmid + Plo, three bf16 terms holding the fp32 weight exactly;
+//   O (16 heads x 256) += P V, 16 column tiles x 3 MFMAs 16x16x16.  V needs
 //       keys along k while rows are stored dims-first: gfx950's transposing
 //       LDS reads (ds_read_b64_tr_b16, ds_read_b64_tr_b8) deliver it.
 // Both K and V reach LDS by direct copies that read whole rows (every copy
@@ -498,11 +498,18 @@ __device__ __forceinline__ void stage1_body(const Stage1Args& a) {
       p[r] = __builtin_amdgcn_exp2f(sv[r] - mref_safe);
       l_row += p[r];
     }
-    // p = hi + lo, both bf16; the row sum takes p itself
+    // p = hi + mid + lo, three bf16 terms that hold the fp32 weight exactly
+    // (each remainder is exact in fp32 and the last one fits bf16's 8 bits;
+    // checked for every weight above 2^-100 -- smaller ones lie below any
+    // output's resolution); the row sum takes p itself
     const uint32_t h01 = pk_bf16(p[0], p[1]), h23 = pk_bf16(p[2], p[3]);
-    const uint32_t l01 = pk_bf16(p[0] - bf16_lo(h01), p[1] - bf16_hi(h01));
-    const uint32_t l23 = pk_bf16(p[2] - bf16_lo(h23), p[3] - bf16_hi(h23));
+    const float r0 = p[0] - bf16_lo(h01), r1 = p[1] - bf16_hi(h01);
+    const float r2 = p[2] - bf16_lo(h23), r3 = p[3] - bf16_hi(h23);
+    const uint32_t m01 = pk_bf16(r0, r1), m23 = pk_bf16(r2, r3);
+    const uint32_t l01 = pk_bf16(r0 - bf16_lo(m01), r1 - bf16_hi(m01));
+    const uint32_t l23 = pk_bf16(r2 - bf16_lo(m23), r3 - bf16_hi(m23));
     const s16x4_t ph = __builtin_bit_cast(s16x4_t, make_uint2(h01, h23));
+    const s16x4_t pm = __builtin_bit_cast(s16x4_t, make_uint2(m01, m23));
     const s16x4_t pl = __builtin_bit_cast(s16x4_t, make_uint2(l01, l23));
     if constexpr (kFp8) {
 #pragma unroll
@@ -523,6 +530,8 @@ __device__ __forceinline__ void stage1_body(const Stage1Args& a) {
               s16x4_t, make_uint2(e4m3x2_to_bf16x2<false>(w[u].y), e4m3x2_to_bf16x2<true>(w[u].y)));
           o[t] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(ph, v0, o[t], 0, 0, 0);
           o[t + 1] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(ph, v1, o[t + 1], 0, 0, 0);
+          o[t] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(pm, v0, o[t], 0, 0, 0);
+          o[t + 1] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(pm, v1, o[t + 1], 0, 0, 0);
           o[t] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(pl, v0, o[t], 0, 0, 0);
           o[t + 1] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(pl, v1, o[t + 1], 0, 0, 0);
         }
@@ -540,6 +549,9 @@ __device__ __forceinline__ void stage1_body(const Stage1Args& a) {
 #pragma unroll
         for (int u = 0; u < 4; ++u)
           o[4 * tg + u] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(ph, vf[u], o[4 * tg + u], 0, 0, 0);
+#pragma unroll
+        for (int u = 0; u < 4; ++u)
+          o[4 * tg + u] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(pm, vf[u], o[4 * tg + u], 0, 0, 0);
 #pragma unroll
         for (int u = 0; u < 4; ++u)
           o[4 * tg + u] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(pl, vf[u], o[4 * tg + u], 0, 0, 0);
