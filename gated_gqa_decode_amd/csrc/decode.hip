@@ -55,8 +55,8 @@ constexpr int kD = 256;          // head dim
 constexpr int kHeads = 16;       // query-head columns of a stage-1 workgroup
 constexpr int kPage = 16;        // tokens per page = keys per tile
 constexpr int kWaves = 8;        // waves per stage-1 workgroup (one workgroup per CU)
-constexpr int kPageRegs = 2;     // page ids per lane: a split spans at most 128 pages
-constexpr int kMaxSplit = 2048;  // tokens of the largest split
+constexpr int kPageRegs = 2;     // page ids per lane: a wave copies at most 128 tiles of a split
+constexpr int kMaxTokSplit = 2048;  // tokens of the largest split at page size 1 (slots in LDS)
 constexpr int kMinSplit = 64;    // tokens of the smallest split a sizing rule asks for
 constexpr int kTileBytes = kPage * kD * 2;  // one bf16 K or V tile in LDS
 constexpr float kLog2e = 1.4426950408889634f;
@@ -211,7 +211,7 @@ __device__ __forceinline__ void stage1_body(const Stage1Args& a) {
   __shared__ __align__(16) char tC[kWaves][kFp8 ? kTile : 16];
   __shared__ __align__(16) char tD[kWaves][kFp8 ? kTile : 16];
   __shared__ float m_w[kWaves][kHeads], l_w[kWaves][kHeads];
-  __shared__ __align__(16) int tok_ids[kTok ? kMaxSplit : 4];  // page size 1: the split's token slots
+  __shared__ __align__(16) int tok_ids[kTok ? kMaxTokSplit : 4];  // page size 1: the split's token slots
 
   // Workgroup id -> (split s, sequence b, kv head g).  Ids are dispatched in
   // order, round-robin over the 8 XCDs; units are split-major (every
@@ -232,21 +232,25 @@ __device__ __forceinline__ void stage1_body(const Stage1Args& a) {
   const int h0 = g * nh;              // first query head of the group
   const int li = lane & 15, lg = lane >> 4;
 
-  // Issued together, before the length is known: the page ids of split s as
-  // it is when the sequence fills its capacity (page j of the split in lane
-  // j % 64 of register j / 64; ids past the sequence's end are never used),
-  // the length, and q.  Other lengths reload the page ids below.
+  // Issued together, before the length is known: the page ids of the tiles
+  // this wave copies when the sequence fills its capacity (its k-th tile,
+  // tile wave + 8k of split s, in lane k % 64 of register k / 64; ids past
+  // the sequence's end are never used), the length, and q.  Other lengths and
+  // windows reload the page ids below.  load_pages(fp, np): the split's
+  // tiles from page fp on, np of them.
   const int32_t* bt_row = a.block_table + (size_t)b * a.max_pages;
-  auto load_pages = [&](int tok_first, int ntok, int (&pages)[kPageRegs]) {
-    const int fp = tok_first / kPage;
-    const int np = min(ntok / kPage, a.max_pages - fp);
+  auto load_pages = [&](int fp, int np, int (&pages)[kPageRegs]) {
 #pragma unroll
-    for (int r = 0; r < kPageRegs; ++r)
-      pages[r] = lane + 64 * r < np ? bt_row[fp + lane + 64 * r] : 0;
+    for (int r = 0; r < kPageRegs; ++r) {
+      const int j = wave + 8 * (lane + 64 * r);
+      pages[r] = j < np ? bt_row[fp + j] : 0;
+    }
   };
   int my_page[kPageRegs] = {0, 0};
   const int full_begin = s * a.tokens_per_split;  // < capacity, since s < num_splits
-  if constexpr (!kTok) load_pages(full_begin, a.tokens_per_split, my_page);
+  if constexpr (!kTok)
+    load_pages(full_begin / kPage, min(a.tokens_per_split / kPage, a.max_pages - full_begin / kPage),
+               my_page);
 
   // q, the B operand of K Q^T: lane (li, lg) holds head li's dims of k-step k
   // -- bf16 pools: 32k + 8lg .. +7; e4m3 pools: k = 2m + e covers
@@ -276,9 +280,11 @@ __device__ __forceinline__ void stage1_body(const Stage1Args& a) {
   if (s >= sr.count) return;  // empty split: stage 2 never reads its slot
   const int tok_begin = sr.base + s * sr.tokens;
   const int tok_end = min(L, tok_begin + sr.tokens);
-  const int first_page = tok_begin / kPage;
+  const int n_tiles = (tok_end - tok_begin + kPage - 1) / kPage;
+  const int vis_lo = max(tok_begin, tok_lo);  // first visible token of the split
+  const int first_tile = (vis_lo - tok_begin) / kPage;
   if constexpr (kTok) {
-    // one slot per token: the split's slots go to LDS (at most kMaxSplit)
+    // one slot per token: the split's slots go to LDS (at most kMaxTokSplit)
     const int32_t* ids = a.kv_indptr != nullptr ? a.kv_indices + first_index : bt_row;
     for (int i = threadIdx.x; i < sr.tokens; i += kWaves * 64) {
       const int tok = tok_begin + i;
@@ -287,15 +293,14 @@ __device__ __forceinline__ void stage1_body(const Stage1Args& a) {
     }
     __syncthreads();
   } else {
-    if (tok_begin != full_begin) load_pages(tok_begin, sr.tokens, my_page);
+    if (tok_begin != full_begin || first_tile != 0)
+      load_pages(tok_begin / kPage + first_tile, n_tiles - first_tile, my_page);
 #pragma unroll
     for (int r = 0; r < kPageRegs; ++r)
       my_page[r] = (int)min((long long)max(my_page[r], 0), a.num_pages - 1);
   }
-
-  const int n_tiles = (tok_end - tok_begin + kPage - 1) / kPage;
-  const int vis_lo = max(tok_begin, tok_lo);  // first visible token of the split
-  const int first_tile = (vis_lo - tok_begin) / kPage;
+  // this wave's last tile index k (its tiles are first_tile + wave + 8k)
+  const int k_last = (n_tiles - 1 - first_tile - wave) >> 3;
 
   constexpr int kElem = kFp8 ? 1 : 2;  // bytes per pool element
   constexpr int kRow = kD * kElem;     // bytes of one head's row
@@ -307,15 +312,16 @@ __device__ __forceinline__ void stage1_body(const Stage1Args& a) {
   const uint32_t extent = kTok ? (uint32_t)min((size_t)a.num_pages * row_bytes - head_bytes,
                                                (size_t)0xffffffffu)
                                : (uint32_t)(page_bytes - head_bytes);
-  // Tile i's rows in a pool.  The loops request the next tile unconditionally
-  // (so the compiler's wait counts stay exact); for a tile past the split's
-  // last one every lane reads the first 16 bytes of the last tile instead.
+  // Tile i's rows in a pool (i is one of this wave's tiles).  The loops
+  // request the next tile unconditionally (so the compiler's wait counts stay
+  // exact); for a tile past the split's end every lane reads the first 16
+  // bytes of the wave's last tile instead.
   auto tile_base = [&](const char* pool, int i) -> const char* {
     if constexpr (kTok) {
       return pool + head_bytes;
     } else {
-      const int j = (tok_begin / kPage + min(i, n_tiles - 1)) - first_page;  // wave-uniform, < 128
-      const int pg = __builtin_amdgcn_readlane(j < 64 ? my_page[0] : my_page[1], j & 63);
+      const int k = min((i - first_tile - wave) >> 3, k_last);  // wave-uniform, < 128
+      const int pg = __builtin_amdgcn_readlane(k < 64 ? my_page[0] : my_page[1], k & 63);
       return pool + (size_t)pg * page_bytes + head_bytes;
     }
   };

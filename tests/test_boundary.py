@@ -50,7 +50,8 @@ def _dims(**kw):
 def test_plan_covers_capacity(B, W):
     p = ga.decode_plan(_dims(batch=B, max_pages_per_seq=W))
     cap = W * 16
-    assert p.tokens_per_split % 64 == 0 and 64 <= p.tokens_per_split <= 2048
+    t_max = 16384 if B * 2 < 256 else 2048
+    assert p.tokens_per_split % 64 == 0 and 64 <= p.tokens_per_split <= t_max
     assert p.num_splits * p.tokens_per_split >= cap
     assert (p.num_splits - 1) * p.tokens_per_split < cap
     rows = B * 16 * p.num_splits
@@ -60,16 +61,31 @@ def test_plan_covers_capacity(B, W):
 
 @pytest.mark.parametrize("G", [1, 2, 3, 4, 5, 6, 7, 8, 10, 12, 14, 16])
 def test_supported_groups_plan(G):
-    """Groups up to 8 use one workgroup per (sequence, kv head, split); even
-    groups of 10..16 use two, which the split plan counts."""
+    """Every group size uses one workgroup per (sequence, kv head, split): the
+    split plan does not depend on the group."""
     d = _dims(batch=64, num_q_heads=2 * G, num_kv_heads=2, max_pages_per_seq=256)
     p = ga.decode_plan(d)
-    parts = 2 if G > 8 else 1
-    units = 64 * 2 * parts
+    units = 64 * 2
     t = -(-(4096 * units) // 256)
-    t = min(max(-(-t // 64) * 64, 64), 2048)
+    t = min(max(-(-t // 64) * 64, 64), 16384)
     assert p.tokens_per_split == t
     assert p.workspace_bytes >= 64 * 2 * G * p.num_splits * 258 * 4
+
+
+@pytest.mark.parametrize("B,Hkv,W,page,t_want,ns_want", [
+    (64, 2, 2048, 16, 16384, 2),   # 128 pairs, capacity 32,768: two long splits
+    (128, 2, 2048, 16, 2048, 16),  # 256 pairs: splits of at most 2,048 tokens
+    (224, 2, 384, 16, 2048, 3),    # the serving shape
+    (64, 2, 32768, 1, 2048, 16),   # page size 1: the token slots of a split fit LDS
+    (1, 2, 2048, 16, 256, 128),    # one sequence: about 256 workgroups
+])
+def test_split_cap(B, Hkv, W, page, t_want, ns_want):
+    """The largest split: 16,384 tokens with 16-token pages while the
+    (sequence, kv head) pairs are fewer than the 256 target workgroups, else
+    2,048 (and always 2,048 at page size 1)."""
+    p = ga.decode_plan(_dims(batch=B, num_q_heads=8 * Hkv, num_kv_heads=Hkv, page_size=page,
+                             max_pages_per_seq=W, num_pages=max(16384, W)))
+    assert (p.tokens_per_split, p.num_splits) == (t_want, ns_want)
 
 
 def test_oversize_stage1_grid_is_declined():

@@ -57,12 +57,13 @@ def test_ragged_lengths_across_steps_pages_and_splits():
 
 
 def test_long_sequences_largest_split():
-    """Capacity 32768 tokens at batch 64 gives the largest split (2048 tokens,
-    128 pages per workgroup, so page ids sit in both per-lane registers)."""
+    """Capacity 32768 tokens at batch 64 gives the largest split (16,384
+    tokens: each wave copies 128 tiles, so its page ids fill both per-lane
+    registers); the short sequences run as few splits of their own size."""
     lens = [32768, 1, 1025, 32767, 0, 4096] + [17] * 58
     c = workloads.make_decode("long", lens, seed=32, max_pages_per_seq=2048)
     plan = ga.decode_plan(ga.decode_dims(**c.dims))
-    assert plan.tokens_per_split == 2048
+    assert (plan.tokens_per_split, plan.num_splits) == (16384, 2)
     res = decode_parity(c)
     assert res["ok"], res
 
