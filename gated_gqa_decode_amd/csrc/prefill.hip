@@ -398,15 +398,23 @@ __global__ __launch_bounds__(kThreads) void prefill_gate_kernel(PrefillArgs a) {
       den = fmaf(lr, f, __builtin_amdgcn_exp2f(sink2 - mtot));
     }
     const size_t rowoff = (((size_t)b * S + qr) * Hq + h) * kD;
+    // The gate: the fast sigmoid for all 16 elements (no branches), then the
+    // fp64 evaluation for the rare ones it cannot decide.
+    uint16_t ob[16], gt[16];
+    uint32_t slow = 0;
 #pragma unroll
     for (int t = 0; t < 16; ++t) {
       const int d = t * 16 + li;
-      uint16_t res = 0;
-      if (!dead) {
-        const uint16_t ob = bf16_rne_f32(o[t][r] * f / den);
-        res = gate_output(ob, a.gate[rowoff + d]);
-      }
-      a.out[rowoff + d] = res;
+      ob[t] = bf16_rne_f32(o[t][r] * f / den);
+      gt[t] = a.gate[rowoff + d];
+      uint16_t sb;
+      if (!sigmoid_bf16_fast(gt[t], sb)) slow |= 1u << t;
+      a.out[rowoff + d] = dead ? (uint16_t)0 : gate_product(ob[t], sb);
+    }
+    if (slow != 0 && !dead) {
+#pragma unroll
+      for (int t = 0; t < 16; ++t)
+        if ((slow >> t) & 1u) a.out[rowoff + t * 16 + li] = gate_product(ob[t], sigmoid_bf16_f64(gt[t]));
     }
     if (a.lse != nullptr && li == 0)
       a.lse[((size_t)b * S + qr) * Hq + h] =

@@ -71,3 +71,17 @@ def test_causal_first_row_is_gated_first_value():
     got = gpu_prefill(p)
     ref, _, _ = oracle.prefill(p.q, p.gate, p.k, p.v, p.scale, causal=True)
     assert np.array_equal(got[:, 0], ref[:, 0])
+
+
+def test_every_gate_bit_pattern_through_prefill():
+    """V = 1.0 everywhere, so O = 1 exactly and out = bf16(sigmoid(gate)):
+    all 65,536 gate values (S = 16 rows x 16 heads x 256 dims) must equal the
+    oracle's correctly rounded table bit for bit, as through decode."""
+    p = workloads.make_prefill("pf_all_gates", 1, 16, seed=62, causal=True)
+    p.v[:] = 0x3F80
+    p.gate = np.arange(65536, dtype=np.uint32).astype(np.uint16).reshape(p.gate.shape)
+    got = gpu_prefill(p)
+    exp = oracle.sigmoid_table()[p.gate]
+    nan = ((exp & 0x7F80) == 0x7F80) & ((exp & 0x7F) != 0)
+    assert np.array_equal(got[~nan], exp[~nan])
+    assert np.all(((got[nan] & 0x7F80) == 0x7F80) & ((got[nan] & 0x7F) != 0))
