@@ -782,21 +782,19 @@ __global__ __launch_bounds__(256) void decode_stage2_gate_kernel(Stage2Args a) {
     }
     const uint16_t gt[4] = {(uint16_t)(graw.x & 0xffff), (uint16_t)(graw.x >> 16),
                             (uint16_t)(graw.y & 0xffff), (uint16_t)(graw.y >> 16)};
-    // the fast sigmoid for the four elements, then the fp64 evaluation for
-    // the rare ones it cannot decide
-    uint16_t ob[4];
+    // the gate: the product in fp32 where that is exact, else in fp64
+    uint16_t ob[4], sb[4];
     uint32_t slow = 0;
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
       ob[e] = bf16_rne_f32(o[e] * a.v_descale / lam);
-      uint16_t sb;
-      if (!sigmoid_bf16_fast(gt[e], sb)) slow |= 1u << e;
-      o16[e] = gate_product(ob[e], sb);
+      sb[e] = sigmoid_bf16(gt[e]);
+      if (!gate_product_fast(ob[e], sb[e], o16[e])) slow |= 1u << e;
     }
     if (slow != 0) {
 #pragma unroll
       for (int e = 0; e < 4; ++e)
-        if ((slow >> e) & 1u) o16[e] = gate_product(ob[e], sigmoid_bf16_f64(gt[e]));
+        if ((slow >> e) & 1u) o16[e] = gate_product(ob[e], sb[e]);
     }
     lse = (M + log2f(lam)) * kLn2;
   }

@@ -49,65 +49,42 @@ __device__ __forceinline__ uint16_t bf16_rne_f64(double x) {
   return (uint16_t)(sign | (uint16_t)((e << 7) | (int64_t)(rounded & 0x7fu)));
 }
 
-// bf16(sigmoid(g)) for a bf16 gate g, correctly rounded.
-//
-// Reference evaluation: sigmoid in fp64 (relative error a few 2^-53), rounded
-// once to bf16.  The closest any of the 65,536 gates comes to a bf16 rounding
-// midpoint is ~2.5e-9 relative, far above the fp64 error.
-__device__ __forceinline__ uint16_t sigmoid_bf16_f64(uint16_t gate) {
-  double g = (double)bf16_to_f32(gate);
-  double s = 1.0 / (1.0 + exp(-g));
-  return bf16_rne_f64(s);
+// bf16(sigmoid(g)) for a bf16 gate g, correctly rounded.  A table holds the
+// 4,096 gates of biased exponent 118..133 (|g| in [2^-9, 128)), written by
+// gen_sigmoid_table.py with 60-digit decimal arithmetic and exact rational
+// rounding; every other gate has a closed form the generator checks:
+// |g| < 2^-9 -> 0.5, g >= 128 -> 1, g <= -128 -> +0, NaN -> NaN.  Entry
+// (sign << 11) | ((exponent - 118) << 7) | mantissa.  All 65,536 gates are
+// checked through the public entry points.
+static __device__ const uint16_t kSigmoidTable[4096] = {
+#include "sigmoid_bf16_table.inc"
+};
+constexpr uint32_t kSigmoidExpLo = 118, kSigmoidExpHi = 133;
+
+__device__ __forceinline__ uint32_t sigmoid_table_slot(uint16_t gate) {
+  const uint32_t e = (gate >> 7) & 0xffu;
+  return ((uint32_t)(gate >> 15) << 11) | (((e - kSigmoidExpLo) & 15u) << 7) | (gate & 0x7fu);
 }
 
-// Fast path: sigmoid in fp32 for |g| <= 80, a few fp32 ulp of error.
-// exp(-g) = 2^(-g log2 e) with Cody and Waite's two-part constant: log2 e =
-// kLog2eHi + kLog2eLo, kLog2eHi = 23637 / 2^14 (15 significant bits), so
-// -g kLog2eHi is exact for a bf16 g (8 significant bits); its nearest integer
-// n splits it exactly into n + (t - n), and 2^(t - n - g kLog2eLo) (argument
-// within +-0.51) comes from the hardware exp2, scaled by 2^n exactly.
-// 1 / (1 + e) is the hardware reciprocal refined by one Newton step.
-// Rounding the result to bf16 gives the correctly rounded sigmoid whenever it
-// lies more than kSigmoidSlack fp32 ulps from a bf16 rounding midpoint, i.e.
-// when its low 16 bits are not within kSigmoidSlack of 0x8000; the function
-// then returns true.  Otherwise (about 0.05% of gates, every one whose
-// sigmoid lies close to a midpoint among them), and for |g| > 80 or NaN, it
-// returns false and the fp64 evaluation must decide.  Branch-free, so a
-// caller can run it over many elements and fix the rare misses afterwards
-// (the fp64 path for every element cost the prefill epilogue about 11% of
-// the kernel's time).  All 65,536 gates are checked through both public entry
-// points that apply the gate.
-constexpr int kSigmoidSlack = 16;
-constexpr float kLog2eHi = 23637.0f / 16384.0f;
-constexpr float kLog2eLo = 7.052607543300837e-06f;  // log2(e) - kLog2eHi, rounded
-
-__device__ __forceinline__ bool sigmoid_bf16_fast(uint16_t gate, uint16_t& res) {
-  const float g = bf16_to_f32(gate);
-  const float gc = __builtin_fminf(__builtin_fmaxf(g, -80.f), 80.f);  // keeps n finite
-  const float t = -gc * kLog2eHi;  // exact
-  const float n = __builtin_rintf(t);
-  const float f = __builtin_fmaf(-gc, kLog2eLo, t - n);
-  const float e = __builtin_ldexpf(__builtin_amdgcn_exp2f(f), (int)n);
-  const float den = 1.0f + e;
-  float s = __builtin_amdgcn_rcpf(den);
-  s = __builtin_fmaf(__builtin_fmaf(-den, s, 1.0f), s, s);
-  res = bf16_rne_f32(s);
-  const int low = (int)(__float_as_uint(s) & 0xffffu) - 0x8000;
-  return __builtin_fabsf(g) <= 80.f && (low > kSigmoidSlack || low < -kSigmoidSlack);
+// The result given the table entry at sigmoid_table_slot(gate) (ignored
+// outside the table's range).
+__device__ __forceinline__ uint16_t sigmoid_from_entry(uint16_t gate, uint16_t entry) {
+  const uint32_t e = (gate >> 7) & 0xffu;
+  uint16_t r = entry;
+  if (e < kSigmoidExpLo) r = 0x3f00;
+  if (e > kSigmoidExpHi) r = (gate & 0x8000u) ? 0 : 0x3f80;
+  if (e == 0xffu && (gate & 0x7fu) != 0) r = 0x7fc0;
+  return r;
 }
 
 __device__ __forceinline__ uint16_t sigmoid_bf16(uint16_t gate) {
-  uint16_t r;
-  return sigmoid_bf16_fast(gate, r) ? r : sigmoid_bf16_f64(gate);
+  return sigmoid_from_entry(gate, kSigmoidTable[sigmoid_table_slot(gate)]);
 }
 
 // bf16(Ob * sigma_b) for bf16 Ob and sigma_b: their product has at most 16
-// significant bits, so it is exact in fp32 whenever it is a normal fp32 value
-// and exact in fp64 at every magnitude (subnormals included); either way the
-// only rounding is the final one.
+// significant bits, so it is exact in fp64 at every magnitude (subnormals
+// included) and the only rounding is the final one.
 __device__ __forceinline__ uint16_t gate_product(uint16_t ob, uint16_t sb) {
-  const float p = bf16_to_f32(ob) * bf16_to_f32(sb);
-  if (__builtin_fabsf(p) >= 0x1p-126f && __builtin_fabsf(p) <= 0x1p127f) return bf16_rne_f32(p);
   const double pd = (double)bf16_to_f32(ob) * (double)bf16_to_f32(sb);
   return bf16_rne_f64(pd);
 }
@@ -115,6 +92,17 @@ __device__ __forceinline__ uint16_t gate_product(uint16_t ob, uint16_t sb) {
 // The gate epilogue: out = bf16(Ob * bf16(sigmoid(g))).
 __device__ __forceinline__ uint16_t gate_output(uint16_t ob, uint16_t gate) {
   return gate_product(ob, sigmoid_bf16(gate));
+}
+
+// The product's fast path, branch-free: true when `res` is
+// gate_product(ob, sb) for certain -- the product is a normal fp32 value, and
+// then exact in fp32.  Zero, subnormal and non-finite products must go
+// through gate_product.
+__device__ __forceinline__ bool gate_product_fast(uint16_t ob, uint16_t sb, uint16_t& res) {
+  const float p = bf16_to_f32(ob) * bf16_to_f32(sb);
+  res = bf16_rne_f32(p);
+  const float ap = __builtin_fabsf(p);
+  return ap >= 0x1p-126f && ap <= 0x1p127f;
 }
 
 // ---------------------------------------------------------------------------

@@ -48,6 +48,7 @@ constexpr int kBN = 64;    // keys per tile
 constexpr int kKRow = kD + 16;  // K row stride: +32 B
 constexpr int kVRow = kD + 16;  // V row stride: +32 B
 constexpr int kThreads = 512;
+constexpr int kWavesPf = kThreads / 64;
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
 constexpr float kSlack = 8.f;  // lazy-rescale threshold, log2 units
@@ -377,9 +378,30 @@ __global__ __launch_bounds__(kThreads) void prefill_gate_kernel(PrefillArgs a) {
   }
 
   // ---- epilogue: O / l -> bf16, gate, store ------------------------------------
+  // bf16(O) of the wave's 16 rows goes through LDS (the loop ended with a
+  // barrier, so the tile buffers are free) from the MFMA layout (lane: 4 rows x
+  // 16 strided columns) to whole 16-byte pieces of rows, so each lane issues 8
+  // gate loads and 8 output stores of 16 bytes instead of 64 of 2 bytes, and
+  // waits for memory once.
   if (!active) return;
   l_row += shfl_xor(l_row, 16);  // the row's four lanes hold disjoint keys
   l_row += shfl_xor(l_row, 32);
+  // LDS (139,264 B): 8 x 8 KiB of bf16(O), 8 x 64 B of row flags, then a copy
+  // of the sigmoid table per wave (8 x 8 KiB): 131,584 B in all
+  char* const lds = reinterpret_cast<char*>(&buf[0]);
+  uint16_t* const ob_lds = reinterpret_cast<uint16_t*>(lds) + wave * (kBM * kD);  // [16 rows][256]
+  uint32_t* const row_flags =
+      reinterpret_cast<uint32_t*>(lds + kWavesPf * kBM * kD * 2) + wave * kBM;  // bit 0 live, bit 1 dead
+  uint16_t* const sig_lds =
+      reinterpret_cast<uint16_t*>(lds + kWavesPf * kBM * (kD * 2 + 4)) + wave * 4096;
+  {  // the table -> this wave's copy by direct copies (no registers), 1 KiB each
+    const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(
+        const_cast<uint16_t*>(kSigmoidTable), 0, (int)sizeof(kSigmoidTable), 0x00020000);
+#pragma unroll
+    for (int k = 0; k < 8; ++k)
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (__attribute__((address_space(3))) void*)(sig_lds + 512 * k),
+                                               16, 16 * lane + 1024 * k, 0, 0, 0);
+  }
   // A sink joins the denominator as one more term exp(sink) (log2 units here,
   // like m_ref); a row with no visible key (l = 0) is dead: out = +0.
   const float sink2 = a.sinks != nullptr ? a.sinks[h] * kLog2e : -INFINITY;
@@ -389,7 +411,6 @@ __global__ __launch_bounds__(kThreads) void prefill_gate_kernel(PrefillArgs a) {
     const float lr = __int_as_float(__builtin_amdgcn_ds_bpermute(row << 2, __float_as_int(l_row)));
     const float mr = __int_as_float(__builtin_amdgcn_ds_bpermute(row << 2, __float_as_int(m_ref)));
     const int qr = p0 + row;
-    if (qr >= S) continue;
     const bool dead = lr == 0.f;
     float mtot = mr, f = 1.f, den = lr;
     if (a.sinks != nullptr) {
@@ -397,28 +418,75 @@ __global__ __launch_bounds__(kThreads) void prefill_gate_kernel(PrefillArgs a) {
       f = __builtin_amdgcn_exp2f(mr - mtot);  // 0 for a dead row
       den = fmaf(lr, f, __builtin_amdgcn_exp2f(sink2 - mtot));
     }
-    const size_t rowoff = (((size_t)b * S + qr) * Hq + h) * kD;
-    // The gate: the fast sigmoid for all 16 elements (no branches), then the
-    // fp64 evaluation for the rare ones it cannot decide.
-    uint16_t ob[16], gt[16];
-    uint32_t slow = 0;
+    // O f / den through one reciprocal per row and a correction step (the
+    // quotient to within about an fp32 ulp; it is rounded to bf16 next)
+    const float inv = 1.f / den;
 #pragma unroll
     for (int t = 0; t < 16; ++t) {
-      const int d = t * 16 + li;
-      ob[t] = bf16_rne_f32(o[t][r] * f / den);
-      gt[t] = a.gate[rowoff + d];
-      uint16_t sb;
-      if (!sigmoid_bf16_fast(gt[t], sb)) slow |= 1u << t;
-      a.out[rowoff + d] = dead ? (uint16_t)0 : gate_product(ob[t], sb);
+      const float x = o[t][r] * f;
+      const float q0 = x * inv;
+      const float q = __builtin_fmaf(__builtin_fmaf(-q0, den, x), inv, q0);
+      ob_lds[row * kD + 16 * t + li] = bf16_rne_f32(q);
     }
-    if (slow != 0 && !dead) {
-#pragma unroll
-      for (int t = 0; t < 16; ++t)
-        if ((slow >> t) & 1u) a.out[rowoff + t * 16 + li] = gate_product(ob[t], sigmoid_bf16_f64(gt[t]));
-    }
-    if (a.lse != nullptr && li == 0)
+    if (li == 0) row_flags[row] = (qr < S ? 1u : 0u) | (dead ? 2u : 0u);
+    if (a.lse != nullptr && li == 0 && qr < S)
       a.lse[((size_t)b * S + qr) * Hq + h] =
           (den > 0.f) ? (mtot + log2f(den)) * kLn2 : -INFINITY;
+  }
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // the table copies have landed
+  // the wave's LDS writes above before its reads of other lanes' values below
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+  // piece j of this lane: row 2j + lane / 32, dims 8 (lane % 32) .. +7
+  const int pc = lane & 31;
+  uint4 ob8[8], gt8[8];
+  uint32_t flg[8];
+#pragma unroll
+  for (int j = 0; j < 8; ++j) {
+    const int row = 2 * j + (lane >> 5);
+    flg[j] = row_flags[row];
+    ob8[j] = *reinterpret_cast<const uint4*>(&ob_lds[row * kD + 8 * pc]);
+    const int qr = min(p0 + row, S - 1);  // rows past S are not stored
+    gt8[j] = *reinterpret_cast<const uint4*>(a.gate + (((size_t)b * S + qr) * Hq + h) * kD + 8 * pc);
+  }
+  // The gate: the sigmoid from the wave's table copy and the product in fp32
+  // for all 64 elements (no branches) and the stores, then the fp64 product
+  // for the rare ones whose fp32 product is not exact (zero, subnormal),
+  // stored over the first result.
+  uint64_t slow = 0;
+#pragma unroll
+  for (int j = 0; j < 8; ++j) {
+    const uint32_t ow[4] = {ob8[j].x, ob8[j].y, ob8[j].z, ob8[j].w};
+    const uint32_t gw[4] = {gt8[j].x, gt8[j].y, gt8[j].z, gt8[j].w};
+    const bool dead = (flg[j] & 2u) != 0;
+    const bool live = (flg[j] & 1u) != 0;  // row inside the sequence
+    uint32_t res[4];
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      const uint16_t obe = (uint16_t)(ow[e >> 1] >> (16 * (e & 1)));
+      const uint16_t ge = (uint16_t)(gw[e >> 1] >> (16 * (e & 1)));
+      const uint16_t sb = sigmoid_from_entry(ge, sig_lds[sigmoid_table_slot(ge)]);
+      uint16_t r;
+      if (!gate_product_fast(obe, sb, r) && live && !dead) slow |= 1ull << (8 * j + e);
+      const uint32_t rv = dead ? 0u : (uint32_t)r;
+      if (e & 1) res[e >> 1] |= rv << 16; else res[e >> 1] = rv;
+    }
+    const int row = 2 * j + (lane >> 5);
+    if (live)
+      *reinterpret_cast<uint4*>(a.out + (((size_t)b * S + p0 + row) * Hq + h) * kD + 8 * pc) =
+          make_uint4(res[0], res[1], res[2], res[3]);
+  }
+  if (slow != 0) {  // rare: re-read the element's bf16(O) and gate
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      const int row = 2 * j + (lane >> 5);
+      const size_t off = (((size_t)b * S + p0 + row) * Hq + h) * kD + 8 * pc;
+#pragma unroll
+      for (int e = 0; e < 8; ++e)
+        if ((slow >> (8 * j + e)) & 1ull)
+          a.out[off + e] = gate_output(ob_lds[row * kD + 8 * pc + e], a.gate[off + e]);
+    }
   }
 }
 
