@@ -79,16 +79,23 @@ class Hip:
 
         self.lib = ctypes.CDLL("libamdhip64.so.7")
         self.lib.hipEventCreate.argtypes = [ctypes.POINTER(ctypes.c_void_p)]
+        self.lib.hipEventCreateWithFlags.argtypes = [ctypes.POINTER(ctypes.c_void_p), ctypes.c_uint]
         self.lib.hipEventElapsedTime.argtypes = [ctypes.POINTER(ctypes.c_float), ctypes.c_void_p,
                                                  ctypes.c_void_p]
         self.lib.hipEventDestroy.argtypes = [ctypes.c_void_p]
+
+    # Timing-only events: no system-scope fence (cache write-back and
+    # invalidation) when they are recorded, so the interval between two of
+    # them holds the kernel, not a flush after it (the stream is synchronised
+    # before the intervals are read).
+    EVENT_DISABLE_SYSTEM_FENCE = 0x20000000
 
     def events(self, n):
         out = []
         for _ in range(n):
             e = ctypes.c_void_p()
-            if self.lib.hipEventCreate(ctypes.byref(e)) != 0:
-                raise RuntimeError("hipEventCreate failed")
+            if self.lib.hipEventCreateWithFlags(ctypes.byref(e), self.EVENT_DISABLE_SYSTEM_FENCE) != 0:
+                raise RuntimeError("hipEventCreateWithFlags failed")
             out.append(e.value)
         return out
 
