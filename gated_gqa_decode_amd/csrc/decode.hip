@@ -716,9 +716,25 @@ struct Stage2Args {
 // from scalar loads (no cross-lane reduction); the partial rows are read eight
 // splits at a time so that their loads are in flight together.
 __global__ __launch_bounds__(256) void decode_stage2_gate_kernel(Stage2Args a) {
-  const int row = blockIdx.x * 4 + (threadIdx.x >> 6);  // b * H_q + h
-  if (row >= a.batch * a.num_q_heads) return;
+  // The sigmoid table -> LDS by direct copies issued first, so the copy runs
+  // alongside the partials' loads and the lookups below read LDS instead of
+  // making a second trip to memory; wave w copies 2 KiB of the 8 KiB.
+  __shared__ uint16_t sig_tab[4096];
+  const int wave = threadIdx.x >> 6;
   const int lane = __lane_id();
+  {
+    const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(
+        const_cast<uint16_t*>(kSigmoidTable), 0, (int)sizeof(kSigmoidTable), 0x00020000);
+#pragma unroll
+    for (int k = 0; k < 2; ++k) {
+      const int c = 2 * wave + k;  // 1 KiB chunk
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (__attribute__((address_space(3))) void*)(sig_tab + 512 * c),
+                                               16, 16 * lane + 1024 * c, 0, 0, 0);
+    }
+  }
+  const int row_raw = blockIdx.x * 4 + wave;  // b * H_q + h
+  const bool valid = row_raw < a.batch * a.num_q_heads;
+  const int row = valid ? row_raw : 0;  // past the last row: loads of row 0, nothing stored
   const int b = row / a.num_q_heads;
   const float* ml = a.part_ml + (size_t)row * a.num_splits * 2;
   const float* pa = a.part_acc + (size_t)row * a.num_splits * kD + lane * 4;
@@ -742,6 +758,8 @@ __global__ __launch_bounds__(256) void decode_stage2_gate_kernel(Stage2Args a) {
   const int L = seq_length(a.seq_lens, a.kv_indptr, a.index_capacity, b, a.capacity,
                            &first_index);  // as in stage 1
   uint16_t o16[4] = {0, 0, 0, 0};
+  uint16_t ob[4] = {0, 0, 0, 0}, gq[4] = {0, 0, 0, 0};
+  bool live = false;
   float lse = sink2 * kLn2;  // a dead row: ln(exp(sink)), or -inf
   if (L > 0) {  // L <= 0: padded slot, output +0
     const int ns = split_range(L, a.window, a.num_splits, a.tokens_per_split, a.split_units,
@@ -783,12 +801,24 @@ __global__ __launch_bounds__(256) void decode_stage2_gate_kernel(Stage2Args a) {
     const uint16_t gt[4] = {(uint16_t)(graw.x & 0xffff), (uint16_t)(graw.x >> 16),
                             (uint16_t)(graw.y & 0xffff), (uint16_t)(graw.y >> 16)};
     // the gate: the product in fp32 where that is exact, else in fp64
-    uint16_t ob[4], sb[4];
-    uint32_t slow = 0;
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
       ob[e] = bf16_rne_f32(o[e] * a.v_descale / lam);
-      sb[e] = sigmoid_bf16(gt[e]);
+      gq[e] = gt[e];
+    }
+    live = true;
+    lse = (M + log2f(lam)) * kLn2;
+  }
+  // every wave: the table copies have landed and are visible to all waves
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+  __syncthreads();
+  if (!valid) return;
+  if (live) {
+    uint16_t sb[4];
+    uint32_t slow = 0;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      sb[e] = sigmoid_from_entry(gq[e], sig_tab[sigmoid_table_slot(gq[e])]);
       if (!gate_product_fast(ob[e], sb[e], o16[e])) slow |= 1u << e;
     }
     if (slow != 0) {
@@ -796,7 +826,6 @@ __global__ __launch_bounds__(256) void decode_stage2_gate_kernel(Stage2Args a) {
       for (int e = 0; e < 4; ++e)
         if ((slow >> e) & 1u) o16[e] = gate_product(ob[e], sb[e]);
     }
-    lse = (M + log2f(lam)) * kLn2;
   }
   if (a.lse != nullptr && lane == 0) a.lse[row] = lse;
   uint2 w;
