@@ -665,6 +665,14 @@ def main() -> int:
                                   "sample": f"the whole B=64 L=4096 workload, {reps} call(s) "
                                             f"({busy:.2f} s wall, fp64, {threads} threads)",
                                   "seconds_per_call": round(busy / reps, 3)}
+        # and one thread on the B=1, L=512 workload (latency, not throughput)
+        small = workloads.workload(0, poison=False)
+        reps1, t = 0, time.time()
+        while reps1 == 0 or time.time() - t < 0.5:
+            oracle.decode(small.q, small.gate, small.k_pool, small.v_pool, small.block_table,
+                          small.seq_lens, small.scale, nthreads=1)
+            reps1 += 1
+        result["cpu_baseline"]["b1_l512_one_thread_ms"] = round((time.time() - t) / reps1 * 1e3, 3)
     result["settle"] = {"seconds": round(settle_s, 3), "calls": settle_calls}
     result["input_generation_s"] = round(gen_s, 2)
     line = json.dumps(result)
