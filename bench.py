@@ -426,7 +426,7 @@ def main() -> int:
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
         print(f"bench.py measures one GPU only (asked for --gpus {args.gpus}, WORLD_SIZE {world}): "
-              "this build has no multi-GPU path; decode shards by sequence or kv head with no "
+              "the library has no multi-GPU path; decode shards by sequence or kv head with no "
               "exchange, so the per-GPU rate is the number to read.", file=sys.stderr)
         return 2
 
