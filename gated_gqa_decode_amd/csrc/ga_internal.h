@@ -7,16 +7,13 @@
 
 namespace ga {
 
-// GQA groups (G = H_q / H_kv) the kernels take: 1..8, and even groups up to
-// 16.  Decode serves a whole group of up to 16 heads in one workgroup (idle
-// MFMA columns past G).  Prefill runs up to 8 heads per workgroup (one wave
-// each); even groups of 10..16 run as two halves of G/2 heads, each half
-// streaming the kv head's K/V.
+// GQA groups (G = H_q / H_kv) the kernels take: 1..16.  Decode serves a
+// whole group in one workgroup (idle MFMA columns past G).  Prefill runs up to
+// 8 heads per workgroup (one wave each); groups of 9..16 run as two parts of
+// ceil(G/2) and floor(G/2) heads, each part streaming the kv head's K/V.
 constexpr int kMaxHeadsPerPart = 8;
 inline int head_parts(int group) { return group > kMaxHeadsPerPart ? 2 : 1; }
-inline bool group_supported(int group) {
-  return group >= 1 && (group <= kMaxHeadsPerPart || (group <= 2 * kMaxHeadsPerPart && group % 2 == 0));
-}
+inline bool group_supported(int group) { return group >= 1 && group <= 2 * kMaxHeadsPerPart; }
 
 struct DecodeLaunch {
   const uint16_t* q;

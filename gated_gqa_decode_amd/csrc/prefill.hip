@@ -70,7 +70,7 @@ struct PrefillArgs {
   int num_q_heads;
   int num_kv_heads;
   int parts;           // workgroups per (sequence, kv head, query tile): 1 or 2
-  int heads_per_part;  // query heads of a workgroup: G or G / 2 (<= 8)
+  int heads_per_part;  // query heads of part 0: G, or ceil(G / 2) (<= 8); part 1 has the rest
   int batch;
   int num_m_tiles;
   // attention-spec options (null / 0: plain attention)
@@ -160,8 +160,9 @@ __global__ __launch_bounds__(kThreads) void prefill_gate_kernel(PrefillArgs a) {
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int lane = __lane_id();
   // Waves past the workgroup's head count only help stage K/V tiles.
-  const bool active = wave < a.heads_per_part;
-  const int h = g * (Hq / Hkv) + part * a.heads_per_part + min(wave, a.heads_per_part - 1);
+  const int heads = part == 0 ? a.heads_per_part : Hq / Hkv - a.heads_per_part;  // >= 1
+  const bool active = wave < heads;
+  const int h = g * (Hq / Hkv) + part * a.heads_per_part + min(wave, heads - 1);
   const int p0 = mt * kBM;
 
   const int li = lane & 15;  // query row of this lane's S^T column / MFMA column
@@ -504,7 +505,7 @@ hipError_t launch_prefill(const PrefillLaunch& p, hipStream_t stream) {
   a.num_kv_heads = p.num_kv_heads;
   const int group = p.num_q_heads / p.num_kv_heads;
   a.parts = head_parts(group);
-  a.heads_per_part = group / a.parts;
+  a.heads_per_part = (group + a.parts - 1) / a.parts;
   a.batch = p.batch;
   a.num_m_tiles = (p.seq_len + kBM - 1) / kBM;
   a.kv_lens = p.kv_lens;

@@ -49,12 +49,13 @@ typedef enum ga_status {
 
 /* GQA groups (both entry points).  Query head h attends with kv head
  * h / G, G = H_q / H_kv (contiguous groups: cuDNN "Gated Attention Block",
- * Overview, stage (4), GQA H_q / H_kv).  Served: G = 1..8, and even G up to
- * 16 -- among them the h_q = 32, h_kv = 2 geometry of that page's Performance
- * section and the non-power-of-two groups the FreeToken PR #781 tests
- * (Correctness and actual execution).  G = 10..16 runs as two workgroups per
- * kv head, each streaming that head's K/V.  Other G: GA_ERR_UNSUPPORTED;
- * H_q not a multiple of H_kv: GA_ERR_INVALID_ARGUMENT. */
+ * Overview, stage (4), GQA H_q / H_kv).  Served: G = 1..16 -- among them the
+ * h_q = 32, h_kv = 2 geometry of that page's Performance section and the
+ * non-power-of-two groups the FreeToken PR #781 tests (Correctness and actual
+ * execution).  Decode serves a whole group in one workgroup; prefill runs
+ * G = 9..16 as two workgroups per kv head (ceil(G/2) and floor(G/2) heads),
+ * each streaming that head's K/V.  G > 16: GA_ERR_UNSUPPORTED; H_q not a
+ * multiple of H_kv: GA_ERR_INVALID_ARGUMENT. */
 
 /* Shape of a paged decode call. */
 typedef struct ga_decode_dims {

@@ -59,7 +59,7 @@ def test_plan_covers_capacity(B, W):
     assert ga.decode_workspace_size(_dims(batch=B, max_pages_per_seq=W)) == p.workspace_bytes
 
 
-@pytest.mark.parametrize("G", [1, 2, 3, 4, 5, 6, 7, 8, 10, 12, 14, 16])
+@pytest.mark.parametrize("G", list(range(1, 17)))
 def test_supported_groups_plan(G):
     """Every group size uses one workgroup per (sequence, kv head, split): the
     split plan does not depend on the group."""
@@ -104,8 +104,6 @@ def test_plan_depends_on_capacity_not_lengths():
 
 @pytest.mark.parametrize("kw,status", [
     (dict(head_dim=128), ga.GA_ERR_UNSUPPORTED),
-    (dict(num_q_heads=18), ga.GA_ERR_UNSUPPORTED),         # group of 9 (odd, > 8)
-    (dict(num_q_heads=30), ga.GA_ERR_UNSUPPORTED),         # group of 15
     (dict(num_q_heads=34), ga.GA_ERR_UNSUPPORTED),         # group of 17
     (dict(num_q_heads=64, num_kv_heads=2), ga.GA_ERR_UNSUPPORTED),  # group of 32
     (dict(num_q_heads=15), ga.GA_ERR_INVALID_ARGUMENT),    # not a multiple of H_kv
@@ -261,7 +259,7 @@ def test_empty_batch_is_a_no_op():
 
 @pytest.mark.parametrize("dims,status", [
     ((2, 128, 16, 2, 128), ga.GA_ERR_UNSUPPORTED),
-    ((2, 128, 18, 2, 256), ga.GA_ERR_UNSUPPORTED),
+    ((2, 128, 34, 2, 256), ga.GA_ERR_UNSUPPORTED),  # group of 17
     ((2, 128, 66, 2, 256), ga.GA_ERR_UNSUPPORTED),
     ((2, 128, 15, 2, 256), ga.GA_ERR_INVALID_ARGUMENT),
     ((-1, 128, 16, 2, 256), ga.GA_ERR_INVALID_ARGUMENT),

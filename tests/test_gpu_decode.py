@@ -30,10 +30,11 @@ def test_workload_parity(wl):
 
 
 @pytest.mark.parametrize("Hq,Hkv", [(32, 2), (24, 2), (20, 2), (12, 2), (14, 2), (8, 2),
-                                     (2, 2), (7, 1), (6, 3), (40, 8), (3, 1), (16, 1)])
+                                     (2, 2), (7, 1), (6, 3), (40, 8), (3, 1), (16, 1),
+                                     (9, 1), (22, 2), (15, 1), (39, 3)])
 def test_gqa_group_sizes(Hq, Hkv):
-    """Groups 1..8 (idle head slots) and even groups 10..16 (two workgroups
-    per kv head), over ragged lengths, several splits and a dead row."""
+    """Groups 1..16 (idle MFMA columns past the group), over ragged lengths,
+    several splits and a dead row."""
     lens = [700, 1, 2049, 0, 64, 333]
     c = workloads.make_decode(f"gqa_{Hq}_{Hkv}", lens, seed=70 + Hq + Hkv, num_q_heads=Hq,
                               num_kv_heads=Hkv, max_pages_per_seq=160)

@@ -31,10 +31,12 @@ def test_small_prefill_parity(S, causal):
 
 
 @pytest.mark.parametrize("causal", [True, False])
-@pytest.mark.parametrize("Hq,Hkv", [(32, 2), (12, 2), (20, 2), (4, 2), (2, 2), (7, 1), (6, 3)])
+@pytest.mark.parametrize("Hq,Hkv", [(32, 2), (12, 2), (20, 2), (4, 2), (2, 2), (7, 1), (6, 3),
+                                     (9, 1), (22, 2), (15, 1), (39, 3)])
 def test_gqa_group_sizes(Hq, Hkv, causal):
-    """Groups below 8 (idle waves only stage K/V) and even groups 10..16 (two
-    workgroups per kv head); S = 130 spans three key tiles and a ragged tail."""
+    """Groups below 8 (idle waves only stage K/V) and groups 9..16 (two
+    workgroups per kv head, ceil(G/2) and floor(G/2) heads); S = 130 spans
+    three key tiles and a ragged tail."""
     p = workloads.make_prefill(f"pf_gqa_{Hq}_{Hkv}", 2, 130, seed=80 + Hq + Hkv, causal=causal,
                                num_q_heads=Hq, num_kv_heads=Hkv)
     res = _parity(p, gpu_prefill(p))

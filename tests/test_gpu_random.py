@@ -1,6 +1,6 @@
 """Seeded random shapes and options through the C-ABI against the CPU oracle.
 
-Each case draws its own GQA geometry (groups 1..8 and even groups up to 16),
+Each case draws its own GQA geometry (groups 1..16 over 1..8 kv heads),
 batch, ragged lengths (dead rows included), block-table capacity, sliding
 window and sinks from a fixed seed, so a failure names a case that replays
 exactly.  Pass criterion: the floored two-ulp rule of oracle/compare.py on
@@ -20,7 +20,7 @@ import gated_gqa_decode_amd as ga
 pytestmark = pytest.mark.gpu
 
 GEOMETRIES = [(16, 2), (8, 1), (6, 3), (4, 2), (3, 1), (2, 2), (1, 1), (7, 1), (12, 2),
-              (32, 2), (10, 1), (40, 8), (5, 5), (14, 1)]
+              (32, 2), (10, 1), (40, 8), (5, 5), (14, 1), (9, 1), (26, 2), (33, 3), (15, 1)]
 
 
 def _lse_ok(got, ref, name):
