@@ -63,7 +63,8 @@ def parse_args():
                     help="only the timed decode steps (cold, B1, prefill, CPU legs skipped)")
     ap.add_argument("--prefill-only", action="store_true",
                     help="time only the B=2, S=2048 causal prefill (for profiling)")
-    ap.add_argument("--only", choices=["decode_fp8kv", "decode_hq32", "decode_b224"], default=None,
+    ap.add_argument("--only", choices=["decode_fp8kv", "decode_hq32", "decode_b224",
+                                       "decode_fp8kv_page1"], default=None,
                     help="time only this decode variant at B=64, L=4096 (for profiling its kernel)")
     ap.add_argument("--calibration-copy", action="store_true",
                     help="also run one plain 1 GiB device copy (counter calibration)")
@@ -319,6 +320,12 @@ def only_case(workloads, name: str):
                                      max_pages_per_seq=256, kv_dtype="fp8")
     if name == "decode_b224":  # the serving shape: B=224, L ~ U{4094..6142}
         return workloads.workload(3, poison=False)
+    if name == "decode_fp8kv_page1":  # e4m3 pools at page size 1 (token slots, shuffled)
+        c = workloads.make_decode("decode_b64_l4096_fp8_page1", [4096] * 64, seed=2, poison=False,
+                                  max_pages_per_seq=256, kv_dtype="fp8")
+        k1, v1, _, _, table = workloads.csr_layout(c, seed=2, poison=False)
+        return workloads.DecodeCase(c.name, c.q, c.gate, k1, v1, table, c.seq_lens, c.scale,
+                                    c.k_descale, c.v_descale)
     raise ValueError(name)
 
 

@@ -184,7 +184,6 @@ ga_status decode_impl(const uint16_t* q, const uint16_t* gate, const void* k_poo
   if (st != GA_OK) return st;
   const bool csr = ix.kv_indptr != nullptr || ix.kv_indices != nullptr;
   if (csr && dims->page_size != 1) return GA_ERR_UNSUPPORTED;
-  if (kv_fp8 && dims->page_size != kPageSize) return GA_ERR_UNSUPPORTED;
   if (!(std::isfinite(scale) && scale > 0.f)) return GA_ERR_INVALID_ARGUMENT;
   if (!(std::isfinite(k_descale) && k_descale > 0.f && std::isfinite(v_descale) &&
         v_descale > 0.f))

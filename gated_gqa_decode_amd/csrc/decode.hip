@@ -194,9 +194,9 @@ __device__ __forceinline__ int seq_length(const int32_t* seq_lens, const int32_t
   return min(seq_lens[b], capacity);
 }
 
-// The stage-1 body: kFp8 = e4m3 pools (16-token pages); kTok = one token per
-// page (block-table entries or CSR indices are token slots); kWide = a
-// page-size-1 pool whose byte offsets do not fit 32 bits.
+// The stage-1 body: kFp8 = e4m3 pools; kTok = one token per page
+// (block-table entries or CSR indices are token slots); kWide = a page-size-1
+// pool whose byte offsets do not fit 32 bits.
 template <bool kFp8, bool kTok, bool kWide>
 __device__ __forceinline__ void stage1_body(const Stage1Args& a) {
   // Per-wave LDS tiles, separate objects so the compiler can tell a copy into
@@ -690,6 +690,14 @@ __global__ __launch_bounds__(512, 1) void decode_stage1_tok_wide_kernel(Stage1Ar
   stage1_body<false, true, true>(a);
 }
 
+__global__ __launch_bounds__(512, 1) void decode_stage1_fp8_tok_kernel(Stage1Args a) {
+  stage1_body<true, true, false>(a);
+}
+
+__global__ __launch_bounds__(512, 1) void decode_stage1_fp8_tok_wide_kernel(Stage1Args a) {
+  stage1_body<true, true, true>(a);
+}
+
 struct Stage2Args {
   const uint16_t* gate;
   const int32_t* seq_lens;
@@ -876,7 +884,11 @@ hipError_t launch_decode(const DecodeLaunch& d, hipStream_t stream) {
     if (err != hipSuccess) return err;
   }
   const dim3 block(kWaves * 64);
-  if (d.kv_fp8)
+  if (d.kv_fp8 && d.page_size == 1 && wide_offsets(d))
+    hipLaunchKernelGGL(decode_stage1_fp8_tok_wide_kernel, grid1, block, 0, stream, a1);
+  else if (d.kv_fp8 && d.page_size == 1)
+    hipLaunchKernelGGL(decode_stage1_fp8_tok_kernel, grid1, block, 0, stream, a1);
+  else if (d.kv_fp8)
     hipLaunchKernelGGL(decode_stage1_fp8_kernel, grid1, block, 0, stream, a1);
   else if (d.page_size == 1 && wide_offsets(d))
     hipLaunchKernelGGL(decode_stage1_tok_wide_kernel, grid1, block, 0, stream, a1);

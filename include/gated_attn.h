@@ -213,7 +213,8 @@ ga_status gated_attn_decode_ex(const uint16_t *q, const uint16_t *gate, const ui
  * and K = k_descale * value(code), V = v_descale * value(code) with one factor
  * per tensor (the cuDNN "Gated Attention Block" page's FP8 pipeline takes
  * static per-tensor scales, Forward: Quantization specs).  Everything else --
- * layouts ([num_pages][page_size][H_kv][D], one byte per element), q, gate,
+ * layouts ([num_pages][page_size][H_kv][D], one byte per element; page size
+ * 16, or 1 with block-table entries as token slots), q, gate,
  * out, dims, plan, workspace, options, errors -- is as gated_attn_decode_ex.
  * The factors must be finite and > 0 (else GA_ERR_INVALID_ARGUMENT).  The K
  * factor is folded into the score scale and the V factor into O before its

@@ -88,3 +88,23 @@ def test_fp8_single_key_is_bit_exact():
     ref, _, _ = oracle.decode(c.q, c.gate, c.k_pool, c.v_pool, c.block_table, c.seq_lens,
                               c.scale, k_descale=c.k_descale, v_descale=c.v_descale)
     assert np.array_equal(got, ref)
+
+
+@pytest.mark.usefixtures("page1_copies")
+def test_page_size_one_block_table():
+    """e4m3 pools at page size 1: every token its own pool row at a shuffled
+    slot (spare slots NaN codes), the block table holding token slots.  Within
+    the rule against the oracle on that layout, and bit-identical to the same
+    tokens in 16-token pages (the two layouts get the same split plan here)."""
+    lens = [700, 1, 33, 0, 2049, 16]
+    c = workloads.make_decode("fp8_tok", lens, seed=142, kv_dtype="fp8", max_pages_per_seq=160)
+    k1, v1, _, _, table = workloads.csr_layout(c, seed=143)
+    c1 = workloads.DecodeCase(c.name + "_p1", c.q, c.gate, k1, v1, table, c.seq_lens, c.scale,
+                              c.k_descale, c.v_descale)
+    p16 = ga.decode_plan(ga.decode_dims(**c.dims))
+    p1 = ga.decode_plan(ga.decode_dims(**c1.dims))
+    assert p1.tokens_per_split == p16.tokens_per_split
+    got, _ = _run(c1)
+    _parity(c1)
+    paged, _ = _run(c)
+    assert np.array_equal(got, paged)
