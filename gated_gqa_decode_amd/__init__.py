@@ -36,6 +36,7 @@ EXPORTED_SYMBOLS = (
     "gated_attn_decode_ex",
     "gated_attn_decode_fp8kv",
     "gated_attn_decode_csr",
+    "gated_attn_decode_fp8kv_csr",
     "gated_attn_decode_time_stage1",
     "gated_attn_prefill",
     "gated_attn_prefill_ex",
@@ -132,6 +133,11 @@ def _load_library() -> ctypes.CDLL:
     lib.gated_attn_decode_csr.argtypes = [vp, vp, vp, vp, vp, vp, ctypes.c_int64, ctypes.c_float,
                                           vp, vp, ctypes.POINTER(DecodeDims), vp, sz,
                                           ctypes.POINTER(AttnOptions)]
+    lib.gated_attn_decode_fp8kv_csr.restype = ctypes.c_int
+    lib.gated_attn_decode_fp8kv_csr.argtypes = [vp, vp, vp, vp, vp, vp, ctypes.c_int64,
+                                                ctypes.c_float, ctypes.c_float, ctypes.c_float,
+                                                vp, vp, ctypes.POINTER(DecodeDims), vp, sz,
+                                                ctypes.POINTER(AttnOptions)]
     lib.gated_attn_qk_norm_rope.restype = ctypes.c_int
     lib.gated_attn_qk_norm_rope.argtypes = [vp, vp, vp, vp, vp, ctypes.c_float, vp, vp, vp, vp, vp,
                                             vp, vp, ctypes.POINTER(QkNormRopeDims)]
@@ -437,20 +443,25 @@ def qk_norm_rope(q, k, v, *, w_q=None, w_k=None, eps=1e-6, cos=None, sin=None,
 
 def decode_csr(q, gate, k_pool, v_pool, kv_indptr, kv_indices, scale, *, max_seq_len,
                out=None, workspace=None, stream=None, sinks=None, window=0, lse=None,
-               return_lse=False):
+               return_lse=False, k_descale=None, v_descale=None):
     """Gated GQA decode with CSR token indexing (page size 1,
     gated_attn_decode_csr): k_pool, v_pool [N, 1, H_kv, D] bf16 (or [N, H_kv, D]);
     kv_indptr int32 [B + 1]; kv_indices int32 [capacity]; ``max_seq_len`` is
-    the per-sequence capacity in tokens that fixes the plan.  Options as
-    :func:`decode`."""
+    the per-sequence capacity in tokens that fixes the plan.  Pools of e4m3
+    codes (float8_e4m3fn or uint8) with ``k_descale`` / ``v_descale`` go to
+    gated_attn_decode_fp8kv_csr.  Options as :func:`decode`."""
     torch = _torch()
     dev = q.device
     _need(q, "q", torch.bfloat16, 3, dev)
     _need(gate, "gate", torch.bfloat16, 3, dev)
     if k_pool.dim() == 3:
         k_pool, v_pool = k_pool.unsqueeze(1), v_pool.unsqueeze(1)
-    _need(k_pool, "k_pool", torch.bfloat16, 4, dev)
-    _need(v_pool, "v_pool", torch.bfloat16, 4, dev)
+    fp8 = k_pool.dtype in (torch.uint8, torch.float8_e4m3fn)
+    pool_dtype = k_pool.dtype if fp8 else torch.bfloat16
+    if fp8 != (k_descale is not None and v_descale is not None):
+        raise ValueError("e4m3 pools take k_descale and v_descale; bf16 pools take neither")
+    _need(k_pool, "k_pool", pool_dtype, 4, dev)
+    _need(v_pool, "v_pool", pool_dtype, 4, dev)
     _need(kv_indptr, "kv_indptr", torch.int32, 1, dev)
     _need(kv_indices, "kv_indices", torch.int32, 1, dev)
     B, Hq, D = q.shape
@@ -466,11 +477,15 @@ def decode_csr(q, gate, k_pool, v_pool, kv_indptr, kv_indices, scale, *, max_seq
     if return_lse and lse is None:
         lse = torch.empty((B, Hq), dtype=torch.float32, device=dev)
     opts = _options(sinks, window, lse, None, Hq, dev)
-    st = lib.gated_attn_decode_csr(
-        q.data_ptr(), gate.data_ptr(), k_pool.data_ptr(), v_pool.data_ptr(), kv_indptr.data_ptr(),
-        kv_indices.data_ptr(), kv_indices.numel(), float(scale), out.data_ptr(),
-        _stream_handle(stream, dev), ctypes.byref(dims), workspace.data_ptr(), workspace.numel(),
-        None if opts is None else ctypes.byref(opts))
-    check(st, "gated_attn_decode_csr")
+    head = [q.data_ptr(), gate.data_ptr(), k_pool.data_ptr(), v_pool.data_ptr(),
+            kv_indptr.data_ptr(), kv_indices.data_ptr(), kv_indices.numel(), float(scale)]
+    tail = [out.data_ptr(), _stream_handle(stream, dev), ctypes.byref(dims), workspace.data_ptr(),
+            workspace.numel(), None if opts is None else ctypes.byref(opts)]
+    if fp8:
+        st = lib.gated_attn_decode_fp8kv_csr(*head, float(k_descale), float(v_descale), *tail)
+        check(st, "gated_attn_decode_fp8kv_csr")
+    else:
+        st = lib.gated_attn_decode_csr(*head, *tail)
+        check(st, "gated_attn_decode_csr")
     return (out, lse) if return_lse else out
 

@@ -288,6 +288,19 @@ ga_status gated_attn_decode_fp8kv(const uint16_t* q, const uint16_t* gate, const
                      dims, workspace, workspace_bytes, opts);
 }
 
+ga_status gated_attn_decode_fp8kv_csr(const uint16_t* q, const uint16_t* gate,
+                                      const uint8_t* k_pool, const uint8_t* v_pool,
+                                      const int32_t* kv_indptr, const int32_t* kv_indices,
+                                      int64_t index_capacity, float scale, float k_descale,
+                                      float v_descale, uint16_t* out, void* stream,
+                                      const ga_decode_dims* dims, void* workspace,
+                                      size_t workspace_bytes, const ga_attn_options* opts) {
+  if (kv_indptr == nullptr || kv_indices == nullptr) return GA_ERR_INVALID_ARGUMENT;
+  const Indexing ix = {nullptr, nullptr, kv_indptr, kv_indices, index_capacity};
+  return decode_impl(q, gate, k_pool, v_pool, ix, scale, 1, k_descale, v_descale, out, stream,
+                     dims, workspace, workspace_bytes, opts);
+}
+
 ga_status gated_attn_decode(const uint16_t* q, const uint16_t* gate, const uint16_t* k_pool,
                             const uint16_t* v_pool, const int32_t* block_table,
                             const int32_t* seq_lens, float scale, uint16_t* out, void* stream,

@@ -251,6 +251,20 @@ ga_status gated_attn_decode_csr(const uint16_t *q, const uint16_t *gate, const u
                                 void *workspace, size_t workspace_bytes,
                                 const ga_attn_options *opts);
 
+/*
+ * gated_attn_decode_csr over e4m3 pools: the CSR token indexing of
+ * gated_attn_decode_csr with the e4m3 codes and per-tensor factors of
+ * gated_attn_decode_fp8kv (k_pool / v_pool [num_pages][1][H_kv][D], one byte
+ * per element).  Arguments, ownership and errors as those two entry points.
+ */
+ga_status gated_attn_decode_fp8kv_csr(const uint16_t *q, const uint16_t *gate,
+                                      const uint8_t *k_pool, const uint8_t *v_pool,
+                                      const int32_t *kv_indptr, const int32_t *kv_indices,
+                                      int64_t index_capacity, float scale, float k_descale,
+                                      float v_descale, uint16_t *out, void *stream,
+                                      const ga_decode_dims *dims, void *workspace,
+                                      size_t workspace_bytes, const ga_attn_options *opts);
+
 /* gated_attn_prefill with options appended.  opts == NULL is
  * gated_attn_prefill.  GA_ERR_INVALID_ARGUMENT for flags != 0 or a misaligned
  * pointer.  Key lengths mask keys only: a row past its sequence's length

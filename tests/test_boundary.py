@@ -295,3 +295,19 @@ def test_stream_read_argument_checks(src, nbytes, sink):
     """The measurement hook rejects NULL / misaligned pointers and sizes that
     are not whole 16-byte loads before any HIP call."""
     assert ga.lib.gated_attn_stream_read(src, nbytes, sink, None) == ga.GA_ERR_INVALID_ARGUMENT
+
+
+def test_fp8kv_csr_checks():
+    """The e4m3 CSR entry point: null row pointers or indices, and page
+    sizes other than 1, are declined before anything is enqueued."""
+    f = ga.lib.gated_attn_decode_fp8kv_csr
+    d1 = _dims(page_size=1)
+    assert f(FAKE, FAKE, FAKE, FAKE, None, FAKE, 1024, 0.0625, 0.01, 0.01, FAKE, None,
+             ctypes.byref(d1), FAKE, 1 << 40, None) == ga.GA_ERR_INVALID_ARGUMENT
+    assert f(FAKE, FAKE, FAKE, FAKE, FAKE, None, 1024, 0.0625, 0.01, 0.01, FAKE, None,
+             ctypes.byref(d1), FAKE, 1 << 40, None) == ga.GA_ERR_INVALID_ARGUMENT
+    d16 = _dims()
+    assert f(FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 1024, 0.0625, 0.01, 0.01, FAKE, None,
+             ctypes.byref(d16), FAKE, 1 << 40, None) == ga.GA_ERR_UNSUPPORTED
+    assert f(FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 1024, 0.0625, 0.0, 0.01, FAKE, None,
+             ctypes.byref(d1), FAKE, 1 << 40, None) == ga.GA_ERR_INVALID_ARGUMENT

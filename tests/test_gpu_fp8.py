@@ -108,3 +108,28 @@ def test_page_size_one_block_table():
     _parity(c1)
     paged, _ = _run(c)
     assert np.array_equal(got, paged)
+
+
+@pytest.mark.usefixtures("page1_copies")
+def test_csr_indexing():
+    """gated_attn_decode_fp8kv_csr: the same tokens addressed by CSR row
+    pointers and indices.  Within the rule against the oracle and bit-identical
+    to the page-size-1 block table over the same slots."""
+    c = workloads.make_decode("fp8_csr", [700, 1, 33, 0, 2049, 16], seed=144, kv_dtype="fp8",
+                              max_pages_per_seq=160)
+    k1, v1, indptr, idx, table = workloads.csr_layout(c, seed=145)
+    c1 = workloads.DecodeCase(c.name + "_p1", c.q, c.gate, k1, v1, table, c.seq_lens, c.scale,
+                              c.k_descale, c.v_descale)
+    out = ga.decode_csr(to_dev(c.q), to_dev(c.gate), to_dev(k1), to_dev(v1), to_dev(indptr),
+                        to_dev(idx), c.scale, max_seq_len=table.shape[1],
+                        k_descale=c.k_descale, v_descale=c.v_descale)
+    torch.cuda.synchronize()
+    got = to_np(out)
+    ref, o, mref = oracle.decode(c1.q, c1.gate, c1.k_pool, c1.v_pool, c1.block_table,
+                                 c1.seq_lens, c1.scale, k_descale=c1.k_descale,
+                                 v_descale=c1.v_descale)
+    res = check_outputs(got, ref, o, mref, oracle.sigmoid_table()[c.gate])
+    print(f"[parity] {c.name}: n={res['n']} bit-exact={res['n_bit_exact']} "
+          f"max_ulp_floor={res['max_ulp_floor']:.4f}", flush=True)
+    assert res["ok"], res
+    assert np.array_equal(got, _run(c1)[0])
