@@ -30,15 +30,17 @@ namespace {
 constexpr int kHeadDim = 256;
 constexpr int kPageSize = 16;
 constexpr int kSplitQuantum = 64;   // splits are whole 4-page groups
-// The largest split.  Fewer (sequence, kv head) pairs than target workgroups:
-// up to 16,384 tokens with 16-token pages (a wave keeps the page ids of its
-// up to 128 tiles in two registers), so the capacity-fixed grid holds few
-// splits and a short sequence in a large capacity leaves few empty
-// workgroups behind; at page size 1 the split's token slots are staged in
-// LDS, which holds 2,048.  As many pairs as target workgroups or more:
-// 2,048, so long sequences still split into enough workgroups to balance the
-// CUs.
-constexpr int kMaxSplitTokens = 2048;
+// The largest split.  At page size 1 the split's token slots are staged in
+// LDS, which holds 2,048.  With 16-token pages and fewer (sequence, kv head)
+// pairs than target workgroups: up to 16,384 tokens (a wave keeps the page ids
+// of its up to 128 tiles in two registers), so the capacity-fixed grid holds
+// few splits and a short sequence in a large capacity leaves few empty
+// workgroups behind.  As many pairs as target workgroups or more: 4,096, so
+// long sequences still split into several workgroups each, while each
+// workgroup streams enough tokens to amortise its start (measured at B=224,
+// L 4094..6142: 369 us per call with 4,096-token splits, 380 us with 2,048).
+constexpr int kMaxSplitTokens = 4096;
+constexpr int kMaxTokSplitTokens = 2048;
 constexpr int kMaxLongSplitTokens = 16384;
 constexpr int kMaxGridYZ = 65535;
 // A launch's grid size times its workgroup size must stay below 2^32 threads:
@@ -127,8 +129,9 @@ ga_status make_plan(const ga_decode_dims* d, ga_decode_plan* p) {
   int64_t t = (cap * (bkv > 0 ? bkv : 1) + GA_DECODE_TARGET_BLOCKS - 1) / GA_DECODE_TARGET_BLOCKS;
   t = ((t + kSplitQuantum - 1) / kSplitQuantum) * kSplitQuantum;
   if (t < kSplitQuantum) t = kSplitQuantum;
-  const int64_t t_max = (d->page_size == kPageSize && bkv < GA_DECODE_TARGET_BLOCKS)
-                            ? kMaxLongSplitTokens : kMaxSplitTokens;
+  const int64_t t_max = d->page_size != kPageSize           ? kMaxTokSplitTokens
+                        : bkv < GA_DECODE_TARGET_BLOCKS ? kMaxLongSplitTokens
+                                                        : kMaxSplitTokens;
   if (t > t_max) t = t_max;
   const int64_t ns = (cap + t - 1) / t;
   // stage-1 grid: one workgroup per (split, sequence, kv head)

@@ -50,7 +50,7 @@ def _dims(**kw):
 def test_plan_covers_capacity(B, W):
     p = ga.decode_plan(_dims(batch=B, max_pages_per_seq=W))
     cap = W * 16
-    t_max = 16384 if B * 2 < 256 else 2048
+    t_max = 16384 if B * 2 < 256 else 4096
     assert p.tokens_per_split % 64 == 0 and 64 <= p.tokens_per_split <= t_max
     assert p.num_splits * p.tokens_per_split >= cap
     assert (p.num_splits - 1) * p.tokens_per_split < cap
@@ -74,15 +74,15 @@ def test_supported_groups_plan(G):
 
 @pytest.mark.parametrize("B,Hkv,W,page,t_want,ns_want", [
     (64, 2, 2048, 16, 16384, 2),   # 128 pairs, capacity 32,768: two long splits
-    (128, 2, 2048, 16, 2048, 16),  # 256 pairs: splits of at most 2,048 tokens
-    (224, 2, 384, 16, 2048, 3),    # the serving shape
+    (128, 2, 2048, 16, 4096, 8),   # 256 pairs: splits of at most 4,096 tokens
+    (224, 2, 384, 16, 4096, 2),    # the serving shape
     (64, 2, 32768, 1, 2048, 16),   # page size 1: the token slots of a split fit LDS
     (1, 2, 2048, 16, 256, 128),    # one sequence: about 256 workgroups
 ])
 def test_split_cap(B, Hkv, W, page, t_want, ns_want):
     """The largest split: 16,384 tokens with 16-token pages while the
     (sequence, kv head) pairs are fewer than the 256 target workgroups, else
-    2,048 (and always 2,048 at page size 1)."""
+    4,096; always 2,048 at page size 1."""
     p = ga.decode_plan(_dims(batch=B, num_q_heads=8 * Hkv, num_kv_heads=Hkv, page_size=page,
                              max_pages_per_seq=W, num_pages=max(16384, W)))
     assert (p.tokens_per_split, p.num_splits) == (t_want, ns_want)
@@ -90,7 +90,7 @@ def test_split_cap(B, Hkv, W, page, t_want, ns_want):
 
 def test_oversize_stage1_grid_is_declined():
     """B * H_kv * splits beyond one launch's grid: declined before any launch."""
-    d = _dims(batch=65535, num_q_heads=64, num_kv_heads=8, max_pages_per_seq=2048)
+    d = _dims(batch=65535, num_q_heads=64, num_kv_heads=8, max_pages_per_seq=4096)
     p = ga.DecodePlan()
     assert ga.lib.gated_attn_decode_plan(ctypes.byref(d), ctypes.byref(p)) == ga.GA_ERR_UNSUPPORTED
     assert ga.decode_workspace_size(d) == 0
