@@ -69,6 +69,18 @@ def test_long_sequences_largest_split():
     assert res["ok"], res
 
 
+def test_long_sequences_many_pairs():
+    """256 (sequence, kv head) pairs in a capacity of 32,768 tokens: splits of
+    4,096 tokens (8 per sequence); long, page-ragged and short sequences, so
+    most of the short sequences' splits are empty."""
+    lens = [32768, 1, 4097, 32767, 0, 8192] + [17] * 122
+    c = workloads.make_decode("long_many", lens, seed=46, max_pages_per_seq=2048)
+    plan = ga.decode_plan(ga.decode_dims(**c.dims))
+    assert (plan.tokens_per_split, plan.num_splits) == (4096, 8)
+    res = decode_parity(c)
+    assert res["ok"], res
+
+
 def test_single_key_is_bit_exact():
     c = workloads.make_decode("L1", [1] * 24, seed=33)
     got = gpu_decode(c)
