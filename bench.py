@@ -7,13 +7,17 @@ K/V), inputs resident in HBM.  ``value`` is K/V bytes per second over the timed
 steps.  Decode measurements rotate over copies of their inputs (two for this
 workload) so that no call can read K/V the previous one left in the 256 MB
 Infinity Cache.  The same JSON line also carries:
-  * roofline   -- the stage-1 kernel's achieved HBM rate, from HIP events
-                  recorded around each of its launches in a second pass of K
-                  calls (the headline steps run without them);
-                  ``traffic`` from the committed rocprofv3 counter summary when
-                  it was taken on the current kernel source, else null;
+  * roofline   -- the stage-1 kernel's achieved HBM rate: K launches of that
+                  kernel alone (HIP graphs captured from the workload's calls
+                  with the stage-2 node removed), each between two HIP events
+                  on its stream; ``traffic`` from the committed rocprofv3
+                  counter summary when it was taken on the current kernel
+                  source, else null;
+  * launches_per_call -- kernel nodes of a HIP graph captured from one call;
   * cold       -- median of single calls, each after a 1 GiB cache flush;
-  * b1_l512    -- B=1, L=512 µs/call from replays of a 4-call HIP graph;
+  * b1_l512, b4_ragged -- the latency pair (B=1 L=512; B=4 L=512/495/478/461)
+                  in µs/call from replays of a 4-call HIP graph, B=1 also
+                  cold; launch_floor -- two dependent tiny kernels the same way;
   * prefill    -- B=2, S=2048 causal gated prefill µs/call and MFMA rate;
   * cpu_baseline -- the fp64 CPU oracle on the same B=64 workload.
 
@@ -73,17 +77,32 @@ def parse_args():
 
 
 class Hip:
-    """The few HIP event calls the timing needs, from the runtime torch loaded."""
+    """The few HIP runtime calls the timing needs (events and graphs), from the
+    runtime torch loaded."""
 
     def __init__(self):
         import torch  # noqa: F401  (loads the runtime this binds to)
 
-        self.lib = ctypes.CDLL("libamdhip64.so.7")
-        self.lib.hipEventCreate.argtypes = [ctypes.POINTER(ctypes.c_void_p)]
-        self.lib.hipEventCreateWithFlags.argtypes = [ctypes.POINTER(ctypes.c_void_p), ctypes.c_uint]
-        self.lib.hipEventElapsedTime.argtypes = [ctypes.POINTER(ctypes.c_float), ctypes.c_void_p,
-                                                 ctypes.c_void_p]
-        self.lib.hipEventDestroy.argtypes = [ctypes.c_void_p]
+        vp, P = ctypes.c_void_p, ctypes.POINTER
+        self.lib = L = ctypes.CDLL("libamdhip64.so.7")
+        L.hipEventCreateWithFlags.argtypes = [P(vp), ctypes.c_uint]
+        L.hipEventRecord.argtypes = [vp, vp]
+        L.hipEventElapsedTime.argtypes = [P(ctypes.c_float), vp, vp]
+        L.hipEventDestroy.argtypes = [vp]
+        L.hipStreamBeginCapture.argtypes = [vp, ctypes.c_int]
+        L.hipStreamEndCapture.argtypes = [vp, P(vp)]
+        L.hipGraphGetNodes.argtypes = [vp, P(vp), P(ctypes.c_size_t)]
+        L.hipGraphNodeGetType.argtypes = [vp, P(ctypes.c_int)]
+        L.hipGraphNodeGetDependencies.argtypes = [vp, P(vp), P(ctypes.c_size_t)]
+        L.hipGraphDestroyNode.argtypes = [vp]
+        L.hipGraphInstantiate.argtypes = [P(vp), vp, P(vp), ctypes.c_char_p, ctypes.c_size_t]
+        L.hipGraphLaunch.argtypes = [vp, vp]
+        L.hipGraphExecDestroy.argtypes = [vp]
+        L.hipGraphDestroy.argtypes = [vp]
+
+    def _ok(self, err, what):
+        if err != 0:
+            raise RuntimeError(f"{what} failed (hipError_t {err})")
 
     # Timing-only events: no system-scope fence (cache write-back and
     # invalidation) when they are recorded, so the interval between two of
@@ -95,20 +114,141 @@ class Hip:
         out = []
         for _ in range(n):
             e = ctypes.c_void_p()
-            if self.lib.hipEventCreateWithFlags(ctypes.byref(e), self.EVENT_DISABLE_SYSTEM_FENCE) != 0:
-                raise RuntimeError("hipEventCreateWithFlags failed")
+            self._ok(self.lib.hipEventCreateWithFlags(ctypes.byref(e), self.EVENT_DISABLE_SYSTEM_FENCE),
+                     "hipEventCreateWithFlags")
             out.append(e.value)
         return out
 
+    def record(self, ev, stream):
+        self._ok(self.lib.hipEventRecord(ctypes.c_void_p(ev), stream), "hipEventRecord")
+
     def elapsed_ms(self, a, b) -> float:
         ms = ctypes.c_float()
-        if self.lib.hipEventElapsedTime(ctypes.byref(ms), ctypes.c_void_p(a), ctypes.c_void_p(b)) != 0:
-            raise RuntimeError("hipEventElapsedTime failed")
+        self._ok(self.lib.hipEventElapsedTime(ctypes.byref(ms), ctypes.c_void_p(a), ctypes.c_void_p(b)),
+                 "hipEventElapsedTime")
         return float(ms.value)
 
     def destroy(self, evs):
         for e in evs:
             self.lib.hipEventDestroy(ctypes.c_void_p(e))
+
+    # ---- graphs ------------------------------------------------------------
+    KERNEL_NODE = 0   # hipGraphNodeTypeKernel
+    CAPTURE_RELAXED = 2
+
+    def capture(self, fn, stream) -> int:
+        """The hipGraph_t of everything fn() enqueues on `stream` (a torch side
+        stream's handle)."""
+        self._ok(self.lib.hipStreamBeginCapture(stream, self.CAPTURE_RELAXED), "hipStreamBeginCapture")
+        try:
+            fn()
+        finally:
+            g = ctypes.c_void_p()
+            self._ok(self.lib.hipStreamEndCapture(stream, ctypes.byref(g)), "hipStreamEndCapture")
+        return g.value
+
+    def nodes(self, graph):
+        n = ctypes.c_size_t(0)
+        self._ok(self.lib.hipGraphGetNodes(ctypes.c_void_p(graph), None, ctypes.byref(n)), "hipGraphGetNodes")
+        arr = (ctypes.c_void_p * max(n.value, 1))()
+        self._ok(self.lib.hipGraphGetNodes(ctypes.c_void_p(graph), arr, ctypes.byref(n)), "hipGraphGetNodes")
+        out = []
+        for i in range(n.value):
+            t = ctypes.c_int()
+            self._ok(self.lib.hipGraphNodeGetType(ctypes.c_void_p(arr[i]), ctypes.byref(t)),
+                     "hipGraphNodeGetType")
+            d = ctypes.c_size_t(0)
+            self._ok(self.lib.hipGraphNodeGetDependencies(ctypes.c_void_p(arr[i]), None, ctypes.byref(d)),
+                     "hipGraphNodeGetDependencies")
+            out.append((arr[i], t.value, d.value))
+        return out
+
+    def instantiate(self, graph) -> int:
+        e = ctypes.c_void_p()
+        self._ok(self.lib.hipGraphInstantiate(ctypes.byref(e), ctypes.c_void_p(graph), None, None, 0),
+                 "hipGraphInstantiate")
+        return e.value
+
+    def launch(self, exec_, stream):
+        self._ok(self.lib.hipGraphLaunch(ctypes.c_void_p(exec_), stream), "hipGraphLaunch")
+
+
+def call_graph_census(hip, fn, dev) -> dict:
+    """Kernel and non-kernel nodes of one captured call: the measured number of
+    launches a call makes (the gate must add none)."""
+    import torch
+
+    side = torch.cuda.Stream(device=dev)
+    torch.cuda.synchronize()
+    keep = fn.stream
+    fn.stream = ctypes.c_void_p(side.cuda_stream)
+    try:
+        g = hip.capture(fn, fn.stream)
+    finally:
+        fn.stream = keep
+    try:
+        nodes = hip.nodes(g)
+    finally:
+        hip.lib.hipGraphDestroy(ctypes.c_void_p(g))
+    kernels = sum(1 for _, t, _ in nodes if t == Hip.KERNEL_NODE)
+    return {"kernels": kernels, "other_nodes": len(nodes) - kernels,
+            "method": "nodes of a HIP graph captured from one call"}
+
+
+class Stage1Graphs:
+    """Stage 1 of a decode call on its own: each input set's call is captured
+    into a HIP graph, the dependent node (stage 2) is removed, and the rest --
+    the stage-1 kernel node -- is instantiated.  Launching one of these graphs
+    between two events on the same stream times that kernel alone, with no
+    hook in the library."""
+
+    def __init__(self, hip, calls, dev):
+        import torch
+
+        self.hip = hip
+        self.side = torch.cuda.Stream(device=dev)
+        self.stream = ctypes.c_void_p(self.side.cuda_stream)
+        self.execs, self.graphs = [], []
+        torch.cuda.synchronize()
+        for call in calls:
+            keep = call.stream
+            call.stream = self.stream
+            try:
+                g = hip.capture(call, self.stream)
+            finally:
+                call.stream = keep
+            nodes = hip.nodes(g)
+            roots = [n for n, t, d in nodes if t == Hip.KERNEL_NODE and d == 0]
+            dependents = [n for n, t, d in nodes if d > 0]
+            if len(roots) != 1 or len(nodes) != 2 or len(dependents) != 1:
+                raise RuntimeError(f"unexpected decode graph: {nodes}")
+            hip._ok(hip.lib.hipGraphDestroyNode(ctypes.c_void_p(dependents[0])), "hipGraphDestroyNode")
+            self.graphs.append(g)
+            self.execs.append(hip.instantiate(g))
+
+    def time(self, n: int) -> list:
+        """Per-launch ms of n stage-1 launches, input sets in turn."""
+        import torch
+
+        hip = self.hip
+        starts, stops = hip.events(n), hip.events(n)
+        for i in range(3):
+            hip.launch(self.execs[i % len(self.execs)], self.stream)
+        for i in range(n):
+            hip.record(starts[i], self.stream)
+            hip.launch(self.execs[i % len(self.execs)], self.stream)
+            hip.record(stops[i], self.stream)
+        self.side.synchronize()
+        torch.cuda.synchronize()
+        ms = [hip.elapsed_ms(a, b) for a, b in zip(starts, stops)]
+        hip.destroy(starts + stops)
+        return ms
+
+    def close(self):
+        for e in self.execs:
+            self.hip.lib.hipGraphExecDestroy(ctypes.c_void_p(e))
+        for g in self.graphs:
+            self.hip.lib.hipGraphDestroy(ctypes.c_void_p(g))
 
 
 def to_dev(a, dev):
@@ -170,6 +310,27 @@ class DecodeCall:
             self.ga.check(st, "gated_attn_decode")
 
 
+class PrefillCall:
+    """Pre-marshalled arguments of one gated_attn_prefill call (raw C entry)."""
+
+    def __init__(self, ga, p, dev, causal=True):
+        import torch
+
+        self.ga = ga
+        self.t = [to_dev(x, dev) for x in (p.q, p.gate, p.k, p.v)]
+        self.out = torch.empty_like(self.t[0])
+        B, S, Hq, D = p.q.shape
+        self.dims = ga.PrefillDims(B, S, Hq, p.k.shape[2], D)
+        self.args = [ctypes.c_void_p(x.data_ptr()) for x in self.t] + [
+            ctypes.c_float(p.scale), ctypes.c_int(int(causal)), ctypes.c_void_p(self.out.data_ptr())]
+        self.stream = ctypes.c_void_p(torch.cuda.current_stream(dev).cuda_stream)
+
+    def __call__(self):
+        st = self.ga.lib.gated_attn_prefill(*self.args, self.stream, ctypes.byref(self.dims))
+        if st != 0:
+            self.ga.check(st, "gated_attn_prefill")
+
+
 def time_prefill(ga, p, dev, n_calls: int, settle_s: float = 0.0) -> dict:
     """Causal gated prefill on case p: n_calls back-to-back calls."""
     import torch
@@ -204,6 +365,116 @@ def time_prefill(ga, p, dev, n_calls: int, settle_s: float = 0.0) -> dict:
             "mfma_bf16_frac": round(tflops / BF16_MFMA_PEAK_TFLOPS, 4),
             "note": "P is split into two bf16 terms, so the kernel issues 1.5x "
                     "the algorithmic MFMA work"}
+
+
+def _capture_torch_graph(fn, dev):
+    """A torch CUDAGraph of fn(stream): fn enqueues on the stream handle given."""
+    import torch
+
+    s = torch.cuda.Stream(device=dev)
+    s.wait_stream(torch.cuda.current_stream())
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g, stream=s):
+        fn(ctypes.c_void_p(torch.cuda.current_stream().cuda_stream))
+    torch.cuda.synchronize()
+    return g
+
+
+def _replay_samples(g, calls_per_graph: int, replays: int = 50, samples: int = 7) -> list:
+    import torch
+
+    for _ in range(10):
+        g.replay()
+    torch.cuda.synchronize()
+    out = []
+    for _ in range(samples):
+        a = torch.cuda.Event(enable_timing=True)
+        b = torch.cuda.Event(enable_timing=True)
+        a.record()
+        for _ in range(replays):
+            g.replay()
+        b.record()
+        torch.cuda.synchronize()
+        out.append(a.elapsed_time(b) * 1e3 / (replays * calls_per_graph))
+    return out
+
+
+def graph_latency(ga, case, dev) -> dict:
+    """us/call of a latency-bound decode: a HIP graph of 4 calls, 50 replays
+    per sample, median of 7 samples (the FreeToken PR's kernel-window method)."""
+    sc = DecodeCall(ga, case, dev)
+    sc()
+
+    def four(stream):
+        sc.stream = stream
+        for _ in range(4):
+            sc()
+    g = _capture_torch_graph(four, dev)
+    samples = _replay_samples(g, 4)
+    us = statistics.median(samples)
+    lens = ",".join(str(int(x)) for x in case.seq_lens)
+    return {"workload": f"gated GQA decode B={case.q.shape[0]} L={lens}, paged",
+            "us_per_call": round(us, 3),
+            "kv_gbs": round(case.kv_bytes() / (us * 1e-6) / 1e9, 2),
+            "method": "HIP graph of 4 calls, 50 replays per sample, median of 7",
+            "samples_us": [round(x, 3) for x in samples]}
+
+
+def cold_latency(ga, case, dev, blocks: int = 7, per_block: int = 31) -> dict:
+    """us of one call right after a 1 GiB write (every cache level holds other
+    lines): a graph of one call replayed between two events, the flush
+    enqueued before the first event (outside the timed span); 7 blocks of 31
+    samples, median."""
+    import torch
+
+    sc = DecodeCall(ga, case, dev)
+    sc()
+
+    def one(stream):
+        sc.stream = stream
+        sc()
+    g = _capture_torch_graph(one, dev)
+    flush = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
+    block_medians, allv = [], []
+    for _ in range(blocks):
+        xs = []
+        for _ in range(per_block):
+            flush.fill_(1)
+            a = torch.cuda.Event(enable_timing=True)
+            b = torch.cuda.Event(enable_timing=True)
+            a.record()
+            g.replay()
+            b.record()
+            torch.cuda.synchronize()
+            xs.append(a.elapsed_time(b) * 1e3)
+        block_medians.append(statistics.median(xs))
+        allv += xs
+    del flush, g
+    return {"us_per_call": round(statistics.median(allv), 3),
+            "block_medians_us": [round(x, 3) for x in block_medians],
+            "method": "1 GiB write before each single-call graph replay, outside the timed span; "
+                      f"{blocks} blocks x {per_block} samples, median"}
+
+
+def launch_floor(dev) -> dict:
+    """The replay floor of two dependent launches: a graph of 4 pairs of
+    one-element torch kernels, timed like graph_latency.  A decode call is two
+    launches, so this is the least a call can cost in a graph."""
+    import torch
+
+    x = torch.zeros(1, dtype=torch.float32, device=dev)
+
+    def pairs(stream):
+        for _ in range(4):
+            x.add_(1.0)
+            x.mul_(0.5)
+    g = _capture_torch_graph(pairs, dev)
+    samples = _replay_samples(g, 4)
+    return {"us_per_pair": round(statistics.median(samples), 3),
+            "method": "HIP graph of 4 pairs of dependent one-element kernels, 50 replays per "
+                      "sample, median of 7",
+            "samples_us": [round(v, 3) for v in samples]}
 
 
 # The MI355X's 256 MB Infinity Cache (MALL) sits between L2 and HBM.  Back-to-
@@ -501,18 +772,16 @@ def main() -> int:
     torch.cuda.synchronize()
     total_ms = e0.elapsed_time(e1)
 
-    # Stage-1 duration: the same K calls again, each stage-1 launch bracketed by
-    # HIP events on the launch stream (the library records them around it).
-    starts, stops = hip.events(K), hip.events(K)
-    arr_s = (ctypes.c_void_p * K)(*starts)
-    arr_e = (ctypes.c_void_p * K)(*stops)
-    ga.check(ga.lib.gated_attn_decode_time_stage1(arr_s, arr_e, K), "time_stage1")
-    for _ in range(K):
-        call()
-    torch.cuda.synchronize()
-    ga.check(ga.lib.gated_attn_decode_time_stage1(None, None, 0), "time_stage1")
-    kernel_ms = [hip.elapsed_ms(a, b) for a, b in zip(starts, stops)]
-    hip.destroy(starts + stops)
+    # Stage-1 duration: K launches of the stage-1 kernel alone (graphs captured
+    # from this workload's calls with the stage-2 node removed), each between
+    # two HIP events on the stream it is launched on.
+    s1 = Stage1Graphs(hip, call.calls, dev)
+    kernel_ms = s1.time(K)
+    s1.close()
+    census = call_graph_census(hip, call.calls[0], dev)
+    pcall = PrefillCall(ga, workloads.workload(4), dev)
+    census_prefill = call_graph_census(hip, pcall, dev)
+    del pcall
 
     ms_per_step = total_ms / K
     value = kv_bytes / (ms_per_step * 1e-3) / 1e9
@@ -550,7 +819,8 @@ def main() -> int:
         "us_per_call": round(ms_per_step * 1e3, 3),
         "kv_bytes_per_call": kv_bytes,
         "hbm_frac": round(value / HBM_PEAK_GBS, 4),
-        "launches_per_call": 2,
+        "launches_per_call": census["kernels"],
+        "launch_census": {"decode": census, "prefill": census_prefill},
         "roofline": {
             "kernel": "decode_stage1_kernel",
             "bound": "hbm",
@@ -585,40 +855,12 @@ def main() -> int:
                           "hbm_frac": round(kv_bytes / (cold_ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
                           "samples": 31, "flush_bytes": 1 << 30}
 
-        # ---- B=1, L=512: replays of a graph of 4 calls (launch-bound) -------
+        # ---- latency pair: B=1 L=512 and B=4 ragged, graph replays -----------
         small = workloads.workload(0, poison=False)
-        sc = DecodeCall(ga, small, dev)
-        s = torch.cuda.Stream()
-        s.wait_stream(torch.cuda.current_stream())
-        with torch.cuda.stream(s):
-            sc.stream = ctypes.c_void_p(s.cuda_stream)
-            sc()
-        torch.cuda.current_stream().wait_stream(s)
-        torch.cuda.synchronize()
-        g = torch.cuda.CUDAGraph()
-        with torch.cuda.graph(g):
-            sc.stream = ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
-            for _ in range(4):
-                sc()
-        for _ in range(10):
-            g.replay()
-        torch.cuda.synchronize()
-        samples = []
-        for _ in range(7):
-            a = torch.cuda.Event(enable_timing=True)
-            b = torch.cuda.Event(enable_timing=True)
-            a.record()
-            for _ in range(50):
-                g.replay()
-            b.record()
-            torch.cuda.synchronize()
-            samples.append(a.elapsed_time(b) * 1e3 / 200)
-        us = statistics.median(samples)
-        result["b1_l512"] = {"us_per_call": round(us, 3),
-                             "kv_gbs": round(small.kv_bytes() / (us * 1e-6) / 1e9, 2),
-                             "method": "HIP graph of 4 calls, 50 replays per sample, median of 7",
-                             "samples_us": [round(x, 3) for x in samples]}
-        del g
+        result["b1_l512"] = graph_latency(ga, small, dev)
+        result["b1_l512"]["cold"] = cold_latency(ga, small, dev)
+        result["b4_ragged"] = graph_latency(ga, workloads.workload(1, poison=False), dev)
+        result["launch_floor"] = launch_floor(dev)
 
         result["prefill"] = time_prefill(ga, workloads.workload(4), dev, 20, settle_s=0.1)
 
@@ -658,7 +900,8 @@ def main() -> int:
         import oracle
 
         # The oracle as it stands, on the same B=64 workload, repeated until
-        # about 12 thread-seconds of CPU work have been done.
+        # about 12 thread-seconds of CPU work have been done, on every core of
+        # the affinity mask within the process's CPU share.
         threads = oracle.default_threads()
         reps, busy = 0, 0.0
         t = time.time()
@@ -667,19 +910,26 @@ def main() -> int:
                           case.seq_lens, case.scale, nthreads=threads)
             reps += 1
             busy = time.time() - t
-        result["cpu_baseline"] = {"value": round(reps * kv_bytes / busy / 1e9, 4), "unit": "GB/s",
-                                  "cores": threads, "kind": "oracle",
-                                  "sample": f"the whole B=64 L=4096 workload, {reps} call(s) "
-                                            f"({busy:.2f} s wall, fp64, {threads} threads)",
-                                  "seconds_per_call": round(busy / reps, 3)}
-        # and one thread on the B=1, L=512 workload (latency, not throughput)
-        small = workloads.workload(0, poison=False)
-        reps1, t = 0, time.time()
-        while reps1 == 0 or time.time() - t < 0.5:
-            oracle.decode(small.q, small.gate, small.k_pool, small.v_pool, small.block_table,
-                          small.seq_lens, small.scale, nthreads=1)
-            reps1 += 1
-        result["cpu_baseline"]["b1_l512_one_thread_ms"] = round((time.time() - t) / reps1 * 1e3, 3)
+        result["cpu_baseline"] = {
+            "value": round(reps * kv_bytes / busy / 1e9, 4), "unit": "GB/s",
+            "cores": threads, "kind": "oracle",
+            "sample": f"the whole B=64 L=4096 workload, {reps} call(s) "
+                      f"({busy:.2f} s wall, fp64, {threads} threads)",
+            "seconds_per_call": round(busy / reps, 3),
+            "affinity_cores": oracle.affinity_cores(),
+            "cpu_share": oracle.cpu_share(),
+            "cpu_model": oracle.cpu_model()}
+
+        # and one thread on each latency workload (B=1 L=512, B=4 ragged)
+        def one_thread_ms(c) -> float:
+            n, t0 = 0, time.time()
+            while n == 0 or time.time() - t0 < 0.5:
+                oracle.decode(c.q, c.gate, c.k_pool, c.v_pool, c.block_table, c.seq_lens,
+                              c.scale, nthreads=1)
+                n += 1
+            return round((time.time() - t0) / n * 1e3, 3)
+        result["cpu_baseline"]["b1_l512_one_thread_ms"] = one_thread_ms(workloads.workload(0, poison=False))
+        result["cpu_baseline"]["b4_ragged_one_thread_ms"] = one_thread_ms(workloads.workload(1, poison=False))
     result["settle"] = {"seconds": round(settle_s, 3), "calls": settle_calls}
     result["input_generation_s"] = round(gen_s, 2)
     line = json.dumps(result)

@@ -37,7 +37,6 @@ EXPORTED_SYMBOLS = (
     "gated_attn_decode_fp8kv",
     "gated_attn_decode_csr",
     "gated_attn_decode_fp8kv_csr",
-    "gated_attn_decode_time_stage1",
     "gated_attn_prefill",
     "gated_attn_prefill_ex",
     "gated_attn_qk_norm_rope",
@@ -150,9 +149,6 @@ def _load_library() -> ctypes.CDLL:
                                        ctypes.POINTER(PrefillDims)]
     lib.gated_attn_stream_read.restype = ctypes.c_int
     lib.gated_attn_stream_read.argtypes = [vp, sz, vp, vp]
-    lib.gated_attn_decode_time_stage1.restype = ctypes.c_int
-    lib.gated_attn_decode_time_stage1.argtypes = [ctypes.POINTER(ctypes.c_void_p),
-                                                  ctypes.POINTER(ctypes.c_void_p), ctypes.c_int]
     lib.gated_attn_status_string.restype = ctypes.c_char_p
     lib.gated_attn_status_string.argtypes = [ctypes.c_int]
     lib.gated_attn_last_hip_error.restype = ctypes.c_int

@@ -50,15 +50,6 @@ constexpr int64_t kMaxDecodeRows = (int64_t)1 << 26;
 
 thread_local int g_last_hip_error = 0;
 
-// Armed stage-1 timing events of this thread (gated_attn_decode_time_stage1).
-struct TimingHook {
-  void* const* starts = nullptr;
-  void* const* stops = nullptr;
-  int n = 0;
-  int next = 0;
-};
-thread_local TimingHook g_timing;
-
 bool aligned(const void* p, size_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
 
 ga_status hip_fail(hipError_t e) {
@@ -242,13 +233,6 @@ ga_status decode_impl(const uint16_t* q, const uint16_t* gate, const void* k_poo
   L.sinks = opts != nullptr ? opts->sinks : nullptr;
   L.lse = opts != nullptr ? opts->lse : nullptr;
   L.window = opts != nullptr && opts->window > 0 ? opts->window : 0;
-  L.stage1_start = nullptr;
-  L.stage1_stop = nullptr;
-  if (g_timing.next < g_timing.n) {
-    L.stage1_start = static_cast<hipEvent_t>(g_timing.starts[g_timing.next]);
-    L.stage1_stop = static_cast<hipEvent_t>(g_timing.stops[g_timing.next]);
-    ++g_timing.next;
-  }
   hipError_t e = ga::launch_decode(L, static_cast<hipStream_t>(stream));
   if (e != hipSuccess) return hip_fail(e);
   return GA_OK;
@@ -416,15 +400,6 @@ ga_status gated_attn_qk_norm_rope(const uint16_t* q, const uint16_t* k, const ui
   P.rope_dim = dims->rope_dim;
   hipError_t e = ga::launch_qk_norm_rope(P, static_cast<hipStream_t>(stream));
   if (e != hipSuccess) return hip_fail(e);
-  return GA_OK;
-}
-
-ga_status gated_attn_decode_time_stage1(void* const* starts, void* const* stops, int n) {
-  if (n < 0 || (n > 0 && (starts == nullptr || stops == nullptr))) return GA_ERR_INVALID_ARGUMENT;
-  g_timing.starts = n > 0 ? starts : nullptr;
-  g_timing.stops = n > 0 ? stops : nullptr;
-  g_timing.n = n;
-  g_timing.next = 0;
   return GA_OK;
 }
 

@@ -41,9 +41,6 @@
 #include <math.h>
 #include <stdint.h>
 
-#include <cstdlib>
-#include <cstring>
-
 #include "ga_device.h"
 #include "ga_internal.h"
 
@@ -843,15 +840,12 @@ __global__ __launch_bounds__(256) void decode_stage2_gate_kernel(Stage2Args a) {
 }
 
 // Page size 1: the copies address a token's row by a 32-bit offset from the
-// pool's start unless the pool's rows span more bytes than that (or the
-// environment variable GATED_ATTN_DECODE_WIDE is "1", which forces the 64-bit
-// address form for testing it on small pools).
+// pool's start unless the pool's rows span more bytes than that; then the
+// 64-bit address form is used.  The choice follows from the pool's size alone.
 bool wide_offsets(const DecodeLaunch& d) {
   const unsigned long long bytes =
       (unsigned long long)d.num_pages * d.num_kv_heads * kD * (d.kv_fp8 ? 1 : 2);
-  if (bytes > 0xffffffffull) return true;
-  const char* e = std::getenv("GATED_ATTN_DECODE_WIDE");
-  return e != nullptr && std::strcmp(e, "1") == 0;
+  return bytes > 0xffffffffull;
 }
 
 hipError_t launch_decode(const DecodeLaunch& d, hipStream_t stream) {
@@ -879,10 +873,6 @@ hipError_t launch_decode(const DecodeLaunch& d, hipStream_t stream) {
   a1.num_units = d.batch * d.num_kv_heads * d.num_splits;
   dim3 grid1(a1.num_units);
   hipError_t err;
-  if (d.stage1_start != nullptr) {
-    err = hipEventRecord(d.stage1_start, stream);
-    if (err != hipSuccess) return err;
-  }
   const dim3 block(kWaves * 64);
   if (d.kv_fp8 && d.page_size == 1 && wide_offsets(d))
     hipLaunchKernelGGL(decode_stage1_fp8_tok_wide_kernel, grid1, block, 0, stream, a1);
@@ -898,10 +888,6 @@ hipError_t launch_decode(const DecodeLaunch& d, hipStream_t stream) {
     hipLaunchKernelGGL(decode_stage1_kernel, grid1, block, 0, stream, a1);
   err = hipGetLastError();
   if (err != hipSuccess) return err;
-  if (d.stage1_stop != nullptr) {
-    err = hipEventRecord(d.stage1_stop, stream);
-    if (err != hipSuccess) return err;
-  }
 
   Stage2Args a2;
   a2.gate = d.gate;

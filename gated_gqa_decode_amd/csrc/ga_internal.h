@@ -45,8 +45,6 @@ struct DecodeLaunch {
   const float* sinks;  // [H_q] sink logits
   float* lse;          // [B][H_q] log-sum-exp output
   int window;          // > 0: sliding window of that many keys
-  hipEvent_t stage1_start;  // recorded around stage 1 when non-null
-  hipEvent_t stage1_stop;
 };
 
 struct PrefillLaunch {

@@ -99,15 +99,16 @@ size_t gated_attn_decode_workspace_size(const ga_decode_dims *dims);
  * gate and the rounded product -- two kernel launches per call, none of them
  * for the gate.  At page size 1 the first launch addresses token rows by
  * 32-bit offsets from the pool's start, or by 64-bit addresses when the pool's
- * rows span more than 4 GiB; setting the environment variable
- * GATED_ATTN_DECODE_WIDE to "1" forces the 64-bit form (testing; the results
- * are identical either way).
+ * rows span more than 4 GiB (chosen from num_pages alone; the results are
+ * identical either way).
  *
  *   q, gate     [B][H_q][D]                       bf16, read
  *   k_pool,
  *   v_pool      [num_pages][page_size][H_kv][D]   bf16, read
- *   block_table [B][max_pages_per_seq]            int32 page ids, read; entries
- *               at or past ceil(seq_lens[b] / page_size) are never read
+ *   block_table [B][max_pages_per_seq]            int32 page ids, read; any
+ *               entry of row b may be read (they are loaded before the length
+ *               is known), but the values at or past ceil(seq_lens[b] /
+ *               page_size) are ignored: they may hold anything (e.g. -1)
  *   seq_lens    [B]                               int32 KV lengths, read;
  *               <= 0 marks a padded slot (its output row is +0)
  *   scale       softmax scale (finite, > 0), e.g. 1/sqrt(D)
@@ -125,17 +126,6 @@ ga_status gated_attn_decode(const uint16_t *q, const uint16_t *gate, const uint1
                             const uint16_t *v_pool, const int32_t *block_table,
                             const int32_t *seq_lens, float scale, uint16_t *out, void *stream,
                             const ga_decode_dims *dims, void *workspace, size_t workspace_bytes);
-
-/* Measurement hook for benchmarks and profilers.  Arms the calling thread's
- * next n gated_attn_decode calls: the i-th of them records starts[i] on its
- * stream immediately before its stage-1 kernel and stops[i] immediately after
- * it, so hipEventElapsedTime(starts[i], stops[i]) bounds that kernel's
- * duration from above (the interval also holds the event packets and the
- * kernel's dispatch: a few microseconds on MI355X).
- * The events (hipEvent_t) are created, owned and destroyed by the caller and
- * must stay valid until recorded.  n == 0 disarms.  Results are unaffected.
- * GA_ERR_INVALID_ARGUMENT for n < 0, or n > 0 with a NULL array. */
-ga_status gated_attn_decode_time_stage1(void *const *starts, void *const *stops, int n);
 
 /* Measurement hook for benchmarks: reads `bytes` of device memory at `src`
  * once, with the non-temporal 16-byte loads the decode's K/V stream uses, in

@@ -92,13 +92,41 @@ def _load():
     return lib
 
 
-def default_threads() -> int:
-    """Host threads the oracle uses: the process affinity set, at most 16."""
+def affinity_cores() -> int:
+    """Cores in this process's affinity mask."""
     try:
-        n = len(os.sched_getaffinity(0))
+        return len(os.sched_getaffinity(0))
     except AttributeError:  # pragma: no cover
-        n = os.cpu_count() or 1
-    return max(1, min(n, 16))
+        return os.cpu_count() or 1
+
+
+def cpu_share() -> int:
+    """The CPU share granted to this process: OMP_NUM_THREADS when the
+    environment sets it (a machine shared between GPUs grants each GPU's
+    process a fixed number of cores), else the whole affinity mask."""
+    try:
+        n = int(os.environ.get("OMP_NUM_THREADS", "0"))
+    except ValueError:
+        n = 0
+    return n if n > 0 else affinity_cores()
+
+
+def default_threads() -> int:
+    """Host threads the oracle uses: every core of the affinity mask, within
+    the process's CPU share."""
+    return max(1, min(affinity_cores(), cpu_share()))
+
+
+def cpu_model() -> str:
+    """The host CPU's model name (from /proc/cpuinfo), or '' if unknown."""
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return ""
 
 
 def _ptr(a: np.ndarray, ctype):

@@ -48,5 +48,5 @@ def decode_parity(c, got=None) -> dict:
     res["name"] = c.name
     print(f"[parity] {c.name}: n={res['n']} bit-exact={res['n_bit_exact']} "
           f"max_ulp_floor={res['max_ulp_floor']:.4f} strict_fail={res['n_fail_strict']} "
-          f"max_ulp_strict={res['max_ulp_strict']:.3f}", flush=True)
+          f"max_ulp_strict={res['max_ulp_strict']:.3f} model_fail={res['n_fail_model']}", flush=True)
     return res

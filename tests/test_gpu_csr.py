@@ -13,7 +13,7 @@ from oracle.compare import check_outputs
 
 import gated_gqa_decode_amd as ga
 
-pytestmark = [pytest.mark.gpu, pytest.mark.usefixtures("page1_copies")]
+pytestmark = pytest.mark.gpu
 
 
 def _csr_gpu(c, k1, v1, indptr, idx, **kw):

@@ -90,7 +90,6 @@ def test_fp8_single_key_is_bit_exact():
     assert np.array_equal(got, ref)
 
 
-@pytest.mark.usefixtures("page1_copies")
 def test_page_size_one_block_table():
     """e4m3 pools at page size 1: every token its own pool row at a shuffled
     slot (spare slots NaN codes), the block table holding token slots.  Within
@@ -110,7 +109,6 @@ def test_page_size_one_block_table():
     assert np.array_equal(got, paged)
 
 
-@pytest.mark.usefixtures("page1_copies")
 def test_csr_indexing():
     """gated_attn_decode_fp8kv_csr: the same tokens addressed by CSR row
     pointers and indices.  Within the rule against the oracle and bit-identical

@@ -4,7 +4,10 @@ import pytest
 
 import oracle
 import workloads
-from gpu_helpers import gpu_prefill
+import torch
+
+import gated_gqa_decode_amd as ga
+from gpu_helpers import DEV, gpu_prefill, to_dev, to_np
 from oracle.compare import check_outputs
 
 pytestmark = pytest.mark.gpu
@@ -18,7 +21,7 @@ def _parity(p, got, rows=None):
     res = check_outputs(got, ref, o, mref, oracle.sigmoid_table()[gate])
     print(f"[parity] {p.name}: n={res['n']} bit-exact={res['n_bit_exact']} "
           f"max_ulp_floor={res['max_ulp_floor']:.4f} strict_fail={res['n_fail_strict']} "
-          f"max_ulp_strict={res['max_ulp_strict']:.3f}", flush=True)
+          f"max_ulp_strict={res['max_ulp_strict']:.3f} model_fail={res['n_fail_model']}", flush=True)
     return res
 
 
@@ -43,19 +46,20 @@ def test_gqa_group_sizes(Hq, Hkv, causal):
     assert res["ok"], res
 
 
-def test_workload4_full_size_sampled_rows():
-    """B=2, S=2048 causal, in the launch configuration the benchmark times;
-    checked on 72 query positions per sequence (tile edges, ends, random)."""
+def test_workload4_full_size_every_element():
+    """B=2, S=2048 causal, in the launch configuration the benchmark times:
+    every one of the 16.8 M outputs against the oracle.  The output is
+    NaN-poisoned before the call, so a query tile the kernel never writes (or
+    writes elsewhere) fails."""
     p = workloads.workload(4)
-    got = gpu_prefill(p)
-    rng = np.random.default_rng(4)
-    pos = {0, 1, 15, 16, 17, 63, 64, 65, 127, 128, 255, 256, 1023, 1024, 1025, 2031, 2032,
-           2046, 2047}
-    pos |= set(int(x) for x in rng.integers(0, 2048, size=72 - len(pos)))
-    rows = np.array([(b, i) for b in range(2) for i in sorted(pos)], dtype=np.int32)
-    res = _parity(p, got, rows)
+    out = torch.full(p.q.shape, float("nan"), dtype=torch.bfloat16, device=DEV)
+    ga.prefill(to_dev(p.q), to_dev(p.gate), to_dev(p.k), to_dev(p.v), p.scale, causal=True,
+               out=out)
+    torch.cuda.synchronize()
+    got = to_np(out)
+    assert not np.any((got & 0x7F80) == 0x7F80), "non-finite (unwritten?) output"
+    res = _parity(p, got)
     assert res["ok"], res
-    assert not np.any((got & 0x7F80) == 0x7F80), "non-finite output"
 
 
 def test_identical_kv_rows_bit_exact():

@@ -108,9 +108,11 @@ def test_decode_plain_entry_matches_ex_with_zero_options():
 def _prefill_parity(p, kv_lens=None, sinks=None, window=0, rows=None):
     kl = None if kv_lens is None else torch.tensor(kv_lens, dtype=torch.int32, device=DEV)
     sk = None if sinks is None else torch.tensor(sinks, dtype=torch.float32, device=DEV)
-    out, lse = ga.prefill(to_dev(p.q), to_dev(p.gate), to_dev(p.k), to_dev(p.v), p.scale,
-                          causal=p.causal, kv_lens=kl, sinks=sk, window=window,
-                          return_lse=True)
+    # outputs poisoned with NaN first: an element the kernel never writes fails
+    out = torch.full(p.q.shape, float("nan"), dtype=torch.bfloat16, device=DEV)
+    lse = torch.full(p.q.shape[:3], float("nan"), dtype=torch.float32, device=DEV)
+    ga.prefill(to_dev(p.q), to_dev(p.gate), to_dev(p.k), to_dev(p.v), p.scale,
+               causal=p.causal, kv_lens=kl, sinks=sk, window=window, out=out, lse=lse)
     torch.cuda.synchronize()
     got, got_lse = to_np(out), to_np(lse)
     ref, o, mref, ref_lse = oracle.prefill(p.q, p.gate, p.k, p.v, p.scale, causal=p.causal,
@@ -122,7 +124,8 @@ def _prefill_parity(p, kv_lens=None, sinks=None, window=0, rows=None):
         gate = p.gate[rows[:, 0], rows[:, 1]]
     res = check_outputs(got, ref, o, mref, oracle.sigmoid_table()[gate])
     print(f"[parity] {p.name} lens={kv_lens} window={window} sinks={sinks is not None}: "
-          f"n={res['n']} max_ulp_floor={res['max_ulp_floor']:.4f}", flush=True)
+          f"n={res['n']} bit-exact={res['n_bit_exact']} max_ulp_floor={res['max_ulp_floor']:.4f} "
+          f"strict_fail={res['n_fail_strict']} model_fail={res['n_fail_model']}", flush=True)
     assert res["ok"], res
     _check_lse(got_lse, ref_lse, p.name)
 
@@ -145,12 +148,10 @@ def test_prefill_options_groups():
                         .astype(np.float64), 40)
 
 
-def test_prefill_options_full_size_sampled_rows():
+def test_prefill_options_full_size_every_element():
     """B = 2, S = 2048 causal with key lengths (2048, 1500), a 512-key window,
-    sinks and lse; 48 query positions per sequence."""
+    sinks and lse, in the benchmark's launch configuration: every one of the
+    16.8 M outputs and 65,536 lse values against the oracle, out and lse
+    NaN-poisoned before the call."""
     p = workloads.workload(4)
-    rng = np.random.default_rng(7)
-    pos = {0, 1, 63, 64, 511, 512, 513, 1499, 1500, 1501, 2047}
-    pos |= set(int(x) for x in rng.integers(0, 2048, size=48 - len(pos)))
-    rows = np.array([(b, i) for b in range(2) for i in sorted(pos)], dtype=np.int32)
-    _prefill_parity(p, [2048, 1500], np.full(16, -0.5), 512, rows)
+    _prefill_parity(p, [2048, 1500], np.full(16, -0.5), 512)
