@@ -36,6 +36,7 @@ EXPORTED_SYMBOLS = (
     "gated_attn_decode_ex",
     "gated_attn_decode_fp8kv",
     "gated_attn_decode_csr",
+    "gated_attn_decode_noalloc",
     "gated_attn_decode_fp8kv_csr",
     "gated_attn_prefill",
     "gated_attn_prefill_ex",
@@ -120,6 +121,9 @@ def _load_library() -> ctypes.CDLL:
     lib.gated_attn_decode.restype = ctypes.c_int
     lib.gated_attn_decode.argtypes = [vp, vp, vp, vp, vp, vp, ctypes.c_float, vp, vp,
                                       ctypes.POINTER(DecodeDims), vp, sz]
+    lib.gated_attn_decode_noalloc.restype = ctypes.c_int
+    lib.gated_attn_decode_noalloc.argtypes = [vp, vp, vp, vp, vp, vp, ctypes.c_float, vp, vp,
+                                              ctypes.POINTER(DecodeDims)]
     lib.gated_attn_decode_ex.restype = ctypes.c_int
     lib.gated_attn_decode_ex.argtypes = [vp, vp, vp, vp, vp, vp, ctypes.c_float, vp, vp,
                                          ctypes.POINTER(DecodeDims), vp, sz,

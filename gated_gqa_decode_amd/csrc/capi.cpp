@@ -11,6 +11,7 @@
 #include <cmath>
 #include <cstdint>
 #include <cstring>
+#include <mutex>
 
 #include "ga_internal.h"
 #include "gated_attn.h"
@@ -50,6 +51,18 @@ constexpr int64_t kMaxDecodeRows = (int64_t)1 << 26;
 
 thread_local int g_last_hip_error = 0;
 
+// Device memory of gated_attn_decode_noalloc: the fp32 split partials that
+// gated_attn_decode keeps in the caller's workspace.  Every GPU the library
+// runs on holds its own copy from the code object's load until the process
+// ends.  Host code never uses the name itself (on the host it stands for a
+// host-side shadow, not a device address): the device address comes from
+// hipGetSymbolAddress, once per device, and only that pointer is passed on.
+constexpr size_t kScratchBytes = GA_DECODE_SCRATCH_BYTES;
+constexpr int kMaxDevices = 64;
+__device__ __align__(256) unsigned char scratch[kScratchBytes];
+std::atomic<void*> g_scratch_ptr[kMaxDevices];
+std::mutex g_scratch_mu;
+
 bool aligned(const void* p, size_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
 
 ga_status hip_fail(hipError_t e) {
@@ -74,6 +87,28 @@ ga_status check_device() {
   const bool ok = std::strncmp(prop.gcnArchName, "gfx950", 6) == 0;
   if (dev >= 0 && dev < 64) cache[dev].store(ok ? 1 : 2, std::memory_order_relaxed);
   return ok ? GA_OK : GA_ERR_UNSUPPORTED;
+}
+
+// This device's copy of `scratch`: its address is looked up on the first call
+// with the device current and kept.
+ga_status device_scratch(void** out) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return hip_fail(e);
+  if (dev < 0 || dev >= kMaxDevices) return GA_ERR_UNSUPPORTED;
+  void* p = g_scratch_ptr[dev].load(std::memory_order_acquire);
+  if (p == nullptr) {
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    p = g_scratch_ptr[dev].load(std::memory_order_relaxed);
+    if (p == nullptr) {
+      e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+      if (e != hipSuccess) return hip_fail(e);
+      if (p == nullptr) return hip_fail(hipErrorInvalidSymbol);
+      g_scratch_ptr[dev].store(p, std::memory_order_release);
+    }
+  }
+  *out = p;
+  return GA_OK;
 }
 
 ga_status check_heads(int32_t hq, int32_t hkv, int32_t d) {
@@ -294,6 +329,25 @@ ga_status gated_attn_decode(const uint16_t* q, const uint16_t* gate, const uint1
                             const ga_decode_dims* dims, void* workspace, size_t workspace_bytes) {
   return gated_attn_decode_ex(q, gate, k_pool, v_pool, block_table, seq_lens, scale, out, stream,
                               dims, workspace, workspace_bytes, nullptr);
+}
+
+ga_status gated_attn_decode_noalloc(const uint16_t* q, const uint16_t* gate,
+                                    const uint16_t* k_pool, const uint16_t* v_pool,
+                                    const int32_t* block_table, const int32_t* seq_lens,
+                                    float scale, uint16_t* out, void* stream,
+                                    const ga_decode_dims* dims) {
+  ga_decode_plan plan;
+  ga_status st = gated_attn_decode_plan(dims, &plan);
+  if (st != GA_OK) return st;
+  if (plan.workspace_bytes > kScratchBytes) return GA_ERR_WORKSPACE_TOO_SMALL;
+  if (dims->batch == 0) return GA_OK;
+  st = check_device();
+  if (st != GA_OK) return st;
+  void* ws = nullptr;
+  st = device_scratch(&ws);
+  if (st != GA_OK) return st;
+  return gated_attn_decode_ex(q, gate, k_pool, v_pool, block_table, seq_lens, scale, out, stream,
+                              dims, ws, kScratchBytes, nullptr);
 }
 
 ga_status gated_attn_prefill_ex(const uint16_t* q, const uint16_t* gate, const uint16_t* k,

@@ -127,6 +127,34 @@ ga_status gated_attn_decode(const uint16_t *q, const uint16_t *gate, const uint1
                             const int32_t *seq_lens, float scale, uint16_t *out, void *stream,
                             const ga_decode_dims *dims, void *workspace, size_t workspace_bytes);
 
+/* Bytes of device memory gated_attn_decode_noalloc keeps per GPU for the
+ * split partials (16 MiB). */
+#define GA_DECODE_SCRATCH_BYTES (16u << 20)
+
+/*
+ * gated_attn_decode for callers that cannot allocate device memory or pass a
+ * workspace -- code under HIP graph capture, tight serving loops, harnesses
+ * that forbid hipMalloc.  Same operation, kernels, arguments (minus the
+ * workspace) and errors as gated_attn_decode; the split partials go to a
+ * device array of GA_DECODE_SCRATCH_BYTES that the library holds on every GPU
+ * it runs on until the process ends.  Nothing is allocated or freed by the
+ * call; its first call on a device looks up that device's array (call it
+ * once outside graph capture first).
+ *   GA_ERR_WORKSPACE_TOO_SMALL when gated_attn_decode_workspace_size(dims) >
+ *   GA_DECODE_SCRATCH_BYTES (e.g. B = 224 at a 6,144-token capacity needs
+ *   7.4 MB and fits; B * H_q * num_splits past about 16,000 rows does not).
+ * Every call on one GPU shares that GPU's array and leaves its partials
+ * there; nothing in it needs to start at zero (stage 1 writes every partial
+ * stage 2 reads in the same call).  Calls that overlap on one GPU -- on
+ * streams not ordered with each other -- race on the array and must not be
+ * issued.
+ */
+ga_status gated_attn_decode_noalloc(const uint16_t *q, const uint16_t *gate,
+                                    const uint16_t *k_pool, const uint16_t *v_pool,
+                                    const int32_t *block_table, const int32_t *seq_lens,
+                                    float scale, uint16_t *out, void *stream,
+                                    const ga_decode_dims *dims);
+
 /* Measurement hook for benchmarks: reads `bytes` of device memory at `src`
  * once, with the non-temporal 16-byte loads the decode's K/V stream uses, in
  * one kernel launch on `stream`, so a caller can time the device's streaming-

@@ -311,3 +311,18 @@ def test_fp8kv_csr_checks():
              ctypes.byref(d16), FAKE, 1 << 40, None) == ga.GA_ERR_UNSUPPORTED
     assert f(FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 1024, 0.0625, 0.0, 0.01, FAKE, None,
              ctypes.byref(d1), FAKE, 1 << 40, None) == ga.GA_ERR_INVALID_ARGUMENT
+
+
+def test_noalloc_declines_before_touching_a_gpu():
+    """gated_attn_decode_noalloc: invalid dims and partials larger than its
+    scratch array (B = 4096 at a 4,096-token capacity: 64 MiB) are declined
+    before any device call; batch 0 is a no-op."""
+    f = ga.lib.gated_attn_decode_noalloc
+    args = [FAKE] * 6 + [0.0625, FAKE, None]
+    big = _dims(batch=4096, max_pages_per_seq=256, num_pages=1 << 20)
+    assert ga.decode_workspace_size(big) > (16 << 20)
+    assert f(*args, ctypes.byref(big)) == ga.GA_ERR_WORKSPACE_TOO_SMALL
+    assert f(*args, ctypes.byref(_dims(head_dim=128))) == ga.GA_ERR_UNSUPPORTED
+    assert f(*args, ctypes.byref(_dims(num_q_heads=15))) == ga.GA_ERR_INVALID_ARGUMENT
+    assert f(*args, None) == ga.GA_ERR_INVALID_ARGUMENT
+    assert f(*args, ctypes.byref(_dims(batch=0))) == ga.GA_OK
