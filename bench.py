@@ -8,9 +8,9 @@ steps.  Decode measurements rotate over copies of their inputs (two for this
 workload) so that no call can read K/V the previous one left in the 256 MB
 Infinity Cache.  The same JSON line also carries:
   * roofline   -- the stage-1 kernel's achieved HBM rate: K launches of that
-                  kernel alone (HIP graphs captured from the workload's calls
-                  with the stage-2 node removed), each between two HIP events
-                  on its stream; ``traffic`` from the committed rocprofv3
+                  kernel alone, chained in one HIP graph (its node copied from
+                  graphs captured from the workload's calls) with an event
+                  recorded before and after each, on the stream it runs on; ``traffic`` from the committed rocprofv3
                   counter summary when it was taken on the current kernel
                   source, else null;
   * launches_per_call -- kernel nodes of a HIP graph captured from one call;
@@ -195,20 +195,40 @@ def call_graph_census(hip, fn, dev) -> dict:
             "method": "nodes of a HIP graph captured from one call"}
 
 
+class Dim3(ctypes.Structure):
+    _fields_ = [("x", ctypes.c_uint), ("y", ctypes.c_uint), ("z", ctypes.c_uint)]
+
+
+class KernelNodeParams(ctypes.Structure):
+    """hipKernelNodeParams."""
+    _fields_ = [("blockDim", Dim3), ("extra", ctypes.c_void_p), ("func", ctypes.c_void_p),
+                ("gridDim", Dim3), ("kernelParams", ctypes.c_void_p),
+                ("sharedMemBytes", ctypes.c_uint)]
+
+
 class Stage1Graphs:
-    """Stage 1 of a decode call on its own: each input set's call is captured
-    into a HIP graph, the dependent node (stage 2) is removed, and the rest --
-    the stage-1 kernel node -- is instantiated.  Launching one of these graphs
-    between two events on the same stream times that kernel alone, with no
-    hook in the library."""
+    """Stage 1 of a decode call on its own, timed by the GPU.  Each input set's
+    call is captured into a HIP graph and its stage-1 kernel node (the root;
+    stage 2 depends on it) is read back.  time(n) builds one graph that chains
+    n copies of those kernel nodes, input sets in turn, with an event-record
+    node before and after each, and launches it once on a stream: each pair
+    of events brackets one stage-1 kernel on the stream it runs on, with no
+    host work and no hook in the library between them."""
 
     def __init__(self, hip, calls, dev):
         import torch
 
+        L = hip.lib
+        vp, P = ctypes.c_void_p, ctypes.POINTER
+        L.hipGraphKernelNodeGetParams.argtypes = [vp, P(KernelNodeParams)]
+        L.hipGraphCreate.argtypes = [P(vp), ctypes.c_uint]
+        L.hipGraphAddKernelNode.argtypes = [P(vp), vp, P(vp), ctypes.c_size_t,
+                                            P(KernelNodeParams)]
+        L.hipGraphAddEventRecordNode.argtypes = [P(vp), vp, P(vp), ctypes.c_size_t, vp]
         self.hip = hip
         self.side = torch.cuda.Stream(device=dev)
         self.stream = ctypes.c_void_p(self.side.cuda_stream)
-        self.execs, self.graphs = [], []
+        self.graphs, self.params = [], []
         torch.cuda.synchronize()
         for call in calls:
             keep = call.stream
@@ -217,36 +237,60 @@ class Stage1Graphs:
                 g = hip.capture(call, self.stream)
             finally:
                 call.stream = keep
+            self.graphs.append(g)  # kept alive: the node parameters point into it
             nodes = hip.nodes(g)
             roots = [n for n, t, d in nodes if t == Hip.KERNEL_NODE and d == 0]
-            dependents = [n for n, t, d in nodes if d > 0]
-            if len(roots) != 1 or len(nodes) != 2 or len(dependents) != 1:
+            if len(roots) != 1 or len(nodes) != 2:
                 raise RuntimeError(f"unexpected decode graph: {nodes}")
-            hip._ok(hip.lib.hipGraphDestroyNode(ctypes.c_void_p(dependents[0])), "hipGraphDestroyNode")
-            self.graphs.append(g)
-            self.execs.append(hip.instantiate(g))
+            prm = KernelNodeParams()
+            hip._ok(L.hipGraphKernelNodeGetParams(ctypes.c_void_p(roots[0]), ctypes.byref(prm)),
+                    "hipGraphKernelNodeGetParams")
+            self.params.append(prm)
 
-    def time(self, n: int) -> list:
-        """Per-launch ms of n stage-1 launches, input sets in turn."""
+    def time(self, n: int, warm: int = 3) -> list:
+        """Per-launch ms of n stage-1 kernels, input sets in turn, after
+        `warm` untimed ones, all in one graph launch."""
         import torch
 
-        hip = self.hip
+        hip, L = self.hip, self.hip.lib
         starts, stops = hip.events(n), hip.events(n)
-        for i in range(3):
-            hip.launch(self.execs[i % len(self.execs)], self.stream)
+        g = ctypes.c_void_p()
+        hip._ok(L.hipGraphCreate(ctypes.byref(g), 0), "hipGraphCreate")
+        prev = None
+
+        def add(kind, arg):
+            nonlocal prev
+            node = ctypes.c_void_p()
+            deps = (ctypes.c_void_p * 1)(prev) if prev is not None else None
+            nd = 1 if prev is not None else 0
+            if kind == "kernel":
+                hip._ok(L.hipGraphAddKernelNode(ctypes.byref(node), g, deps, nd, ctypes.byref(arg)),
+                        "hipGraphAddKernelNode")
+            else:
+                hip._ok(L.hipGraphAddEventRecordNode(ctypes.byref(node), g, deps, nd,
+                                                     ctypes.c_void_p(arg)),
+                        "hipGraphAddEventRecordNode")
+            prev = node.value
+        k = 0
+        for _ in range(warm):
+            add("kernel", self.params[k % len(self.params)])
+            k += 1
         for i in range(n):
-            hip.record(starts[i], self.stream)
-            hip.launch(self.execs[i % len(self.execs)], self.stream)
-            hip.record(stops[i], self.stream)
+            add("event", starts[i])
+            add("kernel", self.params[k % len(self.params)])
+            k += 1
+            add("event", stops[i])
+        ex = hip.instantiate(g.value)
+        hip.launch(ex, self.stream)
         self.side.synchronize()
         torch.cuda.synchronize()
         ms = [hip.elapsed_ms(a, b) for a, b in zip(starts, stops)]
         hip.destroy(starts + stops)
+        L.hipGraphExecDestroy(ctypes.c_void_p(ex))
+        L.hipGraphDestroy(g)
         return ms
 
     def close(self):
-        for e in self.execs:
-            self.hip.lib.hipGraphExecDestroy(ctypes.c_void_p(e))
         for g in self.graphs:
             self.hip.lib.hipGraphDestroy(ctypes.c_void_p(g))
 
@@ -772,9 +816,8 @@ def main() -> int:
     torch.cuda.synchronize()
     total_ms = e0.elapsed_time(e1)
 
-    # Stage-1 duration: K launches of the stage-1 kernel alone (graphs captured
-    # from this workload's calls with the stage-2 node removed), each between
-    # two HIP events on the stream it is launched on.
+    # Stage-1 duration: K launches of the stage-1 kernel alone, chained in one
+    # graph with an event recorded before and after each (Stage1Graphs).
     s1 = Stage1Graphs(hip, call.calls, dev)
     kernel_ms = s1.time(K)
     s1.close()
