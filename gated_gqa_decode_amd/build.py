@@ -54,5 +54,52 @@ def build(verbose: bool = False, extra_flags=None, out: str = LIB) -> str:
     return out
 
 
+HOST_CHECK_LIB = os.path.join(HERE, "libgated_attn_hostcheck.so")
+CLANGXX = os.environ.get("GA_CLANGXX", "/opt/rocm/llvm/bin/clang++")
+
+
+def build_host_check(sanitize: bool = False, out: str = HOST_CHECK_LIB, verbose: bool = False) -> str:
+    """The C ABI (capi.cpp) linked against csrc/host_stub.cpp instead of the
+    HIP runtime and the kernels: every host-side path of the ABI -- argument
+    checks, split plans, workspace layout, the device-arch decision, the
+    no-allocation entry point's scratch lookup -- runs on a machine without a
+    GPU and reports what it would have launched.  ``sanitize``: AddressSanitizer
+    and UndefinedBehaviorSanitizer on the host code (load with the clang ASan
+    runtime preloaded)."""
+    san = ["-Xarch_host", "-fsanitize=address", "-Xarch_host", "-fsanitize=undefined",
+           "-fno-sanitize-recover=undefined", "-fno-omit-frame-pointer"] if sanitize else []
+    build_dir = os.path.join(HERE, "_build")
+    os.makedirs(build_dir, exist_ok=True)
+    tag = "_san" if sanitize else ""
+    objs = []
+    for src, host_only in (("capi.cpp", False), ("host_stub.cpp", True)):
+        obj = os.path.join(build_dir, f"hostcheck_{src}{tag}.o")
+        cmd = [HIPCC, "-x", "hip", *COMMON_FLAGS, "-g", *san,
+               *(["--cuda-host-only"] if host_only else []),
+               "-c", os.path.join(CSRC, src), "-o", obj]
+        if verbose:
+            print(" ".join(cmd), flush=True)
+        r = subprocess.run(cmd, capture_output=True, text=True)
+        if r.returncode != 0:
+            raise RuntimeError(f"hipcc failed on {src}:\n{r.stdout}{r.stderr}")
+        objs.append(obj)
+    # linked with clang++, not hipcc, so no HIP runtime is pulled in; symbols
+    # bind inside the library first, so the stubs answer capi.cpp's calls even
+    # in a process where torch has loaded the real runtime
+    tmp = out + ".tmp"
+    link_san = ["-fsanitize=address,undefined", "-shared-libasan"] if sanitize else []
+    cmd = [CLANGXX, "-shared", "-fPIC", "-Wl,-Bsymbolic", "-Wl,--no-undefined", *link_san,
+           "-o", tmp, *objs, "-lpthread"]
+    if verbose:
+        print(" ".join(cmd), flush=True)
+    r = subprocess.run(cmd, capture_output=True, text=True)
+    if r.returncode != 0:
+        raise RuntimeError(f"link failed:\n{r.stdout}{r.stderr}")
+    os.replace(tmp, out)
+    return out
+
+
 if __name__ == "__main__":
     print(build(verbose="-v" in sys.argv))
+    if "--host-check" in sys.argv:
+        print(build_host_check(sanitize="--sanitize" in sys.argv, verbose="-v" in sys.argv))

@@ -12,11 +12,17 @@ SRC = os.path.join(HERE, "gqa_oracle.c")
 LIB = os.path.join(HERE, "liboracle.so")
 
 
-def build(verbose: bool = False) -> str:
-    """Compile the oracle; always recompiles.  Returns the library path."""
-    tmp = LIB + ".tmp"
+def build(verbose: bool = False, sanitize: bool = False, out: str = LIB) -> str:
+    """Compile the oracle; always recompiles.  Returns the library path.
+    ``sanitize``: clang with AddressSanitizer and UndefinedBehaviorSanitizer
+    (load with the clang ASan runtime preloaded)."""
+    tmp = out + ".tmp"
+    cc = ["gcc", "-O2"]
+    if sanitize:
+        cc = ["/opt/rocm/llvm/bin/clang", "-O1", "-g", "-fno-omit-frame-pointer",
+              "-fsanitize=address,undefined", "-fno-sanitize-recover=undefined", "-shared-libasan"]
     cmd = [
-        "gcc", "-std=c11", "-D_GNU_SOURCE", "-O2", "-fPIC", "-shared",
+        *cc, "-std=c11", "-D_GNU_SOURCE", "-fPIC", "-shared",
         # IEEE fp64 exactly as written: no contraction into FMA, no fast-math.
         "-ffp-contract=off", "-fno-fast-math",
         "-Wall", "-Wextra",
@@ -25,9 +31,9 @@ def build(verbose: bool = False) -> str:
     if verbose:
         print(" ".join(cmd), flush=True)
     subprocess.run(cmd, check=True)
-    os.replace(tmp, LIB)
-    return LIB
+    os.replace(tmp, out)
+    return out
 
 
 if __name__ == "__main__":
-    print(build(verbose="-v" in sys.argv))
+    print(build(verbose="-v" in sys.argv, sanitize="--sanitize" in sys.argv))

@@ -1,0 +1,180 @@
+"""The C ABI's host logic linked against stand-ins for the HIP runtime and
+the kernel launchers (csrc/host_stub.cpp), so the paths that end in a launch
+run without a GPU: the device-arch decision (cuDNN "Gated Attention Block",
+Requirements and limits: a device the library does not serve is declined with
+a typed error), the launch descriptors the plan produces, and the
+no-allocation entry point's scratch lookup.  Fake device addresses are only
+recorded, never dereferenced.
+"""
+import ctypes
+import importlib.util
+import os
+import shutil
+
+import pytest
+
+import gated_gqa_decode_amd as ga
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+FAKE_SCRATCH = 0x7e0000000000
+Q, GATE, K, V, BT, SL, OUT, WS = (0x7f0000000000 + (i << 24) for i in range(8))
+
+
+@pytest.fixture(scope="module")
+def host_lib(tmp_path_factory):
+    spec = importlib.util.spec_from_file_location(
+        "_ga_build", os.path.join(ROOT, "gated_gqa_decode_amd", "build.py"))
+    mod = importlib.util.module_from_spec(spec)
+    spec.loader.exec_module(mod)
+    out = str(tmp_path_factory.mktemp("hostcheck") / "libgated_attn_hostcheck.so")
+    return mod.build_host_check(out=out)
+
+
+def _load(path, tmp_path, arch):
+    """A fresh instance of the library (its own device-arch cache) whose fake
+    device reports `arch`."""
+    copy = tmp_path / f"lib_{arch.split(':')[0]}.so"
+    shutil.copy(path, copy)
+    lib = ctypes.CDLL(str(copy))
+    lib.ga_stub_set_arch(arch.encode())
+    vp, f = ctypes.c_void_p, ctypes.c_float
+    lib.gated_attn_decode.argtypes = [vp] * 6 + [f, vp, vp, ctypes.POINTER(ga.DecodeDims), vp,
+                                                 ctypes.c_size_t]
+    lib.gated_attn_decode_noalloc.argtypes = [vp] * 6 + [f, vp, vp, ctypes.POINTER(ga.DecodeDims)]
+    lib.gated_attn_decode_fp8kv.argtypes = [vp] * 6 + [f, f, f, vp, vp,
+                                                       ctypes.POINTER(ga.DecodeDims), vp,
+                                                       ctypes.c_size_t, vp]
+    lib.gated_attn_decode_csr.argtypes = [vp] * 6 + [ctypes.c_int64, f, vp, vp,
+                                                     ctypes.POINTER(ga.DecodeDims), vp,
+                                                     ctypes.c_size_t, vp]
+    lib.gated_attn_prefill.argtypes = [vp] * 4 + [f, ctypes.c_int, vp, vp,
+                                                  ctypes.POINTER(ga.PrefillDims)]
+    lib.gated_attn_qk_norm_rope.argtypes = [vp] * 5 + [f] + [vp] * 7 + [
+        ctypes.POINTER(ga.QkNormRopeDims)]
+    lib.gated_attn_stream_read.argtypes = [vp, ctypes.c_size_t, vp, vp]
+    return lib
+
+
+def _counts(lib):
+    c = (ctypes.c_int * 4)()
+    lib.ga_stub_launch_counts(c)
+    return list(c)
+
+
+def _last_decode(lib):
+    i8 = (ctypes.c_int32 * 8)()
+    p3 = (ctypes.c_uint64 * 3)()
+    f3 = (ctypes.c_float * 3)()
+    lib.ga_stub_last_decode(i8, p3, f3)
+    keys = ("tokens_per_split", "num_splits", "split_target", "batch", "page_size", "kv_fp8",
+            "window", "num_q_heads")
+    d = dict(zip(keys, list(i8)))
+    d.update(part_acc=p3[0], part_ml=p3[1], out=p3[2], scale=f3[0], k_descale=f3[1],
+             v_descale=f3[2])
+    return d
+
+
+def _dims(**kw):
+    base = dict(batch=64, num_q_heads=16, num_kv_heads=2, head_dim=256, page_size=16,
+                max_pages_per_seq=256, num_pages=16384)
+    base.update(kw)
+    return ga.decode_dims(**base)
+
+
+def _calls(lib):
+    """One valid call of every entry point that launches."""
+    d = _dims()
+    ws = ga.decode_workspace_size(d)
+    pd = ga.PrefillDims(2, 128, 16, 2, 256)
+    rd = ga.QkNormRopeDims(4, 16, 2, 256, 64, 16, 0, 8)
+    return {
+        "decode": lambda: lib.gated_attn_decode(Q, GATE, K, V, BT, SL, 0.0625, OUT, None,
+                                                ctypes.byref(d), WS, ws),
+        "decode_noalloc": lambda: lib.gated_attn_decode_noalloc(Q, GATE, K, V, BT, SL, 0.0625,
+                                                                OUT, None, ctypes.byref(d)),
+        "decode_fp8kv": lambda: lib.gated_attn_decode_fp8kv(Q, GATE, K, V, BT, SL, 0.0625, 0.5,
+                                                            0.25, OUT, None, ctypes.byref(d), WS,
+                                                            ws, None),
+        "decode_csr": lambda: lib.gated_attn_decode_csr(
+            Q, GATE, K, V, BT, SL, 1 << 20, 0.0625, OUT, None,
+            ctypes.byref(_dims(page_size=1, max_pages_per_seq=4096, num_pages=1 << 20)), WS,
+            ga.decode_workspace_size(_dims(page_size=1, max_pages_per_seq=4096,
+                                           num_pages=1 << 20)), None),
+        "prefill": lambda: lib.gated_attn_prefill(Q, GATE, K, V, 0.0625, 1, OUT, None,
+                                                  ctypes.byref(pd)),
+        "qk_norm_rope": lambda: lib.gated_attn_qk_norm_rope(Q, K, V, GATE, GATE, 1e-6, BT, SL,
+                                                            WS, OUT, K, V, None,
+                                                            ctypes.byref(rd)),
+        "stream_read": lambda: lib.gated_attn_stream_read(Q, 1 << 20, SL, None),
+    }
+
+
+def test_other_device_is_declined_before_any_launch(host_lib, tmp_path):
+    lib = _load(host_lib, tmp_path, "gfx942:sramecc+:xnack-")
+    for name, call in _calls(lib).items():
+        assert call() == ga.GA_ERR_UNSUPPORTED, name
+    assert _counts(lib) == [0, 0, 0, 0]
+    assert lib.ga_stub_device_calls() > 0  # the arch query was made
+
+
+def test_gfx950_reaches_every_launch(host_lib, tmp_path):
+    lib = _load(host_lib, tmp_path, "gfx950:sramecc+:xnack-")
+    calls = _calls(lib)
+    for name, call in calls.items():
+        assert call() == ga.GA_OK, name
+    # decode, noalloc, fp8kv and csr launch decode; then prefill, rope, read
+    assert _counts(lib) == [4, 1, 1, 1]
+
+
+def test_decode_launch_follows_the_plan(host_lib, tmp_path):
+    lib = _load(host_lib, tmp_path, "gfx950")
+    for B, W in ((1, 32), (4, 32), (64, 256), (224, 384)):
+        d = _dims(batch=B, max_pages_per_seq=W)
+        p = ga.decode_plan(d)
+        st = lib.gated_attn_decode(Q, GATE, K, V, BT, SL, 0.0625, OUT, None, ctypes.byref(d), WS,
+                                   p.workspace_bytes)
+        assert st == ga.GA_OK
+        r = _last_decode(lib)
+        assert (r["tokens_per_split"], r["num_splits"], r["batch"]) == (p.tokens_per_split,
+                                                                       p.num_splits, B)
+        rows = B * 16 * p.num_splits
+        assert r["part_acc"] == WS and r["part_ml"] == WS + rows * 256 * 4
+        assert rows * 258 * 4 <= p.workspace_bytes
+        assert r["out"] == OUT and r["scale"] == 0.0625 and r["k_descale"] == 1.0
+        # one byte short of the plan's workspace: declined, nothing launched
+        n = _counts(lib)[0]
+        assert lib.gated_attn_decode(Q, GATE, K, V, BT, SL, 0.0625, OUT, None, ctypes.byref(d),
+                                     WS, p.workspace_bytes - 1) == ga.GA_ERR_WORKSPACE_TOO_SMALL
+        assert _counts(lib)[0] == n
+
+
+def test_noalloc_uses_the_device_scratch_address(host_lib, tmp_path):
+    lib = _load(host_lib, tmp_path, "gfx950")
+    for B, W in ((64, 256), (1, 32), (224, 384)):
+        d = _dims(batch=B, max_pages_per_seq=W)
+        p = ga.decode_plan(d)
+        assert lib.gated_attn_decode_noalloc(Q, GATE, K, V, BT, SL, 0.0625, OUT, None,
+                                             ctypes.byref(d)) == ga.GA_OK
+        r = _last_decode(lib)
+        rows = B * 16 * p.num_splits
+        assert r["part_acc"] == FAKE_SCRATCH
+        assert r["part_ml"] == FAKE_SCRATCH + rows * 256 * 4
+    n = _counts(lib)[0]
+    big = _dims(batch=4096, max_pages_per_seq=256, num_pages=1 << 20)
+    assert lib.gated_attn_decode_noalloc(Q, GATE, K, V, BT, SL, 0.0625, OUT, None,
+                                         ctypes.byref(big)) == ga.GA_ERR_WORKSPACE_TOO_SMALL
+    assert _counts(lib)[0] == n
+
+
+def test_fp8_factors_reach_the_launch(host_lib, tmp_path):
+    lib = _load(host_lib, tmp_path, "gfx950")
+    d = _dims()
+    ws = ga.decode_workspace_size(d)
+    assert lib.gated_attn_decode_fp8kv(Q, GATE, K, V, BT, SL, 0.0625, 0.5, 0.25, OUT, None,
+                                       ctypes.byref(d), WS, ws, None) == ga.GA_OK
+    r = _last_decode(lib)
+    assert (r["kv_fp8"], r["k_descale"], r["v_descale"]) == (1, 0.5, 0.25)
+    for bad in (0.0, -1.0, float("inf"), float("nan")):
+        assert lib.gated_attn_decode_fp8kv(Q, GATE, K, V, BT, SL, 0.0625, bad, 0.25, OUT, None,
+                                           ctypes.byref(d), WS, ws,
+                                           None) == ga.GA_ERR_INVALID_ARGUMENT
