@@ -7,14 +7,17 @@
 // bf16 rounding chain of the gate (bf16 O, bf16 sigmoid, rounded product) is
 // the one of FreeToken PR #781, Summary.
 //
-// Workgroup = (16 query positions, kv head g, sequence b); 8 waves, wave w is
-// query head 8g + w, so every 64-key K/V tile staged in LDS feeds 8 heads x 16
-// rows.  Tiles are double-buffered in LDS; the next tile's global loads are in
-// flight (in registers) while the current one is computed.
+// Workgroup = (16 query positions, kv head g, sequence b, head part); 4 waves,
+// one per SIMD, wave w serving query heads 2w and 2w + 1 of the part (up to 8
+// heads), so every K or V fragment read from LDS feeds two heads' MFMAs.
+// 64-key K and V tiles reach LDS by direct copies (buffer loads into LDS, no
+// registers), K one tile ahead of V: while a wave runs the softmax of tile t on
+// its vector ALU, its matrix core computes the scores of tile t + 1; then P V
+// of tile t.  One barrier per tile.
 //
 // MFMA v_mfma_f32_16x16x32_bf16 operand layout (wave64): A row = lane % 16,
 // k = 8*(lane/16) + 0..7; B column = lane % 16, same k; C row = 4*(lane/16) + r,
-// column = lane % 16, r = 0..3.  Per tile and wave:
+// column = lane % 16, r = 0..3.  Per tile, wave and head:
 //   S^T (64 keys x 16 rows) = K Q^T : 4 key tiles x 8 k-steps.  Computing the
 //        transpose leaves each lane 4 consecutive keys of one query row, which
 //        is already the A-operand layout of P for the P V product (k-slot
@@ -23,11 +26,14 @@
 //   P = Phi + Plo, two bf16 values per fp32 probability (~16 significant bits);
 //   O (16 rows x 256) += Phi V + Plo V : 16 column tiles x 2 k-steps x 2.  The
 //        B operand (4 consecutive keys of one V column per lane and read) comes
-//        straight from row-major V in LDS through the gfx950 transpose read
-//        ds_read_b64_tr_b16: within a 16-lane group, lane i of the result gets
-//        element (i % 4) of the source lane 4k + i/4 in slot k, so source lane
-//        s points at V[key0 + s/4][d0 + 4*(s % 4)] and result lane i receives
+//        from V in LDS through the gfx950 transpose read ds_read_b64_tr_b16:
+//        within a 16-lane group, lane i of the result gets element (i % 4) of
+//        the source lane 4k + i/4 in slot k, so source lane s points at
+//        V[key0 + s/4][d0 + 4*(s % 4)] and result lane i receives
 //        V[key0 + k][d0 + i], k = 0..3.
+// LDS rows are 512 bytes with 16-byte chunks swizzled by row (K: chunk c of
+// row r at c ^ (r & 15); V: at c ^ 2(r & 7)), so each 16-lane read touches
+// every bank group once; each copy instruction fills two whole rows.
 #include <hip/hip_runtime.h>
 #include <math.h>
 #include <stdint.h>
@@ -42,21 +48,23 @@ namespace {
 constexpr int kD = 256;
 constexpr int kBM = 16;    // query positions per workgroup
 constexpr int kBN = 64;    // keys per tile
-// Row strides in LDS (bf16 elements).  32 bytes of padding per row spread a
-// wave's K-fragment reads (16 rows x 64 B) and V transpose reads over all
-// banks; measured on gfx950, 16 bytes of padding leaves K reads ~1.5x slower.
-constexpr int kKRow = kD + 16;  // K row stride: +32 B
-constexpr int kVRow = kD + 16;  // V row stride: +32 B
-constexpr int kThreads = 512;
-constexpr int kWavesPf = kThreads / 64;
+constexpr int kH = 1;                // query heads per wave
+constexpr int kWavesPf = kMaxHeadsPerPart / kH;
+constexpr int kThreads = 64 * kWavesPf;
+constexpr int kCopyRows = kBN / kWavesPf;     // tile rows each wave copies
+constexpr int kCopies = kCopyRows / 2;        // copy instructions per wave per tile (K or V)
+constexpr int kTileBytes = kBN * kD * 2;  // one K or V tile (32 KiB)
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
 constexpr float kSlack = 8.f;  // lazy-rescale threshold, log2 units
+static_assert(kH * kWavesPf == kMaxHeadsPerPart, "a workgroup serves a head part");
+static_assert(kCopies == 4 || kCopies == 8, "copy instructions ride with the P V groups");
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef short s16x4 __attribute__((ext_vector_type(4)));
 typedef s16x4 __attribute__((address_space(3))) lds_s16x4;
+typedef __attribute__((address_space(3))) void lds_void;
 
 struct PrefillArgs {
   const uint16_t* q;
@@ -122,15 +130,10 @@ __host__ __forceinline__ int grid_size(int slices, int nm) {
   return slices * nm;
 }
 
-struct alignas(16) TileBuf {
-  uint16_t k[kBN * kKRow];
-  uint16_t v[kBN * kVRow];
-};
-
 __device__ __forceinline__ bf16x8 as_bf16x8(uint4 u) { return __builtin_bit_cast(bf16x8, u); }
 
 // p must point into LDS (8-byte aligned).
-__device__ __forceinline__ uint2 tr_read(const uint16_t* p) {
+__device__ __forceinline__ uint2 tr_read(const char* p) {
   const s16x4 r = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(p));
   return __builtin_bit_cast(uint2, r);
 }
@@ -147,8 +150,15 @@ __device__ __forceinline__ uint32_t cvt_pk_bf16(float x, float y) {
 
 }  // namespace
 
-__global__ __launch_bounds__(kThreads) void prefill_gate_kernel(PrefillArgs a) {
-  __shared__ TileBuf buf[2];
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(kWavesPf / 4, kWavesPf / 4)))
+void prefill_gate_kernel(PrefillArgs a) {
+  // K and V tiles, two of each, as separate objects: the compiler then tells
+  // a direct copy into one tile from a read of another, and waits only for
+  // the copies a read needs.
+  __shared__ __align__(16) char k0[kTileBytes];
+  __shared__ __align__(16) char k1[kTileBytes];
+  __shared__ __align__(16) char v0[kTileBytes];
+  __shared__ __align__(16) char v1[kTileBytes];
 
   int mt, gp, b;
   if (!map_workgroup(a, (int)blockIdx.x, mt, gp, b)) return;
@@ -159,32 +169,22 @@ __global__ __launch_bounds__(kThreads) void prefill_gate_kernel(PrefillArgs a) {
   const int part = gp - g * a.parts;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int lane = __lane_id();
-  // Waves past the workgroup's head count only help stage K/V tiles.
+  // Heads of this part; wave w serves part heads 2w and 2w + 1.  A wave past
+  // the part's heads only helps copy K/V; a missing second head computes a
+  // copy of the first and is not stored.
   const int heads = part == 0 ? a.heads_per_part : Hq / Hkv - a.heads_per_part;  // >= 1
-  const bool active = wave < heads;
-  const int h = g * (Hq / Hkv) + part * a.heads_per_part + min(wave, heads - 1);
+  const bool active = kH * wave < heads;
+  const bool second = kH * wave + 1 < heads;  // (kH == 2) the wave's second head is real
+  const int hbase = g * (Hq / Hkv) + part * a.heads_per_part;
+  int hw[kH];
+#pragma unroll
+  for (int h = 0; h < kH; ++h) hw[h] = hbase + min(kH * wave + h, heads - 1);
   const int p0 = mt * kBM;
 
   const int li = lane & 15;  // query row of this lane's S^T column / MFMA column
   const int lg = lane >> 4;  // lane group: k-slot block / C row block
-
-  // Q fragments (B operand of K Q^T): row p0 + li, d = 32*ks + 8*lg .. +7
-  bf16x8 qf[8];
-  {
-    const int pos = min(p0 + li, S - 1);
-    const uint16_t* qrow = a.q + (((size_t)b * S + pos) * Hq + h) * kD;
-#pragma unroll
-    for (int s = 0; s < 8; ++s)
-      qf[s] = as_bf16x8(*reinterpret_cast<const uint4*>(qrow + 32 * s + 8 * lg));
-  }
-
-  f32x4 o[16];  // O[row 4*lg + r][d = 16*t + li]
-#pragma unroll
-  for (int t = 0; t < 16; ++t) o[t] = f32x4{0.f, 0.f, 0.f, 0.f};
-  float m_ref = -INFINITY;  // reference max (log2 units) of row li
-  float l_row = 0.f;        // this lane's share of the sum of row li
-
   const int qi = p0 + li;
+
   // Keys this query tile can see: [kv_lo, kv_end).  The key length masks keys
   // only; the causal mask ends at the tile's last row; the window starts at
   // the first row's window.
@@ -193,90 +193,122 @@ __global__ __launch_bounds__(kThreads) void prefill_gate_kernel(PrefillArgs a) {
   const int kv_lo = a.window > 0 ? max(0, p0 - a.window + 1) : 0;
   const int kt_lo = kv_lo / kBN;
   const int n_tiles = (kv_end + kBN - 1) / kBN;  // key tiles kt_lo .. n_tiles - 1
-  const size_t kv_row_stride = (size_t)Hkv * kD;
-  const uint16_t* kbase = a.k + ((size_t)b * S * Hkv + g) * kD;
-  const uint16_t* vbase = a.v + ((size_t)b * S * Hkv + g) * kD;
+  const int row_bytes = Hkv * kD * 2;            // between consecutive keys
 
-  // staging: thread covers 16-byte pieces idx = it*512 + tid of each 64 x 256
-  // tile: key it*16 + tid/32, column chunk tid%32 (offsets fixed per thread)
-  const int st_key = threadIdx.x >> 5;
-  const int st_c = threadIdx.x & 31;
-  const unsigned g_off = (unsigned)(st_key * (int)kv_row_stride + st_c * 8);
-  uint4 sk[4], sv[4];
-  auto load_tile = [&](int kt) {
-    const int j0 = kt * kBN;
-    const uint16_t* kb = kbase + (size_t)j0 * kv_row_stride;
-    const uint16_t* vb = vbase + (size_t)j0 * kv_row_stride;
-#pragma unroll
-    for (int it = 0; it < 4; ++it) {
-      const unsigned off = g_off + (unsigned)(it * 16 * (int)kv_row_stride);
-      sk[it] = make_uint4(0, 0, 0, 0);
-      sv[it] = make_uint4(0, 0, 0, 0);
-      const int j = j0 + it * 16 + st_key;
-      if (j < kv_end && j >= kv_lo) {  // keys no row of the tile sees stay zero
-        sk[it] = *reinterpret_cast<const uint4*>(kb + off);
-        sv[it] = *reinterpret_cast<const uint4*>(vb + off);
-      }
-    }
+  // ---- direct HBM/L2 -> LDS copies of one tile ---------------------------------
+  // Wave w copies rows 16w .. 16w + 15 of the tile (8 instructions, two whole
+  // rows each).  A row outside the visible range [kv_lo, kv_end) copies the
+  // nearest visible row instead: finite data whose probability is exactly 0
+  // (or, for K, whose score is replaced by -inf).
+  const size_t head0 = ((size_t)b * S * Hkv + g) * kD;  // elements to key 0 of head g
+  const int extent = (int)((size_t)S * row_bytes - (size_t)g * kD * 2);  // bytes from there on
+  // copy_one(.., d): instruction d (0..7) of this wave's share of a tile
+  auto copy_one = [&](const uint16_t* base, int kt, char* buf, bool is_v, int d) {
+    // the descriptor from wave-uniform values, kept in scalar registers
+    const uintptr_t addr = reinterpret_cast<uintptr_t>(base + head0);
+    const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)addr);
+    const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(addr >> 32));
+    const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(
+        reinterpret_cast<void*>(((uintptr_t)hi << 32) | lo), 0,
+        __builtin_amdgcn_readfirstlane(extent), 0x00020000);
+    const int r = kCopyRows * wave + 2 * d + (lane >> 5);  // tile row
+    const int p = lane & 31;                         // 16-byte slot in the row
+    const int c = is_v ? p ^ ((r & 7) << 1) : p ^ (r & 15);  // chunk stored there
+    const int j = min(max(kt * kBN + r, kv_lo), kv_end - 1);
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_void*)(buf + (kCopyRows * wave + 2 * d) * 512), 16,
+                                             (uint32_t)j * (uint32_t)row_bytes + 16 * c, 0, 0, 0);
   };
-  auto store_tile = [&](TileBuf& tb) {
+  auto copy_tile = [&](const uint16_t* base, int kt, char* buf, bool is_v) {
 #pragma unroll
-    for (int it = 0; it < 4; ++it) {
-      const int key = it * 16 + st_key;
-      *reinterpret_cast<uint4*>(&tb.k[key * kKRow + st_c * 8]) = sk[it];
-      *reinterpret_cast<uint4*>(&tb.v[key * kVRow + st_c * 8]) = sv[it];
-    }
+    for (int d = 0; d < kCopies; ++d) copy_one(base, kt, buf, is_v, d);
   };
 
-  if (kt_lo < n_tiles) {
-    load_tile(kt_lo);
-    store_tile(buf[0]);
-    if (kt_lo + 1 < n_tiles) load_tile(kt_lo + 1);
+  // Q fragments (B operand of K Q^T) of both heads: row p0 + li, d = 32*ks + 8*lg .. +7
+  bf16x8 qf[kH][8];
+  {
+    const int pos = min(qi, S - 1);
+#pragma unroll
+    for (int h = 0; h < kH; ++h) {
+      const uint16_t* qrow = a.q + (((size_t)b * S + pos) * Hq + hw[h]) * kD;
+#pragma unroll
+      for (int s = 0; s < 8; ++s)
+        qf[h][s] = as_bf16x8(*reinterpret_cast<const uint4*>(qrow + 32 * s + 8 * lg));
+    }
   }
-  __syncthreads();
 
-  for (int kt = kt_lo; kt < n_tiles; ++kt) {
-    const TileBuf& tb = buf[(kt - kt_lo) & 1];
-    const int j0 = kt * kBN;
+  f32x4 o[kH][16];  // O[head][row 4*lg + r][d = 16*t + li]
+#pragma unroll
+  for (int h = 0; h < kH; ++h)
+#pragma unroll
+    for (int t = 0; t < 16; ++t) o[h][t] = f32x4{0.f, 0.f, 0.f, 0.f};
+  float m_ref[kH], l_row[kH];  // reference max (log2 units) of row li; this lane's share of its sum
+#pragma unroll
+  for (int h = 0; h < kH; ++h) {
+    m_ref[h] = -INFINITY;
+    l_row[h] = 0.f;
+  }
 
-    if (active) {
-      // ---- S^T = K Q^T ---------------------------------------------------------
-      // k-step outer, key tile inner: the four accumulators interleave, so no
-      // MFMA waits on the one just issued.
-      f32x4 st[4];  // st[ct][r] = S[row li][key j0 + 16*ct + 4*lg + r]
+  // ---- S^T = K Q^T of one tile for both heads ------------------------------------
+  // k-step outer, key tile inner: eight accumulators interleave.
+  // hook(s) runs after the K reads of k-step s + 1 are issued: the next
+  // tile's copies ride along with the MFMAs (issued early, so they have the
+  // whole tile to land) instead of stalling on their own
+  auto scores = [&](const char* kb, f32x4 (&st)[kH][4], auto&& hook) {
 #pragma unroll
-      for (int ct = 0; ct < 4; ++ct) st[ct] = f32x4{0.f, 0.f, 0.f, 0.f};
-      {
-        const uint16_t* krow = &tb.k[li * kKRow + 8 * lg];
-        bf16x8 kf[2][4];
+    for (int h = 0; h < kH; ++h)
 #pragma unroll
-        for (int ct = 0; ct < 4; ++ct)
-          kf[0][ct] = as_bf16x8(*reinterpret_cast<const uint4*>(krow + ct * 16 * kKRow));
+      for (int ct = 0; ct < 4; ++ct) st[h][ct] = f32x4{0.f, 0.f, 0.f, 0.f};
+    // key row 16*ct + li, chunk 4*s + lg at (4*s + lg) ^ li.  The lane's
+    // offsets are recomputed for every tile (a few VALU operations) instead of
+    // being kept in registers across the loop.
+    int lx = li;
+    asm volatile("" : "+v"(lx));
+    const char* krow = kb + lx * 512;
+    bf16x8 kf[2][4];
+    auto read_k = [&](int s, bf16x8 (&dst)[4]) {
 #pragma unroll
-        for (int s = 0; s < 8; ++s) {
-          if (s + 1 < 8) {
+      for (int ct = 0; ct < 4; ++ct)
+        dst[ct] = as_bf16x8(*reinterpret_cast<const uint4*>(krow + ct * 16 * 512 +
+                                                            16 * ((4 * s + lg) ^ lx)));
+    };
+    read_k(0, kf[0]);
 #pragma unroll
-            for (int ct = 0; ct < 4; ++ct)
-              kf[(s + 1) & 1][ct] =
-                  as_bf16x8(*reinterpret_cast<const uint4*>(krow + ct * 16 * kKRow + 32 * (s + 1)));
-          }
-#pragma unroll
-          for (int ct = 0; ct < 4; ++ct)
-            st[ct] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf[s & 1][ct], qf[s], st[ct], 0, 0, 0);
-        }
-      }
-
-      // ---- mask, lazy online softmax (row li), split P ------------------------
-      // Only a tile that reaches past the first row of the query tile (causal)
-      // or past the last key needs the mask; the test is uniform.
-      const bool need_mask = (j0 + kBN > kv_end) || (a.causal && j0 + kBN - 1 > p0) ||
-                             (a.window > 0 && j0 < p0 + kBM - a.window);
-      float sv_[4][4];
-      bool raise = false;
+    for (int s = 0; s < 8; ++s) {
+      if (s + 1 < 8) read_k(s + 1, kf[(s + 1) & 1]);
+      hook(s);
 #pragma unroll
       for (int ct = 0; ct < 4; ++ct)
 #pragma unroll
-        for (int r = 0; r < 4; ++r) sv_[ct][r] = st[ct][r] * a.scale_log2;
+        for (int h = 0; h < kH; ++h)
+          st[h][ct] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf[s & 1][ct], qf[h][s], st[h][ct], 0, 0, 0);
+    }
+    // issue order: the fragments of k-step s + 1 are read before the MFMAs of
+    // k-step s, so each read has eight MFMAs to land
+    __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);
+#pragma unroll
+    for (int s = 0; s < 8; ++s) {
+      if (s + 1 < 8) __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);
+      __builtin_amdgcn_sched_group_barrier(0x020, kCopies / 4, 0);
+      __builtin_amdgcn_sched_group_barrier(0x008, 4 * kH, 0);
+    }
+  };
+
+  // ---- mask, lazy online softmax (row li), split P ----------------------------------
+  // p = hi + lo, both bf16 (hardware round-to-nearest-even conversion); the row
+  // sum takes p itself (hi + lo equals p to ~2^-18 relative).
+  auto softmax = [&](int kt, f32x4 (&st)[kH][4], uint32_t (&phw)[kH][2][4], uint32_t (&plw)[kH][2][4]) {
+    const int j0 = kt * kBN;
+    // Only a tile that reaches past the first row of the query tile (causal),
+    // past the last key, or before the window needs the mask; the test is uniform.
+    const bool need_mask = (j0 + kBN > kv_end) || (a.causal && j0 + kBN - 1 > p0) ||
+                           (a.window > 0 && j0 < p0 + kBM - a.window);
+#pragma unroll
+    for (int h = 0; h < kH; ++h) {
+      float sv[4][4];
+#pragma unroll
+      for (int ct = 0; ct < 4; ++ct)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) sv[ct][r] = st[h][ct][r] * a.scale_log2;
       if (need_mask) {
 #pragma unroll
         for (int ct = 0; ct < 4; ++ct)
@@ -285,208 +317,280 @@ __global__ __launch_bounds__(kThreads) void prefill_gate_kernel(PrefillArgs a) {
             const int kj = j0 + ct * 16 + 4 * lg + r;
             const bool ok = (kj < kv_end) && (!a.causal || kj <= qi) &&
                             (a.window <= 0 || kj > qi - a.window);
-            sv_[ct][r] = ok ? sv_[ct][r] : -INFINITY;
+            sv[ct][r] = ok ? sv[ct][r] : -INFINITY;
           }
       }
+      bool raise = false;
 #pragma unroll
       for (int ct = 0; ct < 4; ++ct)
 #pragma unroll
-        for (int r = 0; r < 4; ++r) raise |= sv_[ct][r] > m_ref + kSlack;
+        for (int r = 0; r < 4; ++r) raise |= sv[ct][r] > m_ref[h] + kSlack;
       if (__builtin_amdgcn_ballot_w64(raise) != 0) {  // wave-uniform, rare
         float mx = -INFINITY;
 #pragma unroll
         for (int ct = 0; ct < 4; ++ct)
 #pragma unroll
-          for (int r = 0; r < 4; ++r) mx = fmaxf(mx, sv_[ct][r]);
+          for (int r = 0; r < 4; ++r) mx = fmaxf(mx, sv[ct][r]);
         mx = fmaxf(mx, shfl_xor(mx, 16));
         mx = fmaxf(mx, shfl_xor(mx, 32));
-        const float m_new = fmaxf(m_ref, mx);
+        const float m_new = fmaxf(m_ref[h], mx);
         // a row with no visible key so far keeps -inf; its factor is then 1
-        const float alpha = (m_new == -INFINITY) ? 1.f : __builtin_amdgcn_exp2f(m_ref - m_new);
-        l_row *= alpha;
-        m_ref = m_new;
+        const float alpha = (m_new == -INFINITY) ? 1.f : __builtin_amdgcn_exp2f(m_ref[h] - m_new);
+        l_row[h] *= alpha;
+        m_ref[h] = m_new;
         // O holds rows 4*lg + r: fetch those rows' factors from lanes li = 4*lg + r
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
           const float ar = __int_as_float(
               __builtin_amdgcn_ds_bpermute((4 * lg + r) << 2, __float_as_int(alpha)));
 #pragma unroll
-          for (int t = 0; t < 16; ++t) o[t][r] *= ar;
+          for (int t = 0; t < 16; ++t) o[h][t][r] *= ar;
         }
       }
-      // p = hi + lo, both bf16 (hardware round-to-nearest-even conversion); the
-      // row sum takes p itself (hi + lo equals p to ~2^-18 relative).
-      const float mref_safe = (m_ref == -INFINITY) ? 0.f : m_ref;
-      uint32_t phw[2][4], plw[2][4];  // packed bf16 A operands, k-step ks = ct / 2
+      const float mref_safe = (m_ref[h] == -INFINITY) ? 0.f : m_ref[h];
 #pragma unroll
       for (int ct = 0; ct < 4; ++ct) {
 #pragma unroll
         for (int rp = 0; rp < 2; ++rp) {
-          const float pa = __builtin_amdgcn_exp2f(sv_[ct][2 * rp] - mref_safe);
-          const float pb = __builtin_amdgcn_exp2f(sv_[ct][2 * rp + 1] - mref_safe);
-          l_row += pa + pb;
+          const float pa = __builtin_amdgcn_exp2f(sv[ct][2 * rp] - mref_safe);
+          const float pb = __builtin_amdgcn_exp2f(sv[ct][2 * rp + 1] - mref_safe);
+          l_row[h] += pa + pb;
           const uint32_t hi = cvt_pk_bf16(pa, pb);
           const uint32_t lo = cvt_pk_bf16(pa - bf16_lo(hi), pb - bf16_hi(hi));
-          phw[ct >> 1][(ct & 1) * 2 + rp] = hi;
-          plw[ct >> 1][(ct & 1) * 2 + rp] = lo;
-        }
-      }
-
-      // ---- O += P V  (B operand through the LDS transpose read) ---------------
-      // The V fragments of the next group of four column tiles are requested
-      // before the current group's MFMAs are issued.
-#pragma unroll
-      for (int ks = 0; ks < 2; ++ks) {
-        const bf16x8 ph = as_bf16x8(make_uint4(phw[ks][0], phw[ks][1], phw[ks][2], phw[ks][3]));
-        const bf16x8 pl = as_bf16x8(make_uint4(plw[ks][0], plw[ks][1], plw[ks][2], plw[ks][3]));
-        // k-slots 0..3: keys 32ks + 4lg + 0..3; k-slots 4..7: keys 32ks + 16 + 4lg + 0..3
-        const uint16_t* v0 = &tb.v[(32 * ks + 4 * lg + (li >> 2)) * kVRow + 4 * (li & 3)];
-        const uint16_t* v1 = v0 + 16 * kVRow;
-        bf16x8 vf[2][4];
-#pragma unroll
-        for (int u = 0; u < 4; ++u) {
-          const uint2 a0 = tr_read(v0 + 16 * u);
-          const uint2 a1 = tr_read(v1 + 16 * u);
-          vf[0][u] = as_bf16x8(make_uint4(a0.x, a0.y, a1.x, a1.y));
-        }
-#pragma unroll
-        for (int tg = 0; tg < 4; ++tg) {
-          if (tg + 1 < 4) {
-#pragma unroll
-            for (int u = 0; u < 4; ++u) {
-              const int t = 4 * (tg + 1) + u;
-              const uint2 a0 = tr_read(v0 + 16 * t);
-              const uint2 a1 = tr_read(v1 + 16 * t);
-              vf[(tg + 1) & 1][u] = as_bf16x8(make_uint4(a0.x, a0.y, a1.x, a1.y));
-            }
-          }
-#pragma unroll
-          for (int u = 0; u < 4; ++u)
-            o[4 * tg + u] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ph, vf[tg & 1][u], o[4 * tg + u], 0, 0, 0);
-#pragma unroll
-          for (int u = 0; u < 4; ++u)
-            o[4 * tg + u] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(pl, vf[tg & 1][u], o[4 * tg + u], 0, 0, 0);
+          phw[h][ct >> 1][(ct & 1) * 2 + rp] = hi;
+          plw[h][ct >> 1][(ct & 1) * 2 + rp] = lo;
         }
       }
     }
+  };
 
-    // ---- next tile: staged registers -> the other buffer ---------------------
-    if (kt + 1 < n_tiles) {
-      store_tile(buf[(kt + 1 - kt_lo) & 1]);
-      if (kt + 2 < n_tiles) load_tile(kt + 2);
+  // ---- O += P V  (B operand through the LDS transpose read) ---------------------
+  // V row r, dims 16t + 4(li % 4) .. +3 sit at r * 512 + 32 (t8 ^ (r & 7)) +
+  // 256 (t / 8) + 8 (li % 4), t8 = t % 8; k-slots 0..3 of k-step ks are keys
+  // 32ks + 4lg + 0..3 (rows 32ks + 4lg + li / 4 as sources), k-slots 4..7 the
+  // same 16 keys later.
+  auto pv = [&](const char* vb, const uint32_t (&phw)[kH][2][4], const uint32_t (&plw)[kH][2][4]) {
+    // the lane's offsets, recomputed for every tile (see scores)
+    int lx = lane;
+    asm volatile("" : "+v"(lx));
+    const int vr = 4 * (lx >> 4) + ((lx & 15) >> 2);  // source row within a 16-key group
+    int voff[8];
+#pragma unroll
+    for (int t8 = 0; t8 < 8; ++t8) voff[t8] = vr * 512 + 32 * (t8 ^ (vr & 7)) + 8 * (lx & 3);
+    bf16x8 ph[2][kH], pl[2][kH];  // [k-step][head]
+#pragma unroll
+    for (int ks = 0; ks < 2; ++ks)
+#pragma unroll
+      for (int h = 0; h < kH; ++h) {
+        ph[ks][h] = as_bf16x8(make_uint4(phw[h][ks][0], phw[h][ks][1], phw[h][ks][2], phw[h][ks][3]));
+        pl[ks][h] = as_bf16x8(make_uint4(plw[h][ks][0], plw[h][ks][1], plw[h][ks][2], plw[h][ks][3]));
+      }
+    // group gi = (k-step gi / 4, column tiles 4 (gi % 4) .. +3)
+    auto read_v = [&](int gi, bf16x8 (&dst)[4]) {
+      const char* va = vb + 32 * (gi >> 2) * 512;
+      const char* vc = va + 16 * 512;
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        const int t = 4 * (gi & 3) + u;
+        const int off = voff[t & 7] + 256 * (t >> 3);
+        const uint2 x0 = tr_read(va + off);
+        const uint2 x1 = tr_read(vc + off);
+        dst[u] = as_bf16x8(make_uint4(x0.x, x0.y, x1.x, x1.y));
+      }
+    };
+    bf16x8 vf[2][4];
+    read_v(0, vf[0]);
+#pragma unroll
+    for (int gi = 0; gi < 8; ++gi) {
+      if (gi + 1 < 8) read_v(gi + 1, vf[(gi + 1) & 1]);
+      const int ks = gi >> 2, tg = gi & 3;
+      // every head's P_hi terms, then the P_lo terms: each accumulator's two
+      // MFMAs are 4 kH MFMAs apart
+#pragma unroll
+      for (int h = 0; h < kH; ++h)
+#pragma unroll
+        for (int u = 0; u < 4; ++u)
+          o[h][4 * tg + u] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ph[ks][h], vf[gi & 1][u], o[h][4 * tg + u], 0, 0, 0);
+#pragma unroll
+      for (int h = 0; h < kH; ++h)
+#pragma unroll
+        for (int u = 0; u < 4; ++u)
+          o[h][4 * tg + u] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(pl[ks][h], vf[gi & 1][u], o[h][4 * tg + u], 0, 0, 0);
     }
-    __syncthreads();
+    // issue order: the V fragments of group gi + 1 are read before the 16
+    // MFMAs of group gi
+    __builtin_amdgcn_sched_group_barrier(0x100, 8, 0);
+#pragma unroll
+    for (int gi = 0; gi < 8; ++gi) {
+      if (gi + 1 < 8) __builtin_amdgcn_sched_group_barrier(0x100, 8, 0);
+      __builtin_amdgcn_sched_group_barrier(0x008, 8 * kH, 0);
+    }
+  };
+
+  // ---- the tile loop ----------------------------------------------------------------
+  // Iteration t (buffers named statically: the loop is unrolled twice):
+  //   barrier -- K(t) and V(t) have landed; every wave is done with tile t - 1
+  //   copies of K(t+1) and V(t+1) into the buffers tile t - 1 used
+  //   S(t) = K(t) Q^T;  softmax -> P(t);  O += P(t) V(t)
+  if (kt_lo < n_tiles) {
+    copy_tile(a.k, kt_lo, k0, false);
+    copy_tile(a.v, kt_lo, v0, true);
+    f32x4 st[kH][4];
+    uint32_t phw[kH][2][4], plw[kH][2][4];
+    auto step = [&](int kt, char* kc, char* vc, char* kn, char* vn) {
+      asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+      __syncthreads();
+      // The next tile's copies, requested unconditionally (past the last tile
+      // they re-read visible rows into buffers nothing reads any more), so no
+      // branch splits the scheduling region they share with P V.
+      if (active) {
+        // the K instructions with k-steps 0..3, the V ones with 4..7
+        scores(kc, st, [&](int gi) {
+#pragma unroll
+          for (int e = 0; e < kCopies / 4; ++e)
+            copy_one(gi < 4 ? a.k : a.v, kt + 1, gi < 4 ? kn : vn, gi >= 4,
+                     (kCopies / 4) * (gi & 3) + e);
+        });
+        softmax(kt, st, phw, plw);
+        pv(vc, phw, plw);
+      } else {
+        copy_tile(a.k, kt + 1, kn, false);
+        copy_tile(a.v, kt + 1, vn, true);
+      }
+    };
+    for (int kt = kt_lo;;) {
+      step(kt, k0, v0, k1, v1);
+      if (++kt >= n_tiles) break;
+      step(kt, k1, v1, k0, v0);
+      if (++kt >= n_tiles) break;
+    }
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
   }
 
   // ---- epilogue: O / l -> bf16, gate, store ------------------------------------
-  // bf16(O) of the wave's 16 rows goes through LDS (the loop ended with a
-  // barrier, so the tile buffers are free) from the MFMA layout (lane: 4 rows x
-  // 16 strided columns) to whole 16-byte pieces of rows, so each lane issues 8
-  // gate loads and 8 output stores of 16 bytes instead of 64 of 2 bytes, and
-  // waits for memory once.
+  // The gate rows of both heads are requested first, before the last barrier,
+  // so their latency overlaps the normalisation.  bf16(O) of the wave's 2 x 16
+  // rows goes through LDS from the MFMA layout (lane: 4 rows x 16 strided
+  // columns) to whole 16-byte pieces of rows, so each lane issues 16 gate loads
+  // and 16 output stores of 16 bytes instead of 128 of 2 bytes.  LDS per wave
+  // (one of the four tile buffers): 16 KiB of bf16(O), 128 B of row flags, and
+  // a copy of the sigmoid table (8 KiB).
+  const int pc = lane & 31;  // piece j of this lane: row 2j + lane / 32, dims 8 (lane % 32) .. +7
+  uint4 gt8[kH][8];
+  if (active) {
+#pragma unroll
+    for (int h = 0; h < kH; ++h)
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        const int qr = min(p0 + 2 * j + (lane >> 5), S - 1);  // rows past S are not stored
+        gt8[h][j] = *reinterpret_cast<const uint4*>(a.gate + (((size_t)b * S + qr) * Hq + hw[h]) * kD + 8 * pc);
+      }
+  }
+  __syncthreads();  // every wave is done with the tiles: their LDS is reused below
   if (!active) return;
-  l_row += shfl_xor(l_row, 16);  // the row's four lanes hold disjoint keys
-  l_row += shfl_xor(l_row, 32);
-  // LDS (139,264 B): 8 x 8 KiB of bf16(O), 8 x 64 B of row flags, then a copy
-  // of the sigmoid table per wave (8 x 8 KiB): 131,584 B in all
-  char* const lds = reinterpret_cast<char*>(&buf[0]);
-  uint16_t* const ob_lds = reinterpret_cast<uint16_t*>(lds) + wave * (kBM * kD);  // [16 rows][256]
-  uint32_t* const row_flags =
-      reinterpret_cast<uint32_t*>(lds + kWavesPf * kBM * kD * 2) + wave * kBM;  // bit 0 live, bit 1 dead
-  uint16_t* const sig_lds =
-      reinterpret_cast<uint16_t*>(lds + kWavesPf * kBM * (kD * 2 + 4)) + wave * 4096;
+  // this wave's region: kH x 8 KiB of bf16(O), then 8 KiB of sigmoid table
+  constexpr int kRegion = kH * kBM * kD * 2 + 8192;
+  constexpr int kPerTile = kTileBytes / kRegion;  // regions per tile buffer
+  static_assert(kPerTile * 4 >= kWavesPf, "the epilogue regions fit the tile buffers");
+  const int tb = wave / kPerTile;
+  char* const lds = (tb == 0 ? k0 : tb == 1 ? k1 : tb == 2 ? v0 : v1) + (wave % kPerTile) * kRegion;
+  uint16_t* const ob_lds = reinterpret_cast<uint16_t*>(lds);  // [head][16 rows][256]
+  uint16_t* const sig_lds = reinterpret_cast<uint16_t*>(lds + kH * kBM * kD * 2);
   {  // the table -> this wave's copy by direct copies (no registers), 1 KiB each
     const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(
         const_cast<uint16_t*>(kSigmoidTable), 0, (int)sizeof(kSigmoidTable), 0x00020000);
 #pragma unroll
     for (int k = 0; k < 8; ++k)
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (__attribute__((address_space(3))) void*)(sig_lds + 512 * k),
-                                               16, 16 * lane + 1024 * k, 0, 0, 0);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_void*)(sig_lds + 512 * k), 16,
+                                               16 * lane + 1024 * k, 0, 0, 0);
   }
-  // A sink joins the denominator as one more term exp(sink) (log2 units here,
-  // like m_ref); a row with no visible key (l = 0) is dead: out = +0.
-  const float sink2 = a.sinks != nullptr ? a.sinks[h] * kLog2e : -INFINITY;
 #pragma unroll
-  for (int r = 0; r < 4; ++r) {
-    const int row = 4 * lg + r;
-    const float lr = __int_as_float(__builtin_amdgcn_ds_bpermute(row << 2, __float_as_int(l_row)));
-    const float mr = __int_as_float(__builtin_amdgcn_ds_bpermute(row << 2, __float_as_int(m_ref)));
-    const int qr = p0 + row;
-    const bool dead = lr == 0.f;
-    float mtot = mr, f = 1.f, den = lr;
-    if (a.sinks != nullptr) {
-      mtot = fmaxf(mr, sink2);
-      f = __builtin_amdgcn_exp2f(mr - mtot);  // 0 for a dead row
-      den = fmaf(lr, f, __builtin_amdgcn_exp2f(sink2 - mtot));
-    }
-    // O f / den through one reciprocal per row and a correction step (the
-    // quotient to within about an fp32 ulp; it is rounded to bf16 next)
-    const float inv = 1.f / den;
+  for (int h = 0; h < kH; ++h) {
+    const int hq = hw[h];
+    float lr_own = l_row[h];
+    lr_own += shfl_xor(lr_own, 16);  // the row's four lanes hold disjoint keys
+    lr_own += shfl_xor(lr_own, 32);
+    // A sink joins the denominator as one more term exp(sink) (log2 units here,
+    // like m_ref); a row with no visible key (l = 0) is dead: out = +0.
+    const float sink2 = a.sinks != nullptr ? a.sinks[hq] * kLog2e : -INFINITY;
 #pragma unroll
-    for (int t = 0; t < 16; ++t) {
-      const float x = o[t][r] * f;
-      const float q0 = x * inv;
-      const float q = __builtin_fmaf(__builtin_fmaf(-q0, den, x), inv, q0);
-      ob_lds[row * kD + 16 * t + li] = bf16_rne_f32(q);
+    for (int r = 0; r < 4; ++r) {
+      const int row = 4 * lg + r;
+      const float lr = __int_as_float(__builtin_amdgcn_ds_bpermute(row << 2, __float_as_int(lr_own)));
+      const float mr = __int_as_float(__builtin_amdgcn_ds_bpermute(row << 2, __float_as_int(m_ref[h])));
+      const int qr = p0 + row;
+      float mtot = mr, f = 1.f, den = lr;
+      if (a.sinks != nullptr) {
+        mtot = fmaxf(mr, sink2);
+        f = __builtin_amdgcn_exp2f(mr - mtot);  // 0 for a dead row
+        den = fmaf(lr, f, __builtin_amdgcn_exp2f(sink2 - mtot));
+      }
+      // O f / den through one reciprocal per row and a correction step (the
+      // quotient to within about an fp32 ulp; it is rounded to bf16 next)
+      const float inv = 1.f / den;
+#pragma unroll
+      for (int t = 0; t < 16; ++t) {
+        const float x = o[h][t][r] * f;
+        const float q0 = x * inv;
+        const float q = __builtin_fmaf(__builtin_fmaf(-q0, den, x), inv, q0);
+        ob_lds[(h * kBM + row) * kD + 16 * t + li] = bf16_rne_f32(q);
+      }
+      if (a.lse != nullptr && li == 0 && qr < S && (h == 0 || second))
+        a.lse[((size_t)b * S + qr) * Hq + hq] = (den > 0.f) ? (mtot + log2f(den)) * kLn2 : -INFINITY;
     }
-    if (li == 0) row_flags[row] = (qr < S ? 1u : 0u) | (dead ? 2u : 0u);
-    if (a.lse != nullptr && li == 0 && qr < S)
-      a.lse[((size_t)b * S + qr) * Hq + h] =
-          (den > 0.f) ? (mtot + log2f(den)) * kLn2 : -INFINITY;
   }
-  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // the table copies have landed
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // the table copies and gate rows have landed
   // the wave's LDS writes above before its reads of other lanes' values below
   __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
   __builtin_amdgcn_wave_barrier();
   __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-  // piece j of this lane: row 2j + lane / 32, dims 8 (lane % 32) .. +7
-  const int pc = lane & 31;
-  uint4 ob8[8], gt8[8];
-  uint32_t flg[8];
-#pragma unroll
-  for (int j = 0; j < 8; ++j) {
-    const int row = 2 * j + (lane >> 5);
-    flg[j] = row_flags[row];
-    ob8[j] = *reinterpret_cast<const uint4*>(&ob_lds[row * kD + 8 * pc]);
-    const int qr = min(p0 + row, S - 1);  // rows past S are not stored
-    gt8[j] = *reinterpret_cast<const uint4*>(a.gate + (((size_t)b * S + qr) * Hq + h) * kD + 8 * pc);
-  }
   // The gate: the sigmoid from the wave's table copy and the product in fp32
-  // for all 64 elements (no branches) and the stores, then the fp64 product
-  // for the rare ones whose fp32 product is not exact (zero, subnormal),
-  // stored over the first result.
-  uint64_t slow = 0;
+  // for all elements (no branches) and the stores, then the fp64 product for
+  // the rare ones whose fp32 product is not exact (zero, subnormal), stored
+  // over the first result.
 #pragma unroll
-  for (int j = 0; j < 8; ++j) {
-    const uint32_t ow[4] = {ob8[j].x, ob8[j].y, ob8[j].z, ob8[j].w};
-    const uint32_t gw[4] = {gt8[j].x, gt8[j].y, gt8[j].z, gt8[j].w};
-    const bool dead = (flg[j] & 2u) != 0;
-    const bool live = (flg[j] & 1u) != 0;  // row inside the sequence
-    uint32_t res[4];
-#pragma unroll
-    for (int e = 0; e < 8; ++e) {
-      const uint16_t obe = (uint16_t)(ow[e >> 1] >> (16 * (e & 1)));
-      const uint16_t ge = (uint16_t)(gw[e >> 1] >> (16 * (e & 1)));
-      const uint16_t sb = sigmoid_from_entry(ge, sig_lds[sigmoid_table_slot(ge)]);
-      uint16_t r;
-      if (!gate_product_fast(obe, sb, r) && live && !dead) slow |= 1ull << (8 * j + e);
-      const uint32_t rv = dead ? 0u : (uint32_t)r;
-      if (e & 1) res[e >> 1] |= rv << 16; else res[e >> 1] = rv;
-    }
-    const int row = 2 * j + (lane >> 5);
-    if (live)
-      *reinterpret_cast<uint4*>(a.out + (((size_t)b * S + p0 + row) * Hq + h) * kD + 8 * pc) =
-          make_uint4(res[0], res[1], res[2], res[3]);
-  }
-  if (slow != 0) {  // rare: re-read the element's bf16(O) and gate
+  for (int h = 0; h < kH; ++h) {
+    if (h == 1 && !second) break;
+    const int hq = hw[h];
+    float lr_own = l_row[h];  // as above: row li's sum, for the dead-row test
+    lr_own += shfl_xor(lr_own, 16);
+    lr_own += shfl_xor(lr_own, 32);
+    uint64_t slow = 0;
 #pragma unroll
     for (int j = 0; j < 8; ++j) {
       const int row = 2 * j + (lane >> 5);
-      const size_t off = (((size_t)b * S + p0 + row) * Hq + h) * kD + 8 * pc;
+      const float lr = __int_as_float(__builtin_amdgcn_ds_bpermute(row << 2, __float_as_int(lr_own)));
+      const uint32_t flg = (p0 + row < S ? 1u : 0u) | (lr == 0.f ? 2u : 0u);
+      const uint4 ob8 = *reinterpret_cast<const uint4*>(&ob_lds[(h * kBM + row) * kD + 8 * pc]);
+      const uint32_t ow[4] = {ob8.x, ob8.y, ob8.z, ob8.w};
+      const uint32_t gw[4] = {gt8[h][j].x, gt8[h][j].y, gt8[h][j].z, gt8[h][j].w};
+      const bool dead = (flg & 2u) != 0;
+      const bool live = (flg & 1u) != 0;  // row inside the sequence
+      uint32_t res[4];
 #pragma unroll
-      for (int e = 0; e < 8; ++e)
-        if ((slow >> (8 * j + e)) & 1ull)
-          a.out[off + e] = gate_output(ob_lds[row * kD + 8 * pc + e], a.gate[off + e]);
+      for (int e = 0; e < 8; ++e) {
+        const uint16_t obe = (uint16_t)(ow[e >> 1] >> (16 * (e & 1)));
+        const uint16_t ge = (uint16_t)(gw[e >> 1] >> (16 * (e & 1)));
+        const uint16_t sb = sigmoid_from_entry(ge, sig_lds[sigmoid_table_slot(ge)]);
+        uint16_t r;
+        if (!gate_product_fast(obe, sb, r) && live && !dead) slow |= 1ull << (8 * j + e);
+        const uint32_t rv = dead ? 0u : (uint32_t)r;
+        if (e & 1) res[e >> 1] |= rv << 16; else res[e >> 1] = rv;
+      }
+      if (live)
+        *reinterpret_cast<uint4*>(a.out + (((size_t)b * S + p0 + row) * Hq + hq) * kD + 8 * pc) =
+            make_uint4(res[0], res[1], res[2], res[3]);
+    }
+    if (slow != 0) {  // rare: re-read the element's bf16(O) and gate
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        const int row = 2 * j + (lane >> 5);
+        const size_t off = (((size_t)b * S + p0 + row) * Hq + hq) * kD + 8 * pc;
+#pragma unroll
+        for (int e = 0; e < 8; ++e)
+          if ((slow >> (8 * j + e)) & 1ull)
+            a.out[off + e] = gate_output(ob_lds[(h * kBM + row) * kD + 8 * pc + e], a.gate[off + e]);
+      }
     }
   }
 }
