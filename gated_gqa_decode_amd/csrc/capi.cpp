@@ -421,15 +421,15 @@ ga_status gated_attn_qk_norm_rope(const uint16_t* q, const uint16_t* k, const ui
     num_slots = dims->num_pages * kPageSize;
   }
   if (T == 0) return GA_OK;
-  const void* need8[] = {q, k, v, q_out, k_out};
-  for (const void* p : need8)
-    if (p == nullptr || !aligned(p, 8)) return GA_ERR_INVALID_ARGUMENT;
+  const void* need16[] = {q, k, v, q_out, k_out};
+  for (const void* p : need16)
+    if (p == nullptr || !aligned(p, 16)) return GA_ERR_INVALID_ARGUMENT;
   if (slot_mapping != nullptr && (v_out == nullptr || !aligned(slot_mapping, 8)))
     return GA_ERR_INVALID_ARGUMENT;
-  if (!aligned(v_out, 8) || !aligned(w_q_norm, 8) || !aligned(w_k_norm, 8))
+  if (!aligned(v_out, 16) || !aligned(w_q_norm, 16) || !aligned(w_k_norm, 16))
     return GA_ERR_INVALID_ARGUMENT;
   if (dims->rope_dim > 0 &&
-      (cos == nullptr || sin == nullptr || !aligned(cos, 8) || !aligned(sin, 8)))
+      (cos == nullptr || sin == nullptr || !aligned(cos, 16) || !aligned(sin, 16)))
     return GA_ERR_INVALID_ARGUMENT;
   ga_status st = check_device();
   if (st != GA_OK) return st;

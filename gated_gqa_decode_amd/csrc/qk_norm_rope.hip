@@ -8,11 +8,13 @@
 // activation dtype with the rotate-half convention, w_q_norm / w_k_norm [D];
 // Fusion knobs: the rows are normed and rotated in fp32 and written once.
 //
-// Rows are (token, head row): H_q query rows, then H_kv key rows, each of
-// which also copies that kv head's V row.  Lane l owns dims 4l .. 4l+3, so a
-// row is one 8-byte load and one 8-byte store per lane; the RoPE partner of
-// dim d (d +- rope_dim/2) sits in the lane rope_dim/8 away, at the same
-// position, and is fetched with one cross-lane permute per element.
+// One wave per (token, pair of head rows) -- H_q query rows, then H_kv key
+// rows -- one row per half-wave: lane l handles dims 8(l % 32) .. +7 of its
+// row, so every load and store moves a 512-byte row in 16-byte pieces, and
+// all of a wave's loads (row, norm weights, cos / sin, V, and the RoPE
+// partner dims d +- rope_dim/2 of the row and the weights) are issued before
+// any is used; the only cross-lane step left is the norm's sum.  Key rows also
+// carry that kv head's V row to the slot.
 #include <hip/hip_runtime.h>
 #include <math.h>
 #include <stdint.h>
@@ -46,129 +48,182 @@ struct RopeArgs {
   int rope_dim;
 };
 
-__device__ __forceinline__ void unpack4(uint2 u, float (&f)[4]) {
-  f[0] = bf16_lo(u.x);
-  f[1] = bf16_hi(u.x);
-  f[2] = bf16_lo(u.y);
-  f[3] = bf16_hi(u.y);
+__device__ __forceinline__ void unpack8(uint2 lo, uint2 hi, float (&f)[8]) {
+  f[0] = bf16_lo(lo.x);
+  f[1] = bf16_hi(lo.x);
+  f[2] = bf16_lo(lo.y);
+  f[3] = bf16_hi(lo.y);
+  f[4] = bf16_lo(hi.x);
+  f[5] = bf16_hi(hi.x);
+  f[6] = bf16_lo(hi.y);
+  f[7] = bf16_hi(hi.y);
 }
 
-__device__ __forceinline__ uint2 pack4(const float (&f)[4]) {
-  uint2 u;
-  u.x = (uint32_t)bf16_rne_f32(f[0]) | ((uint32_t)bf16_rne_f32(f[1]) << 16);
-  u.y = (uint32_t)bf16_rne_f32(f[2]) | ((uint32_t)bf16_rne_f32(f[3]) << 16);
-  return u;
+__device__ __forceinline__ uint32_t pack2(float x, float y) {
+  return (uint32_t)bf16_rne_f32(x) | ((uint32_t)bf16_rne_f32(y) << 16);
 }
 
-__device__ __forceinline__ float from_lane(float v, int src_lane) {
-  return __int_as_float(__builtin_amdgcn_ds_bpermute(src_lane << 2, __float_as_int(v)));
+// 16 bytes at p (16-byte aligned), as two halves of 4 bf16 each.
+struct Piece {
+  uint2 lo, hi;
+};
+__device__ __forceinline__ Piece load16(const uint16_t* p) {
+  const uint4 u = *reinterpret_cast<const uint4*>(p);
+  return {make_uint2(u.x, u.y), make_uint2(u.z, u.w)};
+}
+__device__ __forceinline__ void store16(uint16_t* p, Piece v) {
+  *reinterpret_cast<uint4*>(p) = make_uint4(v.lo.x, v.lo.y, v.hi.x, v.hi.y);
 }
 
 }  // namespace
 
-// Rows per wave.  More than one keeps more bytes in flight but lengthens
-// each wave's chain of cross-lane steps; measured at T = 4096 and T = 64, one
-// row per wave is as fast or faster.
-constexpr int kRows = 1;
-
-// Sum over the wave: DPP sums within each 16-lane row, then the four row sums
-// read into scalar registers (no LDS-routed permutes on the chain).
-__device__ __forceinline__ float wave_sum_rows(float v) {
+// Sum over each half-wave (32 lanes): DPP sums within each 16-lane row, then
+// the two row sums of the lane's half read into scalar registers.
+__device__ __forceinline__ float half_sum(float v, int half) {
   v = sum16(v);
   const int b = __float_as_int(v);
-  return (__int_as_float(__builtin_amdgcn_readlane(b, 0)) +
-          __int_as_float(__builtin_amdgcn_readlane(b, 16))) +
-         (__int_as_float(__builtin_amdgcn_readlane(b, 32)) +
-          __int_as_float(__builtin_amdgcn_readlane(b, 48)));
+  const float h0 = __int_as_float(__builtin_amdgcn_readlane(b, 0)) +
+                   __int_as_float(__builtin_amdgcn_readlane(b, 16));
+  const float h1 = __int_as_float(__builtin_amdgcn_readlane(b, 32)) +
+                   __int_as_float(__builtin_amdgcn_readlane(b, 48));
+  return half ? h1 : h0;
 }
 
-__global__ __launch_bounds__(256) void qk_norm_rope_kernel(RopeArgs a) {
-  const int rows_per_token = a.num_q_heads + a.num_kv_heads;
-  const long long total = a.num_tokens * rows_per_token;
-  const long long row0 = ((long long)blockIdx.x * 4 + (threadIdx.x >> 6)) * kRows;
-  if (row0 >= total) return;
-  const int lane = __lane_id();
+// One (token, row pair) unit of work: what its loads bring, then what is
+// stored.  load_pair issues every load; finish_pair uses them.
+struct PairLoads {
+  long long t;
+  int row_raw;
+  Piece x, xp, w, wp, c, s, v;
+};
+
+__device__ __forceinline__ PairLoads load_pair(const RopeArgs& a, long long w, int lane) {
+  const int Hq = a.num_q_heads, Hkv = a.num_kv_heads;
+  const int rows = Hq + Hkv;
+  const int pairs = (rows + 1) >> 1;
+  const int half = lane >> 5;
+  const int p = lane & 31;  // dims 8p .. 8p + 7
+  PairLoads L;
+  L.t = w / pairs;
+  L.row_raw = 2 * (int)(w - L.t * pairs) + half;
+  const int row = min(L.row_raw, rows - 1);  // past the end: a repeat, not stored
+  const bool is_q = row < Hq;
+  const int kvh = row - Hq;
   const int R = a.rope_dim;
-  const bool rotated = 4 * lane < R;
-
-  long long tok[kRows];
-  int hrow[kRows];
-  uint2 xraw[kRows], wraw[kRows], craw[kRows], sraw[kRows];
+  const bool rotated = 8 * p < R;
+  const uint16_t* wn = is_q ? a.w_q : a.w_k;  // both or neither are given
+  // The row, its norm weights, the token's tables, the V row, and -- instead
+  // of a cross-lane exchange after the norm -- the RoPE partner dims of the
+  // row and of the weights straight from memory (the partner's value is
+  // formed from them with the same operations the partner lane applies, so it
+  // is bitwise the same).  Dims 8p + 4g .. +3 (g = 0, 1) have partners
+  // 4g-aligned at +- R/2 (R/2 is a multiple of 4).
+  const uint16_t* xrow =
+      is_q ? a.q + ((size_t)L.t * Hq + row) * kD : a.k + ((size_t)L.t * Hkv + kvh) * kD;
+  L.x = load16(xrow + 8 * p);
+  const Piece zero = {make_uint2(0, 0), make_uint2(0, 0)};
+  L.xp = L.w = L.wp = L.c = L.s = L.v = zero;
+  if (wn != nullptr) L.w = load16(wn + 8 * p);
+  if (rotated) {
+    const int hr = R >> 1;
+    int pofs[2];
 #pragma unroll
-  for (int j = 0; j < kRows; ++j) {
-    const long long row = min(row0 + j, total - 1);  // past the end: redo the last row, unstored
-    tok[j] = row / rows_per_token;
-    hrow[j] = (int)(row - tok[j] * rows_per_token);
-    const bool is_q = hrow[j] < a.num_q_heads;
-    const uint16_t* src = is_q ? a.q + ((size_t)tok[j] * a.num_q_heads + hrow[j]) * kD
-                               : a.k + ((size_t)tok[j] * a.num_kv_heads + (hrow[j] - a.num_q_heads)) * kD;
-    xraw[j] = *reinterpret_cast<const uint2*>(src + 4 * lane);
-    const uint16_t* w = is_q ? a.w_q : a.w_k;
-    wraw[j] = w != nullptr ? *reinterpret_cast<const uint2*>(w + 4 * lane) : make_uint2(0, 0);
-    craw[j] = sraw[j] = make_uint2(0, 0);
-    if (rotated) {
-      craw[j] = *reinterpret_cast<const uint2*>(a.cos + (size_t)tok[j] * R + 4 * lane);
-      sraw[j] = *reinterpret_cast<const uint2*>(a.sin + (size_t)tok[j] * R + 4 * lane);
+    for (int g = 0; g < 2; ++g) {
+      const int gd = 8 * p + 4 * g;
+      pofs[g] = gd < hr ? gd + hr : gd - hr;
+    }
+    L.c = load16(a.cos + (size_t)L.t * R + 8 * p);
+    L.s = load16(a.sin + (size_t)L.t * R + 8 * p);
+    if ((hr & 4) == 0) {  // the partners of all 8 dims are 8 contiguous dims
+      L.xp = load16(xrow + pofs[0]);
+      if (wn != nullptr) L.wp = load16(wn + pofs[0]);
+    } else {              // two groups of 4 in different places
+      L.xp = {*reinterpret_cast<const uint2*>(xrow + pofs[0]),
+              *reinterpret_cast<const uint2*>(xrow + pofs[1])};
+      if (wn != nullptr)
+        L.wp = {*reinterpret_cast<const uint2*>(wn + pofs[0]),
+                *reinterpret_cast<const uint2*>(wn + pofs[1])};
     }
   }
+  if (!is_q && a.v_out != nullptr) L.v = load16(a.v + ((size_t)L.t * Hkv + kvh) * kD + 8 * p);
+  return L;
+}
 
+__device__ __forceinline__ void finish_pair(const RopeArgs& a, const PairLoads& L, int lane) {
+  const int Hq = a.num_q_heads, Hkv = a.num_kv_heads;
+  const int rows = Hq + Hkv;
+  const int half = lane >> 5;
+  const int p = lane & 31;
+  const int row = min(L.row_raw, rows - 1);
+  const bool is_q = row < Hq;
+  const int kvh = row - Hq;
+  const int R = a.rope_dim;
+  const bool rotated = 8 * p < R;
+  const int hr = R >> 1;
+  float x[8], xp[8];
+  unpack8(L.x.lo, L.x.hi, x);
+  unpack8(L.xp.lo, L.xp.hi, xp);
+  // RMSNorm over the row's D values, in fp32
+  float y[8], yp[8];
+  if (a.w_q != nullptr) {  // wave-uniform
+    float ss = 0.f;
 #pragma unroll
-  for (int j = 0; j < kRows; ++j) {
-    const long long t = tok[j];
-    const int hr = hrow[j];
-    const bool is_q = hr < a.num_q_heads;
-    float x[4];
-    unpack4(xraw[j], x);
-
-    // RMSNorm over the head's D values, in fp32
-    float y[4] = {x[0], x[1], x[2], x[3]};
-    if ((is_q ? a.w_q : a.w_k) != nullptr) {
-      const float ss = wave_sum_rows(x[0] * x[0] + x[1] * x[1] + x[2] * x[2] + x[3] * x[3]);
-      const float r = 1.0f / sqrtf(ss / (float)kD + a.eps);
-      float wf[4];
-      unpack4(wraw[j], wf);
+    for (int e = 0; e < 8; ++e) ss += x[e] * x[e];
+    ss = half_sum(ss, half);
+    const float rr = 1.0f / sqrtf(ss / (float)kD + a.eps);
+    float wf[8], wpf[8];
+    unpack8(L.w.lo, L.w.hi, wf);
+    unpack8(L.wp.lo, L.wp.hi, wpf);
 #pragma unroll
-      for (int e = 0; e < 4; ++e) y[e] = x[e] * r * wf[e];
+    for (int e = 0; e < 8; ++e) {
+      y[e] = x[e] * rr * wf[e];
+      yp[e] = xp[e] * rr * wpf[e];
     }
-
-    // rotate-half RoPE on dims < R: first half z = y c - y' s, second half
-    // z = y c + y' s, with y' the partner dim R/2 away (R/8 lanes away)
-    float z[4] = {y[0], y[1], y[2], y[3]};
-    {
-      const int half_lanes = R >> 3;
-      const bool first = lane < half_lanes;
-      const int partner = first ? lane + half_lanes : lane - half_lanes;
-      float yp[4];
+  } else {
 #pragma unroll
-      for (int e = 0; e < 4; ++e) yp[e] = from_lane(y[e], rotated ? partner : lane);
-      if (rotated) {
-        float c[4], s[4];
-        unpack4(craw[j], c);
-        unpack4(sraw[j], s);
-#pragma unroll
-        for (int e = 0; e < 4; ++e)
-          z[e] = first ? y[e] * c[e] - yp[e] * s[e] : y[e] * c[e] + yp[e] * s[e];
-      }
+    for (int e = 0; e < 8; ++e) {
+      y[e] = x[e];
+      yp[e] = xp[e];
     }
-    if (row0 + j >= total) continue;  // a repeated last row: nothing to store
-    const uint2 zout = pack4(z);
-    if (is_q) {
-      *reinterpret_cast<uint2*>(a.q_out + ((size_t)t * a.num_q_heads + hr) * kD + 4 * lane) = zout;
-      continue;
-    }
-    // key row: K and V to the token's slot (or dense position)
-    const int kvh = hr - a.num_q_heads;
-    long long slot = t;
-    if (a.slot_mapping != nullptr) {
-      slot = a.slot_mapping[t];
-      if (slot < 0 || slot >= a.num_slots) continue;  // padded token / outside the pools
-    }
-    const size_t off = ((size_t)slot * a.num_kv_heads + kvh) * kD + 4 * lane;
-    *reinterpret_cast<uint2*>(a.k_out + off) = zout;
-    if (a.v_out != nullptr)
-      *reinterpret_cast<uint2*>(a.v_out + off) =
-          *reinterpret_cast<const uint2*>(a.v + ((size_t)t * a.num_kv_heads + kvh) * kD + 4 * lane);
   }
+  // rotate-half RoPE on dims < R: first half z = y c - y' s, second half
+  // z = y c + y' s, y' the partner dim d +- R/2
+  float c[8], sn[8];
+  unpack8(L.c.lo, L.c.hi, c);
+  unpack8(L.s.lo, L.s.hi, sn);
+  float z[8];
+#pragma unroll
+  for (int e = 0; e < 8; ++e) {
+    const bool first = 8 * p + 4 * (e >> 2) < hr;
+    z[e] = !rotated ? y[e] : first ? y[e] * c[e] - yp[e] * sn[e] : y[e] * c[e] + yp[e] * sn[e];
+  }
+  if (L.row_raw >= rows) return;  // the repeated last row: nothing to store
+  const Piece zo = {make_uint2(pack2(z[0], z[1]), pack2(z[2], z[3])),
+                    make_uint2(pack2(z[4], z[5]), pack2(z[6], z[7]))};
+  if (is_q) {
+    store16(a.q_out + ((size_t)L.t * Hq + row) * kD + 8 * p, zo);
+    return;
+  }
+  // key row: K and V to the token's slot (or dense position)
+  long long slot = L.t;
+  if (a.slot_mapping != nullptr) {
+    slot = a.slot_mapping[L.t];
+    if (slot < 0 || slot >= a.num_slots) return;  // padded token / outside the pools
+  }
+  const size_t off = ((size_t)slot * Hkv + kvh) * kD + 8 * p;
+  store16(a.k_out + off, zo);
+  if (a.v_out != nullptr) store16(a.v_out + off, L.v);
+}
+
+// One row pair per wave, all its loads issued before any is used.  (Two or
+// four pairs per wave keep more bytes in flight per wave but need so many
+// registers that fewer waves fit: measured slower at T = 4096.)
+__global__ __launch_bounds__(256) void qk_norm_rope_kernel(RopeArgs a) {
+  const long long units = a.num_tokens * ((a.num_q_heads + a.num_kv_heads + 1) >> 1);
+  const long long w = (long long)blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (w >= units) return;
+  const int lane = __lane_id();
+  finish_pair(a, load_pair(a, w, lane), lane);
 }
 
 hipError_t launch_qk_norm_rope(const RopeLaunch& p, hipStream_t stream) {
@@ -190,9 +245,10 @@ hipError_t launch_qk_norm_rope(const RopeLaunch& p, hipStream_t stream) {
   a.num_q_heads = p.num_q_heads;
   a.num_kv_heads = p.num_kv_heads;
   a.rope_dim = p.rope_dim;
-  const long long rows = p.num_tokens * (p.num_q_heads + p.num_kv_heads);
-  const long long waves = (rows + kRows - 1) / kRows;
-  hipLaunchKernelGGL(qk_norm_rope_kernel, dim3((unsigned)((waves + 3) / 4)), dim3(256), 0, stream, a);
+  // one (token, pair of head rows) unit per wave, four waves per workgroup
+  const long long units = p.num_tokens * ((p.num_q_heads + p.num_kv_heads + 1) / 2);
+  hipLaunchKernelGGL(qk_norm_rope_kernel, dim3((unsigned)((units + 3) / 4)), dim3(256), 0, stream,
+                     a);
   return hipGetLastError();
 }
 

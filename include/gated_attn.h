@@ -321,7 +321,8 @@ typedef struct ga_qk_norm_rope_dims {
  * ([num_pages][16][H_kv][D]; slot s is page s / 16, row s % 16); s < 0 or
  * s >= num_pages * 16 writes nothing.  Without it: k_out is dense [T][H_kv][D]
  * and v_out is a dense copy of v, or NULL (not written).
- * Errors: GA_ERR_INVALID_ARGUMENT for null / misaligned (8-byte) pointers,
+ * Errors: GA_ERR_INVALID_ARGUMENT for null or misaligned pointers (16 bytes;
+ * slot_mapping 8),
  * one norm weight without the other, eps < 0 or not finite, odd R, missing
  * tables with R > 0; GA_ERR_UNSUPPORTED for D != 256, R not a multiple of 8,
  * page size != 16, T * (H_q + H_kv) > 2^30, or a non-gfx950 device.  One

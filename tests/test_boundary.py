@@ -227,6 +227,8 @@ def _rope_call(dims, eps=1e-6, wq=FAKE, wk=FAKE, cos=FAKE, sin=FAKE, slots=None,
     ({}, dict(wk=None), ga.GA_ERR_INVALID_ARGUMENT),        # one weight only
     ({}, dict(cos=None), ga.GA_ERR_INVALID_ARGUMENT),       # R > 0 without tables
     ({}, dict(q=FAKE + 4), ga.GA_ERR_INVALID_ARGUMENT),     # misaligned
+    ({}, dict(q=FAKE + 8), ga.GA_ERR_INVALID_ARGUMENT),     # rows are read in 16-byte pieces
+    ({}, dict(cos=FAKE + 8), ga.GA_ERR_INVALID_ARGUMENT),
     ({}, dict(slots=FAKE, v_out=None), ga.GA_ERR_INVALID_ARGUMENT),  # pools need v_out
     (dict(page_size=8), dict(slots=FAKE), ga.GA_ERR_UNSUPPORTED),
     (dict(num_pages=0), dict(slots=FAKE), ga.GA_ERR_INVALID_ARGUMENT),
