@@ -21,10 +21,11 @@ __device__ __forceinline__ float bf16_to_f32(uint16_t b) { return __uint_as_floa
 // the upper half of binary32, so subnormals and the overflow to infinity follow
 // from the same carry).  NaN stays NaN.
 __device__ __forceinline__ uint16_t bf16_rne_f32(float f) {
-  uint32_t u = __float_as_uint(f);
-  if ((u & 0x7fffffffu) > 0x7f800000u) return (uint16_t)((u >> 16) | 0x0040u);
-  u += 0x7fffu + ((u >> 16) & 1u);
-  return (uint16_t)(u >> 16);
+  // both results computed and one selected: no branch per element
+  const uint32_t u = __float_as_uint(f);
+  const uint32_t rounded = (u + 0x7fffu + ((u >> 16) & 1u)) >> 16;
+  const uint32_t quiet_nan = (u >> 16) | 0x0040u;
+  return (uint16_t)(((u & 0x7fffffffu) > 0x7f800000u) ? quiet_nan : rounded);
 }
 
 // fp64 -> bf16, round to nearest even, with bf16 subnormals and overflow.
