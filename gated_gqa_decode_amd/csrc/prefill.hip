@@ -528,12 +528,20 @@ void prefill_gate_kernel(PrefillArgs a) {
       // O f / den through one reciprocal per row and a correction step (the
       // quotient to within about an fp32 ulp; it is rounded to bf16 next)
       const float inv = 1.f / den;
+      // rounded two at a time by the hardware conversion (round to nearest
+      // even; denormals are kept)
 #pragma unroll
-      for (int t = 0; t < 16; ++t) {
-        const float x = o[h][t][r] * f;
-        const float q0 = x * inv;
-        const float q = __builtin_fmaf(__builtin_fmaf(-q0, den, x), inv, q0);
-        ob_lds[(h * kBM + row) * kD + 16 * t + li] = bf16_rne_f32(q);
+      for (int t = 0; t < 16; t += 2) {
+        float qv[2];
+#pragma unroll
+        for (int u = 0; u < 2; ++u) {
+          const float x = o[h][t + u][r] * f;
+          const float q0 = x * inv;
+          qv[u] = __builtin_fmaf(__builtin_fmaf(-q0, den, x), inv, q0);
+        }
+        const uint32_t pk = cvt_pk_bf16(qv[0], qv[1]);
+        ob_lds[(h * kBM + row) * kD + 16 * t + li] = (uint16_t)pk;
+        ob_lds[(h * kBM + row) * kD + 16 * (t + 1) + li] = (uint16_t)(pk >> 16);
       }
       if (a.lse != nullptr && li == 0 && qr < S && (h == 0 || second))
         a.lse[((size_t)b * S + qr) * Hq + hq] = (den > 0.f) ? (mtot + log2f(den)) * kLn2 : -INFINITY;
@@ -566,16 +574,23 @@ void prefill_gate_kernel(PrefillArgs a) {
       const uint32_t gw[4] = {gt8[h][j].x, gt8[h][j].y, gt8[h][j].z, gt8[h][j].w};
       const bool dead = (flg & 2u) != 0;
       const bool live = (flg & 1u) != 0;  // row inside the sequence
+      // the products of two neighbouring elements rounded together by the
+      // hardware conversion; exact wherever the fp32 product is a normal
+      // number (checked per element, the rest marked slow)
       uint32_t res[4];
 #pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        const uint16_t obe = (uint16_t)(ow[e >> 1] >> (16 * (e & 1)));
-        const uint16_t ge = (uint16_t)(gw[e >> 1] >> (16 * (e & 1)));
-        const uint16_t sb = sigmoid_from_entry(ge, sig_lds[sigmoid_table_slot(ge)]);
-        uint16_t r;
-        if (!gate_product_fast(obe, sb, r) && live && !dead) slow |= 1ull << (8 * j + e);
-        const uint32_t rv = dead ? 0u : (uint32_t)r;
-        if (e & 1) res[e >> 1] |= rv << 16; else res[e >> 1] = rv;
+      for (int e2 = 0; e2 < 4; ++e2) {
+        float pr[2];
+#pragma unroll
+        for (int u = 0; u < 2; ++u) {
+          const int e = 2 * e2 + u;
+          const uint16_t ge = (uint16_t)(gw[e2] >> (16 * u));
+          const uint16_t sb = sigmoid_from_entry(ge, sig_lds[sigmoid_table_slot(ge)]);
+          pr[u] = (u ? bf16_hi(ow[e2]) : bf16_lo(ow[e2])) * bf16_to_f32(sb);
+          const float ap = __builtin_fabsf(pr[u]);
+          if (!(ap >= 0x1p-126f && ap <= 0x1p127f) && live && !dead) slow |= 1ull << (8 * j + e);
+        }
+        res[e2] = dead ? 0u : cvt_pk_bf16(pr[0], pr[1]);
       }
       if (live)
         *reinterpret_cast<uint4*>(a.out + (((size_t)b * S + p0 + row) * Hq + hq) * kD + 8 * pc) =
