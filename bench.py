@@ -68,8 +68,11 @@ def parse_args():
     ap.add_argument("--prefill-only", action="store_true",
                     help="time only the B=2, S=2048 causal prefill (for profiling)")
     ap.add_argument("--only", choices=["decode_fp8kv", "decode_hq32", "decode_b224",
-                                       "decode_fp8kv_page1"], default=None,
-                    help="time only this decode variant at B=64, L=4096 (for profiling its kernel)")
+                                       "decode_fp8kv_page1", "b1_l512", "qk_norm_rope_t4096"],
+                    default=None,
+                    help="time only this variant (for profiling its kernels): a decode variant at "
+                         "B=64, L=4096, the B=224 serving shape, the B=1 L=512 graph replays, or "
+                         "the dense T=4096 QK-norm + RoPE step")
     ap.add_argument("--calibration-copy", action="store_true",
                     help="also run one plain 1 GiB device copy (counter calibration)")
     ap.add_argument("--json-out", default=None)
@@ -743,6 +746,19 @@ def time_qk_norm_rope(ga, workloads, dev, T: int, slots: bool, n_calls: int = 20
             "input_sets": n_sets}
 
 
+def calibration_copy(dev) -> None:
+    """One plain device copy of 1 GiB (reads 1 GiB, writes 1 GiB): the known
+    size that scales the FETCH_SIZE / WRITE_SIZE counter readings."""
+    import torch
+
+    src = torch.empty(1 << 30, dtype=torch.uint8, device=dev).fill_(1)
+    dst = torch.empty_like(src)
+    torch.cuda.synchronize()
+    dst.copy_(src)
+    torch.cuda.synchronize()
+    del src, dst
+
+
 def main() -> int:
     args = parse_args()
     world = int(os.environ.get("WORLD_SIZE", "1"))
@@ -766,6 +782,16 @@ def main() -> int:
         print(json.dumps({"prefill": time_prefill(ga, workloads.workload(4), dev, K,
                                                   settle_s=args.settle_s)}), flush=True)
         return 0
+    if args.calibration_copy:
+        calibration_copy(dev)
+    if args.only == "b1_l512":
+        print(json.dumps({args.only: graph_latency(ga, workloads.workload(0, poison=False), dev)}),
+              flush=True)
+        return 0
+    if args.only == "qk_norm_rope_t4096":
+        print(json.dumps({args.only: time_qk_norm_rope(ga, workloads, dev, 4096, False, K)}),
+              flush=True)
+        return 0
     if args.only:
         extra = only_case(workloads, args.only)
         print(json.dumps({args.only: time_decode(ga, extra, dev, K, settle_s=args.settle_s)}),
@@ -780,14 +806,6 @@ def main() -> int:
     n_sets = rotation_sets(kv_bytes)
     call = Rotation(lambda: DecodeCall(ga, case, dev), n_sets)
     torch.cuda.synchronize()
-
-    if args.calibration_copy:
-        src = torch.empty(1 << 30, dtype=torch.uint8, device=dev).fill_(1)
-        dst = torch.empty_like(src)
-        torch.cuda.synchronize()
-        dst.copy_(src)  # plain copy kernel: reads 1 GiB, writes 1 GiB
-        torch.cuda.synchronize()
-        del src, dst
 
     # Clock settling: the first few milliseconds of work after idle run at a
     # lower clock (20 warm-up calls left the next 200 at 100.6 us/call vs a
