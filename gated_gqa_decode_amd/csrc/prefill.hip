@@ -7,13 +7,14 @@
 // bf16 rounding chain of the gate (bf16 O, bf16 sigmoid, rounded product) is
 // the one of FreeToken PR #781, Summary.
 //
-// Workgroup = (16 query positions, kv head g, sequence b, head part); 4 waves,
-// one per SIMD, wave w serving query heads 2w and 2w + 1 of the part (up to 8
-// heads), so every K or V fragment read from LDS feeds two heads' MFMAs.
-// 64-key K and V tiles reach LDS by direct copies (buffer loads into LDS, no
-// registers), K one tile ahead of V: while a wave runs the softmax of tile t on
-// its vector ALU, its matrix core computes the scores of tile t + 1; then P V
-// of tile t.  One barrier per tile.
+// Workgroup = (16 query positions, kv head g, sequence b, head part); 8 waves,
+// two per SIMD, wave w serving query head w of the part (up to 8 heads), so a
+// 64-key K or V tile staged in LDS feeds the whole part.  The tiles reach LDS
+// by direct copies (buffer loads into LDS, no registers), two buffers each for
+// K and V: the copies of tile t + 1 are issued while the scores of tile t are
+// computed, so they have the whole of tile t to land.  One barrier per tile;
+// all waves are in the same phase (scores, softmax, P V) at about the same
+// time, which keeps the LDS reading one kind of operand at a time.
 //
 // MFMA v_mfma_f32_16x16x32_bf16 operand layout (wave64): A row = lane % 16,
 // k = 8*(lane/16) + 0..7; B column = lane % 16, same k; C row = 4*(lane/16) + r,
