@@ -11,10 +11,19 @@
 // One wave per (token, pair of head rows) -- H_q query rows, then H_kv key
 // rows -- one row per half-wave: lane l handles dims 8(l % 32) .. +7 of its
 // row, so every load and store moves a 512-byte row in 16-byte pieces, and
-// all of a wave's loads (row, norm weights, cos / sin, V, and the RoPE
-// partner dims d +- rope_dim/2 of the row and the weights) are issued before
-// any is used; the only cross-lane step left is the norm's sum.  Key rows also
-// carry that kv head's V row to the slot.
+// all of a wave's loads (row, norm weights, cos / sin, V) are issued before
+// any is used.  At T = 4096 the kernel is bound by its vector instructions,
+// not by memory, so the work per lane is kept small and free of divergent
+// branches: the mean of squares takes one multiply by 1/D, the reciprocal
+// square root is the hardware's, the bf16 rounding is the hardware's packed
+// round-to-nearest-even conversion, and every lane loads the tables (lanes
+// past rope_dim / 8 at a clamped, in-bounds address) and selects its result.
+// The RoPE partner dims d +- rope_dim/2 sit rope_dim/16 lanes away; when that
+// distance is a power of two they come from the partner lane's own normalised
+// values by a swizzle (lane i reads lane i ^ (rope_dim/16) within its 32 lanes,
+// bitwise what that lane computed); otherwise the partner's row and weights
+// are loaded from memory and normalised with the same operations.  Key rows
+// also carry that kv head's V row to the slot.
 #include <hip/hip_runtime.h>
 #include <math.h>
 #include <stdint.h>
@@ -48,31 +57,45 @@ struct RopeArgs {
   int rope_dim;
 };
 
-__device__ __forceinline__ void unpack8(uint2 lo, uint2 hi, float (&f)[8]) {
-  f[0] = bf16_lo(lo.x);
-  f[1] = bf16_hi(lo.x);
-  f[2] = bf16_lo(lo.y);
-  f[3] = bf16_hi(lo.y);
-  f[4] = bf16_lo(hi.x);
-  f[5] = bf16_hi(hi.x);
-  f[6] = bf16_lo(hi.y);
-  f[7] = bf16_hi(hi.y);
+__device__ __forceinline__ void unpack8(uint4 u, float (&f)[8]) {
+  f[0] = bf16_lo(u.x);
+  f[1] = bf16_hi(u.x);
+  f[2] = bf16_lo(u.y);
+  f[3] = bf16_hi(u.y);
+  f[4] = bf16_lo(u.z);
+  f[5] = bf16_hi(u.z);
+  f[6] = bf16_lo(u.w);
+  f[7] = bf16_hi(u.w);
 }
 
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+
+// Two fp32 -> packed bf16 (v_cvt_pk_bf16_f32: round to nearest even, denormals kept)
 __device__ __forceinline__ uint32_t pack2(float x, float y) {
-  return (uint32_t)bf16_rne_f32(x) | ((uint32_t)bf16_rne_f32(y) << 16);
+  const f32x2 v = {x, y};
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, bf16x2));
 }
 
-// 16 bytes at p (16-byte aligned), as two halves of 4 bf16 each.
-struct Piece {
-  uint2 lo, hi;
-};
-__device__ __forceinline__ Piece load16(const uint16_t* p) {
-  const uint4 u = *reinterpret_cast<const uint4*>(p);
-  return {make_uint2(u.x, u.y), make_uint2(u.z, u.w)};
+__device__ __forceinline__ uint4 zero4() { return make_uint4(0, 0, 0, 0); }
+__device__ __forceinline__ uint4 load16(const uint16_t* p) { return *reinterpret_cast<const uint4*>(p); }
+// the same from an address the compiler cannot see through (an integer made
+// opaque, then a global pointer, so the load stays a global, not a flat, one)
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef const u32x4 __attribute__((address_space(1)))* global_u32x4_ptr;
+__device__ __forceinline__ uint4 load16_opaque(const uint16_t* p) {
+  uint64_t u = reinterpret_cast<uintptr_t>(p);
+  asm volatile("" : "+v"(u));
+  const u32x4 v = *reinterpret_cast<global_u32x4_ptr>(u);
+  return make_uint4(v.x, v.y, v.z, v.w);
 }
-__device__ __forceinline__ void store16(uint16_t* p, Piece v) {
-  *reinterpret_cast<uint4*>(p) = make_uint4(v.lo.x, v.lo.y, v.hi.x, v.hi.y);
+__device__ __forceinline__ void store16(uint16_t* p, uint4 v) { *reinterpret_cast<uint4*>(p) = v; }
+
+// lane i reads lane i ^ X of its 32-lane group (ds_swizzle, bit mode:
+// and-mask 0x1f, or-mask 0, xor-mask X)
+template <int X>
+__device__ __forceinline__ float swizzle_xor(float v) {
+  return __int_as_float(__builtin_amdgcn_ds_swizzle(__float_as_int(v), 0x1f | (X << 10)));
 }
 
 }  // namespace
@@ -89,141 +112,152 @@ __device__ __forceinline__ float half_sum(float v, int half) {
   return half ? h1 : h0;
 }
 
-// One (token, row pair) unit of work: what its loads bring, then what is
-// stored.  load_pair issues every load; finish_pair uses them.
-struct PairLoads {
-  long long t;
-  int row_raw;
-  Piece x, xp, w, wp, c, s, v;
-};
-
-__device__ __forceinline__ PairLoads load_pair(const RopeArgs& a, long long w, int lane) {
+// kXor > 0: the RoPE partner is lane p ^ kXor (rope_dim = 16 kXor); 0: the
+// partner dims are loaded from memory; -1: no rotation (rope_dim = 0).
+template <int kXor>
+__global__ __launch_bounds__(256) void qk_norm_rope_kernel(RopeArgs a) {
   const int Hq = a.num_q_heads, Hkv = a.num_kv_heads;
   const int rows = Hq + Hkv;
   const int pairs = (rows + 1) >> 1;
+  const long long w = (long long)blockIdx.x * 4 + __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  if (w >= a.num_tokens * pairs) return;
+  const long long t = w / pairs;  // wave-uniform
+  const int pr = (int)(w - t * pairs);
+  const int lane = __lane_id();
   const int half = lane >> 5;
   const int p = lane & 31;  // dims 8p .. 8p + 7
-  PairLoads L;
-  L.t = w / pairs;
-  L.row_raw = 2 * (int)(w - L.t * pairs) + half;
-  const int row = min(L.row_raw, rows - 1);  // past the end: a repeat, not stored
+  const int row_raw = 2 * pr + half;
+  const int row = min(row_raw, rows - 1);  // past the end: a repeat, not stored
   const bool is_q = row < Hq;
   const int kvh = row - Hq;
   const int R = a.rope_dim;
-  const bool rotated = 8 * p < R;
-  const uint16_t* wn = is_q ? a.w_q : a.w_k;  // both or neither are given
-  // The row, its norm weights, the token's tables, the V row, and -- instead
-  // of a cross-lane exchange after the norm -- the RoPE partner dims of the
-  // row and of the weights straight from memory (the partner's value is
-  // formed from them with the same operations the partner lane applies, so it
-  // is bitwise the same).  Dims 8p + 4g .. +3 (g = 0, 1) have partners
-  // 4g-aligned at +- R/2 (R/2 is a multiple of 4).
-  const uint16_t* xrow =
-      is_q ? a.q + ((size_t)L.t * Hq + row) * kD : a.k + ((size_t)L.t * Hkv + kvh) * kD;
-  L.x = load16(xrow + 8 * p);
-  const Piece zero = {make_uint2(0, 0), make_uint2(0, 0)};
-  L.xp = L.w = L.wp = L.c = L.s = L.v = zero;
-  if (wn != nullptr) L.w = load16(wn + 8 * p);
-  if (rotated) {
-    const int hr = R >> 1;
+  const int hr = R >> 1;
+  const bool norm = a.w_q != nullptr;  // both or neither are given
+  const uint16_t* xrow = is_q ? a.q + ((size_t)t * Hq + row) * kD : a.k + ((size_t)t * Hkv + kvh) * kD;
+  const uint16_t* wn = is_q ? a.w_q : a.w_k;
+
+  // ---- loads ------------------------------------------------------------------
+  // All unconditional, so they are all in flight before the first wait: an
+  // input that is not used this time (no norm, no rotation, no V) is replaced
+  // by a second read of the lane's own row piece.  Lanes past R / 8 read the
+  // last table group and ignore it.
+  // (The selected addresses are made opaque: otherwise the compiler turns a
+  // select of addresses into a select of a load and the row it already has,
+  // and waits for that row before the branch.)
+  const uint16_t* own = xrow + 8 * p;
+  const bool copy_v = !is_q && a.v_out != nullptr;
+  const size_t tab = (size_t)t * R + 8 * min(p, max((R >> 3) - 1, 0));
+  const uint16_t* vsrc = copy_v ? a.v + ((size_t)t * Hkv + kvh) * kD + 8 * p : own;
+  const uint16_t* wsrc = norm ? wn + 8 * p : own;
+  const uint16_t* csrc = kXor >= 0 ? a.cos + tab : own;
+  const uint16_t* ssrc = kXor >= 0 ? a.sin + tab : own;
+  const uint4 xv = load16(own);
+  const uint4 vv = load16_opaque(vsrc);
+  const uint4 wv = load16_opaque(wsrc);
+  uint4 cv = zero4(), sv = zero4();
+  if constexpr (kXor >= 0) {
+    cv = load16_opaque(csrc);
+    sv = load16_opaque(ssrc);
+  }
+  // the token's slot (key rows), read from q's start when there is no mapping
+  uint64_t su = a.slot_mapping != nullptr ? reinterpret_cast<uintptr_t>(a.slot_mapping + t)
+                                          : reinterpret_cast<uintptr_t>(a.q);
+  asm volatile("" : "+v"(su));
+  const long long slot_read = *reinterpret_cast<const long long __attribute__((address_space(1)))*>(su);
+  // kXor = 0: the partner dims of the row and the weights from memory.  Dims
+  // 8p + 4g .. +3 (g = 0, 1) have partners 4g-aligned at +- R/2 (R/2 is a
+  // multiple of 4); lanes past R / 8 read their own dims.
+  uint4 xpv = xv, wpv = wv;
+  if constexpr (kXor == 0) {  // (R > 0)
     int pofs[2];
 #pragma unroll
     for (int g = 0; g < 2; ++g) {
       const int gd = 8 * p + 4 * g;
-      pofs[g] = gd < hr ? gd + hr : gd - hr;
+      pofs[g] = gd >= R ? gd : gd < hr ? gd + hr : gd - hr;  // lanes past R: their own dims
     }
-    L.c = load16(a.cos + (size_t)L.t * R + 8 * p);
-    L.s = load16(a.sin + (size_t)L.t * R + 8 * p);
-    if ((hr & 4) == 0) {  // the partners of all 8 dims are 8 contiguous dims
-      L.xp = load16(xrow + pofs[0]);
-      if (wn != nullptr) L.wp = load16(wn + pofs[0]);
-    } else {              // two groups of 4 in different places
-      L.xp = {*reinterpret_cast<const uint2*>(xrow + pofs[0]),
-              *reinterpret_cast<const uint2*>(xrow + pofs[1])};
-      if (wn != nullptr)
-        L.wp = {*reinterpret_cast<const uint2*>(wn + pofs[0]),
-                *reinterpret_cast<const uint2*>(wn + pofs[1])};
-    }
+    const uint16_t* wrow = norm ? wn : xrow;
+    const uint2 x0 = *reinterpret_cast<const uint2*>(xrow + pofs[0]);
+    const uint2 x1 = *reinterpret_cast<const uint2*>(xrow + pofs[1]);
+    const uint2 w0 = *reinterpret_cast<const uint2*>(wrow + pofs[0]);
+    const uint2 w1 = *reinterpret_cast<const uint2*>(wrow + pofs[1]);
+    xpv = make_uint4(x0.x, x0.y, x1.x, x1.y);
+    wpv = make_uint4(w0.x, w0.y, w1.x, w1.y);
   }
-  if (!is_q && a.v_out != nullptr) L.v = load16(a.v + ((size_t)L.t * Hkv + kvh) * kD + 8 * p);
-  return L;
-}
+  // nothing below moves above the loads
+  __builtin_amdgcn_sched_barrier(0);
 
-__device__ __forceinline__ void finish_pair(const RopeArgs& a, const PairLoads& L, int lane) {
-  const int Hq = a.num_q_heads, Hkv = a.num_kv_heads;
-  const int rows = Hq + Hkv;
-  const int half = lane >> 5;
-  const int p = lane & 31;
-  const int row = min(L.row_raw, rows - 1);
-  const bool is_q = row < Hq;
-  const int kvh = row - Hq;
-  const int R = a.rope_dim;
-  const bool rotated = 8 * p < R;
-  const int hr = R >> 1;
-  float x[8], xp[8];
-  unpack8(L.x.lo, L.x.hi, x);
-  unpack8(L.xp.lo, L.xp.hi, xp);
-  // RMSNorm over the row's D values, in fp32
-  float y[8], yp[8];
-  if (a.w_q != nullptr) {  // wave-uniform
+  // ---- RMSNorm over the row's D values, in fp32 -------------------------------
+  float x[8], y[8];
+  unpack8(xv, x);
+  float rr = 1.f;
+  if (norm) {  // wave-uniform
     float ss = 0.f;
 #pragma unroll
-    for (int e = 0; e < 8; ++e) ss += x[e] * x[e];
+    for (int e = 0; e < 8; ++e) ss = __builtin_fmaf(x[e], x[e], ss);
     ss = half_sum(ss, half);
-    const float rr = 1.0f / sqrtf(ss / (float)kD + a.eps);
-    float wf[8], wpf[8];
-    unpack8(L.w.lo, L.w.hi, wf);
-    unpack8(L.wp.lo, L.wp.hi, wpf);
+    rr = __builtin_amdgcn_rsqf(ss * (1.0f / kD) + a.eps);
+    float wf[8];
+    unpack8(wv, wf);
+#pragma unroll
+    for (int e = 0; e < 8; ++e) y[e] = x[e] * rr * wf[e];
+  } else {
+#pragma unroll
+    for (int e = 0; e < 8; ++e) y[e] = x[e];
+  }
+
+  // ---- rotate-half RoPE on dims < R ---------------------------------------------
+  // first half (d < R/2): z = y c - y' s; second half: z = y c + y' s, y' the
+  // partner dim's normalised value
+  float z[8];
+  if constexpr (kXor >= 0) {
+    float yp[8];
+    if constexpr (kXor > 0) {
+#pragma unroll
+      for (int e = 0; e < 8; ++e) yp[e] = swizzle_xor<kXor>(y[e]);
+    } else {
+      float xp[8];
+      unpack8(xpv, xp);
+      if (norm) {
+        float wpf[8];
+        unpack8(wpv, wpf);
+#pragma unroll
+        for (int e = 0; e < 8; ++e) yp[e] = xp[e] * rr * wpf[e];
+      } else {
+#pragma unroll
+        for (int e = 0; e < 8; ++e) yp[e] = xp[e];
+      }
+    }
+    float c[8], sn[8];
+    unpack8(cv, c);
+    unpack8(sv, sn);
+    const bool rotated = 8 * p < R;
 #pragma unroll
     for (int e = 0; e < 8; ++e) {
-      y[e] = x[e] * rr * wf[e];
-      yp[e] = xp[e] * rr * wpf[e];
+      const bool first = 8 * p + 4 * (e >> 2) < hr;
+      const float r = __builtin_fmaf(first ? -yp[e] : yp[e], sn[e], y[e] * c[e]);
+      z[e] = rotated ? r : y[e];
     }
   } else {
 #pragma unroll
-    for (int e = 0; e < 8; ++e) {
-      y[e] = x[e];
-      yp[e] = xp[e];
-    }
+    for (int e = 0; e < 8; ++e) z[e] = y[e];
   }
-  // rotate-half RoPE on dims < R: first half z = y c - y' s, second half
-  // z = y c + y' s, y' the partner dim d +- R/2
-  float c[8], sn[8];
-  unpack8(L.c.lo, L.c.hi, c);
-  unpack8(L.s.lo, L.s.hi, sn);
-  float z[8];
-#pragma unroll
-  for (int e = 0; e < 8; ++e) {
-    const bool first = 8 * p + 4 * (e >> 2) < hr;
-    z[e] = !rotated ? y[e] : first ? y[e] * c[e] - yp[e] * sn[e] : y[e] * c[e] + yp[e] * sn[e];
-  }
-  if (L.row_raw >= rows) return;  // the repeated last row: nothing to store
-  const Piece zo = {make_uint2(pack2(z[0], z[1]), pack2(z[2], z[3])),
-                    make_uint2(pack2(z[4], z[5]), pack2(z[6], z[7]))};
+
+  // ---- stores -----------------------------------------------------------------------
+  if (row_raw >= rows) return;  // the repeated last row: nothing to store
+  const uint4 zo = make_uint4(pack2(z[0], z[1]), pack2(z[2], z[3]), pack2(z[4], z[5]), pack2(z[6], z[7]));
   if (is_q) {
-    store16(a.q_out + ((size_t)L.t * Hq + row) * kD + 8 * p, zo);
+    store16(a.q_out + ((size_t)t * Hq + row) * kD + 8 * p, zo);
     return;
   }
   // key row: K and V to the token's slot (or dense position)
-  long long slot = L.t;
+  long long slot = t;
   if (a.slot_mapping != nullptr) {
-    slot = a.slot_mapping[L.t];
+    slot = slot_read;
     if (slot < 0 || slot >= a.num_slots) return;  // padded token / outside the pools
   }
   const size_t off = ((size_t)slot * Hkv + kvh) * kD + 8 * p;
   store16(a.k_out + off, zo);
-  if (a.v_out != nullptr) store16(a.v_out + off, L.v);
-}
-
-// One row pair per wave, all its loads issued before any is used.  (Two or
-// four pairs per wave keep more bytes in flight per wave but need so many
-// registers that fewer waves fit: measured slower at T = 4096.)
-__global__ __launch_bounds__(256) void qk_norm_rope_kernel(RopeArgs a) {
-  const long long units = a.num_tokens * ((a.num_q_heads + a.num_kv_heads + 1) >> 1);
-  const long long w = (long long)blockIdx.x * 4 + (threadIdx.x >> 6);
-  if (w >= units) return;
-  const int lane = __lane_id();
-  finish_pair(a, load_pair(a, w, lane), lane);
+  if (copy_v) store16(a.v_out + off, vv);
 }
 
 hipError_t launch_qk_norm_rope(const RopeLaunch& p, hipStream_t stream) {
@@ -247,8 +281,19 @@ hipError_t launch_qk_norm_rope(const RopeLaunch& p, hipStream_t stream) {
   a.rope_dim = p.rope_dim;
   // one (token, pair of head rows) unit per wave, four waves per workgroup
   const long long units = p.num_tokens * ((p.num_q_heads + p.num_kv_heads + 1) / 2);
-  hipLaunchKernelGGL(qk_norm_rope_kernel, dim3((unsigned)((units + 3) / 4)), dim3(256), 0, stream,
-                     a);
+  const dim3 grid((unsigned)((units + 3) / 4));
+  // partners by swizzle when rope_dim / 16 is a power of two; no table at all
+  // for rope_dim 0
+  const int xr = p.rope_dim == 0 ? -1 : (p.rope_dim % 16 == 0) ? p.rope_dim / 16 : 0;
+  switch (xr) {
+    case -1: hipLaunchKernelGGL(qk_norm_rope_kernel<-1>, grid, dim3(256), 0, stream, a); break;
+    case 1: hipLaunchKernelGGL(qk_norm_rope_kernel<1>, grid, dim3(256), 0, stream, a); break;
+    case 2: hipLaunchKernelGGL(qk_norm_rope_kernel<2>, grid, dim3(256), 0, stream, a); break;
+    case 4: hipLaunchKernelGGL(qk_norm_rope_kernel<4>, grid, dim3(256), 0, stream, a); break;
+    case 8: hipLaunchKernelGGL(qk_norm_rope_kernel<8>, grid, dim3(256), 0, stream, a); break;
+    case 16: hipLaunchKernelGGL(qk_norm_rope_kernel<16>, grid, dim3(256), 0, stream, a); break;
+    default: hipLaunchKernelGGL(qk_norm_rope_kernel<0>, grid, dim3(256), 0, stream, a); break;
+  }
   return hipGetLastError();
 }
 

@@ -48,7 +48,10 @@ def _gpu(c, norm=True, slots=None, k_pool=None, v_pool=None, cos=None, sin=None)
     return [to_np(x) for x in out]
 
 
-@pytest.mark.parametrize("R", [0, 8, 64, 256])
+# rope_dim 16..128 in steps of 16 take the RoPE partners from the partner lane
+# (DPP row shifts of 1..8 lanes); 8, 200 and 256 load them from memory (200:
+# partner groups split in two)
+@pytest.mark.parametrize("R", [0, 8, 16, 48, 64, 128, 200, 256])
 @pytest.mark.parametrize("norm", [True, False])
 def test_dense_parity(R, norm):
     c = workloads.make_rope(f"rope_R{R}", 37, seed=20 + R, rope_dim=R)
@@ -62,8 +65,9 @@ def test_dense_parity(R, norm):
         assert np.array_equal(qo, c.q) and np.array_equal(ko, c.k)
 
 
-def test_quarter_turn_is_bit_exact():
-    c = workloads.make_rope("rope_qt", 9, seed=30, rope_dim=64)
+@pytest.mark.parametrize("R", [16, 64, 128, 200])
+def test_quarter_turn_is_bit_exact(R):
+    c = workloads.make_rope(f"rope_qt{R}", 9, seed=30 + R, rope_dim=R)
     cos = np.zeros_like(c.cos)
     sin = np.full_like(c.sin, 0x3F80)
     qo, ko, _ = _gpu(c, norm=False, cos=cos, sin=sin)
