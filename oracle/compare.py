@@ -28,6 +28,12 @@ sigma_b >= 0, so the GPU output must then lie in
 exactly, with no ulp allowance.  This bounds the error of every element by
 the size of the terms summed -- also where O cancels and the strict rule
 cannot hold -- at 2^-10 of them, 16x tighter than the floored rule's 2^-6.
+It is also what bounds the strict-rule violations: where |O| >= Mref / 2
+(no cancellation to speak of), eta * Mref is below half a bf16 ulp of O, the
+interval holds at most the two bf16 neighbours of O (times sigma_b, rounded),
+and an output more than one or two ulp from the oracle's fails.  A strict
+violation can only pass on an element whose |O| / Mref is below 1/2, and
+there only by as many ulp of |O| as the cancellation allows.
 """
 from __future__ import annotations
 
