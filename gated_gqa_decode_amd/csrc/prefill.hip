@@ -473,9 +473,7 @@ void prefill_gate_kernel(PrefillArgs a) {
   // so their latency overlaps the normalisation.  bf16(O) of the wave's 2 x 16
   // rows goes through LDS from the MFMA layout (lane: 4 rows x 16 strided
   // columns) to whole 16-byte pieces of rows, so each lane issues 16 gate loads
-  // and 16 output stores of 16 bytes instead of 128 of 2 bytes.  LDS per wave
-  // (one of the four tile buffers): 16 KiB of bf16(O), 128 B of row flags, and
-  // a copy of the sigmoid table (8 KiB).
+  // and 16 output stores of 16 bytes instead of 128 of 2 bytes.
   const int pc = lane & 31;  // piece j of this lane: row 2j + lane / 32, dims 8 (lane % 32) .. +7
   uint4 gt8[kH][8];
   if (active) {
@@ -488,75 +486,87 @@ void prefill_gate_kernel(PrefillArgs a) {
       }
   }
   __syncthreads();  // every wave is done with the tiles: their LDS is reused below
-  if (!active) return;
-  // this wave's region: kH x 8 KiB of bf16(O), then 8 KiB of sigmoid table
-  constexpr int kRegion = kH * kBM * kD * 2 + 8192;
-  constexpr int kPerTile = kTileBytes / kRegion;  // regions per tile buffer
-  static_assert(kPerTile * 4 >= kWavesPf, "the epilogue regions fit the tile buffers");
-  const int tb = wave / kPerTile;
-  char* const lds = (tb == 0 ? k0 : tb == 1 ? k1 : tb == 2 ? v0 : v1) + (wave % kPerTile) * kRegion;
+  // Regions: this wave's kH x 8 KiB of bf16(O) in the K tiles, and one sigmoid
+  // table for the workgroup in the first V tile, extended so that it holds
+  // every gate's result without range tests: index
+  //   (sign * 18 + clamp(exponent, 117, 134) - 117) * 128 + mantissa
+  // where bucket 117 stands for |g| < 2^-9 (result 0.5), buckets 118 .. 133
+  // are the correctly rounded table, and bucket 134 for |g| >= 128 (1, or +0
+  // for negative g).  Only NaN gates need a test of their own.
+  constexpr int kRegion = kH * kBM * kD * 2;
+  constexpr int kPerTile = kTileBytes / kRegion;  // regions per K tile buffer
+  static_assert(kPerTile * 2 >= kWavesPf, "the epilogue regions fit the K tile buffers");
+  static_assert(2 * 18 * 128 * 2 <= kTileBytes, "the extended table fits a V tile buffer");
+  char* const lds = (wave < kPerTile ? k0 : k1) + (wave % kPerTile) * kRegion;
   uint16_t* const ob_lds = reinterpret_cast<uint16_t*>(lds);  // [head][16 rows][256]
-  uint16_t* const sig_lds = reinterpret_cast<uint16_t*>(lds + kH * kBM * kD * 2);
-  {  // the table -> this wave's copy by direct copies (no registers), 1 KiB each
+  uint16_t* const sig_lds = reinterpret_cast<uint16_t*>(v0);
+  {
+    // the 4,096-entry table by direct copies: 512 pieces of 16 bytes, one per
+    // lane of the 8 waves; piece c holds entries 8c .. 8c + 7 (sign c / 256)
     const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(
         const_cast<uint16_t*>(kSigmoidTable), 0, (int)sizeof(kSigmoidTable), 0x00020000);
-#pragma unroll
-    for (int k = 0; k < 8; ++k)
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_void*)(sig_lds + 512 * k), 16,
-                                               16 * lane + 1024 * k, 0, 0, 0);
-  }
-#pragma unroll
-  for (int h = 0; h < kH; ++h) {
-    const int hq = hw[h];
-    float lr_own = l_row[h];
-    lr_own += shfl_xor(lr_own, 16);  // the row's four lanes hold disjoint keys
-    lr_own += shfl_xor(lr_own, 32);
-    // A sink joins the denominator as one more term exp(sink) (log2 units here,
-    // like m_ref); a row with no visible key (l = 0) is dead: out = +0.
-    const float sink2 = a.sinks != nullptr ? a.sinks[hq] * kLog2e : -INFINITY;
-#pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      const int row = 4 * lg + r;
-      const float lr = __int_as_float(__builtin_amdgcn_ds_bpermute(row << 2, __float_as_int(lr_own)));
-      const float mr = __int_as_float(__builtin_amdgcn_ds_bpermute(row << 2, __float_as_int(m_ref[h])));
-      const int qr = p0 + row;
-      float mtot = mr, f = 1.f, den = lr;
-      if (a.sinks != nullptr) {
-        mtot = fmaxf(mr, sink2);
-        f = __builtin_amdgcn_exp2f(mr - mtot);  // 0 for a dead row
-        den = fmaf(lr, f, __builtin_amdgcn_exp2f(sink2 - mtot));
-      }
-      // O f / den through one reciprocal per row and a correction step (the
-      // quotient to within about an fp32 ulp; it is rounded to bf16 next)
-      const float inv = 1.f / den;
-      // rounded two at a time by the hardware conversion (round to nearest
-      // even; denormals are kept)
-#pragma unroll
-      for (int t = 0; t < 16; t += 2) {
-        float qv[2];
-#pragma unroll
-        for (int u = 0; u < 2; ++u) {
-          const float x = o[h][t + u][r] * f;
-          const float q0 = x * inv;
-          qv[u] = __builtin_fmaf(__builtin_fmaf(-q0, den, x), inv, q0);
-        }
-        const uint32_t pk = cvt_pk_bf16(qv[0], qv[1]);
-        ob_lds[(h * kBM + row) * kD + 16 * t + li] = (uint16_t)pk;
-        ob_lds[(h * kBM + row) * kD + 16 * (t + 1) + li] = (uint16_t)(pk >> 16);
-      }
-      if (a.lse != nullptr && li == 0 && qr < S && (h == 0 || second))
-        a.lse[((size_t)b * S + qr) * Hq + hq] = (den > 0.f) ? (mtot + log2f(den)) * kLn2 : -INFINITY;
+    static_assert(kWavesPf == 8, "one table piece per lane of 8 waves");
+    const int sgn = wave >> 2;
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(
+        rs, (lds_void*)(sig_lds + sgn * 2304 + 128 + 512 * (wave & 3)), 16, 16 * lane + 1024 * wave, 0, 0,
+        0);
+    // the constant buckets: waves 0 / 1 write sign 0 / 1, lanes 0-31 bucket
+    // 117 and lanes 32-63 bucket 134, four entries each
+    if (wave < 2) {
+      const uint32_t big = wave == 0 ? 0x3f803f80u : 0u;
+      const uint32_t v = lane < 32 ? 0x3f003f00u : big;
+      const int ent = wave * 2304 + (lane < 32 ? 0 : 2176) + 4 * (lane & 31);
+      *reinterpret_cast<uint2*>(sig_lds + ent) = make_uint2(v, v);
     }
   }
-  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // the table copies and gate rows have landed
-  // the wave's LDS writes above before its reads of other lanes' values below
-  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-  __builtin_amdgcn_wave_barrier();
-  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-  // The gate: the sigmoid from the wave's table copy and the product in fp32
-  // for all elements (no branches) and the stores, then the fp64 product for
-  // the rare ones whose fp32 product is not exact (zero, subnormal), stored
-  // over the first result.
+  if (active) {
+#pragma unroll
+    for (int h = 0; h < kH; ++h) {
+      const int hq = hw[h];
+      float lr_own = l_row[h];
+      lr_own += shfl_xor(lr_own, 16);  // the row's four lanes hold disjoint keys
+      lr_own += shfl_xor(lr_own, 32);
+      // A sink joins the denominator as one more term exp(sink) (log2 units
+      // here, like m_ref); a row with no visible key (l = 0) is dead: out = +0.
+      const float sink2 = a.sinks != nullptr ? a.sinks[hq] * kLog2e : -INFINITY;
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int row = 4 * lg + r;
+        const float lr = __int_as_float(__builtin_amdgcn_ds_bpermute(row << 2, __float_as_int(lr_own)));
+        const float mr = __int_as_float(__builtin_amdgcn_ds_bpermute(row << 2, __float_as_int(m_ref[h])));
+        const int qr = p0 + row;
+        float mtot = mr, f = 1.f, den = lr;
+        if (a.sinks != nullptr) {
+          mtot = fmaxf(mr, sink2);
+          f = __builtin_amdgcn_exp2f(mr - mtot);  // 0 for a dead row
+          den = fmaf(lr, f, __builtin_amdgcn_exp2f(sink2 - mtot));
+        }
+        // O f / den as O times one factor per row (within about an fp32 ulp
+        // of the quotient; it is rounded to bf16 next), rounded two at a time
+        // by the hardware conversion (round to nearest even; denormals kept)
+        const float gq = f / den;
+#pragma unroll
+        for (int t = 0; t < 16; t += 2) {
+          const uint32_t pk = cvt_pk_bf16(o[h][t][r] * gq, o[h][t + 1][r] * gq);
+          ob_lds[(h * kBM + row) * kD + 16 * t + li] = (uint16_t)pk;
+          ob_lds[(h * kBM + row) * kD + 16 * (t + 1) + li] = (uint16_t)(pk >> 16);
+        }
+        if (a.lse != nullptr && li == 0 && qr < S && (h == 0 || second))
+          a.lse[((size_t)b * S + qr) * Hq + hq] = (den > 0.f) ? (mtot + log2f(den)) * kLn2 : -INFINITY;
+      }
+    }
+  }
+  // the table copies and the gate rows have landed; the whole table and every
+  // wave's bf16(O) are in LDS
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+  __syncthreads();
+  if (!active) return;
+  // The gate: bf16(O) times the sigmoid, in fp32, rounded once by the
+  // conversion.  Both factors are bf16, so their product has at most 16
+  // significant bits and fp32 holds it exactly down to 2^-134 (fp32
+  // denormals are kept); below that the fp32 rounding cannot move it across
+  // 2^-134, half the smallest bf16 step, so its bf16 rounding is the exact
+  // product's in every case.
 #pragma unroll
   for (int h = 0; h < kH; ++h) {
     if (h == 1 && !second) break;
@@ -564,49 +574,35 @@ void prefill_gate_kernel(PrefillArgs a) {
     float lr_own = l_row[h];  // as above: row li's sum, for the dead-row test
     lr_own += shfl_xor(lr_own, 16);
     lr_own += shfl_xor(lr_own, 32);
-    uint64_t slow = 0;
 #pragma unroll
     for (int j = 0; j < 8; ++j) {
       const int row = 2 * j + (lane >> 5);
       const float lr = __int_as_float(__builtin_amdgcn_ds_bpermute(row << 2, __float_as_int(lr_own)));
-      const uint32_t flg = (p0 + row < S ? 1u : 0u) | (lr == 0.f ? 2u : 0u);
+      const bool dead = lr == 0.f;
       const uint4 ob8 = *reinterpret_cast<const uint4*>(&ob_lds[(h * kBM + row) * kD + 8 * pc]);
       const uint32_t ow[4] = {ob8.x, ob8.y, ob8.z, ob8.w};
       const uint32_t gw[4] = {gt8[h][j].x, gt8[h][j].y, gt8[h][j].z, gt8[h][j].w};
-      const bool dead = (flg & 2u) != 0;
-      const bool live = (flg & 1u) != 0;  // row inside the sequence
-      // the products of two neighbouring elements rounded together by the
-      // hardware conversion; exact wherever the fp32 product is a normal
-      // number (checked per element, the rest marked slow)
       uint32_t res[4];
 #pragma unroll
       for (int e2 = 0; e2 < 4; ++e2) {
         float pr[2];
 #pragma unroll
         for (int u = 0; u < 2; ++u) {
-          const int e = 2 * e2 + u;
-          const uint16_t ge = (uint16_t)(gw[e2] >> (16 * u));
-          const uint16_t sb = sigmoid_from_entry(ge, sig_lds[sigmoid_table_slot(ge)]);
-          pr[u] = (u ? bf16_hi(ow[e2]) : bf16_lo(ow[e2])) * bf16_to_f32(sb);
-          const float ap = __builtin_fabsf(pr[u]);
-          if (!(ap >= 0x1p-126f && ap <= 0x1p127f) && live && !dead) slow |= 1ull << (8 * j + e);
+          const uint32_t g = (gw[e2] >> (16 * u)) & 0xffffu;
+          const uint32_t ec = min(max((g >> 7) & 0xffu, 117u), 134u);
+          const uint32_t idx = (((g >> 15) * 18u + ec - 117u) << 7) | (g & 0x7fu);
+          // read for every gate (the index is in range for NaN gates too), then
+          // the NaN gate's result selected: kept from becoming a branch per element
+          uint32_t te = sig_lds[idx];
+          asm volatile("" : "+v"(te));
+          const uint32_t sb = (g & 0x7fffu) > 0x7f80u ? 0x7fc0u : te;  // NaN gate
+          pr[u] = (u ? bf16_hi(ow[e2]) : bf16_lo(ow[e2])) * bf16_to_f32((uint16_t)sb);
         }
         res[e2] = dead ? 0u : cvt_pk_bf16(pr[0], pr[1]);
       }
-      if (live)
+      if (p0 + row < S)  // rows past the sequence are not stored
         *reinterpret_cast<uint4*>(a.out + (((size_t)b * S + p0 + row) * Hq + hq) * kD + 8 * pc) =
             make_uint4(res[0], res[1], res[2], res[3]);
-    }
-    if (slow != 0) {  // rare: re-read the element's bf16(O) and gate
-#pragma unroll
-      for (int j = 0; j < 8; ++j) {
-        const int row = 2 * j + (lane >> 5);
-        const size_t off = (((size_t)b * S + p0 + row) * Hq + hq) * kD + 8 * pc;
-#pragma unroll
-        for (int e = 0; e < 8; ++e)
-          if ((slow >> (8 * j + e)) & 1ull)
-            a.out[off + e] = gate_output(ob_lds[(h * kBM + row) * kD + 8 * pc + e], a.gate[off + e]);
-      }
     }
   }
 }
