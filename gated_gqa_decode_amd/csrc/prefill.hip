@@ -305,11 +305,13 @@ void prefill_gate_kernel(PrefillArgs a) {
                            (a.window > 0 && j0 < p0 + kBM - a.window);
 #pragma unroll
     for (int h = 0; h < kH; ++h) {
+      // raw scores (the scale is applied inside the exponent below); masked
+      // keys get -inf
       float sv[4][4];
 #pragma unroll
       for (int ct = 0; ct < 4; ++ct)
 #pragma unroll
-        for (int r = 0; r < 4; ++r) sv[ct][r] = st[h][ct][r] * a.scale_log2;
+        for (int r = 0; r < 4; ++r) sv[ct][r] = st[h][ct][r];
       if (need_mask) {
 #pragma unroll
         for (int ct = 0; ct < 4; ++ct)
@@ -321,17 +323,15 @@ void prefill_gate_kernel(PrefillArgs a) {
             sv[ct][r] = ok ? sv[ct][r] : -INFINITY;
           }
       }
-      bool raise = false;
+      // the lane's largest score, scaled (the scale is positive, so this is the
+      // largest scaled score)
+      float mx = sv[0][0];
 #pragma unroll
       for (int ct = 0; ct < 4; ++ct)
 #pragma unroll
-        for (int r = 0; r < 4; ++r) raise |= sv[ct][r] > m_ref[h] + kSlack;
-      if (__builtin_amdgcn_ballot_w64(raise) != 0) {  // wave-uniform, rare
-        float mx = -INFINITY;
-#pragma unroll
-        for (int ct = 0; ct < 4; ++ct)
-#pragma unroll
-          for (int r = 0; r < 4; ++r) mx = fmaxf(mx, sv[ct][r]);
+        for (int r = 0; r < 4; ++r) mx = fmaxf(mx, sv[ct][r]);
+      mx *= a.scale_log2;
+      if (__builtin_amdgcn_ballot_w64(mx > m_ref[h] + kSlack) != 0) {  // wave-uniform, rare
         mx = fmaxf(mx, shfl_xor(mx, 16));
         mx = fmaxf(mx, shfl_xor(mx, 32));
         const float m_new = fmaxf(m_ref[h], mx);
@@ -348,13 +348,13 @@ void prefill_gate_kernel(PrefillArgs a) {
           for (int t = 0; t < 16; ++t) o[h][t][r] *= ar;
         }
       }
-      const float mref_safe = (m_ref[h] == -INFINITY) ? 0.f : m_ref[h];
+      const float neg_m = (m_ref[h] == -INFINITY) ? 0.f : -m_ref[h];
 #pragma unroll
       for (int ct = 0; ct < 4; ++ct) {
 #pragma unroll
         for (int rp = 0; rp < 2; ++rp) {
-          const float pa = __builtin_amdgcn_exp2f(sv[ct][2 * rp] - mref_safe);
-          const float pb = __builtin_amdgcn_exp2f(sv[ct][2 * rp + 1] - mref_safe);
+          const float pa = __builtin_amdgcn_exp2f(__builtin_fmaf(sv[ct][2 * rp], a.scale_log2, neg_m));
+          const float pb = __builtin_amdgcn_exp2f(__builtin_fmaf(sv[ct][2 * rp + 1], a.scale_log2, neg_m));
           l_row[h] += pa + pb;
           const uint32_t hi = cvt_pk_bf16(pa, pb);
           const uint32_t lo = cvt_pk_bf16(pa - bf16_lo(hi), pb - bf16_hi(hi));
