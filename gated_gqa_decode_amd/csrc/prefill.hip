@@ -170,9 +170,9 @@ void prefill_gate_kernel(PrefillArgs a) {
   const int part = gp - g * a.parts;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int lane = __lane_id();
-  // Heads of this part; wave w serves part heads 2w and 2w + 1.  A wave past
-  // the part's heads only helps copy K/V; a missing second head computes a
-  // copy of the first and is not stored.
+  // Heads of this part; wave w serves part heads kH w .. kH w + kH - 1 (kH = 1:
+  // head w).  A wave past the part's heads only helps copy K/V; with kH = 2 a
+  // missing second head computes a copy of the first and is not stored.
   const int heads = part == 0 ? a.heads_per_part : Hq / Hkv - a.heads_per_part;  // >= 1
   const bool active = kH * wave < heads;
   const bool second = kH * wave + 1 < heads;  // (kH == 2) the wave's second head is real
@@ -224,7 +224,7 @@ void prefill_gate_kernel(PrefillArgs a) {
     for (int d = 0; d < kCopies; ++d) copy_one(base, kt, buf, is_v, d);
   };
 
-  // Q fragments (B operand of K Q^T) of both heads: row p0 + li, d = 32*ks + 8*lg .. +7
+  // Q fragments (B operand of K Q^T) of the wave's heads: row p0 + li, d = 32*ks + 8*lg .. +7
   bf16x8 qf[kH][8];
   {
     const int pos = min(qi, S - 1);
@@ -249,7 +249,7 @@ void prefill_gate_kernel(PrefillArgs a) {
     l_row[h] = 0.f;
   }
 
-  // ---- S^T = K Q^T of one tile for both heads ------------------------------------
+  // ---- S^T = K Q^T of one tile for the wave's heads -------------------------------
   // k-step outer, key tile inner: eight accumulators interleave.
   // hook(s) runs after the K reads of k-step s + 1 are issued: the next
   // tile's copies ride along with the MFMAs (issued early, so they have the
@@ -469,11 +469,11 @@ void prefill_gate_kernel(PrefillArgs a) {
   }
 
   // ---- epilogue: O / l -> bf16, gate, store ------------------------------------
-  // The gate rows of both heads are requested first, before the last barrier,
-  // so their latency overlaps the normalisation.  bf16(O) of the wave's 2 x 16
-  // rows goes through LDS from the MFMA layout (lane: 4 rows x 16 strided
-  // columns) to whole 16-byte pieces of rows, so each lane issues 16 gate loads
-  // and 16 output stores of 16 bytes instead of 128 of 2 bytes.
+  // The gate rows of the wave's heads are requested first, before the last
+  // barrier, so their latency overlaps the normalisation.  bf16(O) of the
+  // wave's kH x 16 rows goes through LDS from the MFMA layout (lane: 4 rows x 16
+  // strided columns) to whole 16-byte pieces of rows, so each lane issues 8 kH
+  // gate loads and 8 kH output stores of 16 bytes instead of 64 kH of 2 bytes.
   const int pc = lane & 31;  // piece j of this lane: row 2j + lane / 32, dims 8 (lane % 32) .. +7
   uint4 gt8[kH][8];
   if (active) {
