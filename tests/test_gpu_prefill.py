@@ -91,3 +91,58 @@ def test_every_gate_bit_pattern_through_prefill():
     nan = ((exp & 0x7F80) == 0x7F80) & ((exp & 0x7F) != 0)
     assert np.array_equal(got[~nan], exp[~nan])
     assert np.all(((got[nan] & 0x7F80) == 0x7F80) & ((got[nan] & 0x7F) != 0))
+
+
+def _every_row_written(got):
+    assert not np.any((got & 0x7F80) == 0x7F80), "non-finite (unwritten?) output"
+
+
+@pytest.mark.parametrize("B,S,Hq,Hkv", [
+    (1, 8192, 16, 2),   # 512 query tiles per (sequence, kv head); 2 slices, 4 XCDs each
+    (4, 520, 32, 4),    # 16 slices: several slices per XCD; a ragged last query tile
+])
+def test_long_and_many_slice_prefill_sampled_rows(B, S, Hq, Hkv):
+    """Shapes past the other tests' (query tiles per slice, slices per XCD):
+    the NaN-poisoned output must be written everywhere, and sampled rows --
+    first and last positions, tile and key-tile boundaries, seeded picks --
+    match the oracle."""
+    p = workloads.make_prefill(f"pf_B{B}_S{S}", B, S, seed=90 + S, causal=True, num_q_heads=Hq,
+                               num_kv_heads=Hkv)
+    out = torch.full(p.q.shape, float("nan"), dtype=torch.bfloat16, device=DEV)
+    ga.prefill(to_dev(p.q), to_dev(p.gate), to_dev(p.k), to_dev(p.v), p.scale, causal=True,
+               out=out)
+    torch.cuda.synchronize()
+    got = to_np(out)
+    _every_row_written(got)
+    rng = np.random.default_rng(S)
+    pos = {0, 1, 15, 16, 17, 63, 64, 65, S // 2, S - 17, S - 16, S - 2, S - 1}
+    pos |= set(int(x) for x in rng.integers(0, S, size=24))
+    rows = np.array([(b, s) for b in range(B) for s in sorted(pos)], dtype=np.int64)
+    res = _parity(p, got, rows=rows)
+    assert res["ok"], res
+
+
+def test_prefill_graph_replay_with_changed_inputs():
+    """A prefill call captured into a HIP graph, replayed with new q / gate /
+    k / v: every replay equals an eager call, bit for bit."""
+    p = workloads.make_prefill("pf_graph", 2, 200, seed=95, causal=True)
+    args = [to_dev(x) for x in (p.q, p.gate, p.k, p.v)]
+    out = torch.empty_like(args[0])
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        ga.prefill(*args, p.scale, causal=True, out=out)  # warm-up outside capture
+    torch.cuda.current_stream().wait_stream(s)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        ga.prefill(*args, p.scale, causal=True, out=out)
+    for it in range(4):
+        for i, (x, std) in enumerate(((p.q, 1.0), (p.gate, 2.0), (p.k, 1.0), (p.v, 1.0))):
+            args[i].copy_(to_dev(workloads.normal_bf16(300 + 10 * it + i, 1, x.shape, std=std)))
+        graph.replay()
+        torch.cuda.synchronize()
+        replayed = to_np(out)
+        eager = to_np(ga.prefill(*args, p.scale, causal=True))
+        torch.cuda.synchronize()
+        assert np.array_equal(replayed, eager), it

@@ -149,3 +149,48 @@ def test_decode_after_norm_rope_append():
     for s in slots[slots >= 0]:
         d = np.abs(bf16_bits_to_f64(fk[s]) - bf16_bits_to_f64(frk[s]))
         assert np.all(d <= bf16_ulp(np.abs(bf16_bits_to_f64(frk[s]))) * 2)
+
+
+def test_graph_replay_with_changed_inputs():
+    """The decode step's norm/rope/append captured into a HIP graph (slot
+    mode, caller-owned q_out and pools: nothing is allocated inside), replayed
+    with new rows and slots: every replay equals an eager call, bit for bit."""
+    T, P = 24, 4
+    c = workloads.make_rope("rope_graph", T, seed=36, rope_dim=64)
+    t = {n: to_dev(getattr(c, n)) for n in ("q", "k", "v", "w_q", "w_k", "cos", "sin")}
+    slots = torch.arange(T, dtype=torch.int64, device=DEV)
+    kp = torch.zeros((P, 16, 2, 256), dtype=torch.bfloat16, device=DEV)
+    vp = torch.zeros_like(kp)
+    q_out = torch.empty_like(t["q"])
+
+    def call(kpool, vpool, qo):
+        ga.qk_norm_rope(t["q"], t["k"], t["v"], w_q=t["w_q"], w_k=t["w_k"], eps=c.eps,
+                        cos=t["cos"], sin=t["sin"], slot_mapping=slots, k_pool=kpool,
+                        v_pool=vpool, q_out=qo)
+
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        call(kp, vp, q_out)  # warm-up outside capture
+    torch.cuda.current_stream().wait_stream(s)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        call(kp, vp, q_out)
+    rng = np.random.default_rng(7)
+    for it in range(4):
+        for i, n in enumerate(("q", "k", "v")):
+            t[n].copy_(to_dev(workloads.normal_bf16(400 + 10 * it + i, 1, getattr(c, n).shape)))
+        perm = rng.permutation(P * 16)[:T]
+        perm[rng.integers(0, T)] = -1  # one skipped token
+        slots.copy_(torch.from_numpy(perm.astype(np.int64)).to(DEV))
+        kp.zero_()
+        vp.zero_()
+        graph.replay()
+        torch.cuda.synchronize()
+        got = [to_np(x) for x in (q_out, kp, vp)]
+        kp2, vp2, qo2 = torch.zeros_like(kp), torch.zeros_like(vp), torch.empty_like(q_out)
+        call(kp2, vp2, qo2)
+        torch.cuda.synchronize()
+        for a, b in zip(got, (to_np(qo2), to_np(kp2), to_np(vp2))):
+            assert np.array_equal(a, b), it
