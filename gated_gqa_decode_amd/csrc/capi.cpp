@@ -45,8 +45,10 @@ constexpr int kMaxTokSplitTokens = 2048;
 constexpr int kMaxLongSplitTokens = 16384;
 constexpr int kMaxGridYZ = 65535;
 // A launch's grid size times its workgroup size must stay below 2^32 threads:
-// stage 1 has 512 threads per workgroup, stage 2 has 256 (4 rows each).
+// decode stage 1 and prefill have 512 threads per workgroup, decode stage 2
+// has 256 (4 rows each).
 constexpr int64_t kMaxStage1Workgroups = (int64_t)1 << 22;
+constexpr int64_t kMaxPrefillWorkgroups = (int64_t)1 << 22;
 constexpr int64_t kMaxDecodeRows = (int64_t)1 << 26;
 
 thread_local int g_last_hip_error = 0;
@@ -361,10 +363,17 @@ ga_status gated_attn_prefill_ex(const uint16_t* q, const uint16_t* gate, const u
   if (!(std::isfinite(scale) && scale > 0.f)) return GA_ERR_INVALID_ARGUMENT;
   st = check_options(opts, /*prefill=*/true);
   if (st != GA_OK) return st;
-  if (dims->batch > kMaxGridYZ) return GA_ERR_UNSUPPORTED;
   if (dims->batch == 0 || dims->seq_len == 0) return GA_OK;
-  // q/gate/out hold B*S*H_q*D elements; keep every element index in int32 range.
-  if ((int64_t)dims->batch * dims->seq_len * dims->num_q_heads * kHeadDim > INT32_MAX)
+  // The kernel addresses q, gate and out with 64-bit offsets.  Two limits
+  // remain: one sequence's K or V rows of all kv heads, S * H_kv * D bf16,
+  // are read through a buffer descriptor of at most 2^31 - 1 bytes, and the
+  // grid (one workgroup per sequence, kv head, head part and 16 query
+  // positions) stays below 2^22 workgroups.
+  if ((int64_t)dims->seq_len * dims->num_kv_heads * kHeadDim * 2 > INT32_MAX)
+    return GA_ERR_UNSUPPORTED;
+  const int parts = ga::head_parts(dims->num_q_heads / dims->num_kv_heads);
+  if ((int64_t)dims->batch * dims->num_kv_heads * parts * ((dims->seq_len + 15) / 16) >
+      kMaxPrefillWorkgroups)
     return GA_ERR_UNSUPPORTED;
   const void* ptr16[] = {q, gate, k, v, out};
   for (const void* p : ptr16)

@@ -184,6 +184,15 @@ typedef struct ga_prefill_dims {
  *   q, gate, out  [B][S][H_q][D]   bf16 (q, gate read; out written)
  *   k, v          [B][S][H_kv][D]  bf16, read
  *   causal        non-zero: query i sees keys j <= i; zero: every key
+ *
+ * All buffers 16-byte aligned and device-resident, owned by the caller; out
+ * is written in full.  GA_ERR_INVALID_ARGUMENT for a NULL or misaligned
+ * pointer, negative sizes or a scale that is not finite and positive;
+ * GA_ERR_UNSUPPORTED for D != 256, groups above 16, a device other than
+ * gfx950, one sequence's K (or V) rows spanning more than 2^31 - 1 bytes
+ * (S * H_kv * D * 2), or more than 2^22 workgroups (B * H_kv * parts *
+ * ceil(S / 16), parts = 2 for groups above 8, else 1).  B = 0 or S = 0 does
+ * nothing and returns GA_OK.
  */
 ga_status gated_attn_prefill(const uint16_t *q, const uint16_t *gate, const uint16_t *k,
                              const uint16_t *v, float scale, int causal, uint16_t *out,

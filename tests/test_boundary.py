@@ -266,6 +266,12 @@ def test_empty_batch_is_a_no_op():
     ((2, 128, 15, 2, 256), ga.GA_ERR_INVALID_ARGUMENT),
     ((-1, 128, 16, 2, 256), ga.GA_ERR_INVALID_ARGUMENT),
     ((2, -5, 16, 2, 256), ga.GA_ERR_INVALID_ARGUMENT),
+    # one sequence's K rows (S * H_kv * D * 2 bytes) past one buffer descriptor's 2^31 - 1
+    ((1, 1 << 21, 16, 2, 256), ga.GA_ERR_UNSUPPORTED),
+    ((1, 1 << 18, 128, 16, 256), ga.GA_ERR_UNSUPPORTED),
+    # more than 2^22 workgroups: B * H_kv * parts * ceil(S / 16)
+    ((4097, 16384, 16, 2, 256), ga.GA_ERR_UNSUPPORTED),
+    ((2049, 16384, 32, 2, 256), ga.GA_ERR_UNSUPPORTED),  # group 16: two parts
 ])
 def test_prefill_bad_dims(dims, status):
     d = ga.PrefillDims(*dims)

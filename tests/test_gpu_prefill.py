@@ -146,3 +146,49 @@ def test_prefill_graph_replay_with_changed_inputs():
         eager = to_np(ga.prefill(*args, p.scale, causal=True))
         torch.cuda.synchronize()
         assert np.array_equal(replayed, eager), it
+
+
+def test_prefill_past_2_31_elements_sampled_rows():
+    """q, gate and out of 2.18e9 elements each (B=65, S=2048, H_q=64, H_kv=8),
+    so the last sequence's rows sit past element 2^31 and past byte 2^32
+    (where a 32-bit element or byte offset would wrap onto sequence 0).  The
+    inputs are seeded draws on the device (torch's generator), every sequence
+    its own; the NaN-poisoned output must be written everywhere, and sampled
+    rows of the first, a middle and the last sequences match the oracle on
+    those sequences' inputs copied back."""
+    B, S, Hq, Hkv, D = 65, 2048, 64, 8, 256
+    assert B * S * Hq * D > 2 ** 31
+    gen = torch.Generator(device=DEV)
+    gen.manual_seed(2031)
+
+    def draw(shape, std):
+        x = torch.randn(shape, generator=gen, device=DEV, dtype=torch.float32)
+        return (x * std).to(torch.bfloat16)
+
+    # drawn in per-sequence slabs (fp32 temporaries stay small)
+    q = torch.empty((B, S, Hq, D), dtype=torch.bfloat16, device=DEV)
+    gate = torch.empty_like(q)
+    k = torch.empty((B, S, Hkv, D), dtype=torch.bfloat16, device=DEV)
+    v = torch.empty_like(k)
+    for b in range(B):
+        q[b] = draw((S, Hq, D), 1.0)
+        gate[b] = draw((S, Hq, D), 2.0)
+        k[b] = draw((S, Hkv, D), 1.0)
+        v[b] = draw((S, Hkv, D), 1.0)
+    out = torch.full_like(q, float("nan"))
+    scale = 1.0 / 16
+    ga.prefill(q, gate, k, v, scale, causal=True, out=out)
+    torch.cuda.synchronize()
+    bits = out.view(torch.int16)
+    assert not bool(((bits & 0x7F80) == 0x7F80).any()), "non-finite (unwritten?) output"
+    rng = np.random.default_rng(2031)
+    for b in (0, 32, B - 1):
+        pos = {0, 1, 15, 16, 1023, 1024, S - 2, S - 1} | set(int(x) for x in rng.integers(0, S, 6))
+        rows = np.array([(0, s) for s in sorted(pos)], dtype=np.int64)
+        qb, gb, kb, vb = (to_np(x[b:b + 1]) for x in (q, gate, k, v))
+        ref, o, mref = oracle.prefill(qb, gb, kb, vb, scale, causal=True, rows=rows)
+        got = to_np(out[b:b + 1])[rows[:, 0], rows[:, 1]]
+        res = check_outputs(got, ref, o, mref, oracle.sigmoid_table()[gb[rows[:, 0], rows[:, 1]]])
+        print(f"[parity] pf_2_31 sequence {b}: n={res['n']} bit-exact={res['n_bit_exact']} "
+              f"max_ulp_floor={res['max_ulp_floor']:.4f}", flush=True)
+        assert res["ok"], (b, res)

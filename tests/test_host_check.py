@@ -126,6 +126,31 @@ def test_gfx950_reaches_every_launch(host_lib, tmp_path):
     assert _counts(lib) == [4, 1, 1, 1]
 
 
+def test_prefill_size_limits(host_lib, tmp_path):
+    """q, gate and out past 2^31 elements are served (the kernel addresses them
+    with 64-bit offsets); the two real limits -- one sequence's K or V rows in
+    one 2^31 - 1 byte buffer descriptor, at most 2^22 workgroups -- are
+    declined before any launch, right at their edges."""
+    lib = _load(host_lib, tmp_path, "gfx950")
+
+    def call(B, S, Hq, Hkv):
+        d = ga.PrefillDims(B, S, Hq, Hkv, 256)
+        return lib.gated_attn_prefill(Q, GATE, K, V, 0.0625, 1, OUT, None, ctypes.byref(d))
+
+    served = [
+        (65, 2048, 64, 8),              # B*S*H_q*D = 2.18e9 elements > 2^31
+        (1, (1 << 21) - 2, 16, 2),      # K rows of one sequence: 2^31 - 2048 bytes
+        (2048, 16384, 16, 2),           # exactly 2^22 workgroups
+        (1024, 16384, 32, 2),           # group 16 (two parts): exactly 2^22
+    ]
+    for i, shape in enumerate(served):
+        assert call(*shape) == ga.GA_OK, shape
+        assert _counts(lib)[1] == i + 1, shape
+    for shape in [(1, 1 << 21, 16, 2), (2049, 16384, 16, 2), (1025, 16384, 32, 2)]:
+        assert call(*shape) == ga.GA_ERR_UNSUPPORTED, shape
+    assert _counts(lib)[1] == len(served)
+
+
 def test_decode_launch_follows_the_plan(host_lib, tmp_path):
     lib = _load(host_lib, tmp_path, "gfx950")
     for B, W in ((1, 32), (4, 32), (64, 256), (224, 384)):
