@@ -197,27 +197,37 @@ void prefill_gate_kernel(PrefillArgs a) {
   const int row_bytes = Hkv * kD * 2;            // between consecutive keys
 
   // ---- direct HBM/L2 -> LDS copies of one tile ---------------------------------
-  // Wave w copies rows 16w .. 16w + 15 of the tile (8 instructions, two whole
-  // rows each).  A row outside the visible range [kv_lo, kv_end) copies the
-  // nearest visible row instead: finite data whose probability is exactly 0
-  // (or, for K, whose score is replaced by -inf).
-  const size_t head0 = ((size_t)b * S * Hkv + g) * kD;  // elements to key 0 of head g
-  const int extent = (int)((size_t)S * row_bytes - (size_t)g * kD * 2);  // bytes from there on
-  // copy_one(.., d): instruction d (0..7) of this wave's share of a tile
+  // Wave w copies rows kCopyRows w .. + kCopyRows - 1 of the tile's K and of
+  // its V (kCopies instructions each, two whole rows per instruction).  The
+  // copies go through one buffer descriptor per tensor whose range is the
+  // visible keys [kv_lo, kv_end): a row outside it reads as zeros (finite data
+  // whose probability is exactly 0, or, for K, whose score is replaced by
+  // -inf), so no offset needs clamping.  The per-lane part of every offset is
+  // fixed; a tile adds one uniform term.
+  const size_t key_lo = ((size_t)b * S * Hkv + (size_t)kv_lo * Hkv + g) * kD;  // elements
+  const int vis_bytes = max(kv_end - kv_lo, 0) * row_bytes;  // the descriptors' range (0: no key)
+  uint32_t lane_off[2][kCopies];                        // [K / V][instruction]
+#pragma unroll
+  for (int d = 0; d < kCopies; ++d) {
+    const int r = kCopyRows * wave + 2 * d + (lane >> 5);  // tile row
+    const int p = lane & 31;                               // 16-byte slot in the row
+    lane_off[0][d] = (uint32_t)(r * row_bytes + 16 * (p ^ (r & 15)));         // K chunk stored there
+    lane_off[1][d] = (uint32_t)(r * row_bytes + 16 * (p ^ ((r & 7) << 1)));  // V chunk
+  }
+  // copy_one(.., d): instruction d (0 .. kCopies - 1) of this wave's share of
+  // tile kt of K (is_v false) or V
   auto copy_one = [&](const uint16_t* base, int kt, char* buf, bool is_v, int d) {
     // the descriptor from wave-uniform values, kept in scalar registers
-    const uintptr_t addr = reinterpret_cast<uintptr_t>(base + head0);
+    const uintptr_t addr = reinterpret_cast<uintptr_t>(base + key_lo);
     const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)addr);
     const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(addr >> 32));
     const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(
         reinterpret_cast<void*>(((uintptr_t)hi << 32) | lo), 0,
-        __builtin_amdgcn_readfirstlane(extent), 0x00020000);
-    const int r = kCopyRows * wave + 2 * d + (lane >> 5);  // tile row
-    const int p = lane & 31;                         // 16-byte slot in the row
-    const int c = is_v ? p ^ ((r & 7) << 1) : p ^ (r & 15);  // chunk stored there
-    const int j = min(max(kt * kBN + r, kv_lo), kv_end - 1);
+        __builtin_amdgcn_readfirstlane(vis_bytes), 0x00020000);
+    // rows before kv_lo wrap to offsets far past the range (modulo 2^32)
+    const uint32_t tile = (uint32_t)(kt * kBN - kv_lo) * (uint32_t)row_bytes;
     __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_void*)(buf + (kCopyRows * wave + 2 * d) * 512), 16,
-                                             (uint32_t)j * (uint32_t)row_bytes + 16 * c, 0, 0, 0);
+                                             lane_off[is_v][d] + tile, 0, 0, 0);
   };
   auto copy_tile = [&](const uint16_t* base, int kt, char* buf, bool is_v) {
 #pragma unroll
@@ -254,23 +264,21 @@ void prefill_gate_kernel(PrefillArgs a) {
   // hook(s) runs after the K reads of k-step s + 1 are issued: the next
   // tile's copies ride along with the MFMAs (issued early, so they have the
   // whole tile to land) instead of stalling on their own
+  // LDS offsets of the lane's K fragment pieces, fixed for the whole loop: key
+  // row 16 ct + li, chunk 4 s + lg stored at (4 s + lg) ^ li (ct: immediate)
+  uint32_t k_lane[8];
+#pragma unroll
+  for (int s = 0; s < 8; ++s) k_lane[s] = (uint32_t)(li * 512 + 16 * ((4 * s + lg) ^ li));
   auto scores = [&](const char* kb, f32x4 (&st)[kH][4], auto&& hook) {
 #pragma unroll
     for (int h = 0; h < kH; ++h)
 #pragma unroll
       for (int ct = 0; ct < 4; ++ct) st[h][ct] = f32x4{0.f, 0.f, 0.f, 0.f};
-    // key row 16*ct + li, chunk 4*s + lg at (4*s + lg) ^ li.  The lane's
-    // offsets are recomputed for every tile (a few VALU operations) instead of
-    // being kept in registers across the loop.
-    int lx = li;
-    asm volatile("" : "+v"(lx));
-    const char* krow = kb + lx * 512;
     bf16x8 kf[2][4];
     auto read_k = [&](int s, bf16x8 (&dst)[4]) {
 #pragma unroll
       for (int ct = 0; ct < 4; ++ct)
-        dst[ct] = as_bf16x8(*reinterpret_cast<const uint4*>(krow + ct * 16 * 512 +
-                                                            16 * ((4 * s + lg) ^ lx)));
+        dst[ct] = as_bf16x8(*reinterpret_cast<const uint4*>(kb + k_lane[s] + ct * 16 * 512));
     };
     read_k(0, kf[0]);
 #pragma unroll
@@ -370,14 +378,16 @@ void prefill_gate_kernel(PrefillArgs a) {
   // 256 (t / 8) + 8 (li % 4), t8 = t % 8; k-slots 0..3 of k-step ks are keys
   // 32ks + 4lg + 0..3 (rows 32ks + 4lg + li / 4 as sources), k-slots 4..7 the
   // same 16 keys later.
-  auto pv = [&](const char* vb, const uint32_t (&phw)[kH][2][4], const uint32_t (&plw)[kH][2][4]) {
-    // the lane's offsets, recomputed for every tile (see scores)
-    int lx = lane;
-    asm volatile("" : "+v"(lx));
-    const int vr = 4 * (lx >> 4) + ((lx & 15) >> 2);  // source row within a 16-key group
-    int voff[8];
+  // LDS offsets of the lane's transpose-read sources, fixed for the whole loop:
+  // row vr = 4 lg + li / 4 of a 16-key group, dims 16 t + 4 (li % 4) .. +3 of
+  // column tile t at 32 (t % 8 ^ (vr & 7)) + 256 (t / 8) + 8 (li % 4)
+  // (as addresses in v0: a read of v1 adds a constant, which fits the read's
+  // immediate offset, so no tile adds a base)
+  const int vr = 4 * lg + (li >> 2);
+  const char* vsrc[8];
 #pragma unroll
-    for (int t8 = 0; t8 < 8; ++t8) voff[t8] = vr * 512 + 32 * (t8 ^ (vr & 7)) + 8 * (lx & 3);
+  for (int t8 = 0; t8 < 8; ++t8) vsrc[t8] = v0 + vr * 512 + 32 * (t8 ^ (vr & 7)) + 8 * (li & 3);
+  auto pv = [&](const char* vb, const uint32_t (&phw)[kH][2][4], const uint32_t (&plw)[kH][2][4]) {
     bf16x8 ph[2][kH], pl[2][kH];  // [k-step][head]
 #pragma unroll
     for (int ks = 0; ks < 2; ++ks)
@@ -388,14 +398,13 @@ void prefill_gate_kernel(PrefillArgs a) {
       }
     // group gi = (k-step gi / 4, column tiles 4 (gi % 4) .. +3)
     auto read_v = [&](int gi, bf16x8 (&dst)[4]) {
-      const char* va = vb + 32 * (gi >> 2) * 512;
-      const char* vc = va + 16 * 512;
+      const int ks = (int)(vb - v0) + 32 * (gi >> 2) * 512;  // a constant
 #pragma unroll
       for (int u = 0; u < 4; ++u) {
         const int t = 4 * (gi & 3) + u;
-        const int off = voff[t & 7] + 256 * (t >> 3);
-        const uint2 x0 = tr_read(va + off);
-        const uint2 x1 = tr_read(vc + off);
+        const char* const src = vsrc[t & 7] + ks + 256 * (t >> 3);
+        const uint2 x0 = tr_read(src);
+        const uint2 x1 = tr_read(src + 16 * 512);
         dst[u] = as_bf16x8(make_uint4(x0.x, x0.y, x1.x, x1.y));
       }
     };
