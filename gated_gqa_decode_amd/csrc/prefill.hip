@@ -305,6 +305,10 @@ void prefill_gate_kernel(PrefillArgs a) {
   // ---- mask, lazy online softmax (row li), split P ----------------------------------
   // p = hi + lo, both bf16 (hardware round-to-nearest-even conversion); the row
   // sum takes p itself (hi + lo equals p to ~2^-18 relative).
+  // The visible keys of row qi, less the lane's key offset 4 lg within a
+  // 16-key group: j < kv_end, j <= qi when causal, j > qi - window with a window
+  const int key_last = min(kv_end - 1, a.causal ? qi : INT_MAX) - 4 * lg;
+  const int key_first = (a.window > 0 ? qi - a.window + 1 : 0) - 4 * lg;
   auto softmax = [&](int kt, f32x4 (&st)[kH][4], uint32_t (&phw)[kH][2][4], uint32_t (&plw)[kH][2][4]) {
     const int j0 = kt * kBN;
     // Only a tile that reaches past the first row of the query tile (causal),
@@ -321,15 +325,19 @@ void prefill_gate_kernel(PrefillArgs a) {
 #pragma unroll
         for (int r = 0; r < 4; ++r) sv[ct][r] = st[h][ct][r];
       if (need_mask) {
+        // key j0 + 16 ct + 4 lg + r is visible iff 16 ct + r lies in
+        // [key_first - j0, key_last - j0] (the lane's bounds, fixed per row)
+        const int hi_c = key_last - j0, lo_c = key_first - j0;
 #pragma unroll
         for (int ct = 0; ct < 4; ++ct)
 #pragma unroll
-          for (int r = 0; r < 4; ++r) {
-            const int kj = j0 + ct * 16 + 4 * lg + r;
-            const bool ok = (kj < kv_end) && (!a.causal || kj <= qi) &&
-                            (a.window <= 0 || kj > qi - a.window);
-            sv[ct][r] = ok ? sv[ct][r] : -INFINITY;
-          }
+          for (int r = 0; r < 4; ++r) sv[ct][r] = 16 * ct + r <= hi_c ? sv[ct][r] : -INFINITY;
+        if (a.window > 0) {
+#pragma unroll
+          for (int ct = 0; ct < 4; ++ct)
+#pragma unroll
+            for (int r = 0; r < 4; ++r) sv[ct][r] = 16 * ct + r >= lo_c ? sv[ct][r] : -INFINITY;
+        }
       }
       // the lane's largest score, scaled (the scale is positive, so this is the
       // largest scaled score)
