@@ -86,6 +86,31 @@ struct RopeLaunch {
   int rope_dim;
 };
 
+// Unsigned 32-bit division by a divisor fixed for a launch, through one high
+// multiply (Granlund and Montgomery, "Division by Invariant Integers using
+// Multiplication", PLDI 1994, the unsigned algorithm of section 4): with
+// l = ceil(log2 d) and m = floor(2^32 (2^l - d) / d) + 1 (< 2^32),
+// n / d = (t + ((n - t) >> min(l, 1))) >> max(l - 1, 0), t = (m n) >> 32,
+// for every n < 2^32 and 1 <= d < 2^32.  divu32_make runs on the host;
+// divu32 on either side.
+struct DivU32 {
+  uint32_t m;
+  uint32_t s1, s2;
+};
+inline DivU32 divu32_make(uint32_t d) {
+  uint32_t l = 0;
+  while (l < 32 && ((uint64_t)1 << l) < d) ++l;
+  DivU32 r;
+  r.m = (uint32_t)((((uint64_t)1 << 32) * (((uint64_t)1 << l) - d)) / d + 1);
+  r.s1 = l < 1 ? l : 1;
+  r.s2 = l > 1 ? l - 1 : 0;
+  return r;
+}
+__host__ __device__ inline uint32_t divu32(uint32_t n, DivU32 c) {
+  const uint32_t t = (uint32_t)(((uint64_t)c.m * n) >> 32);
+  return (t + ((n - t) >> c.s1)) >> c.s2;
+}
+
 hipError_t launch_decode(const DecodeLaunch& d, hipStream_t stream);
 hipError_t launch_qk_norm_rope(const RopeLaunch& p, hipStream_t stream);
 hipError_t launch_stream_read(const void* src, size_t bytes, uint32_t* sink, hipStream_t stream);

@@ -98,6 +98,10 @@ void ga_stub_last_decode(int32_t* i8, uint64_t* p3, float* f3) {
 
 int ga_stub_device_calls(void) { return g_device_calls; }
 
+// The launchers' invariant-divisor division, host side (the kernels use the
+// same inline function).
+uint32_t ga_stub_divu32(uint32_t n, uint32_t d) { return ga::divu32(n, ga::divu32_make(d)); }
+
 }  // extern "C"
 
 // ---- the kernel launchers ------------------------------------------------------

@@ -55,6 +55,8 @@ struct RopeArgs {
   int num_q_heads;
   int num_kv_heads;
   int rope_dim;
+  uint32_t units;   // num_tokens * pairs (< 2^32: rows are at most 2^30)
+  DivU32 by_pairs;  // division by pairs = ceil((H_q + H_kv) / 2)
 };
 
 __device__ __forceinline__ void unpack8(uint4 u, float (&f)[8]) {
@@ -119,10 +121,10 @@ __global__ __launch_bounds__(256) void qk_norm_rope_kernel(RopeArgs a) {
   const int Hq = a.num_q_heads, Hkv = a.num_kv_heads;
   const int rows = Hq + Hkv;
   const int pairs = (rows + 1) >> 1;
-  const long long w = (long long)blockIdx.x * 4 + __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  if (w >= a.num_tokens * pairs) return;
-  const long long t = w / pairs;  // wave-uniform
-  const int pr = (int)(w - t * pairs);
+  const uint32_t w = blockIdx.x * 4 + __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  if (w >= a.units) return;
+  const uint32_t t = divu32(w, a.by_pairs);  // wave-uniform
+  const int pr = (int)(w - t * (uint32_t)pairs);
   const int lane = __lane_id();
   const int half = lane >> 5;
   const int p = lane & 31;  // dims 8p .. 8p + 7
@@ -280,7 +282,10 @@ hipError_t launch_qk_norm_rope(const RopeLaunch& p, hipStream_t stream) {
   a.num_kv_heads = p.num_kv_heads;
   a.rope_dim = p.rope_dim;
   // one (token, pair of head rows) unit per wave, four waves per workgroup
-  const long long units = p.num_tokens * ((p.num_q_heads + p.num_kv_heads + 1) / 2);
+  const int pairs = (p.num_q_heads + p.num_kv_heads + 1) / 2;
+  const long long units = p.num_tokens * pairs;
+  a.units = (uint32_t)units;
+  a.by_pairs = divu32_make((uint32_t)pairs);
   const dim3 grid((unsigned)((units + 3) / 4));
   // partners by swizzle when rope_dim / 16 is a power of two; no table at all
   // for rope_dim 0

@@ -126,6 +126,31 @@ def test_gfx950_reaches_every_launch(host_lib, tmp_path):
     assert _counts(lib) == [4, 1, 1, 1]
 
 
+def test_invariant_divisor_division(host_lib, tmp_path):
+    """The launchers' division by a divisor fixed per launch (one high
+    multiply, an add and two shifts; the rope kernel's token index) equals
+    n // d: every divisor up to 300 and every power of two and its neighbours
+    up to 2^32 - 1, against numerators at 0, around multiples of d, at the top
+    of the range, and seeded random ones."""
+    import random
+    lib = _load(host_lib, tmp_path, "gfx950")
+    lib.ga_stub_divu32.restype = ctypes.c_uint32
+    lib.ga_stub_divu32.argtypes = [ctypes.c_uint32, ctypes.c_uint32]
+    top = (1 << 32) - 1
+    rng = random.Random(32)
+    divisors = list(range(1, 301))
+    for k in range(9, 33):
+        divisors += [(1 << k) - 1, min(1 << k, top), (1 << k) + 1]
+    divisors += [rng.randrange(1, top + 1) for _ in range(200)]
+    for d in sorted(set(x for x in divisors if 1 <= x <= top)):
+        ns = {0, 1, d - 1, d, d + 1, top, top - 1, top - top % d, (top - top % d) - 1}
+        ns |= {m * d + e for m in (1, 2, 3, 1000, top // d) for e in (-1, 0, 1)}
+        ns |= {rng.randrange(0, top + 1) for _ in range(40)}
+        for n in ns:
+            if 0 <= n <= top:
+                assert lib.ga_stub_divu32(n, d) == n // d, (n, d)
+
+
 def test_prefill_size_limits(host_lib, tmp_path):
     """q, gate and out past 2^31 elements are served (the kernel addresses them
     with 64-bit offsets); the two real limits -- one sequence's K or V rows in
