@@ -25,6 +25,8 @@
 // leaving half the CU idle for the last third of the kernel.
 #define GA_DECODE_TARGET_BLOCKS 256
 #endif
+static_assert((GA_DECODE_TARGET_BLOCKS & (GA_DECODE_TARGET_BLOCKS - 1)) == 0,
+              "the device divides by the target with a shift");
 
 namespace {
 

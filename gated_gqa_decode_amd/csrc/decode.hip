@@ -81,7 +81,10 @@ struct Stage1Args {
   int num_splits;
   int window;        // > 0: only the last `window` tokens of a sequence are visible
   int split_units;   // B * H_kv (the split sizing rule's units)
-  int split_target;  // the workgroups the sizing rule aims for
+  int split_shift;   // log2 of the workgroups the sizing rule aims for
+  DivU32 by_splits;  // division by num_splits
+  DivU32 by_units;   // division by B * H_kv
+  DivU32 by_kv;      // division by H_kv
 };
 
 typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
@@ -152,8 +155,8 @@ struct SplitRange {
   int count;   // non-empty splits (<= num_splits)
 };
 
-__device__ __forceinline__ SplitRange split_range(int L, int window, int num_splits,
-                                                  int max_tokens, int units, int target_blocks) {
+__device__ __forceinline__ SplitRange split_range(int L, int window, int max_tokens, int units,
+                                                  int target_shift, DivU32 by_splits) {
   SplitRange r;
   const int tok_lo = window > 0 ? max(0, L - window) : 0;
   r.base = tok_lo & ~(kPage - 1);
@@ -163,11 +166,12 @@ __device__ __forceinline__ SplitRange split_range(int L, int window, int num_spl
     r.count = 0;
     return r;
   }
-  long long t = ((long long)n * units + target_blocks - 1) / target_blocks;
+  // ceil(n units / target); the target is a power of two
+  long long t = ((long long)n * units + ((1LL << target_shift) - 1)) >> target_shift;
   t = max(t, (long long)kMinSplit);
-  t = max(t, (long long)((n + num_splits - 1) / num_splits));  // at most num_splits splits
-  t = min(t, (long long)max_tokens);
-  const int count = (int)((n + t - 1) / t);
+  t = max(t, (long long)divu32((uint32_t)(n - 1), by_splits) + 1);  // at most num_splits splits
+  const int ti = (int)min(t, (long long)max_tokens);
+  const int count = (n + ti - 1) / ti;  // 32-bit divisions from here on
   r.tokens = (((n + count - 1) / count) + kPage - 1) & ~(kPage - 1);
   r.count = (n + r.tokens - 1) / r.tokens;
   return r;
@@ -216,10 +220,11 @@ __device__ __forceinline__ void stage1_body(const Stage1Args& a) {
   // leaves empty come last and the busy ones spread over all XCDs.
   const int unit = blockIdx.x;  // (s * B + b) * H_kv + g
   if (unit >= a.num_units) return;
-  const int seq_heads = a.num_units / a.num_splits;  // B * H_kv
-  const int s = unit / seq_heads;
-  const int g = (unit - s * seq_heads) % a.num_kv_heads;
-  const int b = (unit - s * seq_heads) / a.num_kv_heads;
+  const int seq_heads = a.split_units;  // B * H_kv
+  const int s = (int)divu32((uint32_t)unit, a.by_units);
+  const int rem = unit - s * seq_heads;
+  const int b = (int)divu32((uint32_t)rem, a.by_kv);
+  const int g = rem - b * a.num_kv_heads;
   const int lane = __lane_id();
   // wave-uniform by construction; readfirstlane keeps it in a scalar register
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -272,8 +277,8 @@ __device__ __forceinline__ void stage1_body(const Stage1Args& a) {
   const int L = seq_length(a.seq_lens, a.kv_indptr, a.index_capacity, b, capacity, &first_index);
   // First visible token: the sliding window keeps the last `window` tokens.
   const int tok_lo = a.window > 0 ? max(0, L - a.window) : 0;
-  const SplitRange sr = split_range(L, a.window, a.num_splits, a.tokens_per_split,
-                                    a.split_units, a.split_target);
+  const SplitRange sr = split_range(L, a.window, a.tokens_per_split, a.split_units, a.split_shift,
+                                    a.by_splits);
   if (s >= sr.count) return;  // empty split: stage 2 never reads its slot
   const int tok_begin = sr.base + s * sr.tokens;
   const int tok_end = min(L, tok_begin + sr.tokens);
@@ -713,7 +718,8 @@ struct Stage2Args {
   int capacity;  // max_pages * page size
   int window;
   int split_units;
-  int split_target;
+  int split_shift;
+  DivU32 by_splits;
 };
 
 // One wave per (b, h); lane owns d = 4*lane .. 4*lane+3.  4 waves per block.
@@ -767,8 +773,8 @@ __global__ __launch_bounds__(256) void decode_stage2_gate_kernel(Stage2Args a) {
   bool live = false;
   float lse = sink2 * kLn2;  // a dead row: ln(exp(sink)), or -inf
   if (L > 0) {  // L <= 0: padded slot, output +0
-    const int ns = split_range(L, a.window, a.num_splits, a.tokens_per_split, a.split_units,
-                               a.split_target).count;  // >= 1 here
+    const int ns = split_range(L, a.window, a.tokens_per_split, a.split_units, a.split_shift,
+                               a.by_splits).count;  // >= 1 here
     float M = sink2;
 #pragma unroll
     for (int u = 0; u < 8; ++u)
@@ -869,7 +875,11 @@ hipError_t launch_decode(const DecodeLaunch& d, hipStream_t stream) {
   a1.num_splits = d.num_splits;
   a1.window = d.window;
   a1.split_units = d.batch * d.num_kv_heads;
-  a1.split_target = d.split_target;
+  a1.split_shift = 0;
+  while ((1 << a1.split_shift) < d.split_target) ++a1.split_shift;  // a power of two
+  a1.by_splits = divu32_make((uint32_t)d.num_splits);
+  a1.by_units = divu32_make((uint32_t)(a1.split_units > 0 ? a1.split_units : 1));
+  a1.by_kv = divu32_make((uint32_t)d.num_kv_heads);
   a1.num_units = d.batch * d.num_kv_heads * d.num_splits;
   dim3 grid1(a1.num_units);
   hipError_t err;
@@ -903,7 +913,8 @@ hipError_t launch_decode(const DecodeLaunch& d, hipStream_t stream) {
   a2.window = d.window;
   a2.tokens_per_split = d.tokens_per_split;
   a2.split_units = a1.split_units;
-  a2.split_target = d.split_target;
+  a2.split_shift = a1.split_shift;
+  a2.by_splits = a1.by_splits;
   a2.num_q_heads = d.num_q_heads;
   a2.num_splits = d.num_splits;
   a2.batch = d.batch;
