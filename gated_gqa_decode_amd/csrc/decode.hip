@@ -195,6 +195,29 @@ __device__ __forceinline__ int seq_length(const int32_t* seq_lens, const int32_t
   return min(seq_lens[b], capacity);
 }
 
+// The same in two steps, so that the loads go out first: len_load reads the
+// two words the length comes from (for a block table the second is the first
+// again), len_value interprets them.
+struct LenWords {
+  int w0, w1;
+};
+__device__ __forceinline__ LenWords len_load(const int32_t* seq_lens, const int32_t* indptr, int b) {
+  const int32_t* p0 = indptr != nullptr ? indptr + b : seq_lens + b;
+  const int32_t* p1 = indptr != nullptr ? indptr + b + 1 : p0;
+  return LenWords{*p0, *p1};
+}
+__device__ __forceinline__ int len_value(LenWords w, bool csr, long long index_capacity,
+                                         int capacity, long long* first_index) {
+  if (csr) {
+    const long long lo = min(max((long long)w.w0, 0LL), index_capacity);
+    const long long hi = min(max((long long)w.w1, lo), index_capacity);
+    *first_index = lo;
+    return (int)min(hi - lo, (long long)capacity);
+  }
+  *first_index = 0;
+  return min(w.w0, capacity);
+}
+
 // The stage-1 body: kFp8 = e4m3 pools; kTok = one token per page
 // (block-table entries or CSR indices are token slots); kWide = a page-size-1
 // pool whose byte offsets do not fit 32 bits.
@@ -218,13 +241,14 @@ __device__ __forceinline__ void stage1_body(const Stage1Args& a) {
   // order, round-robin over the 8 XCDs; units are split-major (every
   // sequence's split 0, then split 1, ...), so the splits a short sequence
   // leaves empty come last and the busy ones spread over all XCDs.
-  const int unit = blockIdx.x;  // (s * B + b) * H_kv + g
-  if (unit >= a.num_units) return;
+  const int unit = blockIdx.x;  // (s * B + b) * H_kv + g; the grid has exactly num_units
   const int seq_heads = a.split_units;  // B * H_kv
   const int s = (int)divu32((uint32_t)unit, a.by_units);
   const int rem = unit - s * seq_heads;
   const int b = (int)divu32((uint32_t)rem, a.by_kv);
   const int g = rem - b * a.num_kv_heads;
+  // the length's words first: the split's range, and so every copy, waits on them
+  const LenWords len_words = len_load(a.seq_lens, a.kv_indptr, b);
   const int lane = __lane_id();
   // wave-uniform by construction; readfirstlane keeps it in a scalar register
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -274,7 +298,7 @@ __device__ __forceinline__ void stage1_body(const Stage1Args& a) {
   // in its own row instead of an access outside the buffers.
   const int capacity = kTok ? a.max_pages : a.max_pages * kPage;
   long long first_index = 0;
-  const int L = seq_length(a.seq_lens, a.kv_indptr, a.index_capacity, b, capacity, &first_index);
+  const int L = len_value(len_words, a.kv_indptr != nullptr, a.index_capacity, capacity, &first_index);
   // First visible token: the sliding window keeps the last `window` tokens.
   const int tok_lo = a.window > 0 ? max(0, L - a.window) : 0;
   const SplitRange sr = split_range(L, a.window, a.tokens_per_split, a.split_units, a.split_shift,
