@@ -170,10 +170,11 @@ __device__ __forceinline__ SplitRange split_range(int L, int window, int max_tok
   long long t = ((long long)n * units + ((1LL << target_shift) - 1)) >> target_shift;
   t = max(t, (long long)kMinSplit);
   t = max(t, (long long)divu32((uint32_t)(n - 1), by_splits) + 1);  // at most num_splits splits
-  const int ti = (int)min(t, (long long)max_tokens);
-  const int count = (n + ti - 1) / ti;  // 32-bit divisions from here on
-  r.tokens = (((n + count - 1) / count) + kPage - 1) & ~(kPage - 1);
-  r.count = (n + r.tokens - 1) / r.tokens;
+  // unsigned 32-bit divisions from here on (every operand is positive)
+  const uint32_t un = (uint32_t)n, ti = (uint32_t)min(t, (long long)max_tokens);
+  const uint32_t count = (un + ti - 1) / ti;
+  r.tokens = (int)((((un + count - 1) / count) + kPage - 1) & ~(uint32_t)(kPage - 1));
+  r.count = (int)((un + (uint32_t)r.tokens - 1) / (uint32_t)r.tokens);
   return r;
 }
 
@@ -835,7 +836,6 @@ __global__ __launch_bounds__(256) void decode_stage2_gate_kernel(Stage2Args a) {
     }
     const uint16_t gt[4] = {(uint16_t)(graw.x & 0xffff), (uint16_t)(graw.x >> 16),
                             (uint16_t)(graw.y & 0xffff), (uint16_t)(graw.y >> 16)};
-    // the gate: the product in fp32 where that is exact, else in fp64
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
       ob[e] = bf16_rne_f32(o[e] * a.v_descale / lam);
@@ -849,17 +849,15 @@ __global__ __launch_bounds__(256) void decode_stage2_gate_kernel(Stage2Args a) {
   __syncthreads();
   if (!valid) return;
   if (live) {
-    uint16_t sb[4];
-    uint32_t slow = 0;
+    // The product of two bf16 values has at most 16 significant bits: fp32
+    // (denormals kept) holds it exactly down to 2^-134, and below that its
+    // fp32 rounding cannot carry it across 2^-134, half the smallest bf16
+    // step.  So one rounding of the fp32 product to bf16 is the exact
+    // product's rounding for every input.
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
-      sb[e] = sigmoid_from_entry(gq[e], sig_tab[sigmoid_table_slot(gq[e])]);
-      if (!gate_product_fast(ob[e], sb[e], o16[e])) slow |= 1u << e;
-    }
-    if (slow != 0) {
-#pragma unroll
-      for (int e = 0; e < 4; ++e)
-        if ((slow >> e) & 1u) o16[e] = gate_product(ob[e], sb[e]);
+      const uint16_t sb = sigmoid_from_entry(gq[e], sig_tab[sigmoid_table_slot(gq[e])]);
+      o16[e] = bf16_rne_f32(bf16_to_f32(ob[e]) * bf16_to_f32(sb));
     }
   }
   if (a.lse != nullptr && lane == 0) a.lse[row] = lse;

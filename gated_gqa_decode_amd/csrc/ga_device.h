@@ -11,7 +11,7 @@ namespace ga {
 typedef __attribute__((ext_vector_type(2))) __bf16 bf16x2_t;
 
 // ---------------------------------------------------------------------------
-// bf16 <-> fp32 / fp64
+// bf16 <-> fp32
 // ---------------------------------------------------------------------------
 __device__ __forceinline__ float bf16_lo(uint32_t pair) { return __uint_as_float(pair << 16); }
 __device__ __forceinline__ float bf16_hi(uint32_t pair) { return __uint_as_float(pair & 0xffff0000u); }
@@ -26,28 +26,6 @@ __device__ __forceinline__ uint16_t bf16_rne_f32(float f) {
   const uint32_t rounded = (u + 0x7fffu + ((u >> 16) & 1u)) >> 16;
   const uint32_t quiet_nan = (u >> 16) | 0x0040u;
   return (uint16_t)(((u & 0x7fffffffu) > 0x7f800000u) ? quiet_nan : rounded);
-}
-
-// fp64 -> bf16, round to nearest even, with bf16 subnormals and overflow.
-// Normal range: round the 52-bit fraction to 7 bits on the integer image of the
-// value (a carry out of the fraction bumps the exponent, as it should).
-// Subnormal range (|x| < 2^-126): the bf16 grid is the multiples of 2^-133, so
-// scale by 2^133 (exact) and round to an integer with the hardware's
-// ties-to-even rounding.
-__device__ __forceinline__ uint16_t bf16_rne_f64(double x) {
-  uint64_t u = (uint64_t)__double_as_longlong(x);
-  uint16_t sign = (uint16_t)((u >> 48) & 0x8000u);
-  uint64_t a = u & 0x7fffffffffffffffull;
-  if (a > 0x7ff0000000000000ull) return (uint16_t)(sign | 0x7fc0u);
-  double ad = __longlong_as_double((long long)a);
-  if (ad < 0x1p-126) {
-    double r = __builtin_rint(ad * 0x1p133);  // 0..128; 128 is the smallest normal
-    return (uint16_t)(sign | (uint16_t)r);
-  }
-  uint64_t rounded = (a + 0x00000fffffffffffull + ((a >> 45) & 1ull)) >> 45;
-  int64_t e = (int64_t)(rounded >> 7) - 1023 + 127;
-  if (e >= 255) return (uint16_t)(sign | 0x7f80u);
-  return (uint16_t)(sign | (uint16_t)((e << 7) | (int64_t)(rounded & 0x7fu)));
 }
 
 // bf16(sigmoid(g)) for a bf16 gate g, correctly rounded.  A table holds the
@@ -76,34 +54,6 @@ __device__ __forceinline__ uint16_t sigmoid_from_entry(uint16_t gate, uint16_t e
   if (e > kSigmoidExpHi) r = (gate & 0x8000u) ? 0 : 0x3f80;
   if (e == 0xffu && (gate & 0x7fu) != 0) r = 0x7fc0;
   return r;
-}
-
-__device__ __forceinline__ uint16_t sigmoid_bf16(uint16_t gate) {
-  return sigmoid_from_entry(gate, kSigmoidTable[sigmoid_table_slot(gate)]);
-}
-
-// bf16(Ob * sigma_b) for bf16 Ob and sigma_b: their product has at most 16
-// significant bits, so it is exact in fp64 at every magnitude (subnormals
-// included) and the only rounding is the final one.
-__device__ __forceinline__ uint16_t gate_product(uint16_t ob, uint16_t sb) {
-  const double pd = (double)bf16_to_f32(ob) * (double)bf16_to_f32(sb);
-  return bf16_rne_f64(pd);
-}
-
-// The gate epilogue: out = bf16(Ob * bf16(sigmoid(g))).
-__device__ __forceinline__ uint16_t gate_output(uint16_t ob, uint16_t gate) {
-  return gate_product(ob, sigmoid_bf16(gate));
-}
-
-// The product's fast path, branch-free: true when `res` is
-// gate_product(ob, sb) for certain -- the product is a normal fp32 value, and
-// then exact in fp32.  Zero, subnormal and non-finite products must go
-// through gate_product.
-__device__ __forceinline__ bool gate_product_fast(uint16_t ob, uint16_t sb, uint16_t& res) {
-  const float p = bf16_to_f32(ob) * bf16_to_f32(sb);
-  res = bf16_rne_f32(p);
-  const float ap = __builtin_fabsf(p);
-  return ap >= 0x1p-126f && ap <= 0x1p127f;
 }
 
 // ---------------------------------------------------------------------------
