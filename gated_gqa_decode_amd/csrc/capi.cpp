@@ -45,13 +45,13 @@ constexpr int kSplitQuantum = 64;   // splits are whole 4-page groups
 constexpr int kMaxSplitTokens = 4096;
 constexpr int kMaxTokSplitTokens = 2048;
 constexpr int kMaxLongSplitTokens = 16384;
-constexpr int kMaxGridYZ = 65535;
 // A launch's grid size times its workgroup size must stay below 2^32 threads:
-// decode stage 1 and prefill have 512 threads per workgroup, decode stage 2
-// has 256 (4 rows each).
+// decode stage 1 and prefill have 512 threads per workgroup (2^22 workgroups:
+// 2^31 threads), decode stage 2 has 256 threads for 4 (sequence, query head)
+// rows (2^25 rows: 2^31 threads).  These are the only limits on the batch.
 constexpr int64_t kMaxStage1Workgroups = (int64_t)1 << 22;
 constexpr int64_t kMaxPrefillWorkgroups = (int64_t)1 << 22;
-constexpr int64_t kMaxDecodeRows = (int64_t)1 << 26;
+constexpr int64_t kMaxDecodeRows = (int64_t)1 << 25;
 
 thread_local int g_last_hip_error = 0;
 
@@ -120,7 +120,6 @@ ga_status check_heads(int32_t hq, int32_t hkv, int32_t d) {
   if (hq % hkv != 0) return GA_ERR_INVALID_ARGUMENT;
   if (!ga::group_supported(hq / hkv)) return GA_ERR_UNSUPPORTED;
   if (d != kHeadDim) return GA_ERR_UNSUPPORTED;
-  if ((int64_t)hkv * ga::head_parts(hq / hkv) > kMaxGridYZ) return GA_ERR_UNSUPPORTED;
   return GA_OK;
 }
 
@@ -131,7 +130,6 @@ ga_status check_decode_dims(const ga_decode_dims* d) {
   ga_status st = check_heads(d->num_q_heads, d->num_kv_heads, d->head_dim);
   if (st != GA_OK) return st;
   if (d->page_size != kPageSize && d->page_size != 1) return GA_ERR_UNSUPPORTED;
-  if (d->batch > kMaxGridYZ) return GA_ERR_UNSUPPORTED;
   if ((int64_t)d->batch * d->num_q_heads > kMaxDecodeRows) return GA_ERR_UNSUPPORTED;
   // capacity in tokens must fit an int32
   if ((int64_t)d->max_pages_per_seq * d->page_size > INT32_MAX / 2) return GA_ERR_UNSUPPORTED;

@@ -84,8 +84,8 @@ typedef struct ga_decode_plan {
 
 /* Fill *plan for dims.  GA_ERR_INVALID_ARGUMENT / GA_ERR_UNSUPPORTED as
  * gated_attn_decode would return for these dims (GA_ERR_UNSUPPORTED also when
- * the split grid would exceed one launch: more than 2^22 stage-1 workgroups,
- * or B * H_q > 2^26). */
+ * a grid would exceed one launch: more than 2^22 stage-1 workgroups, i.e.
+ * B * H_kv * num_splits > 2^22, or B * H_q > 2^25; nothing else bounds B). */
 ga_status gated_attn_decode_plan(const ga_decode_dims *dims, ga_decode_plan *plan);
 
 /* Bytes of device workspace gated_attn_decode needs for dims (0 if dims are

@@ -46,7 +46,7 @@ def _dims(**kw):
 
 
 @pytest.mark.parametrize("B,W", [(1, 32), (4, 32), (64, 256), (224, 384), (2, 2048), (65535, 1),
-                                 (1, 1), (3, 100000)])
+                                 (1, 1), (3, 100000), (70000, 3), (1 << 20, 2)])
 def test_plan_covers_capacity(B, W):
     p = ga.decode_plan(_dims(batch=B, max_pages_per_seq=W))
     cap = W * 16
@@ -110,7 +110,7 @@ def test_plan_depends_on_capacity_not_lengths():
     (dict(page_size=32), ga.GA_ERR_UNSUPPORTED),
     (dict(page_size=0), ga.GA_ERR_INVALID_ARGUMENT),
     (dict(batch=-1), ga.GA_ERR_INVALID_ARGUMENT),
-    (dict(batch=70000), ga.GA_ERR_UNSUPPORTED),
+    (dict(batch=70000, max_pages_per_seq=16384), ga.GA_ERR_UNSUPPORTED),  # 8.96e6 workgroups
     (dict(num_pages=0), ga.GA_ERR_INVALID_ARGUMENT),
     (dict(max_pages_per_seq=0), ga.GA_ERR_INVALID_ARGUMENT),
     (dict(num_kv_heads=0), ga.GA_ERR_INVALID_ARGUMENT),

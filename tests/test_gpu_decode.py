@@ -12,6 +12,7 @@ import torch
 import oracle
 import workloads
 from gpu_helpers import DEV, decode_parity, gpu_decode, to_dev, to_np
+from oracle.compare import check_outputs
 
 import gated_gqa_decode_amd as ga
 
@@ -78,6 +79,60 @@ def test_long_sequences_many_pairs():
     plan = ga.decode_plan(ga.decode_dims(**c.dims))
     assert (plan.tokens_per_split, plan.num_splits) == (4096, 8)
     res = decode_parity(c)
+    assert res["ok"], res
+
+
+def test_batch_past_65535_sampled_sequences():
+    """70,000 sequences (past a 16-bit grid dimension: 140,000 stage-1
+    workgroups and 1.12 M stage-2 rows) with ragged lengths 0..48 in a
+    three-page capacity, pages shuffled over the pool.  Inputs are seeded
+    draws on the device (torch's generator).  The NaN-poisoned output must be
+    written everywhere, padded slots must be +0, and sampled sequences -- the
+    first and last ones, the ones around index 65,535 and random ones -- match
+    the oracle on their inputs copied back."""
+    B, Hq, Hkv, D, W = 70000, 16, 2, 256, 3
+    P = B * W + 5
+    gen = torch.Generator(device=DEV)
+    gen.manual_seed(65536)
+
+    def draw(shape, std):
+        return (torch.randn(shape, generator=gen, device=DEV) * std).to(torch.bfloat16)
+
+    q = draw((B, Hq, D), 1.0)
+    gate = draw((B, Hq, D), 2.0)
+    k_pool = torch.empty((P, 16, Hkv, D), dtype=torch.bfloat16, device=DEV)
+    v_pool = torch.empty_like(k_pool)
+    for lo in range(0, P, 16384):  # fp32 temporaries stay small
+        hi = min(P, lo + 16384)
+        k_pool[lo:hi] = draw((hi - lo, 16, Hkv, D), 1.0)
+        v_pool[lo:hi] = draw((hi - lo, 16, Hkv, D), 1.0)
+    perm = torch.randperm(P, generator=gen, device=DEV)
+    block_table = perm[:B * W].view(B, W).to(torch.int32).contiguous()
+    lens = torch.randint(0, W * 16 + 1, (B,), generator=gen, device=DEV, dtype=torch.int32)
+    for i, n in ((0, 0), (1, 1), (2, 48), (65534, 16), (65535, 17), (65536, 0), (B - 2, 0),
+                 (B - 1, 48)):
+        lens[i] = n
+    out = torch.full_like(q, float("nan"))
+    ga.decode(q, gate, k_pool, v_pool, block_table, lens, 1.0 / 16, out=out)
+    torch.cuda.synchronize()
+    bits = out.view(torch.int16)
+    assert not bool(((bits & 0x7F80) == 0x7F80).any()), "non-finite (unwritten?) output"
+    dead = lens <= 0
+    assert int(dead.sum()) > 0 and not bool(bits[dead].any()), "padded slot not +0"
+
+    rng = np.random.default_rng(65536)
+    idx = sorted(set(range(24)) | set(range(65520, 65552)) | set(range(B - 24, B))
+                 | set(int(x) for x in rng.integers(0, B, 96)))
+    sel = torch.tensor(idx, device=DEV)
+    pages = block_table[sel].reshape(-1).long()
+    c_q, c_gate = to_np(q[sel]), to_np(gate[sel])
+    c_k, c_v = to_np(k_pool[pages]), to_np(v_pool[pages])
+    c_bt = np.arange(len(idx) * W, dtype=np.int32).reshape(len(idx), W)
+    c_lens = to_np(lens[sel])
+    ref, o, mref = oracle.decode(c_q, c_gate, c_k, c_v, c_bt, c_lens, 1.0 / 16)
+    res = check_outputs(to_np(out[sel]), ref, o, mref, oracle.sigmoid_table()[c_gate])
+    print(f"[parity] decode_b70000 sampled {len(idx)} sequences: n={res['n']} "
+          f"bit-exact={res['n_bit_exact']} max_ulp_floor={res['max_ulp_floor']:.4f}", flush=True)
     assert res["ok"], res
 
 

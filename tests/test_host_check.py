@@ -176,6 +176,44 @@ def test_prefill_size_limits(host_lib, tmp_path):
     assert _counts(lib)[1] == len(served)
 
 
+def test_decode_size_limits(host_lib, tmp_path):
+    """The batch is bounded only by one launch's grid (at most 2^32 threads):
+    2^22 stage-1 workgroups of 512 threads (B * H_kv * num_splits) and 2^25
+    (sequence, query head) rows for stage 2 (256 threads per 4 rows).  Served
+    past 65,535 sequences and right at both limits; declined one past them,
+    before any launch."""
+    lib = _load(host_lib, tmp_path, "gfx950")
+
+    def call(B, Hq, Hkv, W):
+        d = _dims(batch=B, num_q_heads=Hq, num_kv_heads=Hkv, max_pages_per_seq=W,
+                  num_pages=1 << 20)
+        return lib.gated_attn_decode(Q, GATE, K, V, BT, SL, 0.0625, OUT, None, ctypes.byref(d),
+                                     WS, 1 << 62), d
+
+    served = [
+        (65536, 16, 2, 4),        # past the 16-bit grid dimension
+        (70000, 16, 2, 3),
+        (1 << 21, 16, 2, 1),      # 2^22 stage-1 workgroups (one split each), 2^25 rows
+        (1 << 21, 16, 1, 1),      # 2^25 rows at a group of 16
+        (1 << 19, 16, 2, 1024),   # 2^20 (sequence, kv head) pairs x 4 splits of 4,096
+    ]
+    for i, (B, Hq, Hkv, W) in enumerate(served):
+        st, d = call(B, Hq, Hkv, W)
+        assert st == ga.GA_OK, (B, Hq, Hkv, W)
+        assert _counts(lib)[0] == i + 1
+        p = ga.decode_plan(d)
+        r = _last_decode(lib)
+        assert (r["batch"], r["num_splits"]) == (B, p.num_splits)
+        assert B * Hkv * p.num_splits <= 1 << 22 and B * Hq <= 1 << 25
+    for B, Hq, Hkv, W in [((1 << 21) + 1, 2, 2, 1),      # stage-1 workgroups only
+                          ((1 << 21) + 1, 16, 1, 1),     # stage-2 rows only
+                          ((1 << 19) + 1, 16, 2, 1024)]:  # workgroups, 4 splits each
+        st, d = call(B, Hq, Hkv, W)
+        assert st == ga.GA_ERR_UNSUPPORTED, (B, Hq, Hkv, W)
+        assert ga.decode_workspace_size(d) == 0
+    assert _counts(lib)[0] == len(served)
+
+
 def test_decode_launch_follows_the_plan(host_lib, tmp_path):
     lib = _load(host_lib, tmp_path, "gfx950")
     for B, W in ((1, 32), (4, 32), (64, 256), (224, 384)):
