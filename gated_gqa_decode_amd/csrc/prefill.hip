@@ -63,6 +63,7 @@ static_assert(kCopies == 4 || kCopies == 8, "copy instructions ride with the P V
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
 typedef short s16x4 __attribute__((ext_vector_type(4)));
 typedef s16x4 __attribute__((address_space(3))) lds_s16x4;
 typedef __attribute__((address_space(3))) void lds_void;
@@ -617,9 +618,11 @@ void prefill_gate_kernel(PrefillArgs a) {
         }
         res[e2] = dead ? 0u : cvt_pk_bf16(pr[0], pr[1]);
       }
-      if (p0 + row < S)  // rows past the sequence are not stored
-        *reinterpret_cast<uint4*>(a.out + (((size_t)b * S + p0 + row) * Hq + hq) * kD + 8 * pc) =
-            make_uint4(res[0], res[1], res[2], res[3]);
+      // rows past the sequence are not stored; the output is written with the
+      // non-temporal hint (it is not read again by this kernel)
+      if (p0 + row < S)
+        __builtin_nontemporal_store(u32x4{res[0], res[1], res[2], res[3]},
+                                    reinterpret_cast<u32x4*>(a.out + (((size_t)b * S + p0 + row) * Hq + hq) * kD + 8 * pc));
     }
   }
 }

@@ -91,7 +91,11 @@ __device__ __forceinline__ uint4 load16_opaque(const uint16_t* p) {
   const u32x4 v = *reinterpret_cast<global_u32x4_ptr>(u);
   return make_uint4(v.x, v.y, v.z, v.w);
 }
-__device__ __forceinline__ void store16(uint16_t* p, uint4 v) { *reinterpret_cast<uint4*>(p) = v; }
+// every output row is written once and not read again by this kernel: the
+// non-temporal hint (T = 4096 dense: 19.3-20.1 -> 17.7-17.9 us)
+__device__ __forceinline__ void store16(uint16_t* p, uint4 v) {
+  __builtin_nontemporal_store(u32x4{v.x, v.y, v.z, v.w}, reinterpret_cast<u32x4*>(p));
+}
 
 // lane i reads lane i ^ X of its 32-lane group (ds_swizzle, bit mode:
 // and-mask 0x1f, or-mask 0, xor-mask X)
