@@ -390,8 +390,9 @@ void prefill_gate_kernel(PrefillArgs a) {
   // LDS offsets of the lane's transpose-read sources, fixed for the whole loop:
   // row vr = 4 lg + li / 4 of a 16-key group, dims 16 t + 4 (li % 4) .. +3 of
   // column tile t at 32 (t % 8 ^ (vr & 7)) + 256 (t / 8) + 8 (li % 4)
-  // (as addresses in v0: a read of v1 adds a constant, which fits the read's
-  // immediate offset, so no tile adds a base)
+  // (as addresses in v0: inside the loop a read of v1 adds a constant, which
+  // fits the read's immediate offset, so no tile adds a base; the last tile's
+  // buffer is chosen at run time and adds one register offset)
   const int vr = 4 * lg + (li >> 2);
   const char* vsrc[8];
 #pragma unroll
@@ -407,7 +408,7 @@ void prefill_gate_kernel(PrefillArgs a) {
       }
     // group gi = (k-step gi / 4, column tiles 4 (gi % 4) .. +3)
     auto read_v = [&](int gi, bf16x8 (&dst)[4]) {
-      const int ks = (int)(vb - v0) + 32 * (gi >> 2) * 512;  // a constant
+      const int ks = (int)(vb - v0) + 32 * (gi >> 2) * 512;  // a constant inside the loop
 #pragma unroll
       for (int u = 0; u < 4; ++u) {
         const int t = 4 * (gi & 3) + u;
@@ -451,6 +452,22 @@ void prefill_gate_kernel(PrefillArgs a) {
   //   barrier -- K(t) and V(t) have landed; every wave is done with tile t - 1
   //   copies of K(t+1) and V(t+1) into the buffers tile t - 1 used
   //   S(t) = K(t) Q^T;  softmax -> P(t);  O += P(t) V(t)
+  // and the last tile the same without copies, after the loop.
+  //
+  // The gate rows of the wave's heads, as 16-byte pieces of rows (piece j:
+  // row 2j + lane / 32, dims 8 (lane % 32) .. +7), requested at the start of
+  // the last tile so that their latency overlaps its work.
+  const int pc = lane & 31;
+  uint4 gt8[kH][8];
+  auto load_gate = [&]() {
+#pragma unroll
+    for (int h = 0; h < kH; ++h)
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        const int qr = min(p0 + 2 * j + (lane >> 5), S - 1);  // rows past S are not stored
+        gt8[h][j] = *reinterpret_cast<const uint4*>(a.gate + (((size_t)b * S + qr) * Hq + hw[h]) * kD + 8 * pc);
+      }
+  };
   if (kt_lo < n_tiles) {
     copy_tile(a.k, kt_lo, k0, false);
     copy_tile(a.v, kt_lo, v0, true);
@@ -459,9 +476,8 @@ void prefill_gate_kernel(PrefillArgs a) {
     auto step = [&](int kt, char* kc, char* vc, char* kn, char* vn) {
       asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
       __syncthreads();
-      // The next tile's copies, requested unconditionally (past the last tile
-      // they re-read visible rows into buffers nothing reads any more), so no
-      // branch splits the scheduling region they share with P V.
+      // The next tile's copies (a step never runs the last tile), issued
+      // among the score MFMAs.
       if (active) {
         // the K instructions with k-steps 0..3, the V ones with 4..7
         scores(kc, st, [&](int gi) {
@@ -477,32 +493,40 @@ void prefill_gate_kernel(PrefillArgs a) {
         copy_tile(a.v, kt + 1, vn, true);
       }
     };
-    for (int kt = kt_lo;;) {
-      step(kt, k0, v0, k1, v1);
-      if (++kt >= n_tiles) break;
-      step(kt, k1, v1, k0, v0);
-      if (++kt >= n_tiles) break;
+    // The last tile: no copies to issue; the gate rows are requested first.
+    // It runs after the loop, from the buffers its parity selects, so the gate
+    // registers are live only from here on (a loop body that could be the
+    // last tile would hold them through every tile).
+    auto last_step = [&](int kt, char* kc, char* vc) {
+      asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+      __syncthreads();
+      if (active) {
+        load_gate();
+        scores(kc, st, [&](int) {});
+        softmax(kt, st, phw, plw);
+        pv(vc, phw, plw);
+      }
+    };
+    int kt = kt_lo;
+    if (kt + 1 < n_tiles) {
+      for (;;) {
+        step(kt, k0, v0, k1, v1);
+        if (++kt + 1 >= n_tiles) break;
+        step(kt, k1, v1, k0, v0);
+        if (++kt + 1 >= n_tiles) break;
+      }
     }
-    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    const bool odd = ((kt - kt_lo) & 1) != 0;  // uniform: which buffers hold the last tile
+    last_step(kt, odd ? k1 : k0, odd ? v1 : v0);
+  } else if (active) {
+    load_gate();  // no visible key: every row is dead, the values are not used
   }
 
   // ---- epilogue: O / l -> bf16, gate, store ------------------------------------
-  // The gate rows of the wave's heads are requested first, before the last
-  // barrier, so their latency overlaps the normalisation.  bf16(O) of the
+  // The gate rows are in flight since the last tile.  bf16(O) of the
   // wave's kH x 16 rows goes through LDS from the MFMA layout (lane: 4 rows x 16
   // strided columns) to whole 16-byte pieces of rows, so each lane issues 8 kH
   // gate loads and 8 kH output stores of 16 bytes instead of 64 kH of 2 bytes.
-  const int pc = lane & 31;  // piece j of this lane: row 2j + lane / 32, dims 8 (lane % 32) .. +7
-  uint4 gt8[kH][8];
-  if (active) {
-#pragma unroll
-    for (int h = 0; h < kH; ++h)
-#pragma unroll
-      for (int j = 0; j < 8; ++j) {
-        const int qr = min(p0 + 2 * j + (lane >> 5), S - 1);  // rows past S are not stored
-        gt8[h][j] = *reinterpret_cast<const uint4*>(a.gate + (((size_t)b * S + qr) * Hq + hw[h]) * kD + 8 * pc);
-      }
-  }
   __syncthreads();  // every wave is done with the tiles: their LDS is reused below
   // Regions: this wave's kH x 8 KiB of bf16(O) in the K tiles, and one sigmoid
   // table for the workgroup in the first V tile, extended so that it holds
