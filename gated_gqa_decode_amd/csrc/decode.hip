@@ -339,28 +339,24 @@ __device__ __forceinline__ void stage1_body(const Stage1Args& a) {
   const uint32_t extent = kTok ? (uint32_t)min((size_t)a.num_pages * row_bytes - head_bytes,
                                                (size_t)0xffffffffu)
                                : (uint32_t)(page_bytes - head_bytes);
-  // Tile i's rows in a pool (i is one of this wave's tiles).  The loops
-  // request the next tile unconditionally (so the compiler's wait counts stay
-  // exact); for a tile past the split's end every lane reads the first 16
-  // bytes of the wave's last tile instead.
+  // Tile i's rows in a pool (i is one of this wave's tiles, i < n_tiles: a
+  // wave's last tile runs after its loop and requests no next tile).
   auto tile_base = [&](const char* pool, int i) -> const char* {
     if constexpr (kTok) {
       return pool + head_bytes;
     } else {
-      const int k = min((i - first_tile - wave) >> 3, k_last);  // wave-uniform, < 128
+      const int k = min((i - first_tile - wave) >> 3, k_last);  // wave-uniform, < 128 (clamp: a guard)
       const int pg = __builtin_amdgcn_readlane(k < 64 ? my_page[0] : my_page[1], k & 63);
       return pool + (size_t)pg * page_bytes + head_bytes;
     }
   };
-  // byte offset of row r of tile i from tile_base (0 for tiles past the end)
+  // byte offset of row r of tile i from tile_base
   auto row_off = [&](int i, int r) -> size_t {
-    size_t off;
     if constexpr (kTok) {
-      off = (size_t)tok_ids[min(i, n_tiles - 1) * kPage + r] * row_bytes;
+      return (size_t)tok_ids[i * kPage + r] * row_bytes;
     } else {
-      off = (size_t)r * row_bytes;
+      return (size_t)r * row_bytes;
     }
-    return i < n_tiles ? off : 0;
   };
   // Rows outside the visible range [lo, hi) of a tile copy the nearest
   // visible row of V instead (finite data whose probability is exactly 0).
@@ -378,12 +374,11 @@ __device__ __forceinline__ void stage1_body(const Stage1Args& a) {
     constexpr int kChunks = kRow / 16;       // 32 (bf16) or 16 (e4m3)
     constexpr int kRowsPerCopy = 64 / kChunks;
     const char* base = tile_base(a.k_pool, i);
-    const int live = i < n_tiles ? 1 : 0;
 #pragma unroll
     for (int d = 0; d < kPage / kRowsPerCopy; ++d) {
       const int r = kRowsPerCopy * d + lane / kChunks;
       const int p = lane % kChunks;
-      copy16<kWide>(base, extent, row_off(i, r) + live * 16 * (p ^ (r & 15)), buf + d * 1024);
+      copy16<kWide>(base, extent, row_off(i, r) + 16 * (p ^ (r & 15)), buf + d * 1024);
     }
   };
   // bf16 V: copy d fills rows 2d, 2d + 1; chunk c of row r is stored at
@@ -392,13 +387,12 @@ __device__ __forceinline__ void stage1_body(const Stage1Args& a) {
     int lo, hi;
     visible_rows(i, lo, hi);
     const char* base = tile_base(a.v_pool, i);
-    const int live = i < n_tiles ? 1 : 0;
 #pragma unroll
     for (int d = 0; d < 8; ++d) {
       const int r = 2 * d + (lane >> 5);
       const int rc = min(max(r, lo), hi - 1);
       const int p = lane & 31;
-      copy16<kWide>(base, extent, row_off(i, rc) + live * 16 * (p ^ ((r & 7) << 1)), buf + d * 1024);
+      copy16<kWide>(base, extent, row_off(i, rc) + 16 * (p ^ ((r & 7) << 1)), buf + d * 1024);
     }
   };
   // e4m3 V: 32-dim granule G of row r is stored at 2048(r / 8) + 256 G +
@@ -409,13 +403,12 @@ __device__ __forceinline__ void stage1_body(const Stage1Args& a) {
     int lo, hi;
     visible_rows(i, lo, hi);
     const char* base = tile_base(a.v_pool, i);
-    const int live = i < n_tiles ? 1 : 0;
 #pragma unroll
     for (int d = 0; d < 4; ++d) {
       const int r = 8 * (d >> 1) + ((lane >> 1) & 7);
       const int rc = min(max(r, lo), hi - 1);
       copy16<kWide>(base, extent,
-                    row_off(i, rc) + live * (128 * (d & 1) + 32 * (lane >> 4) + 16 * (lane & 1)),
+                    row_off(i, rc) + (128 * (d & 1) + 32 * (lane >> 4) + 16 * (lane & 1)),
                     buf + d * 1024);
     }
   };
@@ -597,43 +590,57 @@ __device__ __forceinline__ void stage1_body(const Stage1Args& a) {
     KFrag kf;
     if constexpr (kFp8) {
       // double-buffered: the next tile's K and V are requested before this
-      // tile's K fragments are read; unrolled twice so every tile is named
-      // statically
+      // tile's K fragments are read; unrolled twice so every tile in the loop
+      // is named statically.  The wave's last tile runs after the loop and
+      // requests nothing, so the wave does not end waiting for a copy that
+      // nothing reads.
       char* const kA = tC[wave];
       char* const kB = tD[wave];
       char* const vA = tA[wave];
       char* const vB = tB[wave];
       stage_k(i, kA);
       stage_v8(i, vA);
-      for (;;) {
-        lds_reads_done();
-        stage_k(i + kWaves, kB);
-        stage_v8(i + kWaves, vB);
-        read_k(kA, kf);
-        const f32x4_t st = scores(kf);
-        __builtin_amdgcn_sched_barrier(0);
-        softmax_pv(i, st, vA);
-        i += kWaves;
-        if (i >= n_tiles) break;
-        lds_reads_done();
-        stage_k(i + kWaves, kA);
-        stage_v8(i + kWaves, vA);
-        read_k(kB, kf);
-        const f32x4_t st2 = scores(kf);
-        __builtin_amdgcn_sched_barrier(0);
-        softmax_pv(i, st2, vB);
-        i += kWaves;
-        if (i >= n_tiles) break;
+      bool last_in_b = false;  // which buffers hold the wave's last tile
+      if (i + kWaves < n_tiles) {
+        for (;;) {
+          lds_reads_done();
+          stage_k(i + kWaves, kB);
+          stage_v8(i + kWaves, vB);
+          read_k(kA, kf);
+          const f32x4_t st = scores(kf);
+          __builtin_amdgcn_sched_barrier(0);
+          softmax_pv(i, st, vA);
+          i += kWaves;
+          if (i + kWaves >= n_tiles) {
+            last_in_b = true;
+            break;
+          }
+          lds_reads_done();
+          stage_k(i + kWaves, kA);
+          stage_v8(i + kWaves, vA);
+          read_k(kB, kf);
+          const f32x4_t st2 = scores(kf);
+          __builtin_amdgcn_sched_barrier(0);
+          softmax_pv(i, st2, vB);
+          i += kWaves;
+          if (i + kWaves >= n_tiles) break;
+        }
       }
+      // the wave's last tile: nothing more to request
+      read_k(last_in_b ? kB : kA, kf);
+      const f32x4_t st = scores(kf);
+      __builtin_amdgcn_sched_barrier(0);
+      softmax_pv(i, st, last_in_b ? vB : vA);
     } else {
       // single-buffered (two bf16 tiles per wave fill the LDS): the next K
       // is requested once this tile's fragments are in registers, the next V
-      // once P V has read this tile's
+      // once P V has read this tile's; the wave's last tile, after the loop,
+      // requests nothing
       char* const kbuf = tB[wave];
       char* const vbuf = tA[wave];
       stage_k(i, kbuf);
       stage_v(i, vbuf);
-      for (;;) {
+      while (i + kWaves < n_tiles) {
         read_k(kbuf, kf);
         lds_reads_done();
         stage_k(i + kWaves, kbuf);
@@ -644,10 +651,15 @@ __device__ __forceinline__ void stage1_body(const Stage1Args& a) {
         lds_reads_done();
         stage_v(i + kWaves, vbuf);
         i += kWaves;
-        if (i >= n_tiles) break;
       }
+      // the wave's last tile: nothing more to request
+      read_k(kbuf, kf);
+      const f32x4_t st = scores(kf);
+      __builtin_amdgcn_sched_barrier(0);
+      softmax_pv(i, st, vbuf);
     }
-    // the last requests (past the end) may still be writing a tile
+    // nothing is in flight here (the last tile requested nothing); kept as a
+    // guard before the merge reuses the tiles
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
   }
 
