@@ -64,6 +64,8 @@ static_assert(kCopies == 4 || kCopies == 8, "copy instructions ride with the P V
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+typedef unsigned short u16x2 __attribute__((ext_vector_type(2)));
+typedef short i16x2 __attribute__((ext_vector_type(2)));
 typedef short s16x4 __attribute__((ext_vector_type(4)));
 typedef s16x4 __attribute__((address_space(3))) lds_s16x4;
 typedef __attribute__((address_space(3))) void lds_void;
@@ -531,10 +533,13 @@ void prefill_gate_kernel(PrefillArgs a) {
   // Regions: this wave's kH x 8 KiB of bf16(O) in the K tiles, and one sigmoid
   // table for the workgroup in the first V tile, extended so that it holds
   // every gate's result without range tests: index
-  //   (sign * 18 + clamp(exponent, 117, 134) - 117) * 128 + mantissa
-  // where bucket 117 stands for |g| < 2^-9 (result 0.5), buckets 118 .. 133
-  // are the correctly rounded table, and bucket 134 for |g| >= 128 (1, or +0
-  // for negative g).  Only NaN gates need a test of their own.
+  //   sign * 2304 + (exponent - 117) * 128 + mantissa
+  // for the gate's magnitude bits (exponent, mantissa) clamped to the range
+  // of buckets 117 .. 134, where bucket 117 stands for |g| < 2^-9 (result
+  // 0.5), buckets 118 .. 133 are the correctly rounded table, and bucket 134
+  // for |g| >= 128 (1, or +0 for negative g).  Only NaN gates need a test of
+  // their own.  Two gates (one 32-bit word) are indexed at a time in 16-bit
+  // lanes.
   constexpr int kRegion = kH * kBM * kD * 2;
   constexpr int kPerTile = kTileBytes / kRegion;  // regions per K tile buffer
   static_assert(kPerTile * 2 >= kWavesPf, "the epilogue regions fit the K tile buffers");
@@ -616,6 +621,8 @@ void prefill_gate_kernel(PrefillArgs a) {
     float lr_own = l_row[h];  // as above: row li's sum, for the dead-row test
     lr_own += shfl_xor(lr_own, 16);
     lr_own += shfl_xor(lr_own, 32);
+    // this lane's 16 bytes of row p0 + lane / 32; piece j is 2j rows further
+    uint16_t* const out_row = a.out + (((size_t)b * S + p0 + (lane >> 5)) * Hq + hq) * kD + 8 * pc;
 #pragma unroll
     for (int j = 0; j < 8; ++j) {
       const int row = 2 * j + (lane >> 5);
@@ -627,26 +634,29 @@ void prefill_gate_kernel(PrefillArgs a) {
       uint32_t res[4];
 #pragma unroll
       for (int e2 = 0; e2 < 4; ++e2) {
-        float pr[2];
-#pragma unroll
-        for (int u = 0; u < 2; ++u) {
-          const uint32_t g = (gw[e2] >> (16 * u)) & 0xffffu;
-          const uint32_t ec = min(max((g >> 7) & 0xffu, 117u), 134u);
-          const uint32_t idx = (((g >> 15) * 18u + ec - 117u) << 7) | (g & 0x7fu);
-          // read for every gate (the index is in range for NaN gates too), then
-          // the NaN gate's result selected: kept from becoming a branch per element
-          uint32_t te = sig_lds[idx];
-          asm volatile("" : "+v"(te));
-          const uint32_t sb = (g & 0x7fffu) > 0x7f80u ? 0x7fc0u : te;  // NaN gate
-          pr[u] = (u ? bf16_hi(ow[e2]) : bf16_lo(ow[e2])) * bf16_to_f32((uint16_t)sb);
-        }
-        res[e2] = dead ? 0u : cvt_pk_bf16(pr[0], pr[1]);
+        // both gates of the word at once (16-bit lanes): the magnitude clamped
+        // to [bucket 117, mantissa 0 .. bucket 134, mantissa 127] indexes the
+        // extended table directly, the sign adds one table of 2304 entries
+        const u16x2 g2 = __builtin_bit_cast(u16x2, gw[e2]);
+        const u16x2 mag = g2 & (u16x2)0x7fff;
+        const u16x2 cl = __builtin_elementwise_min(__builtin_elementwise_max(mag, (u16x2)0x3a80),
+                                                   (u16x2)0x437f);
+        const u16x2 soff = __builtin_bit_cast(u16x2, __builtin_bit_cast(i16x2, g2) >> 15) & (u16x2)2304;
+        const uint32_t ix = __builtin_bit_cast(uint32_t, soff + cl);
+        const uint32_t t0 = sig_lds[(ix & 0xffffu) - 0x3a80u];
+        const uint32_t t1 = sig_lds[(ix >> 16) - 0x3a80u];
+        // NaN gates (magnitude above 0x7f80) give NaN: bit 15 of mag + 0x7f
+        const uint32_t nan = __builtin_bit_cast(uint32_t, __builtin_bit_cast(i16x2, mag + (u16x2)0x7f) >> 15);
+        const uint32_t sw = ((t0 | (t1 << 16)) & ~nan) | (0x7fc07fc0u & nan);
+        const float pr0 = bf16_lo(ow[e2]) * bf16_lo(sw);
+        const float pr1 = bf16_hi(ow[e2]) * bf16_hi(sw);
+        res[e2] = dead ? 0u : cvt_pk_bf16(pr0, pr1);
       }
       // rows past the sequence are not stored; the output is written with the
       // non-temporal hint (it is not read again by this kernel)
       if (p0 + row < S)
         __builtin_nontemporal_store(u32x4{res[0], res[1], res[2], res[3]},
-                                    reinterpret_cast<u32x4*>(a.out + (((size_t)b * S + p0 + row) * Hq + hq) * kD + 8 * pc));
+                                    reinterpret_cast<u32x4*>(out_row + (size_t)j * (2 * Hq * kD)));
     }
   }
 }
