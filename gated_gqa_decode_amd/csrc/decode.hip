@@ -156,7 +156,7 @@ struct SplitRange {
 };
 
 __device__ __forceinline__ SplitRange split_range(int L, int window, int max_tokens, int units,
-                                                  int target_shift, DivU32 by_splits) {
+                                                  int target_shift, DivU32 by_splits, bool uneven) {
   SplitRange r;
   const int tok_lo = window > 0 ? max(0, L - window) : 0;
   r.base = tok_lo & ~(kPage - 1);
@@ -175,6 +175,15 @@ __device__ __forceinline__ SplitRange split_range(int L, int window, int max_tok
   const uint32_t count = (un + ti - 1) / ti;
   r.tokens = (int)((((un + count - 1) / count) + kPage - 1) & ~(uint32_t)(kPage - 1));
   r.count = (int)((un + (uint32_t)r.tokens - 1) / (uint32_t)r.tokens);
+  // More workgroups than CUs (several rounds): of two splits, split 0 --
+  // dispatched first, the grid being split-major -- takes about 11/16 of the
+  // tokens (at most max_tokens), so the workgroups that start last are the
+  // short ones and the rounds end closer together (B=224, L 4094..6142:
+  // 367.4 -> 357.1 us per call).
+  if (uneven && r.count == 2) {
+    const uint32_t big = min(((un * 11u + 15u) / 16u + kPage - 1) & ~(uint32_t)(kPage - 1), ti);
+    if (big > (uint32_t)r.tokens && big < un) r.tokens = (int)big;
+  }
   return r;
 }
 
@@ -303,7 +312,7 @@ __device__ __forceinline__ void stage1_body(const Stage1Args& a) {
   // First visible token: the sliding window keeps the last `window` tokens.
   const int tok_lo = a.window > 0 ? max(0, L - a.window) : 0;
   const SplitRange sr = split_range(L, a.window, a.tokens_per_split, a.split_units, a.split_shift,
-                                    a.by_splits);
+                                    a.by_splits, a.split_units * a.num_splits > (1 << a.split_shift));
   if (s >= sr.count) return;  // empty split: stage 2 never reads its slot
   const int tok_begin = sr.base + s * sr.tokens;
   const int tok_end = min(L, tok_begin + sr.tokens);
@@ -811,7 +820,7 @@ __global__ __launch_bounds__(256) void decode_stage2_gate_kernel(Stage2Args a) {
   float lse = sink2 * kLn2;  // a dead row: ln(exp(sink)), or -inf
   if (L > 0) {  // L <= 0: padded slot, output +0
     const int ns = split_range(L, a.window, a.tokens_per_split, a.split_units, a.split_shift,
-                               a.by_splits).count;  // >= 1 here
+                               a.by_splits, a.split_units * a.num_splits > (1 << a.split_shift)).count;  // >= 1 here
     float M = sink2;
 #pragma unroll
     for (int u = 0; u < 8; ++u)

@@ -75,7 +75,9 @@ typedef struct ga_decode_dims {
  * dispatch to the allocated capacity).  On the device, each sequence's visible
  * keys (from the window start, rounded down to a page, to its length) are cut
  * into NS equal page-aligned parts of at least 64 tokens, so a sequence far
- * shorter than the capacity still spreads over its NS blocks. */
+ * shorter than the capacity still spreads over its NS blocks.  When the grid
+ * holds more blocks than one round (B * H_kv * NS above 256), a sequence cut in
+ * two gives its first part about 11/16 of the keys (at most T). */
 typedef struct ga_decode_plan {
     int32_t tokens_per_split;  /* T: the most tokens one (sequence, kv head, split) block covers */
     int32_t num_splits;        /* NS = ceil(W * page_size / T) blocks per (sequence, kv head) */
