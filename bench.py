@@ -46,12 +46,31 @@ KERNEL_SOURCES = ["gated_gqa_decode_amd/csrc/decode.hip", "gated_gqa_decode_amd/
                   "gated_gqa_decode_amd/csrc/ga_internal.h", "gated_gqa_decode_amd/csrc/capi.cpp"]
 
 
-def kernel_source_hash() -> str:
+PREFILL_COUNTERS = os.path.join(ROOT, "profiles", "prefill_b2_s2048_causal_counters.json")
+
+
+def kernel_source_hash(sources=None) -> str:
     h = hashlib.sha256()
-    for rel in KERNEL_SOURCES:
+    for rel in (KERNEL_SOURCES if sources is None else sources):
         with open(os.path.join(ROOT, rel), "rb") as f:
             h.update(f.read())
     return h.hexdigest()
+
+
+def prefill_counters():
+    """MFMA figures of the prefill kernel from its committed rocprofv3 counter
+    passes, or None when those were taken on other kernel sources."""
+    if not os.path.exists(PREFILL_COUNTERS):
+        return None
+    with open(PREFILL_COUNTERS) as f:
+        c = json.load(f)
+    if c.get("kernel_sources_sha256") != kernel_source_hash(c.get("kernel_sources", [])):
+        return None
+    return {"source": os.path.relpath(PREFILL_COUNTERS, ROOT),
+            "mfma_busy_frac": c["mfma_busy_frac_of_counter_run"],
+            "issued_over_algorithmic": c["issued_over_algorithmic"],
+            "mfma_instructions": c["mfma_instructions"],
+            "lds_bank_conflict_frac": c["lds_bank_conflict_frac_of_active"]}
 
 
 def parse_args():
@@ -411,6 +430,7 @@ def time_prefill(ga, p, dev, n_calls: int, settle_s: float = 0.0) -> dict:
             "algorithmic_flop": flops,
             "tflops": round(tflops, 2),
             "mfma_bf16_frac": round(tflops / BF16_MFMA_PEAK_TFLOPS, 4),
+            "counters": prefill_counters() if (B, S, Hq, Hkv, D) == (2, 2048, 16, 2, 256) else None,
             "note": "P is split into two bf16 terms, so the kernel issues 1.5x "
                     "the algorithmic MFMA work"}
 
