@@ -47,6 +47,7 @@ KERNEL_SOURCES = ["gated_gqa_decode_amd/csrc/decode.hip", "gated_gqa_decode_amd/
 
 
 PREFILL_COUNTERS = os.path.join(ROOT, "profiles", "prefill_b2_s2048_causal_counters.json")
+FP8_COUNTERS = os.path.join(ROOT, "profiles", "decode_stage1_fp8_b64_l4096_counters.json")
 
 
 def kernel_source_hash(sources=None) -> str:
@@ -55,6 +56,22 @@ def kernel_source_hash(sources=None) -> str:
         with open(os.path.join(ROOT, rel), "rb") as f:
             h.update(f.read())
     return h.hexdigest()
+
+
+def fp8_stage1_traffic():
+    """HBM bytes per launch of the e4m3 stage-1 kernel (FETCH_SIZE + WRITE_SIZE,
+    calibrated) from its committed rocprofv3 counter summary, or None when that
+    was taken on other kernel sources."""
+    if not os.path.exists(FP8_COUNTERS):
+        return None
+    with open(FP8_COUNTERS) as f:
+        c = json.load(f)
+    if c.get("kernel_sources_sha256") != kernel_source_hash():
+        return None
+    return {"source": os.path.relpath(FP8_COUNTERS, ROOT),
+            "hbm_bytes_per_launch": c["hbm_bytes_per_launch"],
+            "algorithmic_bytes_per_launch": c["algorithmic_bytes_per_launch"],
+            "traffic_over_algorithmic": c["traffic_over_algorithmic"]}
 
 
 def prefill_counters():
@@ -971,6 +988,7 @@ def main() -> int:
         # FP8 (e4m3) K / V pools, same shape as the headline
         c8 = only_case(workloads, "decode_fp8kv")
         result["decode_fp8kv"] = time_decode(ga, c8, dev, 200)
+        result["decode_fp8kv"]["stage1_traffic"] = fp8_stage1_traffic()
         del c8
         del c32
         p32 = workloads.make_prefill("prefill_b2_s2048_hq32", 2, 2048, seed=4, causal=True,
