@@ -47,8 +47,9 @@ constexpr int kMaxTokSplitTokens = 2048;
 constexpr int kMaxLongSplitTokens = 16384;
 // A launch's grid size times its workgroup size must stay below 2^32 threads:
 // decode stage 1 and prefill have 512 threads per workgroup (2^22 workgroups:
-// 2^31 threads), decode stage 2 has 256 threads for 4 (sequence, query head)
-// rows (2^25 rows: 2^31 threads).  These are the only limits on the batch.
+// 2^31 threads), decode stage 2 has one 64-thread workgroup per (sequence,
+// query head) row (2^25 rows: 2^31 threads).  These are the only limits on the
+// batch.
 constexpr int64_t kMaxStage1Workgroups = (int64_t)1 << 22;
 constexpr int64_t kMaxPrefillWorkgroups = (int64_t)1 << 22;
 constexpr int64_t kMaxDecodeRows = (int64_t)1 << 25;

@@ -179,7 +179,7 @@ def test_prefill_size_limits(host_lib, tmp_path):
 def test_decode_size_limits(host_lib, tmp_path):
     """The batch is bounded only by one launch's grid (at most 2^32 threads):
     2^22 stage-1 workgroups of 512 threads (B * H_kv * num_splits) and 2^25
-    (sequence, query head) rows for stage 2 (256 threads per 4 rows).  Served
+    (sequence, query head) rows for stage 2 (one 64-thread workgroup per row).  Served
     past 65,535 sequences and right at both limits; declined one past them,
     before any launch."""
     lib = _load(host_lib, tmp_path, "gfx950")
