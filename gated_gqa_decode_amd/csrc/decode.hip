@@ -231,8 +231,10 @@ __device__ __forceinline__ int len_value(LenWords w, bool csr, long long index_c
 // The stage-1 body: kFp8 = e4m3 pools; kTok = one token per page
 // (block-table entries or CSR indices are token slots); kWide = a page-size-1
 // pool whose byte offsets do not fit 32 bits.
-template <bool kFp8, bool kTok, bool kWide>
+template <bool kFp8, bool kTok, bool kWide, int kW = kWaves>
 __device__ __forceinline__ void stage1_body(const Stage1Args& a) {
+  static_assert(kW == 8 || kW == 4, "tiles go to waves by a shift");
+  constexpr int kLog2W = kW == 8 ? 3 : 2;
   // Per-wave LDS tiles, separate objects so the compiler can tell a copy into
   // one from a read of another (its wait before a read then covers only the
   // copy that read needs).  bf16 pools: tA = the V tile, tB = the K tile.
@@ -240,11 +242,11 @@ __device__ __forceinline__ void stage1_body(const Stage1Args& a) {
   // the loop they hold the wave's O (16 heads x 256 fp32 = 16 KiB) for the
   // merge.
   constexpr int kTile = kFp8 ? kTileBytes / 2 : kTileBytes;
-  __shared__ __align__(16) char tA[kWaves][kTile];
-  __shared__ __align__(16) char tB[kWaves][kTile];
-  __shared__ __align__(16) char tC[kWaves][kFp8 ? kTile : 16];
-  __shared__ __align__(16) char tD[kWaves][kFp8 ? kTile : 16];
-  __shared__ float m_w[kWaves][kHeads], l_w[kWaves][kHeads];
+  __shared__ __align__(16) char tA[kW][kTile];
+  __shared__ __align__(16) char tB[kW][kTile];
+  __shared__ __align__(16) char tC[kW][kFp8 ? kTile : 16];
+  __shared__ __align__(16) char tD[kW][kFp8 ? kTile : 16];
+  __shared__ float m_w[kW][kHeads], l_w[kW][kHeads];
   __shared__ __align__(16) int tok_ids[kTok ? kMaxTokSplit : 4];  // page size 1: the split's token slots
 
   // Workgroup id -> (split s, sequence b, kv head g).  Ids are dispatched in
@@ -270,7 +272,7 @@ __device__ __forceinline__ void stage1_body(const Stage1Args& a) {
 
   // Issued together, before the length is known: the page ids of the tiles
   // this wave copies when the sequence fills its capacity (its k-th tile,
-  // tile wave + 8k of split s, in lane k % 64 of register k / 64; ids past
+  // tile wave + kW k of split s, in lane k % 64 of register k / 64; ids past
   // the sequence's end are never used), the length, and q.  Other lengths and
   // windows reload the page ids below.  load_pages(fp, np): the split's
   // tiles from page fp on, np of them.
@@ -278,7 +280,7 @@ __device__ __forceinline__ void stage1_body(const Stage1Args& a) {
   auto load_pages = [&](int fp, int np, int (&pages)[kPageRegs]) {
 #pragma unroll
     for (int r = 0; r < kPageRegs; ++r) {
-      const int j = wave + 8 * (lane + 64 * r);
+      const int j = wave + kW * (lane + 64 * r);
       pages[r] = j < np ? bt_row[fp + j] : 0;
     }
   };
@@ -322,7 +324,7 @@ __device__ __forceinline__ void stage1_body(const Stage1Args& a) {
   if constexpr (kTok) {
     // one slot per token: the split's slots go to LDS (at most kMaxTokSplit)
     const int32_t* ids = a.kv_indptr != nullptr ? a.kv_indices + first_index : bt_row;
-    for (int i = threadIdx.x; i < sr.tokens; i += kWaves * 64) {
+    for (int i = threadIdx.x; i < sr.tokens; i += kW * 64) {
       const int tok = tok_begin + i;
       const int idv = tok < tok_end ? ids[tok] : 0;
       tok_ids[i] = (int)min((long long)max(idv, 0), a.num_pages - 1);
@@ -335,8 +337,8 @@ __device__ __forceinline__ void stage1_body(const Stage1Args& a) {
     for (int r = 0; r < kPageRegs; ++r)
       my_page[r] = (int)min((long long)max(my_page[r], 0), a.num_pages - 1);
   }
-  // this wave's last tile index k (its tiles are first_tile + wave + 8k)
-  const int k_last = (n_tiles - 1 - first_tile - wave) >> 3;
+  // this wave's last tile index k (its tiles are first_tile + wave + kW k)
+  const int k_last = (n_tiles - 1 - first_tile - wave) >> kLog2W;
 
   constexpr int kElem = kFp8 ? 1 : 2;  // bytes per pool element
   constexpr int kRow = kD * kElem;     // bytes of one head's row
@@ -354,7 +356,7 @@ __device__ __forceinline__ void stage1_body(const Stage1Args& a) {
     if constexpr (kTok) {
       return pool + head_bytes;
     } else {
-      const int k = min((i - first_tile - wave) >> 3, k_last);  // wave-uniform, < 128 (clamp: a guard)
+      const int k = min((i - first_tile - wave) >> kLog2W, k_last);  // wave-uniform, < 128 (clamp: a guard)
       const int pg = __builtin_amdgcn_readlane(k < 64 ? my_page[0] : my_page[1], k & 63);
       return pool + (size_t)pg * page_bytes + head_bytes;
     }
@@ -610,29 +612,29 @@ __device__ __forceinline__ void stage1_body(const Stage1Args& a) {
       stage_k(i, kA);
       stage_v8(i, vA);
       bool last_in_b = false;  // which buffers hold the wave's last tile
-      if (i + kWaves < n_tiles) {
+      if (i + kW < n_tiles) {
         for (;;) {
           lds_reads_done();
-          stage_k(i + kWaves, kB);
-          stage_v8(i + kWaves, vB);
+          stage_k(i + kW, kB);
+          stage_v8(i + kW, vB);
           read_k(kA, kf);
           const f32x4_t st = scores(kf);
           __builtin_amdgcn_sched_barrier(0);
           softmax_pv(i, st, vA);
-          i += kWaves;
-          if (i + kWaves >= n_tiles) {
+          i += kW;
+          if (i + kW >= n_tiles) {
             last_in_b = true;
             break;
           }
           lds_reads_done();
-          stage_k(i + kWaves, kA);
-          stage_v8(i + kWaves, vA);
+          stage_k(i + kW, kA);
+          stage_v8(i + kW, vA);
           read_k(kB, kf);
           const f32x4_t st2 = scores(kf);
           __builtin_amdgcn_sched_barrier(0);
           softmax_pv(i, st2, vB);
-          i += kWaves;
-          if (i + kWaves >= n_tiles) break;
+          i += kW;
+          if (i + kW >= n_tiles) break;
         }
       }
       // the wave's last tile: nothing more to request
@@ -649,17 +651,17 @@ __device__ __forceinline__ void stage1_body(const Stage1Args& a) {
       char* const vbuf = tA[wave];
       stage_k(i, kbuf);
       stage_v(i, vbuf);
-      while (i + kWaves < n_tiles) {
+      while (i + kW < n_tiles) {
         read_k(kbuf, kf);
         lds_reads_done();
-        stage_k(i + kWaves, kbuf);
+        stage_k(i + kW, kbuf);
         const f32x4_t st = scores(kf);
         __builtin_amdgcn_sched_barrier(0);
         softmax_pv(i, st, vbuf);
         __builtin_amdgcn_sched_barrier(0);
         lds_reads_done();
-        stage_v(i + kWaves, vbuf);
-        i += kWaves;
+        stage_v(i + kW, vbuf);
+        i += kW;
       }
       // the wave's last tile: nothing more to request
       read_k(kbuf, kf);
@@ -695,16 +697,16 @@ __device__ __forceinline__ void stage1_body(const Stage1Args& a) {
     for (int t = 0; t < 16; ++t) dst[16 * t + li] = o[t][r];
   }
   __syncthreads();
-  for (int e = threadIdx.x; e < nh * (kD / 4); e += kWaves * 64) {
+  for (int e = threadIdx.x; e < nh * (kD / 4); e += kW * 64) {
     const int h = e / (kD / 4);
     const int c = e - h * (kD / 4);  // 4 values each
     float M = -INFINITY;
 #pragma unroll
-    for (int w = 0; w < kWaves; ++w) M = fmaxf(M, m_w[w][h]);
+    for (int w = 0; w < kW; ++w) M = fmaxf(M, m_w[w][h]);
     float lam = 0.f;
     float out[4] = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-    for (int w = 0; w < kWaves; ++w) {
+    for (int w = 0; w < kW; ++w) {
       const float wgt = __builtin_amdgcn_exp2f(m_w[w][h] - M);  // 0 for a wave without tokens
       lam += l_w[w][h] * wgt;
       const float4 x = *reinterpret_cast<const float4*>(o_row(w, h) + 4 * c);
@@ -724,6 +726,12 @@ __device__ __forceinline__ void stage1_body(const Stage1Args& a) {
 
 __global__ __launch_bounds__(512, 1) void decode_stage1_kernel(Stage1Args a) {
   stage1_body<false, false, false>(a);
+}
+
+// Splits of at most 4 tiles (short sequences at small batch): 4 waves, one
+// tile each, and a 4-way merge.
+__global__ __launch_bounds__(256, 1) void decode_stage1_w4_kernel(Stage1Args a) {
+  stage1_body<false, false, false, 4>(a);
 }
 
 __global__ __launch_bounds__(512, 1) void decode_stage1_fp8_kernel(Stage1Args a) {
@@ -932,6 +940,8 @@ hipError_t launch_decode(const DecodeLaunch& d, hipStream_t stream) {
     hipLaunchKernelGGL(decode_stage1_tok_wide_kernel, grid1, block, 0, stream, a1);
   else if (d.page_size == 1)
     hipLaunchKernelGGL(decode_stage1_tok_kernel, grid1, block, 0, stream, a1);
+  else if (d.tokens_per_split <= 4 * kPage)
+    hipLaunchKernelGGL(decode_stage1_w4_kernel, grid1, dim3(4 * 64), 0, stream, a1);
   else
     hipLaunchKernelGGL(decode_stage1_kernel, grid1, block, 0, stream, a1);
   err = hipGetLastError();
